@@ -1,0 +1,225 @@
+"""Python binding of libmoe_fp8.so, the MI355X (gfx950) routed FP8 W8A8
+block-scale MoE expert path.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are torch tensors used for their device memory (``data_ptr()``) and
+the current HIP stream; nothing here computes any part of the path.  The
+functions carry the C ABI's names (see include/moe_fp8.h) and raise
+``MoeError`` on a non-OK status.  If the shared library has not been built,
+importing this package raises -- there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
+
+MOE_OK = 0
+MOE_IDS_I32, MOE_IDS_I64 = 0, 1
+MOE_SCALE_FP32, MOE_SCALE_UE8M0 = 0, 1
+MOE_F_INTER_UE8M0 = 1
+MOE_F_MMA_E8M0 = 2
+MOE_F_FP8_GATEUP = 4
+MOE_F_SPLITK_SHIFT = 8
+
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
+                4: "MOE_ERR_CAPACITY", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
+
+EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_quant_act",
+            "moe_fp8_experts_workspace_size", "moe_fp8_experts_workspace_layout",
+            "moe_fp8_experts", "moe_status_str", "moe_last_error", "moe_debug_e4m3_encode")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where, detail):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {detail}")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(or python fp8_block_scale_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _u32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p
+_pi64, _psz = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_size_t)
+
+
+def _proto(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_c = {
+    "moe_plan_capacity": _proto("moe_plan_capacity", _i32, _i64, _i32, _i32, _i32, _pi64, _pi64),
+    "moe_plan_workspace_size": _proto("moe_plan_workspace_size", _sz, _i64, _i32, _i32, _i32),
+    "moe_plan": _proto("moe_plan", _i32, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
+                       _vp, _vp, _sz, _vp),
+    "moe_quant_act": _proto("moe_quant_act", _i32, _vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp),
+    "moe_fp8_experts_workspace_size": _proto("moe_fp8_experts_workspace_size", _sz, _i64, _i64,
+                                             _i64, _i32, _i32, _i32, _i64, _u32),
+    "moe_fp8_experts_workspace_layout": _proto("moe_fp8_experts_workspace_layout", _i32, _i64, _i64,
+                                               _i64, _i32, _i32, _i32, _i64, _u32, _psz, _psz),
+    "moe_fp8_experts": _proto("moe_fp8_experts", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp, _sz,
+                              _vp),
+    "moe_status_str": _proto("moe_status_str", ctypes.c_char_p, _i32),
+    "moe_last_error": _proto("moe_last_error", ctypes.c_char_p),
+    "moe_debug_e4m3_encode": _proto("moe_debug_e4m3_encode", _i32, _vp, _vp, _i64, _vp),
+}
+
+
+def _check(st, where):
+    if st != MOE_OK:
+        raise MoeError(st, where, _c["moe_last_error"]().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ plan --
+
+def moe_plan_capacity(M, top_k, E, block_m):
+    sc, bc = ctypes.c_int64(), ctypes.c_int64()
+    _check(_c["moe_plan_capacity"](M, top_k, E, block_m, ctypes.byref(sc), ctypes.byref(bc)),
+           "moe_plan_capacity")
+    return sc.value, bc.value
+
+
+def moe_plan_workspace_size(M, top_k, E, block_m):
+    return _c["moe_plan_workspace_size"](M, top_k, E, block_m)
+
+
+def moe_plan(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded,
+             workspace=None, stream=None):
+    """topk_ids [M, top_k] int32/int64 (device); outputs are preallocated int32 tensors."""
+    M, top_k = topk_ids.shape
+    if topk_ids.dtype == torch.int32:
+        dt = MOE_IDS_I32
+    elif topk_ids.dtype == torch.int64:
+        dt = MOE_IDS_I64
+    else:
+        raise TypeError("topk_ids must be int32 or int64")
+    assert topk_ids.is_contiguous() and sorted_token_ids.dtype == torch.int32
+    assert expert_ids.dtype == torch.int32 and num_tokens_post_padded.dtype == torch.int32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_c["moe_plan"](_ptr(topk_ids), dt, M, top_k, E, block_m, _ptr(sorted_token_ids),
+                          sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(),
+                          _ptr(num_tokens_post_padded), _ptr(workspace), ws_bytes, _stream(stream)),
+           "moe_plan")
+
+
+# ------------------------------------------------------------- quant act --
+
+def moe_quant_act(x_bf16, x_q, x_s, scale_mode=MOE_SCALE_FP32, stream=None):
+    """x_bf16 [M, K] bf16 (row stride may exceed K); x_q uint8 [M, K]; x_s fp32 [M, K/128]."""
+    assert x_bf16.dtype == torch.bfloat16 and x_bf16.dim() == 2 and x_bf16.stride(1) == 1
+    M, K = x_bf16.shape
+    assert x_q.dtype == torch.uint8 and x_q.is_contiguous() and tuple(x_q.shape) == (M, K)
+    assert x_s.dtype == torch.float32 and x_s.is_contiguous() and tuple(x_s.shape) == (M, K // 128)
+    _check(_c["moe_quant_act"](_ptr(x_bf16), M, K, x_bf16.stride(0), _ptr(x_q), _ptr(x_s),
+                               scale_mode, _stream(stream)), "moe_quant_act")
+
+
+def moe_debug_e4m3_encode(inp, out, stream=None):
+    assert inp.dtype == torch.float32 and out.dtype == torch.uint8 and inp.numel() == out.numel()
+    _check(_c["moe_debug_e4m3_encode"](_ptr(inp), _ptr(out), inp.numel(), _stream(stream)),
+           "moe_debug_e4m3_encode")
+
+
+# --------------------------------------------------------------- experts --
+
+def moe_fp8_experts_workspace_size(M, K, I, E, top_k, block_m, sorted_cap, flags=0):
+    return _c["moe_fp8_experts_workspace_size"](M, K, I, E, top_k, block_m, sorted_cap, flags)
+
+
+def moe_fp8_experts_workspace_layout(M, K, I, E, top_k, block_m, sorted_cap, flags=0):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_c["moe_fp8_experts_workspace_layout"](M, K, I, E, top_k, block_m, sorted_cap, flags,
+                                                  ctypes.byref(a), ctypes.byref(b)),
+           "moe_fp8_experts_workspace_layout")
+    return a.value, b.value
+
+
+def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+                    num_tokens_post_padded, top_k, block_m, out_bf16, workspace, flags=0,
+                    stream=None):
+    """Steps 3-5; accumulates into out_bf16 [M, K]."""
+    M, K = x_q.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    for t in (x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+              out_bf16, workspace):
+        assert t.is_contiguous()
+    assert out_bf16.dtype == torch.bfloat16 and topk_weights.dtype == torch.float32
+    _check(_c["moe_fp8_experts"](_ptr(x_q), _ptr(x_s), _ptr(w13), _ptr(w13_s), _ptr(w2),
+                                 _ptr(w2_s), _ptr(topk_weights), _ptr(sorted_token_ids),
+                                 _ptr(expert_ids), _ptr(num_tokens_post_padded), M, K, I, E, top_k,
+                                 block_m, sorted_token_ids.numel(), flags, _ptr(out_bf16),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)),
+           "moe_fp8_experts")
+
+
+def moe_status_str(status):
+    return _c["moe_status_str"](status).decode()
+
+
+def moe_last_error():
+    return _c["moe_last_error"]().decode()
+
+
+# ------------------------------------------------------------- a layer --
+
+class MoeLayerBuffers:
+    """Device buffers for one call of the whole path at a given geometry
+    (allocated once with torch; reused across calls)."""
+
+    def __init__(self, M, K, I, E, top_k, block_m, flags=0, device="cuda"):
+        self.M, self.K, self.I, self.E, self.top_k, self.block_m = M, K, I, E, top_k, block_m
+        self.flags = flags
+        self.sorted_cap, self.blocks_cap = moe_plan_capacity(M, top_k, E, block_m)
+        dev = torch.device(device)
+        self.sorted_ids = torch.empty(self.sorted_cap, dtype=torch.int32, device=dev)
+        self.expert_ids = torch.empty(self.blocks_cap, dtype=torch.int32, device=dev)
+        self.ntp = torch.empty(1, dtype=torch.int32, device=dev)
+        self.x_q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        self.x_s = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+        ws = moe_fp8_experts_workspace_size(M, K, I, E, top_k, block_m, self.sorted_cap, flags)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        pws = moe_plan_workspace_size(M, top_k, E, block_m)
+        self.plan_ws = torch.empty(pws, dtype=torch.uint8, device=dev) if pws else None
+        self.h_q_off, self.h_s_off = moe_fp8_experts_workspace_layout(
+            M, K, I, E, top_k, block_m, self.sorted_cap, flags)
+
+    def intermediate(self):
+        """(h_q [sorted_cap, I] uint8, h_s [sorted_cap, I/128] fp32) views of the workspace."""
+        n_q = self.sorted_cap * self.I
+        n_s = self.sorted_cap * (self.I // 128)
+        hq = self.workspace[self.h_q_off:self.h_q_off + n_q].view(self.sorted_cap, self.I)
+        hs = self.workspace[self.h_s_off:self.h_s_off + 4 * n_s].view(torch.float32)
+        return hq, hs.view(self.sorted_cap, self.I // 128)
+
+
+def moe_layer(bufs, x_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s, out_bf16,
+              act_scale_mode=MOE_SCALE_FP32, stream=None):
+    """All five steps on one stream: plan, activation quantisation, experts."""
+    moe_plan(topk_ids, bufs.E, bufs.block_m, bufs.sorted_ids, bufs.expert_ids, bufs.ntp,
+             bufs.plan_ws, stream)
+    moe_quant_act(x_bf16, bufs.x_q, bufs.x_s, act_scale_mode, stream)
+    moe_fp8_experts(bufs.x_q, bufs.x_s, w13, w13_s, w2, w2_s, topk_weights, bufs.sorted_ids,
+                    bufs.expert_ids, bufs.ntp, bufs.top_k, bufs.block_m, out_bf16,
+                    bufs.workspace, bufs.flags, stream)

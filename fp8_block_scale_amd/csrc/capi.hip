@@ -1,0 +1,313 @@
+// C ABI of libmoe_fp8.so: argument validation, workspace layout and the
+// launch sequence of each entry point (declared in include/moe_fp8.h).
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe_fp8.h"
+#include "internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status hip_check(hipError_t e, const char *what) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr int kMaxE = 1024;
+
+int64_t plan_sorted_cap(int64_t M, int32_t top_k, int32_t E, int32_t bm) {
+    int64_t R = M * top_k;
+    int64_t n = R + (E < R ? E : R) * (int64_t)(bm - 1);
+    return (n + bm - 1) / bm * bm;
+}
+
+bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+// Gate/up split-K factor: enough workgroups to cover the chip at small grids.
+struct SplitChoice {
+    int nsplit;
+    int kb_per_split;
+};
+
+SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t nkb, uint32_t flags) {
+    int64_t tiles = blocks_cap * jtiles;
+    int64_t s = (flags & MOE_F_SPLITK_MASK) >> MOE_F_SPLITK_SHIFT;
+    if (s == 0) {
+        const int64_t target = 512;   // workgroups: two per CU
+        s = tiles >= 256 ? 1 : (target + tiles - 1) / (tiles > 0 ? tiles : 1);
+    }
+    if (s > nkb) s = nkb;
+    if (s < 1) s = 1;
+    int64_t kps = (nkb + s - 1) / s;
+    s = (nkb + kps - 1) / kps;        // no empty splits
+    return {(int)s, (int)kps};
+}
+
+struct WsLayout {
+    size_t hq, hs, acc, cnt, part, total;
+    size_t zero_words;                // acc + counters, zeroed per call
+    SplitChoice sp;
+};
+
+WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t block_m, int64_t sorted_cap,
+                   uint32_t flags) {
+    WsLayout l;
+    int64_t blocks_cap = sorted_cap / block_m;
+    int64_t jtiles = I / 128;
+    l.sp = choose_split(blocks_cap, jtiles, K / 128, flags);
+    size_t off = 0;
+    l.hq = off;
+    off = align256(off + (size_t)sorted_cap * I);
+    l.hs = off;
+    off = align256(off + (size_t)sorted_cap * (I / 128) * 4);
+    l.acc = off;
+    off += (size_t)M * K * 4;
+    l.cnt = off;
+    size_t ntiles = (size_t)blocks_cap * jtiles;
+    off = align256(off + (l.sp.nsplit > 1 ? ntiles * 4 : 0));
+    l.zero_words = (off - l.acc) / 4;
+    l.part = off;
+    if (l.sp.nsplit > 1) off = align256(off + ntiles * l.sp.nsplit * block_m * 256 * 4);
+    l.total = off;
+    return l;
+}
+
+moe_status check_experts_shape(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                               int32_t block_m, int64_t sorted_cap) {
+    if (M < 0 || K <= 0 || I <= 0 || E < 1 || top_k < 1)
+        return fail(MOE_ERR_SHAPE, "need M >= 0, K > 0, I > 0, E >= 1, top_k >= 1");
+    if (K % 128 != 0 || I % 128 != 0)
+        return fail(MOE_ERR_SHAPE, "K (%lld) and I (%lld) must be multiples of 128",
+                    (long long)K, (long long)I);
+    if (!valid_block_m(block_m))
+        return fail(MOE_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", block_m);
+    if (sorted_cap < 0 || sorted_cap % block_m != 0)
+        return fail(MOE_ERR_SHAPE, "sorted_cap must be a non-negative multiple of block_m");
+    if (M * top_k >= (int64_t)1 << 31)
+        return fail(MOE_ERR_SHAPE, "M * top_k must fit in int32");
+    const int64_t blocks = sorted_cap / block_m;
+    const int64_t grid_up = blocks * (I / 128) * (K / 128);   // worst split-K factor
+    const int64_t grid_dn = blocks * ((K + 255) / 256);
+    if (grid_up >= ((int64_t)1 << 31) || grid_dn >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_SHAPE, "plan too large for one launch grid");
+    return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API const char *moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: size out of range or inconsistent";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: misaligned pointer or leading dimension";
+        case MOE_ERR_CAPACITY: return "MOE_ERR_CAPACITY: plan buffers or workspace too small";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: not implemented for these arguments";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    }
+    return "unknown moe_status";
+}
+
+MOE_API const char *moe_last_error(void) { return g_err; }
+
+// ------------------------------------------------------------------ plan
+
+MOE_API moe_status moe_plan_capacity(int64_t M, int32_t top_k, int32_t E, int32_t block_m,
+                                     int64_t *sorted_cap, int64_t *blocks_cap) {
+    if (!sorted_cap || !blocks_cap) return fail(MOE_ERR_NULL, "output pointer is NULL");
+    if (M < 0 || top_k < 1 || E < 1 || block_m < 1)
+        return fail(MOE_ERR_SHAPE, "need M >= 0, top_k >= 1, E >= 1, block_m >= 1");
+    if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E = %d exceeds %d", E, kMaxE);
+    if (block_m > 256) return fail(MOE_ERR_UNSUPPORTED, "block_m = %d exceeds 256", block_m);
+    if (M * top_k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "M * top_k must fit in int32");
+    *sorted_cap = plan_sorted_cap(M, top_k, E, block_m);
+    *blocks_cap = *sorted_cap / block_m;
+    return MOE_OK;
+}
+
+MOE_API size_t moe_plan_workspace_size(int64_t, int32_t, int32_t, int32_t) { return 0; }
+
+MOE_API moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k,
+                            int32_t E, int32_t block_m, int32_t *sorted_token_ids,
+                            int64_t sorted_cap, int32_t *expert_ids, int64_t blocks_cap,
+                            int32_t *num_tokens_post_padded, void *, size_t, void *stream) {
+    int64_t need_sorted, need_blocks;
+    moe_status st = moe_plan_capacity(M, top_k, E, block_m, &need_sorted, &need_blocks);
+    if (st != MOE_OK) return st;
+    if (ids_dtype != MOE_IDS_I32 && ids_dtype != MOE_IDS_I64)
+        return fail(MOE_ERR_SHAPE, "ids_dtype %d is neither MOE_IDS_I32 nor MOE_IDS_I64", ids_dtype);
+    if (!num_tokens_post_padded) return fail(MOE_ERR_NULL, "num_tokens_post_padded is NULL");
+    if (M > 0 && (!topk_ids || !sorted_token_ids || !expert_ids))
+        return fail(MOE_ERR_NULL, "topk_ids, sorted_token_ids and expert_ids are required");
+    if (sorted_cap < need_sorted || blocks_cap < need_blocks)
+        return fail(MOE_ERR_CAPACITY, "plan buffers [%lld, %lld] below capacity [%lld, %lld]",
+                    (long long)sorted_cap, (long long)blocks_cap, (long long)need_sorted,
+                    (long long)need_blocks);
+    if (sorted_cap < blocks_cap * block_m)
+        return fail(MOE_ERR_CAPACITY, "sorted_cap must be >= blocks_cap * block_m");
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {
+        // a fill kernel, not a memset node, so the call stays graph-capturable
+        return hip_check(moe::launch_fill_zero((uint32_t *)num_tokens_post_padded, 1, s),
+                         "moe_plan: clear num_tokens_post_padded");
+    }
+    return hip_check(moe::launch_plan(topk_ids, ids_dtype == MOE_IDS_I64, M * top_k, E, block_m,
+                                      sorted_token_ids, expert_ids, num_tokens_post_padded, s),
+                     "moe_plan: launch");
+}
+
+// ------------------------------------------------------------- quant act
+
+MOE_API moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                                 uint8_t *x_q, float *x_s, int32_t scale_mode, void *stream) {
+    if (M < 0 || K <= 0 || K % 128 != 0)
+        return fail(MOE_ERR_SHAPE, "need M >= 0 and K a positive multiple of 128");
+    if (ld_x < K) return fail(MOE_ERR_SHAPE, "ld_x (%lld) < K (%lld)", (long long)ld_x, (long long)K);
+    if (scale_mode != MOE_SCALE_FP32 && scale_mode != MOE_SCALE_UE8M0)
+        return fail(MOE_ERR_SHAPE, "unknown scale_mode %d", scale_mode);
+    if (M == 0) return MOE_OK;
+    if (!x_bf16 || !x_q || !x_s) return fail(MOE_ERR_NULL, "x_bf16, x_q and x_s are required");
+    if (!aligned16(x_bf16) || ld_x % 8 != 0 || !aligned16(x_q))
+        return fail(MOE_ERR_ALIGN, "x_bf16 and x_q must be 16-byte aligned and ld_x a multiple of 8");
+    if (((uintptr_t)x_s & 3u) != 0) return fail(MOE_ERR_ALIGN, "x_s must be 4-byte aligned");
+    return hip_check(moe::launch_quant_act((const uint16_t *)x_bf16, M, K, ld_x, x_q, x_s,
+                                           scale_mode == MOE_SCALE_UE8M0, (hipStream_t)stream),
+                     "moe_quant_act: launch");
+}
+
+MOE_API moe_status moe_debug_e4m3_encode(const float *in, uint8_t *out, int64_t n, void *stream) {
+    if (n < 0) return fail(MOE_ERR_SHAPE, "n < 0");
+    if (n == 0) return MOE_OK;
+    if (!in || !out) return fail(MOE_ERR_NULL, "in and out are required");
+    return hip_check(moe::launch_e4m3_encode(in, out, n, (hipStream_t)stream),
+                     "moe_debug_e4m3_encode: launch");
+}
+
+// --------------------------------------------------------------- experts
+
+MOE_API size_t moe_fp8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,
+                                              int32_t top_k, int32_t block_m, int64_t sorted_cap,
+                                              uint32_t flags) {
+    if (check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap) != MOE_OK) return 0;
+    return ws_layout(M, K, I, block_m, sorted_cap, flags).total;
+}
+
+MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int32_t E,
+                                                    int32_t top_k, int32_t block_m,
+                                                    int64_t sorted_cap, uint32_t flags,
+                                                    size_t *h_q_offset, size_t *h_s_offset) {
+    moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
+    if (st != MOE_OK) return st;
+    if (!h_q_offset || !h_s_offset) return fail(MOE_ERR_NULL, "output pointer is NULL");
+    WsLayout l = ws_layout(M, K, I, block_m, sorted_cap, flags);
+    *h_q_offset = l.hq;
+    *h_s_offset = l.hs;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                                   const float *w13_s, const uint8_t *w2, const float *w2_s,
+                                   const float *topk_weights, const int32_t *sorted_token_ids,
+                                   const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
+                                   int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                                   int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                                   void *out_bf16, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
+    if (st != MOE_OK) return st;
+    const uint32_t known = MOE_F_INTER_UE8M0 | MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_SPLITK_MASK;
+    if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
+    if ((flags & MOE_F_MMA_E8M0) && !(flags & MOE_F_INTER_UE8M0))
+        return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
+    if (M == 0 || sorted_cap == 0) return MOE_OK;
+    if (!x_q || !x_s || !w13 || !w13_s || !w2 || !w2_s || !topk_weights || !sorted_token_ids ||
+        !expert_ids || !num_tokens_post_padded || !out_bf16 || !workspace)
+        return fail(MOE_ERR_NULL, "all tensor arguments and the workspace are required");
+    if (!aligned16(x_q) || !aligned16(w13) || !aligned16(w2) || !aligned16(out_bf16) ||
+        ((uintptr_t)workspace & 255u) != 0)
+        return fail(MOE_ERR_ALIGN, "x_q, w13, w2, out must be 16-byte and workspace 256-byte aligned");
+    WsLayout l = ws_layout(M, K, I, block_m, sorted_cap, flags);
+    if (workspace_bytes < l.total)
+        return fail(MOE_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = (uint8_t *)workspace;
+    const int64_t blocks_cap = sorted_cap / block_m;
+    const bool e8m0 = (flags & MOE_F_MMA_E8M0) != 0;
+
+    st = hip_check(moe::launch_fill_zero((uint32_t *)(ws + l.acc), l.zero_words, s),
+                   "moe_fp8_experts: clear reduction buffer");
+    if (st != MOE_OK) return st;
+
+    moe::GateUpArgs ga;
+    ga.xq = x_q;
+    ga.xs = x_s;
+    ga.w13 = w13;
+    ga.w13s = w13_s;
+    ga.sorted = sorted_token_ids;
+    ga.eids = expert_ids;
+    ga.ntp = num_tokens_post_padded;
+    ga.hq = ws + l.hq;
+    ga.hs = (float *)(ws + l.hs);
+    ga.part = (float *)(ws + l.part);
+    ga.cnt = (uint32_t *)(ws + l.cnt);
+    ga.K = K;
+    ga.I = I;
+    ga.R = M * top_k;
+    ga.E = E;
+    ga.top_k = top_k;
+    ga.nkb = (int)(K / 128);
+    ga.jtiles = (int)(I / 128);
+    ga.nblocks = (int)blocks_cap;
+    ga.nsplit = l.sp.nsplit;
+    ga.kb_per_split = l.sp.kb_per_split;
+    ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
+    const bool fp8_gateup = (flags & MOE_F_FP8_GATEUP) != 0;
+    st = hip_check(moe::launch_gateup(ga, block_m, fp8_gateup, e8m0, s),
+                   "moe_fp8_experts: gate/up launch");
+    if (st != MOE_OK) return st;
+
+    moe::DownArgs da;
+    da.hq = ws + l.hq;
+    da.hs = (const float *)(ws + l.hs);
+    da.w2 = w2;
+    da.w2s = w2_s;
+    da.topk_w = topk_weights;
+    da.sorted = sorted_token_ids;
+    da.eids = expert_ids;
+    da.ntp = num_tokens_post_padded;
+    da.acc = (float *)(ws + l.acc);
+    da.K = K;
+    da.I = I;
+    da.R = M * top_k;
+    da.E = E;
+    da.top_k = top_k;
+    da.njb = (int)(I / 128);
+    da.ctiles = (int)((K + 255) / 256);
+    da.nblocks = (int)blocks_cap;
+    st = hip_check(moe::launch_down(da, block_m, e8m0, s), "moe_fp8_experts: down launch");
+    if (st != MOE_OK) return st;
+
+    return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const float *)(ws + l.acc), M * K, s),
+                     "moe_fp8_experts: finalize launch");
+}

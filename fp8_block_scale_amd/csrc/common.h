@@ -1,0 +1,154 @@
+// Device helpers shared by the gfx950 kernels of libmoe_fp8.
+//
+// FP8 here is OCP E4M3FN (bias 7, max 448, no infinities), the format the
+// W8A8 block-scale expert PR (FlashInfer #4287, PR summary and public
+// contract) calls FP8; gfx950's v_cvt_pk_fp8_f32 and the f8f6f4 MFMA with
+// format 0 use it natively.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kFltMin = 1.17549435e-38f;  // 2^-126
+
+// ------------------------------------------------------------- conversions
+
+// Four FP32 values -> four E4M3 codes packed little-endian (a in byte 0).
+// Values are clamped to +-448 first (saturation); the hardware converter
+// rounds to nearest even and handles the subnormal range.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    a = fminf(fmaxf(a, -kE4M3Max), kE4M3Max);
+    b = fminf(fmaxf(b, -kE4M3Max), kE4M3Max);
+    c = fminf(fmaxf(c, -kE4M3Max), kE4M3Max);
+    d = fminf(fmaxf(d, -kE4M3Max), kE4M3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// FP32 -> BF16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ------------------------------------------------------------ scale rules
+
+// FP32 rule: s = max(amax / 448, FLT_MIN); inv = 1 / s, both IEEE divisions.
+__device__ __forceinline__ void scale_fp32(float amax, float &s, float &inv) {
+    s = fmaxf(__fdiv_rn(amax, kE4M3Max), kFltMin);
+    inv = __fdiv_rn(1.0f, s);
+}
+
+// Power-of-two rule: s = 2^e, e the least integer with 448 * 2^e >= amax,
+// floored at -126.  With amax = (1 + m / 2^23) * 2^(E - 127) for a normal
+// number and 448 = 1.75 * 2^8, 448 * 2^(E - 135) >= amax exactly when the
+// mantissa fraction is at most 0.75 (m <= 0x600000); otherwise E - 134 is
+// the least exponent (E - 136 never suffices).
+__device__ __forceinline__ void scale_ue8m0(float amax, float &s, float &inv) {
+    uint32_t u = __float_as_uint(amax) & 0x7fffffffu;
+    int ex = (int)(u >> 23);
+    int e;
+    if (ex == 0) {
+        e = -126;  // zero or subnormal amax
+    } else {
+        uint32_t m = u & 0x7fffffu;
+        e = (m <= 0x600000u) ? ex - 135 : ex - 134;
+        e = e < -126 ? -126 : e;
+    }
+    s = __uint_as_float((uint32_t)(e + 127) << 23);
+    inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, |e| <= 126 here
+}
+
+__device__ __forceinline__ void group_scale(float amax, bool ue8m0, float &s, float &inv) {
+    if (ue8m0) scale_ue8m0(amax, s, inv);
+    else scale_fp32(amax, s, inv);
+}
+
+// E8M0 exponent byte of a power-of-two FP32 scale (its biased exponent).
+__device__ __forceinline__ int e8m0_of(float s) {
+    return (int)((__float_as_uint(s) >> 23) & 0xffu);
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// D = A * B over a 16x16x128 FP8 tile, fresh accumulator.
+// A operand: lane l holds 32 codes of row (l % 16); B operand: lane l holds
+// 32 codes of column (l % 16); both lanes hold the same 32 K-indices, a fixed
+// function of (l / 16).  Result: lane l, element i is D[4 * (l / 16) + i][l % 16].
+__device__ __forceinline__ v4f mfma16x16x128(const v8i &a, const v8i &b) {
+    v4f z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// acc += 2^(ea - 127) * 2^(eb - 127) * (A * B), scales given as E8M0 bytes
+// (per lane: row scale for A, column scale for B).
+__device__ __forceinline__ v4f mfma16x16x128_e8m0(const v8i &a, const v8i &b, v4f acc,
+                                                   int ea, int eb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, ea, 0, eb);
+}
+
+// The FP8 MFMA sums the 128 (or 32) products of one instruction in a
+// fixed-point window about 15 bits below the largest product, so its result
+// can be off by ~2^-15 of the largest product.  Where that matters the codes
+// are widened instead: every E4M3 value is exactly an FP16 normal number,
+// FP16 x FP16 products are exact in FP32, and the FP16 MFMA accumulates with
+// FP32 rounding.
+
+// 32 E4M3 codes (two 16-byte halves of one lane's K-slice) -> four 8-wide
+// FP16 operands; operand q holds bytes [8q, 8q + 8).
+__device__ __forceinline__ void e4m3x32_to_f16(const u32x4 &lo, const u32x4 &hi, v8h (&out)[4]) {
+    const unsigned d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q], 1.0f, false);
+        v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q], 1.0f, true);
+        v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q + 1], 1.0f, false);
+        v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q + 1], 1.0f, true);
+        out[q] = v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+    }
+}
+
+// D = A * B over one 128-deep K-block given as four FP16 16x16x32 operands
+// per side (same lane/row mapping as the FP8 16x16x128 tile).
+__device__ __forceinline__ v4f mfma16x16x128_f16(const v8h (&a)[4], const v8h (&b)[4]) {
+    v4f t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[q], t, 0, 0, 0);
+    return t;
+}
+
+// ------------------------------------------------------------ scheduling
+
+// Workgroups are handed to the 8 XCDs round-robin by id.  Renumber them so
+// that XCD i receives one contiguous range of logical tiles: tiles that read
+// the same expert weights (consecutive plan blocks of one expert) then run at
+// the same time on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int x, int n) {
+    int q = n >> 3, r = n & 7;
+    int xcd = x & 7, k = x >> 3;
+    return xcd * q + (xcd < r ? xcd : r) + k;
+}
+
+// ------------------------------------------------------------ wave utils
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+    return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+}  // namespace moe

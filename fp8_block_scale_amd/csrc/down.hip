@@ -1,0 +1,246 @@
+// Step 5: down-projection GEMM over the requantised SwiGLU rows, weighting
+// by the router probability, and the reduce-add into the caller's output.
+//
+// What is computed (FlashInfer PR #4287, PR summary and the FP32-scale note
+// of its final kernel performance section): for plan row p of block b
+// (expert e, route r, token t = r / top_k)
+//   y[p, c] = sum_jb h_s[p, jb] * w2_s[e, c / 128, jb]
+//                    * sum_{j in jb} h_q[p, j] * W2[e, c, j]           (FP32)
+//   out[t, c] += topk_weights[r] * y[p, c]
+// The route sum is accumulated in FP32 (device atomics into a workspace
+// buffer) and rounded to BF16 once by the finalize kernel, which adds the
+// caller's previous BF16 output -- the output is an accumulator.
+//
+// Tiling: one workgroup = one plan block (BM rows) x 256 output columns; four
+// waves take 64 columns each (four 16-row W2 subtiles, all inside one
+// 128-column scale block).  The intermediate rows of a block are contiguous
+// in the workspace (plan-row order), so the B tile is a plain 128-byte-row
+// copy into LDS; W2 rows stream into registers as in the gate/up kernel.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+template <int BM>
+struct DNCfg {
+    static constexpr int TM = BM < 64 ? BM : 64;
+    static constexpr int WM = BM / TM;
+    static constexpr int NW = 4 * WM;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NU = TM / 16;
+    static constexpr int ROWB = 144;
+    static constexpr int CHUNKS = BM * 8;
+    static constexpr int CPT = (CHUNKS + NT - 1) / NT;
+};
+
+__device__ __forceinline__ v8i join8d(const u32x4 &lo, const u32x4 &hi) {
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+template <int BM, bool E8M0>
+__global__ void __launch_bounds__(DNCfg<BM>::NT)
+down_kernel(DownArgs a) {
+    using C = DNCfg<BM>;
+    __shared__ __attribute__((aligned(16))) uint8_t sH[2][BM * C::ROWB];
+    __shared__ float sHs[2][BM];
+    __shared__ int sRt[BM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int wn = w & 3, wm = w >> 2;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = L % a.nblocks;
+    const int ct = L / a.nblocks;
+
+    if (b * BM >= a.ntp[0]) return;              // padded-block early exit
+    const int e = a.eids[b];
+    if (e < 0 || e >= a.E) return;
+
+    if (tid < BM) {
+        int r = a.sorted[(int64_t)b * BM + tid];
+        sRt[tid] = (r >= 0 && (int64_t)r < a.R) ? r : -1;
+    }
+    __syncthreads();
+
+    const int64_t I = a.I, K = a.K;
+    const int64_t col0 = (int64_t)ct * 256 + 64 * wn;   // this wave's first column
+    const bool wave_on = col0 < K;
+    const int njb = a.njb;
+
+    const uint8_t *wrow[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        int64_t c = wave_on ? col0 + 16 * s + l16 : 0;
+        wrow[s] = a.w2 + ((int64_t)e * K + c) * I + 16 * g;
+    }
+    const float *sb_ptr = a.w2s + ((int64_t)e * (K >> 7) + (wave_on ? (col0 >> 7) : 0)) * njb;
+    const uint8_t *hbase = a.hq + (int64_t)b * BM * I;
+    const float *hsbase = a.hs + (int64_t)b * BM * njb;
+
+    v4f acc[4][C::NU];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    v8i wcur[4], wnxt[4];
+    u32x4 hbuf[C::CPT];
+    float hs_reg = 0.f;
+
+    auto load_w = [&](int jb, v8i (&dst)[4]) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(wrow[s] + (int64_t)jb * 128);
+            dst[s] = join8d(p[0], p[4]);
+        }
+    };
+    auto load_h = [&](int jb) {
+#pragma unroll
+        for (int i = 0; i < C::CPT; ++i) {
+            int c = tid + i * C::NT;
+            if (c < C::CHUNKS)
+                hbuf[i] = *reinterpret_cast<const u32x4 *>(hbase + (int64_t)(c >> 3) * I +
+                                                           (int64_t)jb * 128 + (c & 7) * 16);
+        }
+        if (tid < BM) hs_reg = hsbase[(int64_t)tid * njb + jb];
+    };
+    auto store_h = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < C::CPT; ++i) {
+            int c = tid + i * C::NT;
+            if (c < C::CHUNKS)
+                *reinterpret_cast<u32x4 *>(&sH[buf][(c >> 3) * C::ROWB + (c & 7) * 16]) = hbuf[i];
+        }
+        if (tid < BM) sHs[buf][tid] = hs_reg;
+    };
+
+    if (wave_on) load_w(0, wcur);
+    load_h(0);
+    store_h(0);
+    __syncthreads();
+
+    for (int jb = 0; jb < njb; ++jb) {
+        const int buf = jb & 1;
+        const bool more = jb + 1 < njb;
+        if (more) {
+            if (wave_on) load_w(jb + 1, wnxt);
+            load_h(jb + 1);
+        }
+        if (wave_on) {
+            const float sb = sb_ptr[jb];
+#pragma unroll
+            for (int u = 0; u < C::NU; ++u) {
+                const int row = wm * C::TM + u * 16 + l16;
+                const uint8_t *bp = &sH[buf][row * C::ROWB + 16 * g];
+                v8i B = join8d(*reinterpret_cast<const u32x4 *>(bp),
+                               *reinterpret_cast<const u32x4 *>(bp + 64));
+                const float sa = sHs[buf][row];
+                if constexpr (E8M0) {
+                    const int ea = e8m0_of(sb), eb = e8m0_of(sa);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[s][u] = mfma16x16x128_e8m0(wcur[s], B, acc[s][u], ea, eb);
+                } else {
+                    const float f = sa * sb;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        v4f t = mfma16x16x128(wcur[s], B);
+                        acc[s][u] = t * f + acc[s][u];
+                    }
+                }
+            }
+        }
+        if (more) {
+            store_h(buf ^ 1);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wcur[s] = wnxt[s];
+        }
+        __syncthreads();
+    }
+
+    if (!wave_on) return;
+#pragma unroll
+    for (int u = 0; u < C::NU; ++u) {
+        const int row = wm * C::TM + u * 16 + l16;
+        const int r = sRt[row];
+        if (r < 0) continue;
+        const int64_t t = r / a.top_k;
+        const float wr = a.topk_w[r];
+        float *dst = a.acc + t * K + col0 + 4 * g;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + 16 * s + i, wr * acc[s][u][i]);
+    }
+}
+
+__global__ void __launch_bounds__(256)
+fill_zero_kernel(uint32_t *__restrict__ p, size_t n) {
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * 256;
+    for (; i < n; i += stride) p[i] = 0u;
+}
+
+// out = bf16(out + acc), eight elements per thread (n is a multiple of 8).
+__global__ void __launch_bounds__(256)
+finalize_kernel(uint16_t *__restrict__ out, const float *__restrict__ acc, int64_t n) {
+    int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= n) return;
+    u32x4 o = *reinterpret_cast<const u32x4 *>(out + i);
+    v4f a0 = *reinterpret_cast<const v4f *>(acc + i);
+    v4f a1 = *reinterpret_cast<const v4f *>(acc + i + 4);
+    float f[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    uint32_t r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float lo = bf16_bits_to_f32(o[k] & 0xffffu) + f[2 * k];
+        float hi = bf16_bits_to_f32(o[k] >> 16) + f[2 * k + 1];
+        r[k] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    }
+    *reinterpret_cast<u32x4 *>(out + i) = u32x4{r[0], r[1], r[2], r[3]};
+}
+
+template <int BM, bool E8M0>
+hipError_t launch_dn(const DownArgs &a, hipStream_t st) {
+    int64_t grid = (int64_t)a.nblocks * a.ctiles;
+    if (grid == 0) return hipSuccess;
+    down_kernel<BM, E8M0><<<(unsigned)grid, DNCfg<BM>::NT, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st) {
+    switch (block_m) {
+        case 16: return e8m0 ? launch_dn<16, true>(a, st) : launch_dn<16, false>(a, st);
+        case 32: return e8m0 ? launch_dn<32, true>(a, st) : launch_dn<32, false>(a, st);
+        case 64: return e8m0 ? launch_dn<64, true>(a, st) : launch_dn<64, false>(a, st);
+        case 128: return e8m0 ? launch_dn<128, true>(a, st) : launch_dn<128, false>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st) {
+    if (n_words == 0) return hipSuccess;
+    size_t blocks = (n_words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, n_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(uint16_t *out, const float *acc, int64_t n, hipStream_t st) {
+    int64_t blocks = (n / 8 + 255) / 256;
+    if (blocks == 0) return hipSuccess;
+    finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(out, acc, n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,68 @@
+// Host-side launchers of the libmoe_fp8 kernels (internal interface between
+// the C ABI layer and the kernel translation units).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- step 1: routing plan (plan.hip)
+hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
+                       int32_t *sorted, int32_t *expert_ids, int32_t *ntp, hipStream_t st);
+
+// ---- step 2: activation quantisation (quant.hip)
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
+                            uint8_t *xq, float *xs, bool ue8m0, hipStream_t st);
+hipError_t launch_e4m3_encode(const float *in, uint8_t *out, int64_t n, hipStream_t st);
+
+// ---- steps 3-5 (gateup.hip, down.hip)
+struct GateUpArgs {
+    const uint8_t *xq;
+    const float *xs;
+    const uint8_t *w13;
+    const float *w13s;
+    const int32_t *sorted;
+    const int32_t *eids;
+    const int32_t *ntp;
+    uint8_t *hq;
+    float *hs;
+    float *part;        // split-K partial sums (nsplit > 1)
+    uint32_t *cnt;      // split-K arrival counters, one per (block, j-tile)
+    int64_t K, I, R;
+    int E, top_k;
+    int nkb;            // K / 128
+    int jtiles;         // I / 128
+    int nblocks;        // blocks_cap
+    int nsplit;         // split-K factor
+    int kb_per_split;
+    int inter_ue8m0;
+};
+
+struct DownArgs {
+    const uint8_t *hq;
+    const float *hs;
+    const uint8_t *w2;
+    const float *w2s;
+    const float *topk_w;
+    const int32_t *sorted;
+    const int32_t *eids;
+    const int32_t *ntp;
+    float *acc;         // FP32 [M, K] reduction buffer
+    int64_t K, I, R;
+    int E, top_k;
+    int njb;            // I / 128
+    int ctiles;         // column tiles of 256
+    int nblocks;
+};
+
+// fp8_mma: FP8 MFMA instead of the exact FP16-widened product path;
+// e8m0: (with fp8_mma) power-of-two scales applied inside the MFMA.
+hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
+                         hipStream_t st);
+hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
+hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st);
+hipError_t launch_finalize(uint16_t *out, const float *acc, int64_t n, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,161 @@
+// Step 1: the moe_align_block_size routing plan on one workgroup.
+//
+// What is built (FlashInfer PR #4287, PR summary and public-contract
+// section; masked int32/int64 routes from sglang-glm53-flash-sm120 PR #13,
+// description and validation): valid routes grouped by expert in ascending
+// expert id, ascending flat route index r inside an expert, every expert's
+// segment padded with the sentinel R to a multiple of block_m, one expert id
+// per block and the padded length P written on the device.
+//
+// How (one workgroup of NW wavefronts):
+//   pass 1  each wave owns a contiguous chunk of routes and walks it 64 at a
+//           time; lanes holding the same expert are found with one ballot
+//           per bit of the expert id (an exact match mask), and the group's
+//           lowest lane adds the group size to the wave's LDS histogram row;
+//   scan    per expert: total count, round-up to block_m, exclusive prefix
+//           over experts (block scan), per-wave base offsets, sentinel fill
+//           and expert_ids;
+//   pass 2  the waves walk their chunks again in the same order; a lane's
+//           slot is its wave base + the number of lower lanes in its match
+//           group, so the scatter is stable (ascending r) without atomics.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ uint64_t match_mask(int key, int nbits) {
+    uint64_t m = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+        int bit = (key >> b) & 1;
+        uint64_t bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+template <typename IdT>
+__global__ void __launch_bounds__(kPlanThreads)
+plan_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwaves,
+            int32_t *__restrict__ sorted, int32_t *__restrict__ expert_ids,
+            int32_t *__restrict__ ntp) {
+    extern __shared__ int smem[];
+    int *hist = smem;                     // [nwaves][E]: counts, then bases
+    int *cnt = hist + nwaves * E;         // [E] per-expert totals
+    int *wsum = cnt + E;                  // [32] wave totals for the scan
+
+    const int tid = threadIdx.x;
+    const int T = blockDim.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int nbits = 32 - __clz(E);      // keys 0..E fit (E = masked)
+    const uint64_t lower = (1ull << lane) - 1ull;
+
+    for (int i = tid; i < nwaves * E; i += T) hist[i] = 0;
+    __syncthreads();
+
+    // contiguous chunk per wave, a multiple of 64 routes
+    int64_t chunk = (R + nwaves - 1) / nwaves;
+    chunk = (chunk + 63) & ~int64_t(63);
+    const int64_t beg = (int64_t)w * chunk;
+    const int64_t end = beg + chunk < R ? beg + chunk : R;
+
+    // ---- pass 1: per-wave histogram
+    if (w < nwaves) {
+        for (int64_t base = beg; base < end; base += 64) {
+            int64_t r = base + lane;
+            int key = E;
+            if (r < end) {
+                IdT v = ids[r];
+                if (v >= 0 && v < (IdT)E) key = (int)v;
+            }
+            uint64_t m = match_mask(key, nbits);
+            if (key < E && (m & lower) == 0) hist[w * E + key] += __popcll(m);
+        }
+    }
+    __syncthreads();
+
+    // ---- scan: per-expert totals, padded sizes, offsets, bases, sentinels
+    const int seg = (E + T - 1) / T;
+    const int e0 = tid * seg;
+    const int e1 = e0 + seg < E ? e0 + seg : E;
+    int local = 0;
+    for (int e = e0; e < e1; ++e) {
+        int c = 0;
+        for (int q = 0; q < nwaves; ++q) c += hist[q * E + e];
+        cnt[e] = c;
+        local += (c + bm - 1) / bm * bm;
+    }
+    // block exclusive scan of `local`
+    int incl = local;
+    for (int d = 1; d < 64; d <<= 1) {
+        int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int q = 0; q < T / 64; ++q) {
+            int v = wsum[q];
+            wsum[q] = run;
+            run += v;
+        }
+        ntp[0] = run;                     // P
+    }
+    __syncthreads();
+    int off = wsum[w] + incl - local;
+    for (int e = e0; e < e1; ++e) {
+        int c = cnt[e];
+        int pad = (c + bm - 1) / bm * bm;
+        int run = off;
+        for (int q = 0; q < nwaves; ++q) {
+            int h = hist[q * E + e];
+            hist[q * E + e] = run;
+            run += h;
+        }
+        for (int s = off + c; s < off + pad; ++s) sorted[s] = (int32_t)R;
+        for (int b = off / bm; b < (off + pad) / bm; ++b) expert_ids[b] = e;
+        off += pad;
+    }
+    __syncthreads();
+
+    // ---- pass 2: stable scatter
+    if (w < nwaves) {
+        for (int64_t base = beg; base < end; base += 64) {
+            int64_t r = base + lane;
+            int key = E;
+            if (r < end) {
+                IdT v = ids[r];
+                if (v >= 0 && v < (IdT)E) key = (int)v;
+            }
+            uint64_t m = match_mask(key, nbits);
+            if (key < E) {
+                int slot = hist[w * E + key] + __popcll(m & lower);
+                sorted[slot] = (int32_t)r;
+            }
+            if (key < E && (m & lower) == 0) hist[w * E + key] += __popcll(m);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
+                       int32_t *sorted, int32_t *expert_ids, int32_t *ntp, hipStream_t st) {
+    const int T = kPlanThreads;
+    const int nwaves = E <= 512 ? 16 : 8;
+    size_t lds = ((size_t)nwaves * E + E + 32) * sizeof(int);
+    if (ids_i64)
+        plan_kernel<int64_t><<<1, T, lds, st>>>((const int64_t *)ids, R, E, block_m, nwaves,
+                                               sorted, expert_ids, ntp);
+    else
+        plan_kernel<int32_t><<<1, T, lds, st>>>((const int32_t *)ids, R, E, block_m, nwaves,
+                                               sorted, expert_ids, ntp);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,87 @@
+// Step 2: per-token 1x128 FP8 activation quantisation.
+//
+// FlashInfer PR #4287 (public-contract section) consumes activations as E4M3
+// codes with one FP32 scale per token and 128-column group; its review of the
+// zero-activation scale floors the scale at FLT_MIN before inversion.  The
+// power-of-two scale mode follows SGLang PR #43556 (scales rounded up to
+// powers of two).
+//
+// Layout: 16 lanes per 128-column group, each lane one 16-byte load of eight
+// BF16 values (fully coalesced rows), the group amax by a 16-lane xor
+// reduction, one 8-byte store of codes per lane and one scale per group.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+template <bool UE8M0>
+__global__ void __launch_bounds__(256)
+quant_act_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ld,
+                 uint8_t *__restrict__ xq, float *__restrict__ xs) {
+    const int64_t G = K >> 7;
+    const int64_t gid = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+    const int lig = threadIdx.x & 15;
+    if (gid >= M * G) return;             // whole 16-lane groups leave together
+    const int64_t m = gid / G;
+    const int64_t g = gid - m * G;
+
+    const u32x4 raw = *reinterpret_cast<const u32x4 *>(x + m * ld + g * 128 + lig * 8);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
+        f[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = wave_max_xor(amax, 8);
+    amax = wave_max_xor(amax, 4);
+    amax = wave_max_xor(amax, 2);
+    amax = wave_max_xor(amax, 1);
+
+    float s, inv;
+    group_scale(amax, UE8M0, s, inv);
+    uint32_t lo = pack_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    uint32_t hi = pack_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+    uint2 o;
+    o.x = lo;
+    o.y = hi;
+    *reinterpret_cast<uint2 *>(xq + m * K + g * 128 + lig * 8) = o;
+    if (lig == 0) xs[m * G + g] = s;
+}
+
+__global__ void __launch_bounds__(256)
+e4m3_encode_kernel(const float *__restrict__ in, uint8_t *__restrict__ out, int64_t n) {
+    int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4 && i + j < n; ++j) v[j] = in[i + j];
+    uint32_t w = pack_e4m3x4(v[0], v[1], v[2], v[3]);
+    for (int j = 0; j < 4 && i + j < n; ++j) out[i + j] = (uint8_t)(w >> (8 * j));
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
+                            uint8_t *xq, float *xs, bool ue8m0, hipStream_t st) {
+    int64_t groups = M * (K >> 7);
+    int64_t blocks = (groups + 15) / 16;
+    if (blocks == 0) return hipSuccess;
+    if (ue8m0)
+        quant_act_kernel<true><<<(unsigned)blocks, 256, 0, st>>>(x, M, K, ld, xq, xs);
+    else
+        quant_act_kernel<false><<<(unsigned)blocks, 256, 0, st>>>(x, M, K, ld, xq, xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode(const float *in, uint8_t *out, int64_t n, hipStream_t st) {
+    int64_t blocks = (n + 1023) / 1024;
+    if (blocks == 0) return hipSuccess;
+    e4m3_encode_kernel<<<(unsigned)blocks, 256, 0, st>>>(in, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

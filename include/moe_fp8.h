@@ -1,0 +1,203 @@
+/*
+ * moe_fp8.h -- C ABI of libmoe_fp8.so: the routed FP8 W8A8 block-scale
+ * mixture-of-experts expert path for AMD Instinct MI355X (gfx950).
+ *
+ * The path, as the method's pages define it:
+ *   1. moe_plan        -- the moe_align_block_size routing plan
+ *                         (FlashInfer PR #4287, PR summary; host bound on the
+ *                         plan buffers in its review and public-contract
+ *                         section; masked int32/int64 routes from
+ *                         sglang-glm53-flash-sm120 PR #13, description and
+ *                         validation).
+ *   2. moe_quant_act   -- 1x128 FP8 (E4M3) activation quantisation with one
+ *                         FP32 scale per token and 128-column group
+ *                         (PR #4287, public-contract section).
+ *   3-5. moe_fp8_experts -- gate/up grouped GEMM with FP32 128x128 weight
+ *                         block scales applied per K-block, SwiGLU, FP8
+ *                         requantisation of the SwiGLU output per row and
+ *                         128-column group, down GEMM, weighting by the
+ *                         router probability and reduce-add into the
+ *                         caller's BF16 output (PR #4287, PR summary and
+ *                         public-contract section; power-of-two scales from
+ *                         SGLang PR #43556, motivation and modifications).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument, unless said otherwise, is DEVICE memory owned
+ *     by the caller.  The library allocates nothing, frees nothing and keeps
+ *     no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; buffers must stay alive until the stream has
+ *     executed it.  No call synchronises the host or copies device data to
+ *     the host.
+ *   - Host-checkable problems (NULL pointers, shapes, alignment, capacity,
+ *     workspace size) return a status and enqueue nothing.  Launch failures
+ *     return MOE_ERR_HIP and moe_last_error() holds the HIP message.
+ *   - Data conditions are not errors: ids outside [0, E) are masked routes;
+ *     zero scales contribute zero.
+ *   - All tensors are dense row-major with the shapes given; sizes are in
+ *     elements unless named *_bytes.
+ *
+ * Notation: M tokens, K hidden size, I intermediate size (W13 has 2I rows:
+ * rows [0, I) are the gate projection, rows [I, 2I) the up projection),
+ * E experts, top_k routes per token, R = M * top_k routes, flat route index
+ * r = t * top_k + j.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent        */
+    MOE_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned  */
+    MOE_ERR_CAPACITY = 4,    /* plan buffers or workspace too small           */
+    MOE_ERR_UNSUPPORTED = 5, /* valid request this build does not implement   */
+    MOE_ERR_HIP = 6          /* a HIP runtime call failed                     */
+} moe_status;
+
+enum { MOE_IDS_I32 = 0, MOE_IDS_I64 = 1 };
+
+/* Group scale rules of the quantisers.
+ *   MOE_SCALE_FP32 : s = max(amax / 448, FLT_MIN) (IEEE FP32 division),
+ *                    code = E4M3_RNE_SAT(v * (1 / s)).
+ *   MOE_SCALE_UE8M0: s = 2^e with e the least integer such that
+ *                    448 * 2^e >= amax, floored at -126; code = E4M3(v * 2^-e).
+ * The FLT_MIN floor keeps an all-zero group at code 0 instead of 0 * inf
+ * (PR #4287, review of the zero-activation scale and public contract). */
+enum { MOE_SCALE_FP32 = 0, MOE_SCALE_UE8M0 = 1 };
+
+/* moe_fp8_experts flags. */
+enum {
+    /* requantise the SwiGLU output with MOE_SCALE_UE8M0 scales */
+    MOE_F_INTER_UE8M0 = 1u,
+    /* apply block scales inside the FP8 MFMA as E8M0 exponents instead of
+     * FP32 multiplies (the down GEMM, and the gate/up GEMM when
+     * MOE_F_FP8_GATEUP is set).  Requires MOE_F_INTER_UE8M0, and the caller
+     * guarantees that x_s, w13_s and w2_s hold only powers of two in
+     * [2^-126, 2^127] (no zeros): a non-power-of-two scale is silently
+     * truncated to its exponent. */
+    MOE_F_MMA_E8M0 = 2u,
+    /* run the gate/up GEMM on the FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4)
+     * instead of the default exact path (codes widened to FP16, exact
+     * products, FP32 accumulation).  Faster, but the FP8 MFMA keeps only
+     * ~15 bits below the largest product of each instruction, so about 1e-3
+     * of the requantised SwiGLU codes move by one step relative to an
+     * exactly accumulated reference. */
+    MOE_F_FP8_GATEUP = 4u
+};
+/* Bits 8..15 of `flags` optionally force the gate/up split-K factor
+ * (0 = automatic).  A tuning and test override; the same value must be
+ * given to moe_fp8_experts_workspace_size. */
+#define MOE_F_SPLITK_SHIFT 8
+#define MOE_F_SPLITK_MASK  0xFF00u
+
+/* ---------------------------------------------------------------- plan -- */
+
+/* Worst-case plan sizes for any routing:
+ *   sorted_cap = roundup(R + min(E, R) * (block_m - 1), block_m),
+ *   blocks_cap = sorted_cap / block_m.
+ * M >= 0, 1 <= top_k, 1 <= E <= 1024, 1 <= block_m <= 256. */
+moe_status moe_plan_capacity(int64_t M, int32_t top_k, int32_t E, int32_t block_m,
+                             int64_t *sorted_cap, int64_t *blocks_cap);
+
+/* Device workspace moe_plan needs (bytes; may be 0, then workspace may be NULL). */
+size_t moe_plan_workspace_size(int64_t M, int32_t top_k, int32_t E, int32_t block_m);
+
+/* Build the routing plan on the device.
+ *   topk_ids      [M, top_k] int32 (ids_dtype = MOE_IDS_I32) or int64
+ *                 (MOE_IDS_I64); ids outside [0, E) are masked routes.
+ *   sorted_token_ids [sorted_cap] int32 out: routes grouped by expert in
+ *                 ascending expert id, ascending r inside an expert, each
+ *                 expert's segment padded with the sentinel R to a multiple
+ *                 of block_m.
+ *   expert_ids    [blocks_cap] int32 out: the expert of each block.
+ *   num_tokens_post_padded [1] int32 out: P, the padded length.
+ *   Entries at or beyond P (resp. P / block_m) are left untouched.
+ * Errors: MOE_ERR_CAPACITY if sorted_cap or blocks_cap is below
+ * moe_plan_capacity, or sorted_cap < blocks_cap * block_m. */
+moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k,
+                    int32_t E, int32_t block_m,
+                    int32_t *sorted_token_ids, int64_t sorted_cap,
+                    int32_t *expert_ids, int64_t blocks_cap,
+                    int32_t *num_tokens_post_padded,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------- quant act -- */
+
+/* Quantise BF16 activations per token and 128-column group.
+ *   x_bf16 [M, ld_x] BF16 (first K columns used); K % 128 == 0,
+ *          ld_x >= K, ld_x % 8 == 0, x_bf16 16-byte aligned.
+ *   x_q    [M, K] E4M3 codes out (16-byte aligned).
+ *   x_s    [M, K/128] FP32 scales out.
+ *   scale_mode MOE_SCALE_FP32 or MOE_SCALE_UE8M0. */
+moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                         uint8_t *x_q, float *x_s, int32_t scale_mode, void *stream);
+
+/* --------------------------------------------------------------- experts -- */
+
+/* Device workspace moe_fp8_experts needs, in bytes (flags as passed to the
+ * call).  Holds the intermediate FP8 rows, their scales, an FP32 [M, K]
+ * reduction buffer and, for small grids, split-K partial sums. */
+size_t moe_fp8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,
+                                      int32_t top_k, int32_t block_m, int64_t sorted_cap,
+                                      uint32_t flags);
+
+/* Byte offsets inside that workspace of the intermediate codes
+ * h_q [sorted_cap, I] (E4M3, indexed by plan row) and their scales
+ * h_s [sorted_cap, I/128] (FP32); valid after a call, for inspection. */
+moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int32_t E,
+                                            int32_t top_k, int32_t block_m,
+                                            int64_t sorted_cap, uint32_t flags,
+                                            size_t *h_q_offset, size_t *h_s_offset);
+
+/* Steps 3-5 over a plan built by moe_plan (or any plan of that form):
+ *   out[t, :] += sum over valid routes r of token t of
+ *                topk_weights[r] * down(requant(SwiGLU(gate_up(x_q[t]))))
+ * with FP32 accumulation and one BF16 rounding of out.
+ *   x_q [M, K] E4M3, x_s [M, K/128] FP32          (from moe_quant_act)
+ *   w13 [E, 2I, K] E4M3, w13_s [E, 2I/128, K/128] FP32
+ *   w2  [E, K, I]  E4M3, w2_s  [E, K/128, I/128]  FP32
+ *   topk_weights [M, top_k] FP32 (any routed scaling already folded in)
+ *   sorted_token_ids [sorted_cap], expert_ids [sorted_cap / block_m],
+ *   num_tokens_post_padded [1]: the plan (device); blocks at or beyond P
+ *   exit untouched, so worst-case buffers are fine.
+ *   out_bf16 [M, K] BF16, read and written (accumulated into).
+ * Constraints: K % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128},
+ * sorted_cap % block_m == 0, weights and x_q 16-byte aligned.
+ * Errors: MOE_ERR_CAPACITY if workspace_bytes is below
+ * moe_fp8_experts_workspace_size; MOE_ERR_SHAPE if MOE_F_MMA_E8M0 is set
+ * without MOE_F_INTER_UE8M0. */
+moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s,
+                           const uint8_t *w13, const float *w13_s,
+                           const uint8_t *w2, const float *w2_s,
+                           const float *topk_weights,
+                           const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                           const int32_t *num_tokens_post_padded,
+                           int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                           int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                           void *out_bf16, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* ------------------------------------------------------------ utilities -- */
+
+const char *moe_status_str(moe_status s);
+/* Text of the last MOE_ERR_HIP / validation failure on this thread. */
+const char *moe_last_error(void);
+
+/* Test hook: convert n FP32 values to E4M3 codes with the exact device
+ * routine the quantisers use (clamp to +-448, round to nearest even).
+ * in/out are device pointers; n >= 0. */
+moe_status moe_debug_e4m3_encode(const float *in, uint8_t *out, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

@@ -45,9 +45,13 @@ class ExpertsResult:
     computed_tokens: np.ndarray  # bool [M]   tokens whose routes were evaluated
 
 
-def _expand_blocks(s, rows, cols):
-    """Broadcast a [rows/128, cols/128] block-scale grid to [rows, cols]."""
-    return np.repeat(np.repeat(s.astype(np.float64), 128, axis=0), 128, axis=1)[:rows, :cols]
+def dequant_blocks(codes, s):
+    """E4M3 codes [rows, cols] times their [rows/128, cols/128] block scales,
+    as float64 [rows, cols]."""
+    rows, cols = codes.shape
+    v = e4m3_decode(codes).reshape(rows // 128, 128, cols // 128, 128)
+    v *= s.astype(np.float64)[:, None, :, None]
+    return v.reshape(rows, cols)
 
 
 def silu_mul(gate, up):
@@ -109,7 +113,7 @@ def experts_ref(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_ids,
             continue
         # gathered activation rows, dequantised
         A = e4m3_decode(x_q[t]) * np.repeat(x_s[t].astype(np.float64), 128, axis=1)
-        W13d = e4m3_decode(w13[e]) * _expand_blocks(w13_s[e], twoI, K)
+        W13d = dequant_blocks(w13[e], w13_s[e])
         g = A @ W13d.T                                  # [n, 2I] FP64
         del W13d
         if debug is not None:
@@ -120,7 +124,7 @@ def experts_ref(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_ids,
         h_q[rows] = codes
         h_s[rows] = scales
         Hd = e4m3_decode(codes) * np.repeat(scales.astype(np.float64), 128, axis=1)
-        W2d = e4m3_decode(w2[e]) * _expand_blocks(w2_s[e], K, I)
+        W2d = dequant_blocks(w2[e], w2_s[e])
         y = Hd @ W2d.T                                  # [n, K] FP64
         del W2d
         if debug is not None:

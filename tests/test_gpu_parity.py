@@ -1,0 +1,399 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the CPU oracle
+on the same seeded inputs.
+
+Plan and activation codes/scales must be bit-exact; intermediate FP8 codes
+may differ in at most 1e-4 of valid-row codes and only by one value step;
+outputs must reach relative L2 <= 5e-3 and max abs <= 2e-2 * rms (tests/
+parity.py states the bars).  Small cases run the oracle on every token; the
+full-size workloads (the configuration bench.py times included) compare
+sampled tokens, which the oracle evaluates one route at a time.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scale_amd as moe
+from moe_workloads import make_case, CONFIGS, SKEW_ZERO_SCALE_EXPERT
+from oracle import e4m3_encode, plan_ref, quant_act_ref, FLT_MIN
+from oracle.quant import SCALE_FP32, SCALE_UE8M0
+
+from parity import (check_plan, check_tail_untouched, compare_intermediate, compare_output,
+                    host_inputs, log, run_gpu, run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+_WEIGHTS = {}
+
+
+def case_of(name, M=None, ids_dtype=torch.int32):
+    """Workloads generated on the GPU; weights cached per geometry."""
+    c = CONFIGS[name]
+    key = (name,)
+    w = _WEIGHTS.get(key)
+    cs = make_case(name, M=M, device=DEV, ids_dtype=ids_dtype, weights=w)
+    _WEIGHTS[key] = (cs.w13, cs.w13_s, cs.w2, cs.w2_s)
+    return cs
+
+
+def inter_mode_of(flags):
+    return SCALE_UE8M0 if flags & moe.MOE_F_INTER_UE8M0 else SCALE_FP32
+
+
+def full_parity(cs, flags=0, act_mode=SCALE_FP32, out_init=None, tokens=None, label="",
+                code_budget=None, one_step=True):
+    log(f"[parity] {label} {cs.name} M={cs.M} E={cs.E} K={cs.K} I={cs.I} top_k={cs.top_k} "
+        f"bm={cs.block_m} flags={flags:#x} tokens={'all' if tokens is None else len(tokens)}")
+    g = run_gpu(cs, out_init=out_init, flags=flags, act_mode=act_mode)
+    h = host_inputs(cs)
+    o = run_oracle(cs, h=h, out_init=out_init, act_mode=act_mode, inter_mode=inter_mode_of(flags),
+                   tokens=tokens)
+    check_plan(g, o)
+    check_tail_untouched(g, o, cs.block_m)
+    assert np.array_equal(g.x_q, o.x_q), "activation codes differ"
+    assert np.array_equal(g.x_s, o.x_s), "activation scales differ"
+    rows = o.res.row_valid.copy()
+    if tokens is not None:
+        t_of_row = np.where(rows, o.sorted[:o.P] // cs.top_k, -1)
+        rows &= np.isin(t_of_row, np.asarray(tokens))
+    ic = compare_intermediate(g.h_q[:o.P], g.h_s[:o.P], o.res.h_q, o.res.h_s, rows,
+                              one_step=one_step,
+                              **({} if code_budget is None else dict(max_frac=code_budget)))
+    trows = np.nonzero(o.res.computed_tokens)[0]
+    oc = compare_output(g.out[trows], o.res.ref64[trows])
+    log(f"[parity]   ok: P={o.P} inter={ic} out={oc} oracle_s={o.seconds:.2f}")
+    return g, o
+
+
+# ------------------------------------------------------------ primitives
+
+def test_device_e4m3_encoder_matches_oracle():
+    # every sign/exponent/top-11-mantissa pattern with rounding-relevant low bits
+    hi = np.arange(1 << 20, dtype=np.uint64) << np.uint64(12)
+    lows = np.array([0, 1, 0x7FF, 0x800, 0x801, 0xFFF], dtype=np.uint64)
+    bits = (hi[:, None] | lows[None, :]).reshape(-1).astype(np.uint32)
+    rng = np.random.default_rng(0)
+    bits = np.concatenate([bits, rng.integers(0, 2 ** 32, 4_000_000, dtype=np.uint64).astype(np.uint32)])
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)]
+    log(f"[e4m3] {v.size} values")
+    inp = torch.from_numpy(v).to(DEV)
+    out = torch.empty(v.size, dtype=torch.uint8, device=DEV)
+    moe.moe_debug_e4m3_encode(inp, out)
+    got = out.cpu().numpy()
+    want = e4m3_encode(v)
+    bad = got != want
+    assert not bad.any(), f"{bad.sum()} mismatches, e.g. {v[bad][:5]} -> {got[bad][:5]} vs {want[bad][:5]}"
+
+
+# ------------------------------------------------------------------ plan
+
+PLAN_CASES = [
+    ("tiny", None, torch.int32), ("tiny", None, torch.int64), ("decode", None, torch.int32),
+    ("decode", 16, torch.int64), ("page1", 1024, torch.int32), ("page1", 4096, torch.int32),
+    ("page1", 8192, torch.int64), ("skew", None, torch.int32), ("skew", None, torch.int64),
+    ("zipf", None, torch.int32),
+]
+
+
+@pytest.mark.parametrize("name,M,dt", PLAN_CASES)
+def test_plan_bit_exact(name, M, dt):
+    c = CONFIGS[name]
+    M = M or c["M"]
+    from moe_workloads import make_routing
+    ids, _ = make_routing(c["routing"], M, c["E"], c["top_k"], c["seed"], DEV)
+    ids = ids.to(dt).contiguous()
+    log(f"[plan] {name} M={M} {dt}")
+    sc, bc = moe.moe_plan_capacity(M, c["top_k"], c["E"], c["block_m"])
+    s = torch.full((sc,), 0x7F7F7F7F, dtype=torch.int32, device=DEV)
+    x = torch.full((bc,), 0x7F7F7F7F, dtype=torch.int32, device=DEV)
+    p = torch.empty(1, dtype=torch.int32, device=DEV)
+    moe.moe_plan(ids, c["E"], c["block_m"], s, x, p)
+    torch.cuda.synchronize()
+    rs, rx, rP = plan_ref(ids.cpu().numpy(), c["E"], c["block_m"])
+    P = int(p.item())
+    assert P == rP
+    s, x = s.cpu().numpy(), x.cpu().numpy()
+    assert np.array_equal(s[:P], rs) and np.array_equal(x[:P // c["block_m"]], rx)
+    assert np.all(s[P:] == 0x7F7F7F7F) and np.all(x[P // c["block_m"]:] == 0x7F7F7F7F)
+
+
+@pytest.mark.parametrize("M,top_k,E,bm", [(1, 1, 1, 16), (3, 5, 7, 16), (1000, 3, 1, 128),
+                                          (777, 7, 1024, 32), (5000, 13, 64, 64), (64, 1, 3, 256)])
+def test_plan_edge_shapes(M, top_k, E, bm):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M * 31 + E)
+    ids = torch.randint(-2, E + 2, (M, top_k), generator=g, device=DEV, dtype=torch.int32)
+    sc, bc = moe.moe_plan_capacity(M, top_k, E, bm)
+    s = torch.full((sc,), -7, dtype=torch.int32, device=DEV)
+    x = torch.full((bc,), -7, dtype=torch.int32, device=DEV)
+    p = torch.empty(1, dtype=torch.int32, device=DEV)
+    moe.moe_plan(ids, E, bm, s, x, p)
+    torch.cuda.synchronize()
+    rs, rx, rP = plan_ref(ids.cpu().numpy(), E, bm)
+    P = int(p.item())
+    assert P == rP and np.array_equal(s.cpu().numpy()[:P], rs)
+    assert np.array_equal(x.cpu().numpy()[:P // bm], rx)
+
+
+def test_plan_all_masked_and_empty():
+    ids = torch.full((10, 4), -1, dtype=torch.int64, device=DEV)
+    sc, bc = moe.moe_plan_capacity(10, 4, 8, 16)
+    s = torch.empty(sc, dtype=torch.int32, device=DEV)
+    x = torch.empty(bc, dtype=torch.int32, device=DEV)
+    p = torch.full((1,), 99, dtype=torch.int32, device=DEV)
+    moe.moe_plan(ids, 8, 16, s, x, p)
+    torch.cuda.synchronize()
+    assert int(p.item()) == 0
+    ids0 = torch.empty((0, 4), dtype=torch.int32, device=DEV)
+    p.fill_(99)
+    moe.moe_plan(ids0, 8, 16, s, x, p)
+    torch.cuda.synchronize()
+    assert int(p.item()) == 0
+
+
+# ----------------------------------------------------------------- quant
+
+@pytest.mark.parametrize("mode", [SCALE_FP32, SCALE_UE8M0])
+@pytest.mark.parametrize("M,K,ld", [(1, 7168, 7168), (37, 256, 256), (300, 4096, 4104), (2048, 2048, 2048)])
+def test_quant_bit_exact(mode, M, K, ld):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M + K)
+    base = torch.randn((M, ld), generator=g, device=DEV) * torch.exp(
+        torch.randn((M, 1), generator=g, device=DEV) * 3)
+    x = base.to(torch.bfloat16)
+    if M > 3:
+        x[0, :128] = 0.0                                    # all-zero group
+        x[1, :128] = 1e-40                                  # subnormal group
+        x[2, 128:256] = torch.tensor(3.0e38).to(torch.bfloat16)  # huge values
+        x[3, :] = -x[3, :]
+    xv = x[:, :K]
+    log(f"[quant] M={M} K={K} ld={ld} mode={mode}")
+    xq = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((M, K // 128), dtype=torch.float32, device=DEV)
+    moe.moe_quant_act(xv, xq, xs, mode)
+    torch.cuda.synchronize()
+    rq, rs = quant_act_ref(xv.float().cpu().numpy(), mode)
+    assert np.array_equal(xs.cpu().numpy(), rs)
+    assert np.array_equal(xq.cpu().numpy(), rq)
+
+
+# --------------------------------------------------------- whole path
+
+def test_tiny_full():
+    full_parity(case_of("tiny"), label="auto-split")
+
+
+def test_tiny_no_split():
+    full_parity(case_of("tiny"), flags=1 << moe.MOE_F_SPLITK_SHIFT, label="split=1")
+
+
+def test_tiny_accumulates_into_prefilled_output():
+    cs = case_of("tiny")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    init = (torch.randn((cs.M, cs.K), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    full_parity(cs, out_init=init, label="prefilled out")
+
+
+@pytest.mark.parametrize("flags", [0, 1 << moe.MOE_F_SPLITK_SHIFT, 7 << moe.MOE_F_SPLITK_SHIFT])
+def test_decode_full(flags):
+    full_parity(case_of("decode"), flags=flags, label="decode")
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_decode_sweep_full(M):
+    full_parity(case_of("decode", M=M), label="decode sweep")
+
+
+def test_page1_small_full():
+    full_parity(case_of("page1", M=24), label="page1 small")
+
+
+def test_skew_small_full():
+    full_parity(case_of("skew", M=48), label="skew small")
+
+
+E8 = moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0
+
+
+@pytest.mark.parametrize("flags", [moe.MOE_F_INTER_UE8M0, E8])
+def test_zipf_small_full(flags):
+    full_parity(case_of("zipf", M=40), flags=flags, act_mode=SCALE_UE8M0, label="zipf small")
+
+
+def _sample_tokens(M, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    t = set(rng.choice(M, size=min(n, M), replace=False).tolist()) | set(extra)
+    t |= {0, M - 1}
+    return sorted(t)
+
+
+def test_page1_full_size_sampled():
+    """The configuration bench.py times (E=288, K=4096, I=1024, top-8, M=4096)."""
+    cs = case_of("page1")
+    full_parity(cs, tokens=_sample_tokens(cs.M, 8, 1), label="page1 full size")
+
+
+@pytest.mark.parametrize("M", [1024, 8192])
+def test_page1_sweep_sampled(M):
+    cs = case_of("page1", M=M)
+    full_parity(cs, tokens=_sample_tokens(cs.M, 6, M), label="page1 sweep")
+
+
+@pytest.mark.parametrize("dt", [torch.int32, torch.int64])
+def test_skew_full_size_sampled(dt):
+    cs = case_of("skew", ids_dtype=dt)
+    ids = cs.topk_ids.cpu().numpy()
+    masked_tok = int(np.nonzero((ids < 0).any(1))[0][0])
+    zero_tok = int(np.nonzero((ids == SKEW_ZERO_SCALE_EXPERT).any(1))[0][0])
+    full_parity(cs, tokens=_sample_tokens(cs.M, 8, 3, extra=(masked_tok, zero_tok)),
+                label=f"skew full size {dt}")
+
+
+@pytest.mark.parametrize("flags", [moe.MOE_F_INTER_UE8M0, E8])
+def test_zipf_full_size_sampled(flags):
+    cs = case_of("zipf")
+    full_parity(cs, flags=flags, act_mode=SCALE_UE8M0, tokens=_sample_tokens(cs.M, 6, 4),
+                label="zipf full size")
+
+
+# ------------------------------------------------ FP8-MFMA gate/up mode
+# The FP8 MFMA sums each instruction's products about 15 bits below the
+# largest one, so this mode's SwiGLU inputs differ from exact sums by ~1e-5
+# relative, ~1e-3 of the requantised codes move (small values in the E4M3
+# subnormal range by more than one step).  The output bar is the same; the
+# code budget is widened to 1e-2 and the one-step rule is not applied.
+
+FP8_CODE_BUDGET = 1e-2
+
+
+@pytest.mark.parametrize("name,M", [("tiny", None), ("decode", None), ("page1", 24)])
+def test_fp8_gateup_mode(name, M):
+    full_parity(case_of(name, M=M), flags=moe.MOE_F_FP8_GATEUP, label="fp8 gate/up",
+                code_budget=FP8_CODE_BUDGET, one_step=False)
+
+
+def test_fp8_gateup_mode_full_size_sampled():
+    cs = case_of("page1")
+    full_parity(cs, flags=moe.MOE_F_FP8_GATEUP, tokens=_sample_tokens(cs.M, 6, 11),
+                label="fp8 gate/up page1 full size", code_budget=FP8_CODE_BUDGET, one_step=False)
+
+
+def test_zipf_fp8_gateup_e8m0_full_size_sampled():
+    cs = case_of("zipf")
+    full_parity(cs, flags=E8 | moe.MOE_F_FP8_GATEUP, act_mode=SCALE_UE8M0,
+                tokens=_sample_tokens(cs.M, 6, 12), label="zipf fp8 gate/up e8m0",
+                code_budget=FP8_CODE_BUDGET, one_step=False)
+
+
+# ------------------------------------------------------------ contracts
+
+@pytest.mark.parametrize("fp8_gateup", [False, True])
+def test_e8m0_matches_fp32_scale_kernels(fp8_gateup):
+    """Power-of-two scales: the E8M0-in-MFMA kernels and the FP32-scale
+    kernels see identical inputs and must agree to the parity bars."""
+    cs = case_of("zipf", M=512)
+    fl = moe.MOE_F_INTER_UE8M0 | (moe.MOE_F_FP8_GATEUP if fp8_gateup else 0)
+    a = run_gpu(cs, flags=fl, act_mode=SCALE_UE8M0)
+    b = run_gpu(cs, flags=fl | moe.MOE_F_MMA_E8M0, act_mode=SCALE_UE8M0)
+    assert a.P == b.P and np.array_equal(a.sorted[:a.P], b.sorted[:b.P])
+    rows = (a.sorted[:a.P] < cs.M * cs.top_k)
+    st = compare_intermediate(b.h_q[:a.P], b.h_s[:a.P], a.h_q[:a.P], a.h_s[:a.P], rows,
+                              one_step=not fp8_gateup)
+    if not fp8_gateup:   # same exact gate/up kernel on both sides
+        assert st["mismatched"] == 0
+    compare_output(b.out, a.out)
+
+
+def test_truncated_extent():
+    """num_tokens_post_padded = block_m: only the first block is computed and
+    every block past it exits untouched."""
+    cs = case_of("tiny")
+    g = run_gpu(cs, ntp_override=cs.block_m)
+    o = run_oracle(cs, P_override=cs.block_m)
+    check_plan(g, o)
+    bm = cs.block_m
+    assert o.res.h_q.shape[0] == bm
+    compare_intermediate(g.h_q[:bm], g.h_s[:bm], o.res.h_q, o.res.h_s, o.res.row_valid)
+    # rows beyond the truncated extent keep the workspace fill
+    assert g.P > bm and np.all(g.h_q[bm:g.P] == 0x5A)
+    compare_output(g.out, o.res.ref64)
+
+
+def test_two_calls_accumulate():
+    cs = case_of("decode", M=4)
+    b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, 0, DEV)
+    out = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
+    for _ in range(2):
+        moe.moe_layer(b, cs.x, cs.topk_ids, cs.topk_weights, cs.w13, cs.w13_s, cs.w2, cs.w2_s, out)
+    torch.cuda.synchronize()
+    o = run_oracle(cs)
+    compare_output(out.float().cpu().numpy(), 2 * o.res.ref64)
+
+
+def test_all_routes_masked_leaves_output_unchanged():
+    cs = case_of("tiny")
+    cs.topk_ids = torch.full_like(cs.topk_ids, -1)
+    init = torch.randn((cs.M, cs.K), device=DEV).to(torch.bfloat16)
+    g = run_gpu(cs, out_init=init)
+    assert g.P == 0
+    assert np.array_equal(g.out, init.float().cpu().numpy())
+
+
+def test_zero_scale_expert_contributes_zero():
+    cs = case_of("skew", M=64)
+    ids = cs.topk_ids.clone()
+    g = run_gpu(cs)
+    masked = case_of("skew", M=64)
+    mids = ids.clone()
+    mids[mids == SKEW_ZERO_SCALE_EXPERT] = -1
+    masked.topk_ids = mids
+    gm = run_gpu(masked)
+    compare_output(g.out, gm.out)
+    # that expert's rows requantise an all-zero h: codes 0, scale FLT_MIN
+    rows = [p for p in range(g.P) if g.expert_ids[p // cs.block_m] == SKEW_ZERO_SCALE_EXPERT
+            and g.sorted[p] < cs.M * cs.top_k]
+    assert rows
+    assert np.all(g.h_q[rows] & 0x7F == 0) and np.all(g.h_s[rows] == FLT_MIN)
+    assert np.all(np.isfinite(g.out))
+
+
+def test_int32_int64_ids_agree():
+    a = run_gpu(case_of("skew", M=256, ids_dtype=torch.int32))
+    b = run_gpu(case_of("skew", M=256, ids_dtype=torch.int64))
+    assert a.P == b.P and np.array_equal(a.sorted, b.sorted)
+    assert np.array_equal(a.h_q, b.h_q) and np.array_equal(a.h_s, b.h_s)
+    compare_output(b.out, a.out)
+
+
+def test_repeat_runs_bit_identical_codes():
+    cs = case_of("page1", M=256)
+    a = run_gpu(cs)
+    b = run_gpu(cs)
+    assert np.array_equal(a.sorted, b.sorted) and np.array_equal(a.x_q, b.x_q)
+    rows = a.sorted[:a.P] < cs.M * cs.top_k
+    assert np.array_equal(a.h_q[:a.P][rows], b.h_q[:b.P][rows])
+    compare_output(b.out, a.out)
+
+
+def test_m_zero_is_a_no_op():
+    b = moe.MoeLayerBuffers(0, 256, 256, 8, 2, 16, 0, DEV)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+    w = torch.empty((0, 2), dtype=torch.float32, device=DEV)
+    cs = case_of("tiny")
+    out = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    moe.moe_layer(b, x, ids, w, cs.w13, cs.w13_s, cs.w2, cs.w2_s, out)
+    torch.cuda.synchronize()
+    assert int(b.ntp.item()) == 0

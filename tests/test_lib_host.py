@@ -1,0 +1,129 @@
+"""Library loads, exports every symbol include/moe_fp8.h declares, and its host
+validation rejects bad arguments before launching anything (CPU only: no
+call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe_fp8.h")
+
+import fp8_block_scale_amd as moe  # noqa: E402
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe_fp8.h but not exported"
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_no_internal_symbols_exported():
+    # the library is built with hidden visibility: only the C ABI is public
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in ("launch_plan", "_ZN3moe11launch_planEPKvbliiiPiS2_S2_P12ihipStream_t"):
+        assert not hasattr(lib, n)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert moe.moe_status_str(s).startswith(moe.STATUS_NAMES[s])
+
+
+def test_plan_capacity_values():
+    assert moe.moe_plan_capacity(4, 2, 8, 16) == (128, 8)
+    assert moe.moe_plan_capacity(1, 9, 257, 16) == (144, 9)
+    assert moe.moe_plan_capacity(4096, 8, 288, 64) == (50944, 796)
+    assert moe.moe_plan_capacity(2048, 10, 512, 64) == (52736, 824)
+    assert moe.moe_plan_capacity(8192, 8, 288, 128) == (102144, 798)
+    assert moe.moe_plan_capacity(0, 8, 288, 128) == (0, 0)
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+
+
+def _raw(name):
+    return moe._c[name]
+
+
+def _err(st):
+    return moe.STATUS_NAMES[st]
+
+
+def test_plan_validation():
+    f = _raw("moe_plan")
+    args = dict(ids=FAKE, dt=0, M=4, k=2, E=8, bm=16, s=FAKE, sc=128, x=FAKE, bc=8, p=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["ids"], a["dt"], a["M"], a["k"], a["E"], a["bm"], a["s"], a["sc"], a["x"],
+                 a["bc"], a["p"], None, 0, None)
+
+    assert _err(call(sc=127)) == "MOE_ERR_CAPACITY"
+    assert _err(call(bc=7)) == "MOE_ERR_CAPACITY"
+    assert _err(call(sc=128, bc=9)) == "MOE_ERR_CAPACITY"     # sorted_cap < blocks_cap * block_m
+    assert _err(call(dt=2)) == "MOE_ERR_SHAPE"
+    assert _err(call(E=0)) == "MOE_ERR_SHAPE"
+    assert _err(call(E=1025)) == "MOE_ERR_UNSUPPORTED"
+    assert _err(call(bm=257)) == "MOE_ERR_UNSUPPORTED"
+    assert _err(call(M=-1)) == "MOE_ERR_SHAPE"
+    assert _err(call(p=None)) == "MOE_ERR_NULL"
+    assert _err(call(ids=None)) == "MOE_ERR_NULL"
+    assert _err(call(M=1 << 28, k=8)) == "MOE_ERR_SHAPE"     # R overflows int32
+    assert "capacity" in moe.moe_last_error() or "int32" in moe.moe_last_error()
+
+
+def test_quant_validation():
+    f = _raw("moe_quant_act")
+    assert _err(f(FAKE, 4, 100, 100, FAKE, FAKE, 0, None)) == "MOE_ERR_SHAPE"    # K % 128
+    assert _err(f(FAKE, 4, 256, 128, FAKE, FAKE, 0, None)) == "MOE_ERR_SHAPE"    # ld < K
+    assert _err(f(FAKE, 4, 256, 260, FAKE, FAKE, 0, None)) == "MOE_ERR_ALIGN"    # ld % 8
+    assert _err(f(ctypes.c_void_p(0x10008), 4, 256, 256, FAKE, FAKE, 0, None)) == "MOE_ERR_ALIGN"
+    assert _err(f(FAKE, 4, 256, 256, FAKE, FAKE, 7, None)) == "MOE_ERR_SHAPE"    # scale mode
+    assert _err(f(None, 4, 256, 256, FAKE, FAKE, 0, None)) == "MOE_ERR_NULL"
+    assert _err(f(None, 0, 256, 256, None, None, 0, None)) == "MOE_OK"           # M = 0: no work
+
+
+def test_experts_validation():
+    f = _raw("moe_fp8_experts")
+    base = dict(M=4, K=256, I=256, E=8, k=2, bm=16, sc=128, fl=0, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["M"], a["K"], a["I"],
+                 a["E"], a["k"], a["bm"], a["sc"], a["fl"], FAKE, a["ws"], a["wsb"], None)
+
+    assert _err(call(K=200)) == "MOE_ERR_SHAPE"
+    assert _err(call(I=100)) == "MOE_ERR_SHAPE"
+    assert _err(call(bm=8)) == "MOE_ERR_UNSUPPORTED"
+    assert _err(call(bm=48)) == "MOE_ERR_UNSUPPORTED"
+    assert _err(call(sc=120)) == "MOE_ERR_SHAPE"
+    assert _err(call(fl=moe.MOE_F_MMA_E8M0)) == "MOE_ERR_SHAPE"
+    assert _err(call(fl=1 << 20)) == "MOE_ERR_SHAPE"
+    assert _err(call(wsb=16)) == "MOE_ERR_CAPACITY"
+    assert _err(call(ws=None)) == "MOE_ERR_NULL"
+    assert _err(call(ws=ctypes.c_void_p(0x10010))) == "MOE_ERR_ALIGN"
+    assert _err(call(M=0)) == "MOE_OK"
+
+
+def test_workspace_size_monotone_and_layout():
+    a = moe.moe_fp8_experts_workspace_size(4096, 4096, 1024, 288, 8, 64, 50944)
+    b = moe.moe_fp8_experts_workspace_size(8192, 4096, 1024, 288, 8, 64, 83712)
+    assert 0 < a < b
+    hq, hs = moe.moe_fp8_experts_workspace_layout(4096, 4096, 1024, 288, 8, 64, 50944)
+    assert hq % 256 == 0 and hs % 256 == 0 and hs >= hq + 50944 * 1024
+    # forcing a split-K factor grows the workspace by the partial sums
+    s1 = moe.moe_fp8_experts_workspace_size(4, 256, 256, 8, 2, 16, 128, 1 << 8)
+    s2 = moe.moe_fp8_experts_workspace_size(4, 256, 256, 8, 2, 16, 128, 2 << 8)
+    assert s2 > s1
