@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed FP8 W8A8 block-scale MoE expert path on one MI355X.
+
+One step = the whole hot path over one batch: routing plan, activation
+quantisation, gate/up GEMM + SwiGLU + requantisation, down GEMM + weighted
+reduce-add into the BF16 output -- all HIP kernels of libmoe_fp8 through its
+C ABI, on one stream, with every input already resident in HBM.
+
+Default workload: E=288 experts, hidden K=4096, intermediate I=1024, top-8,
+M=4096 tokens, block_m=64 (synthetic, seeded; weights N(0, 0.02^2) stored as
+E4M3 with 128x128 FP32 block scales).  Prints one JSON line:
+  value        FP8-path TFLOP/s = 2 * valid_routes * 3 * K * I / step time
+  ms_per_step  milliseconds per layer call (all five steps)
+  roofline     the dominant kernel (gate/up) against HBM bandwidth, timed
+               with HIP events on its own stream inside the timed region
+  cpu_baseline the CPU oracle on a bounded sample of the same batch
+
+Runs on a single GPU only; --gpus N > 1 exits with a message.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer + FP8 TFLOPS (HBM GB/s at small M), E288 H4096 I1024 top8"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+FP16_MFMA_PEAK = 2500.0         # TFLOP/s dense
+FP8_MFMA_PEAK = 5000.0          # TFLOP/s dense
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="page1",
+                    choices=["tiny", "decode", "page1", "skew", "zipf"])
+    ap.add_argument("--M", type=int, default=None, help="override the token count")
+    ap.add_argument("--fp8-gateup", action="store_true",
+                    help="gate/up on the FP8 MFMA (MOE_F_FP8_GATEUP)")
+    ap.add_argument("--e8m0", action="store_true",
+                    help="power-of-two scales inside the FP8 MFMA (zipf workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(case, n_touched, R_valid, P, n_tok):
+    """Bytes each stage must move at least once (see the layout notes of the
+    library): touched expert weights and scales, activations once per token,
+    intermediate rows once per valid route, the plan, and the BF16 output
+    read-modify-write."""
+    K, I, M = case.K, case.I, case.M
+    w13 = n_touched * (2 * I * K + (2 * I // 128) * (K // 128) * 4)
+    w2 = n_touched * (K * I + (K // 128) * (I // 128) * 4)
+    xq = n_tok * (K + (K // 128) * 4)
+    h = R_valid * (I + (I // 128) * 4)
+    plan = P * 4 + (P // case.block_m) * 4
+    gate_up = w13 + xq + h + plan
+    down = w2 + h + plan + R_valid * 4 + 2 * M * K * 2
+    layer = w13 + w2 + xq + R_valid * 4 + plan + 2 * M * K * 2
+    return dict(gate_up=gate_up, down=down, layer=layer)
+
+
+def cpu_baseline(case, n_tokens):
+    """The CPU oracle (plain numpy, FP64 dot products) on the first n_tokens
+    tokens of the same batch; reported in the metric's unit."""
+    import numpy as np
+    from oracle import experts_ref, plan_ref, quant_act_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    h = dict(x=case.x[:n_tokens].float().cpu().numpy(), ids=case.topk_ids.cpu().numpy(),
+             w=case.topk_weights.cpu().numpy(), w13=case.w13.cpu().numpy(),
+             w13_s=case.w13_s.cpu().numpy(), w2=case.w2.cpu().numpy(), w2_s=case.w2_s.cpu().numpy())
+    t0 = time.perf_counter()
+    s, e, P = plan_ref(h["ids"], case.E, case.block_m)
+    xq, xs = quant_act_ref(h["x"])
+    xq_full = np.zeros((case.M, case.K), np.uint8)
+    xs_full = np.zeros((case.M, case.K // 128), np.float32)
+    xq_full[:n_tokens], xs_full[:n_tokens] = xq, xs
+    experts_ref(xq_full, xs_full, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"], s, e, P,
+                case.top_k, case.block_m, tokens=range(n_tokens))
+    dt = time.perf_counter() - t0
+    ids = h["ids"][:n_tokens]
+    routes = int(((ids >= 0) & (ids < case.E)).sum())
+    flops = 2.0 * routes * 3 * case.K * case.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_tokens} of {case.M} tokens ({routes} routes, all five steps, "
+                      f"{dt:.1f} s wall, numpy FP64 BLAS)",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the expert path is benchmarked per GPU and its sharding is described, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_block_scale_amd as moe
+    from moe_workloads import make_case
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.time()
+    case = make_case(args.workload, M=args.M, device=dev)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    flags = 0
+    act_mode = moe.MOE_SCALE_FP32
+    if case.pow2:
+        flags |= moe.MOE_F_INTER_UE8M0
+        act_mode = moe.MOE_SCALE_UE8M0
+        if args.e8m0:
+            flags |= moe.MOE_F_MMA_E8M0
+    if args.fp8_gateup:
+        flags |= moe.MOE_F_FP8_GATEUP
+
+    b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
+    out = torch.zeros((case.M, case.K), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_plan(case.topk_ids, case.E, case.block_m, b.sorted_ids, b.expert_ids, b.ntp,
+                     b.plan_ws, stream)
+        moe.moe_quant_act(case.x, b.x_q, b.x_s, act_mode, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_fp8_gate_up(b.x_q, b.x_s, case.w13, case.w13_s, b.sorted_ids, b.expert_ids, b.ntp,
+                            case.top_k, case.block_m, b.workspace, flags, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.moe_fp8_down_reduce(case.w2, case.w2_s, case.topk_weights, b.sorted_ids, b.expert_ids,
+                                b.ntp, case.top_k, case.block_m, out, b.workspace, flags, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+    plan_quant = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    gate_up = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    down = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    ids = case.topk_ids
+    valid = (ids >= 0) & (ids < case.E)
+    R_valid = int(valid.sum())
+    n_touched = int(torch.unique(ids[valid]).numel())
+    P = int(b.ntp.item())
+    flops = 2.0 * R_valid * 3 * case.K * case.I
+    nb = algorithmic_bytes(case, n_touched, R_valid, P, case.M)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gu_gbs = nb["gate_up"] / (gate_up * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{case.name}: E={case.E} K={case.K} I={case.I} top_k={case.top_k} "
+                        f"M={case.M} block_m={case.block_m}",
+            "M": case.M, "E": case.E, "K": case.K, "I": case.I, "top_k": case.top_k,
+            "block_m": case.block_m, "flags": flags, "valid_routes": R_valid,
+            "touched_experts": n_touched, "padded_rows": P,
+        },
+        "stages_ms": {"plan_quant": round(plan_quant, 4), "gate_up": round(gate_up, 4),
+                      "down_reduce": round(down, 4)},
+        "layer_GBs": round(nb["layer"] / (ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "kernel": "gateup_kernel",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": nb["gate_up"],
+            "avg_ms": round(gate_up, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_tokens, case.M))
+    print(f"# generated inputs in {t_gen:.1f} s", file=sys.stderr)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

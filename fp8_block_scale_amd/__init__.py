@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 
 EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_quant_act",
             "moe_fp8_experts_workspace_size", "moe_fp8_experts_workspace_layout",
-            "moe_fp8_experts", "moe_status_str", "moe_last_error", "moe_debug_e4m3_encode")
+            "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
+            "moe_last_error", "moe_debug_e4m3_encode")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +70,10 @@ _c = {
     "moe_fp8_experts": _proto("moe_fp8_experts", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp, _sz,
                               _vp),
+    "moe_fp8_gate_up": _proto("moe_fp8_gate_up", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                              _i64, _i32, _i32, _i32, _i64, _u32, _vp, _sz, _vp),
+    "moe_fp8_down_reduce": _proto("moe_fp8_down_reduce", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                  _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp, _sz, _vp),
     "moe_status_str": _proto("moe_status_str", ctypes.c_char_p, _i32),
     "moe_last_error": _proto("moe_last_error", ctypes.c_char_p),
     "moe_debug_e4m3_encode": _proto("moe_debug_e4m3_encode", _i32, _vp, _vp, _i64, _vp),
@@ -172,6 +177,32 @@ def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_i
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)),
            "moe_fp8_experts")
+
+
+def moe_fp8_gate_up(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                    top_k, block_m, workspace, flags=0, stream=None):
+    """Steps 3-4 into the workspace (see MoeLayerBuffers.intermediate)."""
+    M, K = x_q.shape
+    E, twoI, _ = w13.shape
+    _check(_c["moe_fp8_gate_up"](_ptr(x_q), _ptr(x_s), _ptr(w13), _ptr(w13_s), _ptr(sorted_token_ids),
+                                 _ptr(expert_ids), _ptr(num_tokens_post_padded), M, K, twoI // 2, E,
+                                 top_k, block_m, sorted_token_ids.numel(), flags, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_fp8_gate_up")
+
+
+def moe_fp8_down_reduce(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+                        num_tokens_post_padded, top_k, block_m, out_bf16, workspace, flags=0,
+                        stream=None):
+    """Step 5: out_bf16 += weighted down projections of the workspace rows."""
+    E, K, I = w2.shape
+    M = out_bf16.shape[0]
+    _check(_c["moe_fp8_down_reduce"](_ptr(w2), _ptr(w2_s), _ptr(topk_weights), _ptr(sorted_token_ids),
+                                     _ptr(expert_ids), _ptr(num_tokens_post_padded), M, K, I, E,
+                                     top_k, block_m, sorted_token_ids.numel(), flags,
+                                     _ptr(out_bf16), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_fp8_down_reduce")
 
 
 def moe_status_str(status):

@@ -65,7 +65,7 @@ SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t nkb, uint32
 
 struct WsLayout {
     size_t hq, hs, acc, cnt, part, total;
-    size_t zero_words;                // acc + counters, zeroed per call
+    size_t cnt_words;                 // split-K counters, zeroed per call
     SplitChoice sp;
 };
 
@@ -81,11 +81,11 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t block_m, int64_t sor
     l.hs = off;
     off = align256(off + (size_t)sorted_cap * (I / 128) * 4);
     l.acc = off;
-    off += (size_t)M * K * 4;
+    off = align256(off + (size_t)M * K * 4);
     l.cnt = off;
     size_t ntiles = (size_t)blocks_cap * jtiles;
-    off = align256(off + (l.sp.nsplit > 1 ? ntiles * 4 : 0));
-    l.zero_words = (off - l.acc) / 4;
+    l.cnt_words = l.sp.nsplit > 1 ? ntiles : 0;
+    off = align256(off + l.cnt_words * 4);
     l.part = off;
     if (l.sp.nsplit > 1) off = align256(off + ntiles * l.sp.nsplit * block_m * 256 * 4);
     l.total = off;
@@ -225,40 +225,50 @@ MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_
     return MOE_OK;
 }
 
-MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
-                                   const float *w13_s, const uint8_t *w2, const float *w2_s,
-                                   const float *topk_weights, const int32_t *sorted_token_ids,
-                                   const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
-                                   int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
-                                   int32_t block_m, int64_t sorted_cap, uint32_t flags,
-                                   void *out_bf16, void *workspace, size_t workspace_bytes,
-                                   void *stream) {
+namespace {
+
+// Validation shared by the expert-stage entry points.
+moe_status check_stage(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, int32_t block_m,
+                       int64_t sorted_cap, uint32_t flags, const void *workspace,
+                       size_t workspace_bytes, WsLayout *l) {
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
     const uint32_t known = MOE_F_INTER_UE8M0 | MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_SPLITK_MASK;
     if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     if ((flags & MOE_F_MMA_E8M0) && !(flags & MOE_F_INTER_UE8M0))
         return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
+    *l = ws_layout(M, K, I, block_m, sorted_cap, flags);
     if (M == 0 || sorted_cap == 0) return MOE_OK;
-    if (!x_q || !x_s || !w13 || !w13_s || !w2 || !w2_s || !topk_weights || !sorted_token_ids ||
-        !expert_ids || !num_tokens_post_padded || !out_bf16 || !workspace)
-        return fail(MOE_ERR_NULL, "all tensor arguments and the workspace are required");
-    if (!aligned16(x_q) || !aligned16(w13) || !aligned16(w2) || !aligned16(out_bf16) ||
-        ((uintptr_t)workspace & 255u) != 0)
-        return fail(MOE_ERR_ALIGN, "x_q, w13, w2, out must be 16-byte and workspace 256-byte aligned");
-    WsLayout l = ws_layout(M, K, I, block_m, sorted_cap, flags);
-    if (workspace_bytes < l.total)
-        return fail(MOE_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
+    if (!workspace) return fail(MOE_ERR_NULL, "workspace is required");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < l->total)
+        return fail(MOE_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, l->total);
+    return MOE_OK;
+}
 
+}  // namespace
+
+MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                                   const float *w13_s, const int32_t *sorted_token_ids,
+                                   const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
+                                   int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                                   int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    WsLayout l;
+    moe_status st = check_stage(M, K, I, E, top_k, block_m, sorted_cap, flags, workspace,
+                                workspace_bytes, &l);
+    if (st != MOE_OK || M == 0 || sorted_cap == 0) return st;
+    if (!x_q || !x_s || !w13 || !w13_s || !sorted_token_ids || !expert_ids || !num_tokens_post_padded)
+        return fail(MOE_ERR_NULL, "x_q, x_s, w13, w13_s and the plan are required");
+    if (!aligned16(x_q) || !aligned16(w13))
+        return fail(MOE_ERR_ALIGN, "x_q and w13 must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
-    const int64_t blocks_cap = sorted_cap / block_m;
-    const bool e8m0 = (flags & MOE_F_MMA_E8M0) != 0;
-
-    st = hip_check(moe::launch_fill_zero((uint32_t *)(ws + l.acc), l.zero_words, s),
-                   "moe_fp8_experts: clear reduction buffer");
-    if (st != MOE_OK) return st;
-
+    if (l.sp.nsplit > 1) {
+        st = hip_check(moe::launch_fill_zero((uint32_t *)(ws + l.cnt), l.cnt_words, s),
+                       "moe_fp8_gate_up: clear split-K counters");
+        if (st != MOE_OK) return st;
+    }
     moe::GateUpArgs ga;
     ga.xq = x_q;
     ga.xs = x_s;
@@ -278,15 +288,36 @@ MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const u
     ga.top_k = top_k;
     ga.nkb = (int)(K / 128);
     ga.jtiles = (int)(I / 128);
-    ga.nblocks = (int)blocks_cap;
+    ga.nblocks = (int)(sorted_cap / block_m);
     ga.nsplit = l.sp.nsplit;
     ga.kb_per_split = l.sp.kb_per_split;
     ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
-    const bool fp8_gateup = (flags & MOE_F_FP8_GATEUP) != 0;
-    st = hip_check(moe::launch_gateup(ga, block_m, fp8_gateup, e8m0, s),
-                   "moe_fp8_experts: gate/up launch");
-    if (st != MOE_OK) return st;
+    return hip_check(moe::launch_gateup(ga, block_m, (flags & MOE_F_FP8_GATEUP) != 0,
+                                        (flags & MOE_F_MMA_E8M0) != 0, s),
+                     "moe_fp8_gate_up: launch");
+}
 
+MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
+                                       const float *topk_weights, const int32_t *sorted_token_ids,
+                                       const int32_t *expert_ids,
+                                       const int32_t *num_tokens_post_padded, int64_t M, int64_t K,
+                                       int64_t I, int32_t E, int32_t top_k, int32_t block_m,
+                                       int64_t sorted_cap, uint32_t flags, void *out_bf16,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+    WsLayout l;
+    moe_status st = check_stage(M, K, I, E, top_k, block_m, sorted_cap, flags, workspace,
+                                workspace_bytes, &l);
+    if (st != MOE_OK || M == 0 || sorted_cap == 0) return st;
+    if (!w2 || !w2_s || !topk_weights || !sorted_token_ids || !expert_ids ||
+        !num_tokens_post_padded || !out_bf16)
+        return fail(MOE_ERR_NULL, "w2, w2_s, topk_weights, the plan and out are required");
+    if (!aligned16(w2) || !aligned16(out_bf16))
+        return fail(MOE_ERR_ALIGN, "w2 and out must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = (uint8_t *)workspace;
+    st = hip_check(moe::launch_fill_zero((uint32_t *)(ws + l.acc), (size_t)M * K, s),
+                   "moe_fp8_down_reduce: clear reduction buffer");
+    if (st != MOE_OK) return st;
     moe::DownArgs da;
     da.hq = ws + l.hq;
     da.hs = (const float *)(ws + l.hs);
@@ -304,10 +335,37 @@ MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const u
     da.top_k = top_k;
     da.njb = (int)(I / 128);
     da.ctiles = (int)((K + 255) / 256);
-    da.nblocks = (int)blocks_cap;
-    st = hip_check(moe::launch_down(da, block_m, e8m0, s), "moe_fp8_experts: down launch");
+    da.nblocks = (int)(sorted_cap / block_m);
+    st = hip_check(moe::launch_down(da, block_m, (flags & MOE_F_MMA_E8M0) != 0, s),
+                   "moe_fp8_down_reduce: down launch");
     if (st != MOE_OK) return st;
-
     return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const float *)(ws + l.acc), M * K, s),
-                     "moe_fp8_experts: finalize launch");
+                     "moe_fp8_down_reduce: finalize launch");
+}
+
+MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                                   const float *w13_s, const uint8_t *w2, const float *w2_s,
+                                   const float *topk_weights, const int32_t *sorted_token_ids,
+                                   const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
+                                   int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                                   int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                                   void *out_bf16, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    // validate everything before enqueuing anything
+    WsLayout l;
+    moe_status st = check_stage(M, K, I, E, top_k, block_m, sorted_cap, flags, workspace,
+                                workspace_bytes, &l);
+    if (st != MOE_OK || M == 0 || sorted_cap == 0) return st;
+    if (!x_q || !x_s || !w13 || !w13_s || !w2 || !w2_s || !topk_weights || !sorted_token_ids ||
+        !expert_ids || !num_tokens_post_padded || !out_bf16)
+        return fail(MOE_ERR_NULL, "all tensor arguments and the workspace are required");
+    if (!aligned16(x_q) || !aligned16(w13) || !aligned16(w2) || !aligned16(out_bf16))
+        return fail(MOE_ERR_ALIGN, "x_q, w13, w2 and out must be 16-byte aligned");
+    st = moe_fp8_gate_up(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                         M, K, I, E, top_k, block_m, sorted_cap, flags, workspace, workspace_bytes,
+                         stream);
+    if (st != MOE_OK) return st;
+    return moe_fp8_down_reduce(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+                               num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap,
+                               flags, out_bf16, workspace, workspace_bytes, stream);
 }

@@ -185,6 +185,31 @@ moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s,
                            void *out_bf16, void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/* The two stages of moe_fp8_experts, for callers that schedule them
+ * separately (moe_fp8_experts = moe_fp8_gate_up then moe_fp8_down_reduce on
+ * one stream, same workspace and flags):
+ *   moe_fp8_gate_up      steps 3-4: writes the requantised SwiGLU rows h_q and
+ *                        their scales h_s into the workspace;
+ *   moe_fp8_down_reduce  step 5: reads them, adds the weighted down
+ *                        projections into out_bf16.
+ * Arguments, constraints and errors as for moe_fp8_experts. */
+moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s,
+                           const uint8_t *w13, const float *w13_s,
+                           const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                           const int32_t *num_tokens_post_padded,
+                           int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                           int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
+                               const float *topk_weights,
+                               const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                               const int32_t *num_tokens_post_padded,
+                               int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                               int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                               void *out_bf16, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* ------------------------------------------------------------ utilities -- */
 
 const char *moe_status_str(moe_status s);
