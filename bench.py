@@ -48,6 +48,9 @@ def parse():
                     help="power-of-two scales inside the FP8 MFMA (zipf workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before warm-up (a known-size "
+                         "kernel to scale HBM byte counters against)")
     return ap.parse_args()
 
 
@@ -150,6 +153,14 @@ def main():
                                 b.ntp, case.top_k, case.block_m, out, b.workspace, flags, stream)
         if ev is not None:
             ev[3].record(stream)
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -64,13 +64,13 @@ SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t nkb, uint32
 }
 
 struct WsLayout {
-    size_t hq, hs, acc, cnt, part, total;
+    size_t hq, hs, y, rpos, cnt, part, total;
     size_t cnt_words;                 // split-K counters, zeroed per call
     SplitChoice sp;
 };
 
-WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t block_m, int64_t sorted_cap,
-                   uint32_t flags) {
+WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block_m,
+                   int64_t sorted_cap, uint32_t flags) {
     WsLayout l;
     int64_t blocks_cap = sorted_cap / block_m;
     int64_t jtiles = I / 128;
@@ -80,8 +80,11 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t block_m, int64_t sor
     off = align256(off + (size_t)sorted_cap * I);
     l.hs = off;
     off = align256(off + (size_t)sorted_cap * (I / 128) * 4);
-    l.acc = off;
-    off = align256(off + (size_t)M * K * 4);
+    const size_t R = (size_t)M * top_k;
+    l.y = off;
+    off = align256(off + R * K * 4);
+    l.rpos = off;
+    off = align256(off + R * 4);
     l.cnt = off;
     size_t ntiles = (size_t)blocks_cap * jtiles;
     l.cnt_words = l.sp.nsplit > 1 ? ntiles : 0;
@@ -209,7 +212,7 @@ MOE_API size_t moe_fp8_experts_workspace_size(int64_t M, int64_t K, int64_t I, i
                                               int32_t top_k, int32_t block_m, int64_t sorted_cap,
                                               uint32_t flags) {
     if (check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap) != MOE_OK) return 0;
-    return ws_layout(M, K, I, block_m, sorted_cap, flags).total;
+    return ws_layout(M, K, I, top_k, block_m, sorted_cap, flags).total;
 }
 
 MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int32_t E,
@@ -219,7 +222,7 @@ MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
     if (!h_q_offset || !h_s_offset) return fail(MOE_ERR_NULL, "output pointer is NULL");
-    WsLayout l = ws_layout(M, K, I, block_m, sorted_cap, flags);
+    WsLayout l = ws_layout(M, K, I, top_k, block_m, sorted_cap, flags);
     *h_q_offset = l.hq;
     *h_s_offset = l.hs;
     return MOE_OK;
@@ -237,7 +240,7 @@ moe_status check_stage(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k
     if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     if ((flags & MOE_F_MMA_E8M0) && !(flags & MOE_F_INTER_UE8M0))
         return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
-    *l = ws_layout(M, K, I, block_m, sorted_cap, flags);
+    *l = ws_layout(M, K, I, top_k, block_m, sorted_cap, flags);
     if (M == 0 || sorted_cap == 0) return MOE_OK;
     if (!workspace) return fail(MOE_ERR_NULL, "workspace is required");
     if (((uintptr_t)workspace & 255u) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -264,6 +267,9 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
         return fail(MOE_ERR_ALIGN, "x_q and w13 must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
+    st = hip_check(moe::launch_fill((uint32_t *)(ws + l.rpos), (size_t)M * top_k, 0xffffffffu, s),
+                   "moe_fp8_gate_up: clear route map");
+    if (st != MOE_OK) return st;
     if (l.sp.nsplit > 1) {
         st = hip_check(moe::launch_fill_zero((uint32_t *)(ws + l.cnt), l.cnt_words, s),
                        "moe_fp8_gate_up: clear split-K counters");
@@ -281,6 +287,7 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.hs = (float *)(ws + l.hs);
     ga.part = (float *)(ws + l.part);
     ga.cnt = (uint32_t *)(ws + l.cnt);
+    ga.rpos = (int32_t *)(ws + l.rpos);
     ga.K = K;
     ga.I = I;
     ga.R = M * top_k;
@@ -315,9 +322,6 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
         return fail(MOE_ERR_ALIGN, "w2 and out must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
-    st = hip_check(moe::launch_fill_zero((uint32_t *)(ws + l.acc), (size_t)M * K, s),
-                   "moe_fp8_down_reduce: clear reduction buffer");
-    if (st != MOE_OK) return st;
     moe::DownArgs da;
     da.hq = ws + l.hq;
     da.hs = (const float *)(ws + l.hs);
@@ -327,7 +331,7 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
     da.sorted = sorted_token_ids;
     da.eids = expert_ids;
     da.ntp = num_tokens_post_padded;
-    da.acc = (float *)(ws + l.acc);
+    da.y = (float *)(ws + l.y);
     da.K = K;
     da.I = I;
     da.R = M * top_k;
@@ -339,7 +343,8 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
     st = hip_check(moe::launch_down(da, block_m, (flags & MOE_F_MMA_E8M0) != 0, s),
                    "moe_fp8_down_reduce: down launch");
     if (st != MOE_OK) return st;
-    return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const float *)(ws + l.acc), M * K, s),
+    return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const float *)(ws + l.y),
+                                          (const int32_t *)(ws + l.rpos), M, K, top_k, s),
                      "moe_fp8_down_reduce: finalize launch");
 }
 

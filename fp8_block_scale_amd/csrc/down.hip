@@ -7,9 +7,10 @@
 //   y[p, c] = sum_jb h_s[p, jb] * w2_s[e, c / 128, jb]
 //                    * sum_{j in jb} h_q[p, j] * W2[e, c, j]           (FP32)
 //   out[t, c] += topk_weights[r] * y[p, c]
-// The route sum is accumulated in FP32 (device atomics into a workspace
-// buffer) and rounded to BF16 once by the finalize kernel, which adds the
-// caller's previous BF16 output -- the output is an accumulator.
+// Each route's weighted row goes to a route-indexed FP32 buffer y[r, :]
+// (plain stores, no atomics); the finalize kernel then adds, per token, its
+// top_k rows in route order to the caller's BF16 output and rounds once --
+// the output is an accumulator, and the reduction is deterministic.
 //
 // Tiling: one workgroup = one plan block (BM rows) x 256 output columns; four
 // waves take 64 columns each (four 16-row W2 subtiles, all inside one
@@ -172,32 +173,43 @@ down_kernel(DownArgs a) {
         const int row = wm * C::TM + u * 16 + l16;
         const int r = sRt[row];
         if (r < 0) continue;
-        const int64_t t = r / a.top_k;
         const float wr = a.topk_w[r];
-        float *dst = a.acc + t * K + col0 + 4 * g;
+        float *dst = a.y + (int64_t)r * K + col0 + 4 * g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + 16 * s + i, wr * acc[s][u][i]);
+        for (int s = 0; s < 4; ++s) *reinterpret_cast<v4f *>(dst + 16 * s) = acc[s][u] * wr;
     }
 }
 
 __global__ void __launch_bounds__(256)
-fill_zero_kernel(uint32_t *__restrict__ p, size_t n) {
+fill_kernel(uint32_t *__restrict__ p, size_t n, uint32_t v) {
     size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     size_t stride = (size_t)gridDim.x * 256;
-    for (; i < n; i += stride) p[i] = 0u;
+    for (; i < n; i += stride) p[i] = v;
 }
 
-// out = bf16(out + acc), eight elements per thread (n is a multiple of 8).
+// Route sum + accumulate into the BF16 output: eight columns of one token per
+// thread; the token's routes are added in route order (deterministic), then
+// the previous output, then one round to nearest even BF16.
 __global__ void __launch_bounds__(256)
-finalize_kernel(uint16_t *__restrict__ out, const float *__restrict__ acc, int64_t n) {
-    int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (i >= n) return;
+finalize_kernel(uint16_t *__restrict__ out, const float *__restrict__ y,
+                const int32_t *__restrict__ rpos, int64_t M, int64_t K, int top_k) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;   // element of out
+    if (i >= M * K) return;
+    const int64_t t = i / K;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < top_k; ++j) {
+        const int64_t r = t * top_k + j;
+        if (rpos[r] < 0) continue;                  // masked route
+        const float *src = y + r * K + (i - t * K);
+        v4f a0 = *reinterpret_cast<const v4f *>(src);
+        v4f a1 = *reinterpret_cast<const v4f *>(src + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[q] += a0[q];
+            f[4 + q] += a1[q];
+        }
+    }
     u32x4 o = *reinterpret_cast<const u32x4 *>(out + i);
-    v4f a0 = *reinterpret_cast<const v4f *>(acc + i);
-    v4f a1 = *reinterpret_cast<const v4f *>(acc + i + 4);
-    float f[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     uint32_t r[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -228,18 +240,19 @@ hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st
     }
 }
 
-hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st) {
+hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t st) {
     if (n_words == 0) return hipSuccess;
     size_t blocks = (n_words + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, n_words);
+    fill_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, n_words, value);
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(uint16_t *out, const float *acc, int64_t n, hipStream_t st) {
-    int64_t blocks = (n / 8 + 255) / 256;
+hipError_t launch_finalize(uint16_t *out, const float *y, const int32_t *rpos, int64_t M,
+                           int64_t K, int top_k, hipStream_t st) {
+    int64_t blocks = (M * K / 8 + 255) / 256;
     if (blocks == 0) return hipSuccess;
-    finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(out, acc, n);
+    finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(out, y, rpos, M, K, top_k);
     return hipGetLastError();
 }
 

@@ -94,7 +94,9 @@ gateup_kernel(GateUpArgs a) {
 
     if (tid < BM) {
         int r = a.sorted[(int64_t)b * BM + tid];
-        sTok[tid] = (r >= 0 && (int64_t)r < a.R) ? r / a.top_k : -1;
+        const bool ok = r >= 0 && (int64_t)r < a.R;
+        sTok[tid] = ok ? r / a.top_k : -1;
+        if (ok && jt == 0 && split == 0) a.rpos[r] = b * BM + tid;   // inverse plan map
     }
     __syncthreads();
 

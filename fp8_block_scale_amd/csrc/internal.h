@@ -30,6 +30,7 @@ struct GateUpArgs {
     float *hs;
     float *part;        // split-K partial sums (nsplit > 1)
     uint32_t *cnt;      // split-K arrival counters, one per (block, j-tile)
+    int32_t *rpos;      // [R] plan row of each route (pre-filled with -1)
     int64_t K, I, R;
     int E, top_k;
     int nkb;            // K / 128
@@ -49,7 +50,7 @@ struct DownArgs {
     const int32_t *sorted;
     const int32_t *eids;
     const int32_t *ntp;
-    float *acc;         // FP32 [M, K] reduction buffer
+    float *y;           // FP32 [R, K]: weighted down projection of each route
     int64_t K, I, R;
     int E, top_k;
     int njb;            // I / 128
@@ -62,7 +63,12 @@ struct DownArgs {
 hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                          hipStream_t st);
 hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
-hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st);
-hipError_t launch_finalize(uint16_t *out, const float *acc, int64_t n, hipStream_t st);
+hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t st);
+inline hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st) {
+    return launch_fill(p, n_words, 0u, st);
+}
+// out[t, :] = bf16(out[t, :] + sum_{j < top_k, rpos[t*top_k+j] >= 0} y[t*top_k+j, :])
+hipError_t launch_finalize(uint16_t *out, const float *y, const int32_t *rpos, int64_t M,
+                           int64_t K, int top_k, hipStream_t st);
 
 }  // namespace moe

@@ -374,17 +374,18 @@ def test_int32_int64_ids_agree():
     b = run_gpu(case_of("skew", M=256, ids_dtype=torch.int64))
     assert a.P == b.P and np.array_equal(a.sorted, b.sorted)
     assert np.array_equal(a.h_q, b.h_q) and np.array_equal(a.h_s, b.h_s)
-    compare_output(b.out, a.out)
+    # the route sum is taken in route order: the outputs are bit-identical
+    assert np.array_equal(a.out, b.out)
 
 
-def test_repeat_runs_bit_identical_codes():
+def test_repeat_runs_bit_identical():
     cs = case_of("page1", M=256)
     a = run_gpu(cs)
     b = run_gpu(cs)
     assert np.array_equal(a.sorted, b.sorted) and np.array_equal(a.x_q, b.x_q)
     rows = a.sorted[:a.P] < cs.M * cs.top_k
     assert np.array_equal(a.h_q[:a.P][rows], b.h_q[:b.P][rows])
-    compare_output(b.out, a.out)
+    assert np.array_equal(a.out, b.out)
 
 
 def test_m_zero_is_a_no_op():
