@@ -54,7 +54,7 @@ SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t nkb, uint32
     int64_t s = (flags & MOE_F_SPLITK_MASK) >> MOE_F_SPLITK_SHIFT;
     if (s == 0) {
         const int64_t target = 512;   // workgroups: two per CU
-        s = tiles >= 256 ? 1 : (target + tiles - 1) / (tiles > 0 ? tiles : 1);
+        s = tiles >= target ? 1 : (target + tiles - 1) / (tiles > 0 ? tiles : 1);
     }
     if (s > nkb) s = nkb;
     if (s < 1) s = 1;
@@ -299,9 +299,10 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.nsplit = l.sp.nsplit;
     ga.kb_per_split = l.sp.kb_per_split;
     ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
-    return hip_check(moe::launch_gateup(ga, block_m, (flags & MOE_F_FP8_GATEUP) != 0,
-                                        (flags & MOE_F_MMA_E8M0) != 0, s),
-                     "moe_fp8_gate_up: launch");
+    const bool fp8 = (flags & MOE_F_FP8_GATEUP) != 0, e8 = (flags & MOE_F_MMA_E8M0) != 0;
+    if (l.sp.nsplit == 1 && !(flags & MOE_F_SPLITK_MASK) && K <= 32768)
+        return hip_check(moe::launch_gateup_pipe(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
+    return hip_check(moe::launch_gateup(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
 }
 
 MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,

@@ -1,0 +1,343 @@
+// Steps 3 + 4 for large grids: the gate/up tile kernel with a three-stage
+// LDS pipeline fed by direct global->LDS loads.
+//
+// Same arithmetic as gateup.hip (FlashInfer PR #4287, PR summary and
+// public-contract section): per plan row, the gate/up sums over 128-deep
+// K-blocks with one activation scale and one 128x128 weight-block scale per
+// K-block, SwiGLU, and FP8 requantisation per row and 128-column group.
+//
+// Tiling.  A workgroup (8 waves) takes up to 128 consecutive plan rows that
+// belong to one expert -- several plan blocks when block_m < 128 -- and one
+// 128-wide intermediate tile (its 128 gate and 128 up rows of W13), so the
+// W13 tile is streamed once for all of the expert's rows it covers.  The
+// tile starts where the expert's run of blocks starts (found by a binary
+// search over the non-decreasing expert ids of the plan) and every
+// 128 / block_m blocks after it; the other workgroups of the grid exit.
+//
+// Pipeline.  Each K-block stage holds the W13 tile (256 rows x 128 B) and the
+// gathered activation tile (128 rows x 128 B) in LDS; all waves issue
+// global_load_lds_dwordx4 (64 lanes x 16 B straight into LDS, no registers)
+// two stages ahead of the one being multiplied, so ~96 KB per CU are in
+// flight while the MFMAs run.  Rows are stored with their eight 16-byte
+// chunks XOR-swizzled by (row & 7), so the MFMA operand reads (16 rows at one
+// chunk) hit distinct banks.  Waves: wn = 0..3 take 32 gate + 32 up columns,
+// wm = 0..1 take 64 rows each.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRows = 128;        // tile rows
+constexpr int kNT = 512;          // threads (8 waves)
+constexpr int kStages = 3;
+constexpr int kWBytes = 256 * 128;            // W13 tile per stage
+constexpr int kABytes = kRows * 128;          // activation tile per stage
+constexpr int kWInstr = kWBytes / 1024 / 8;   // DMA instructions per wave per stage (W)
+constexpr int kAInstr = kABytes / 1024 / 8;   // (A)
+constexpr int kSInstr = 1;                    // (activation scales: 16 rows per wave)
+constexpr int kPerStage = kWInstr + kAInstr + kSInstr;
+constexpr int kMaxKb = 256;                   // K <= 32768
+
+enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
+
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4]
+// << 14, expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const uint8_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ v8i join8p(const u32x4 &lo, const u32x4 &hi) {
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+template <int BM, int MODE>
+__global__ void __launch_bounds__(kNT, 1)
+gateup_pipe_kernel(GateUpArgs a) {
+    constexpr int MB = kRows / BM;                   // plan blocks per tile
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *sW = smem;                                        // [kStages][256][128]
+    uint8_t *sA = smem + kStages * kWBytes;                    // [kStages][128][128]
+    float *sSa = reinterpret_cast<float *>(sA + kStages * kABytes);  // [kStages][128] x_s
+    float *sSw = sSa + kStages * kRows;                        // [2][kMaxKb] w13_s gate, up
+    int *sTok = reinterpret_cast<int *>(sSw + 2 * kMaxKb);      // [128] token or -1
+    float *sRed = reinterpret_cast<float *>(sTok + kRows);      // [4][128]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wn = w & 3, wm = w >> 2;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = L % a.nblocks;
+    const int jt = L / a.nblocks;
+
+    const int P = a.ntp[0];
+    if (b * BM >= P) return;
+    const int e = a.eids[b];
+    if (e < 0 || e >= a.E) return;
+    // run start: first block of expert e (expert ids are non-decreasing)
+    int nb = 1;
+    if (MB > 1) {
+        int lo = 0, hi = b;
+        while (lo < hi) {
+            int mid = (lo + hi) >> 1;
+            if (a.eids[mid] < e) lo = mid + 1; else hi = mid;
+        }
+        if ((b - lo) % MB != 0) return;              // another workgroup covers b
+        const int pb = P / BM;
+        while (nb < MB && b + nb < pb && a.eids[b + nb] == e) ++nb;
+    }
+    const int nrows = nb * BM;
+    const int64_t p0 = (int64_t)b * BM;
+
+    if (tid < kRows) {
+        int t = -1;
+        if (tid < nrows) {
+            int r = a.sorted[p0 + tid];
+            if (r >= 0 && (int64_t)r < a.R) {
+                t = r / a.top_k;
+                if (jt == 0) a.rpos[r] = (int)(p0 + tid);
+            }
+        }
+        sTok[tid] = t;
+    }
+    const int64_t I = a.I, K = a.K;
+    const int64_t twoI = 2 * I;
+    const int nkb = a.nkb;
+    const int nb13 = (int)(twoI >> 7);
+    {
+        const float *sg = a.w13s + ((int64_t)e * nb13 + jt) * nkb;
+        const float *su = a.w13s + ((int64_t)e * nb13 + (I >> 7) + jt) * nkb;
+        for (int i = tid; i < nkb; i += kNT) {
+            sSw[i] = sg[i];
+            sSw[kMaxKb + i] = su[i];
+        }
+    }
+    __syncthreads();
+
+    // ---- DMA sources of this lane: W13 rows and gathered activation rows
+    const int sub = lane >> 3, slot = lane & 7;
+    const uint8_t *wsrc[kWInstr];
+#pragma unroll
+    for (int i = 0; i < kWInstr; ++i) {
+        const int row = (w * kWInstr + i) * 8 + sub;                  // tile row 0..255
+        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+        const int chunk = slot ^ (row & 7);
+        wsrc[i] = a.w13 + ((int64_t)e * twoI + n) * K + chunk * 16;
+    }
+    int fallback = sTok[0];
+    for (int m = 1; fallback < 0 && m < nrows; ++m) fallback = sTok[m];
+    if (fallback < 0) fallback = 0;                  // tile without valid rows: scale 0
+    const uint8_t *asrc[kAInstr];
+#pragma unroll
+    for (int i = 0; i < kAInstr; ++i) {
+        const int row = (w * kAInstr + i) * 8 + sub;
+        const int t = sTok[row] >= 0 ? sTok[row] : fallback;
+        const int chunk = slot ^ (row & 7);
+        asrc[i] = a.xq + (int64_t)t * K + chunk * 16;
+    }
+    // activation scales: wave w fetches rows 16w .. 16w + 15 (lanes 0..15)
+    const float *ssrc;
+    {
+        const int row = w * 16 + (lane & 15);
+        const int t = sTok[row] >= 0 ? sTok[row] : fallback;
+        ssrc = a.xs + (int64_t)t * nkb;
+    }
+    // Every wave issues exactly kPerStage vector-memory instructions per stage
+    // (the waits in the main loop count on it).
+    auto issue = [&](int stage, int kb) {
+        uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
+#pragma unroll
+        for (int i = 0; i < kWInstr; ++i)
+            __builtin_amdgcn_global_load_lds(wsrc[i] + (int64_t)kb * 128, dw + i * 1024, 16, 0, 0);
+        uint8_t *da = sA + stage * kABytes + (w * kAInstr) * 1024;
+#pragma unroll
+        for (int i = 0; i < kAInstr; ++i)
+            __builtin_amdgcn_global_load_lds(asrc[i] + (int64_t)kb * 128, da + i * 1024, 16, 0, 0);
+        if (lane < 16)
+            __builtin_amdgcn_global_load_lds(ssrc + kb, sSa + stage * kRows + w * 16, 4, 0, 0);
+    };
+
+    constexpr int NU = 4;
+    const bool wave_rows = wm * 64 < nrows;
+
+    v4f acc[4][NU];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    if (nkb > 1) issue(1, 1);
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int stage = kb % kStages;
+        if (kb + 2 < nkb) {
+            issue((kb + 2) % kStages, kb + 2);
+            wait_vmcnt<2 * kPerStage>();
+        } else if (kb + 1 < nkb) {
+            wait_vmcnt<kPerStage>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        // Every wave has waited for its own part of this stage; the barrier
+        // makes the whole stage visible.  A plain s_barrier: __syncthreads()
+        // would also drain the later stages still in flight.
+        __builtin_amdgcn_s_barrier();
+
+        if (wave_rows) {
+            const float sbg = sSw[kb];
+            const float sbu = sSw[kMaxKb + kb];
+            const float *Ss = sSa + stage * kRows;
+            const uint8_t *Ws = sW + stage * kWBytes;
+            const uint8_t *As = sA + stage * kABytes;
+            // W operands of this wave: tile rows 32wn + 16(s&1) (+128 for up)
+            v8i wq[4];
+            v8h wh[4][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = (s < 2 ? 0 : 128) + 32 * wn + 16 * (s & 1) + l16;
+                const uint8_t *rp = Ws + row * 128;
+                const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                if constexpr (MODE == kExact) e4m3x32_to_f16(lo, hi, wh[s]);
+                else wq[s] = join8p(lo, hi);
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (wm * 64 + u * 16 >= nrows) continue;
+                const int row = wm * 64 + u * 16 + l16;
+                const uint8_t *rp = As + row * 128;
+                const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                const float sa = Ss[row];
+                if constexpr (MODE == kExact) {
+                    v8h bh[4];
+                    e4m3x32_to_f16(lo, hi, bh);
+                    const float fg = sa * sbg, fu = sa * sbu;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        v4f t = mfma16x16x128_f16(wh[s], bh);
+                        acc[s][u] = t * (s < 2 ? fg : fu) + acc[s][u];
+                    }
+                } else if constexpr (MODE == kFp8E8) {
+                    const v8i B = join8p(lo, hi);
+                    const int eb = e8m0_of(sa), eg = e8m0_of(sbg), eu = e8m0_of(sbu);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[s][u] = mfma16x16x128_e8m0(wq[s], B, acc[s][u], s < 2 ? eg : eu, eb);
+                } else {
+                    const v8i B = join8p(lo, hi);
+                    const float fg = sa * sbg, fu = sa * sbu;
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        v4f t = mfma16x16x128(wq[s], B);
+                        acc[s][u] = t * (s < 2 ? fg : fu) + acc[s][u];
+                    }
+                }
+            }
+        }
+        // all reads of this stage are consumed (their results fed the MFMAs)
+        // before any wave refills it two iterations later
+        __builtin_amdgcn_s_barrier();
+    }
+    __syncthreads();
+
+    // ---- SwiGLU + per-row 128-group FP8 requantisation
+    float h[NU][2][4];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int row = wm * 64 + u * 16 + l16;
+        const bool valid = sTok[row] >= 0;
+        float amax = 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float gt = acc[s][u][i];
+                const float up = acc[s + 2][u][i];
+                const float hv = valid ? gt / (1.0f + expf(-gt)) * up : 0.f;
+                h[u][s][i] = hv;
+                amax = fmaxf(amax, fabsf(hv));
+            }
+        amax = wave_max_xor(amax, 16);
+        amax = wave_max_xor(amax, 32);
+        if (g == 0) sRed[wn * kRows + row] = amax;
+    }
+    __syncthreads();
+    const bool ue = a.inter_ue8m0 != 0;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int row = wm * 64 + u * 16 + l16;
+        if (row >= nrows) continue;
+        const float amax = fmaxf(fmaxf(sRed[row], sRed[kRows + row]),
+                                 fmaxf(sRed[2 * kRows + row], sRed[3 * kRows + row]));
+        float s, inv;
+        group_scale(amax, ue, s, inv);
+        const int64_t p = p0 + row;
+        uint8_t *dst = a.hq + p * I + (int64_t)jt * 128 + 32 * wn + 4 * g;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint32_t code = pack_e4m3x4(h[u][s2][0] * inv, h[u][s2][1] * inv,
+                                        h[u][s2][2] * inv, h[u][s2][3] * inv);
+            *reinterpret_cast<uint32_t *>(dst + 16 * s2) = code;
+        }
+        if (wn == 0 && g == 0) a.hs[p * (I >> 7) + jt] = s;
+    }
+}
+
+constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + kStages * kRows * 4 +
+                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4;
+
+template <int BM, int MODE>
+hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
+    int64_t grid = (int64_t)a.nblocks * a.jtiles;
+    if (grid == 0) return hipSuccess;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gateup_pipe_kernel<BM, MODE>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    gateup_pipe_kernel<BM, MODE><<<(unsigned)grid, kNT, kSmem, st>>>(a);
+    return hipGetLastError();
+}
+
+template <int BM>
+hipError_t launch_pipe_mode(const GateUpArgs &a, int mode, hipStream_t st) {
+    switch (mode) {
+        case kExact: return launch_pipe<BM, kExact>(a, st);
+        case kFp8: return launch_pipe<BM, kFp8>(a, st);
+        case kFp8E8: return launch_pipe<BM, kFp8E8>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
+                              hipStream_t st) {
+    const int mode = !fp8_mma ? kExact : (e8m0 ? kFp8E8 : kFp8);
+    switch (block_m) {
+        case 16: return launch_pipe_mode<16>(a, mode, st);
+        case 32: return launch_pipe_mode<32>(a, mode, st);
+        case 64: return launch_pipe_mode<64>(a, mode, st);
+        case 128: return launch_pipe_mode<128>(a, mode, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace moe

@@ -62,6 +62,9 @@ struct DownArgs {
 // e8m0: (with fp8_mma) power-of-two scales applied inside the MFMA.
 hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                          hipStream_t st);
+// Large-grid gate/up (no split-K): 128-row tiles, three-stage LDS pipeline.
+hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
+                              hipStream_t st);
 hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
 hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t st);
 inline hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st) {
