@@ -64,7 +64,7 @@ SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t nkb, uint32
 }
 
 struct WsLayout {
-    size_t hq, hs, y, rpos, cnt, part, total;
+    size_t hq, hs, y, rpos, tiles, cnt, part, total;
     size_t cnt_words;                 // split-K counters, zeroed per call
     SplitChoice sp;
 };
@@ -85,6 +85,8 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block
     off = align256(off + R * K * 4);
     l.rpos = off;
     off = align256(off + R * 4);
+    l.tiles = off;                       // row tiles [blocks_cap] int2 + 2 ints
+    off = align256(off + (size_t)blocks_cap * 8 + 16);
     l.cnt = off;
     size_t ntiles = (size_t)blocks_cap * jtiles;
     l.cnt_words = l.sp.nsplit > 1 ? ntiles : 0;
@@ -288,6 +290,8 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.part = (float *)(ws + l.part);
     ga.cnt = (uint32_t *)(ws + l.cnt);
     ga.rpos = (int32_t *)(ws + l.rpos);
+    ga.tiles = (int2 *)(ws + l.tiles);
+    ga.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 8);
     ga.K = K;
     ga.I = I;
     ga.R = M * top_k;

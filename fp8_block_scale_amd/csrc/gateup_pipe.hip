@@ -6,13 +6,15 @@
 // K-blocks with one activation scale and one 128x128 weight-block scale per
 // K-block, SwiGLU, and FP8 requantisation per row and 128-column group.
 //
-// Tiling.  A workgroup (8 waves) takes up to 128 consecutive plan rows that
-// belong to one expert -- several plan blocks when block_m < 128 -- and one
-// 128-wide intermediate tile (its 128 gate and 128 up rows of W13), so the
-// W13 tile is streamed once for all of the expert's rows it covers.  The
-// tile starts where the expert's run of blocks starts (found by a binary
-// search over the non-decreasing expert ids of the plan) and every
-// 128 / block_m blocks after it; the other workgroups of the grid exit.
+// Tiling.  A work item is up to 128 consecutive plan rows that belong to one
+// expert -- several plan blocks when block_m < 128 -- times one 128-wide
+// intermediate tile (its 128 gate and 128 up rows of W13), so the W13 tile is
+// streamed once for all of the expert's rows it covers.  A one-workgroup
+// prep kernel cuts every expert's run of plan blocks into such row tiles
+// (a list in the workspace); the gate/up kernel is persistent -- one
+// workgroup (8 waves) per CU -- and pulls items from a device-wide counter
+// until none are left, so no workgroup is launched only to exit and the
+// per-launch set-up is paid once per CU.
 //
 // Pipeline.  Each K-block stage holds the W13 tile (256 rows x 128 B) and the
 // gathered activation tile (128 rows x 128 B) in LDS; all waves issue
@@ -61,10 +63,59 @@ __device__ __forceinline__ v8i join8p(const u32x4 &lo, const u32x4 &hi) {
     return r;
 }
 
+// Row tiles: every expert's run of blocks [first, first + len) (expert ids of
+// a plan are non-decreasing) becomes ceil(len / mb) tiles of <= mb blocks.
+// One workgroup: pass 1 marks run starts and counts their tiles, an
+// exclusive scan gives each run its first tile slot, pass 2 writes them.
+__global__ void __launch_bounds__(1024)
+tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, int bm, int mb,
+             int nblocks, int2 *__restrict__ tiles, int32_t *__restrict__ meta) {
+    __shared__ int wsum[16];
+    __shared__ int carry;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int nb = ntp[0] / bm;
+    nb = nb < nblocks ? nb : nblocks;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < nb; base += 1024) {
+        const int b = base + tid;
+        int cnt = 0, len = 0;
+        if (b < nb) {
+            const int e = eids[b];
+            if (b == 0 || eids[b - 1] != e) {
+                len = 1;
+                while (b + len < nb && eids[b + len] == e) ++len;
+                cnt = (len + mb - 1) / mb;
+            }
+        }
+        int incl = cnt;
+        for (int d = 1; d < 64; d <<= 1) {
+            int v = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += v;
+        }
+        if (lane == 63) wsum[w] = incl;
+        __syncthreads();
+        int before = carry;
+        for (int q = 0; q < w; ++q) before += wsum[q];
+        int slot = before + incl - cnt;
+        for (int t = 0; t < cnt; ++t) {
+            const int first = b + t * mb;
+            const int rem = len - t * mb;
+            tiles[slot + t] = make_int2(first, rem < mb ? rem : mb);
+        }
+        __syncthreads();
+        if (tid == 1023) carry = before + incl;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        meta[0] = carry;      // number of row tiles
+        meta[1] = 0;          // work counter of the gate/up kernel
+    }
+}
+
 template <int BM, int MODE>
 __global__ void __launch_bounds__(kNT, 1)
 gateup_pipe_kernel(GateUpArgs a) {
-    constexpr int MB = kRows / BM;                   // plan blocks per tile
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *sW = smem;                                        // [kStages][256][128]
     uint8_t *sA = smem + kStages * kWBytes;                    // [kStages][128][128]
@@ -72,6 +123,7 @@ gateup_pipe_kernel(GateUpArgs a) {
     float *sSw = sSa + kStages * kRows;                        // [2][kMaxKb] w13_s gate, up
     int *sTok = reinterpret_cast<int *>(sSw + 2 * kMaxKb);      // [128] token or -1
     float *sRed = reinterpret_cast<float *>(sTok + kRows);      // [4][128]
+    int *sItem = reinterpret_cast<int *>(sRed + 4 * kRows);      // [1]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -79,25 +131,23 @@ gateup_pipe_kernel(GateUpArgs a) {
     const int wn = w & 3, wm = w >> 2;
     const int l16 = lane & 15, g = lane >> 4;
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int b = L % a.nblocks;
-    const int jt = L / a.nblocks;
-
-    const int P = a.ntp[0];
-    if (b * BM >= P) return;
+    const int ntiles = a.tmeta[0];
+    const int nitems = ntiles * a.jtiles;
+    for (;;) {
+    if (tid == 0)
+        sItem[0] = __hip_atomic_fetch_add(&a.tmeta[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = sItem[0];
+    if (item >= nitems) break;                       // every workgroup ends here
+    // items run over the row tiles fastest: row tiles of one expert that
+    // share a W13 column tile are handed out together
+    const int jt = item / ntiles;
+    const int2 tl = a.tiles[item % ntiles];
+    const int b = tl.x, nb = tl.y;
     const int e = a.eids[b];
-    if (e < 0 || e >= a.E) return;
-    // run start: first block of expert e (expert ids are non-decreasing)
-    int nb = 1;
-    if (MB > 1) {
-        int lo = 0, hi = b;
-        while (lo < hi) {
-            int mid = (lo + hi) >> 1;
-            if (a.eids[mid] < e) lo = mid + 1; else hi = mid;
-        }
-        if ((b - lo) % MB != 0) return;              // another workgroup covers b
-        const int pb = P / BM;
-        while (nb < MB && b + nb < pb && a.eids[b + nb] == e) ++nb;
+    if (e < 0 || e >= a.E) {                         // not a plan: skip, keep in step
+        __syncthreads();
+        continue;
     }
     const int nrows = nb * BM;
     const int64_t p0 = (int64_t)b * BM;
@@ -296,15 +346,35 @@ gateup_pipe_kernel(GateUpArgs a) {
         }
         if (wn == 0 && g == 0) a.hs[p * (I >> 7) + jt] = s;
     }
+    __syncthreads();                                 // LDS is reused by the next item
+    }
 }
 
 constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + kStages * kRows * 4 +
-                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4;
+                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16;
+
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 template <int BM, int MODE>
 hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
-    int64_t grid = (int64_t)a.nblocks * a.jtiles;
-    if (grid == 0) return hipSuccess;
+    if (a.nblocks == 0) return hipSuccess;
+    tiles_kernel<<<1, 1024, 0, st>>>(a.eids, a.ntp, BM, kRows / BM, a.nblocks, a.tiles, a.tmeta);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    int64_t grid = num_cus();
+    const int64_t max_items = (int64_t)a.nblocks * a.jtiles;
+    if (grid > max_items) grid = max_items;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)gateup_pipe_kernel<BM, MODE>,

@@ -31,6 +31,8 @@ struct GateUpArgs {
     float *part;        // split-K partial sums (nsplit > 1)
     uint32_t *cnt;      // split-K arrival counters, one per (block, j-tile)
     int32_t *rpos;      // [R] plan row of each route (pre-filled with -1)
+    int2 *tiles;        // [nblocks] row tiles (first block, blocks) of the persistent kernel
+    int32_t *tmeta;     // [2] row-tile count, work counter
     int64_t K, I, R;
     int E, top_k;
     int nkb;            // K / 128
