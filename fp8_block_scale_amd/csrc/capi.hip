@@ -97,6 +97,12 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block
     return l;
 }
 
+// Large grids take the persistent pipelined kernels (both stages share the
+// row-tile list the gate/up stage builds); small grids the split-K ones.
+bool use_persistent(const WsLayout &l, int64_t K, int64_t I, uint32_t flags) {
+    return l.sp.nsplit == 1 && !(flags & MOE_F_SPLITK_MASK) && K <= 32768 && I <= 32768;
+}
+
 moe_status check_experts_shape(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
                                int32_t block_m, int64_t sorted_cap) {
     if (M < 0 || K <= 0 || I <= 0 || E < 1 || top_k < 1)
@@ -304,7 +310,7 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.kb_per_split = l.sp.kb_per_split;
     ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
     const bool fp8 = (flags & MOE_F_FP8_GATEUP) != 0, e8 = (flags & MOE_F_MMA_E8M0) != 0;
-    if (l.sp.nsplit == 1 && !(flags & MOE_F_SPLITK_MASK) && K <= 32768)
+    if (use_persistent(l, K, I, flags))
         return hip_check(moe::launch_gateup_pipe(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
     return hip_check(moe::launch_gateup(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
 }
@@ -345,7 +351,11 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
     da.njb = (int)(I / 128);
     da.ctiles = (int)((K + 255) / 256);
     da.nblocks = (int)(sorted_cap / block_m);
-    st = hip_check(moe::launch_down(da, block_m, (flags & MOE_F_MMA_E8M0) != 0, s),
+    da.tiles = (const int2 *)(ws + l.tiles);
+    da.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 8);
+    const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
+    st = hip_check(use_persistent(l, K, I, flags) ? moe::launch_down_pipe(da, block_m, e8, s)
+                                                   : moe::launch_down(da, block_m, e8, s),
                    "moe_fp8_down_reduce: down launch");
     if (st != MOE_OK) return st;
     return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const float *)(ws + l.y),

@@ -145,6 +145,33 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
     return xcd * q + (xcd < r ? xcd : r) + k;
 }
 
+// ------------------------------------------------- LDS pipeline helpers
+
+// 16-byte LDS read of an MFMA operand slice.  (Kept as a typed load: the
+// compiler then tells these reads apart from the in-flight global->LDS
+// refills of other stages and adds no wait for them; the pipelines order
+// stages with their own vmcnt waits and barriers.)
+__device__ __forceinline__ u32x4 lds_read16(const uint8_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Workgroup barrier without a memory fence, so refills still in flight stay
+// in flight.  The compiler-only fences keep LDS accesses from being moved
+// across it; they emit no instructions.
+__device__ __forceinline__ void stage_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4]
+// << 14; expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ------------------------------------------------------------ wave utils
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

@@ -44,18 +44,6 @@ constexpr int kMaxKb = 256;                   // K <= 32768
 
 enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
 
-// s_waitcnt with only a vmcnt limit (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4]
-// << 14, expcnt and lgkmcnt left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ u32x4 lds_read16(const uint8_t *p) {
-    return *reinterpret_cast<const u32x4 *>(p);
-}
-
 __device__ __forceinline__ v8i join8p(const u32x4 &lo, const u32x4 &hi) {
     v8i r;
     r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
@@ -110,6 +98,7 @@ tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, 
     if (tid == 0) {
         meta[0] = carry;      // number of row tiles
         meta[1] = 0;          // work counter of the gate/up kernel
+        meta[2] = 0;          // work counter of the down kernel
     }
 }
 
@@ -245,7 +234,7 @@ gateup_pipe_kernel(GateUpArgs a) {
         // Every wave has waited for its own part of this stage; the barrier
         // makes the whole stage visible.  A plain s_barrier: __syncthreads()
         // would also drain the later stages still in flight.
-        __builtin_amdgcn_s_barrier();
+        stage_barrier();
 
         if (wave_rows) {
             const float sbg = sSw[kb];
@@ -301,7 +290,7 @@ gateup_pipe_kernel(GateUpArgs a) {
         }
         // all reads of this stage are consumed (their results fed the MFMAs)
         // before any wave refills it two iterations later
-        __builtin_amdgcn_s_barrier();
+        stage_barrier();
     }
     __syncthreads();
 

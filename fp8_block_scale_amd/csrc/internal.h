@@ -31,8 +31,8 @@ struct GateUpArgs {
     float *part;        // split-K partial sums (nsplit > 1)
     uint32_t *cnt;      // split-K arrival counters, one per (block, j-tile)
     int32_t *rpos;      // [R] plan row of each route (pre-filled with -1)
-    int2 *tiles;        // [nblocks] row tiles (first block, blocks) of the persistent kernel
-    int32_t *tmeta;     // [2] row-tile count, work counter
+    int2 *tiles;        // [nblocks] row tiles (first block, blocks) of the persistent kernels
+    int32_t *tmeta;     // [3] row-tile count, gate/up and down work counters
     int64_t K, I, R;
     int E, top_k;
     int nkb;            // K / 128
@@ -53,6 +53,8 @@ struct DownArgs {
     const int32_t *eids;
     const int32_t *ntp;
     float *y;           // FP32 [R, K]: weighted down projection of each route
+    const int2 *tiles;  // row tiles listed by the gate/up stage (persistent path)
+    int32_t *tmeta;
     int64_t K, I, R;
     int E, top_k;
     int njb;            // I / 128
@@ -68,6 +70,8 @@ hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                               hipStream_t st);
 hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
+// Large-grid down GEMM: persistent, over the gate/up stage's row tiles.
+hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
 hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t st);
 inline hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st) {
     return launch_fill(p, n_words, 0u, st);

@@ -192,8 +192,9 @@ moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s,
  * one stream, same workspace and flags):
  *   moe_fp8_gate_up      steps 3-4: writes the requantised SwiGLU rows h_q and
  *                        their scales h_s into the workspace;
- *   moe_fp8_down_reduce  step 5: reads them, adds the weighted down
- *                        projections into out_bf16.
+ *   moe_fp8_down_reduce  step 5: reads them (and the work list the gate/up
+ *                        stage leaves in the workspace), adds the weighted
+ *                        down projections into out_bf16.
  * Arguments, constraints and errors as for moe_fp8_experts. */
 moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s,
                            const uint8_t *w13, const float *w13_s,
