@@ -46,6 +46,8 @@ def parse():
                     help="gate/up on the FP8 MFMA (MOE_F_FP8_GATEUP)")
     ap.add_argument("--e8m0", action="store_true",
                     help="power-of-two scales inside the FP8 MFMA (zipf workload)")
+    ap.add_argument("--splitk", type=int, default=0,
+                    help="force the small-grid gate/up split-K factor (1..255; 0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=192)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -132,6 +134,8 @@ def main():
             flags |= moe.MOE_F_MMA_E8M0
     if args.fp8_gateup:
         flags |= moe.MOE_F_FP8_GATEUP
+    if args.splitk:
+        flags |= (args.splitk & 0xFF) << moe.MOE_F_SPLITK_SHIFT
 
     b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
     out = torch.zeros((case.M, case.K), dtype=torch.bfloat16, device=dev)

@@ -43,24 +43,39 @@ int64_t plan_sorted_cap(int64_t M, int32_t top_k, int32_t E, int32_t bm) {
 
 bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
-// Gate/up split-K factor: enough workgroups to cover the chip at small grids.
+// Gate/up work split.  Large grids take the persistent pipelined kernels
+// (both stages share the row-tile list the gate/up stage builds); small grids
+// the weight-stream kernel, with K split over enough workgroups to cover the
+// chip and each K-range short enough for its LDS activation tile.
 struct SplitChoice {
     int nsplit;
     int kb_per_split;
+    bool persistent;
 };
 
-SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t nkb, uint32_t flags) {
-    int64_t tiles = blocks_cap * jtiles;
-    int64_t s = (flags & MOE_F_SPLITK_MASK) >> MOE_F_SPLITK_SHIFT;
+constexpr int64_t kPersistentTiles = 512;   // (block, j-tile) pairs
+constexpr int64_t kStreamTarget = 256;      // workgroups of the stream kernel
+
+SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t K, int64_t I, int32_t bm,
+                         uint32_t flags) {
+    const int64_t nkb = K / 128;
+    const int64_t tiles = blocks_cap * jtiles;
+    const int64_t forced = (flags & MOE_F_SPLITK_MASK) >> MOE_F_SPLITK_SHIFT;
+    if (forced == 0 && tiles >= kPersistentTiles && K <= 32768 && I <= 32768)
+        return {1, (int)nkb, true};
+    const int64_t npass = bm > 64 ? bm / 64 : 1;
+    int64_t s = forced;
     if (s == 0) {
-        const int64_t target = 512;   // workgroups: two per CU
-        s = tiles >= target ? 1 : (target + tiles - 1) / (tiles > 0 ? tiles : 1);
+        const int64_t units = tiles * npass > 0 ? tiles * npass : 1;
+        s = (kStreamTarget + units - 1) / units;
     }
+    const int64_t kmax = moe::gateup_stream_kmax(bm);
+    if (s < (nkb + kmax - 1) / kmax) s = (nkb + kmax - 1) / kmax;
     if (s > nkb) s = nkb;
     if (s < 1) s = 1;
-    int64_t kps = (nkb + s - 1) / s;
+    const int64_t kps = (nkb + s - 1) / s;
     s = (nkb + kps - 1) / kps;        // no empty splits
-    return {(int)s, (int)kps};
+    return {(int)s, (int)kps, false};
 }
 
 struct WsLayout {
@@ -74,7 +89,7 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block
     WsLayout l;
     int64_t blocks_cap = sorted_cap / block_m;
     int64_t jtiles = I / 128;
-    l.sp = choose_split(blocks_cap, jtiles, K / 128, flags);
+    l.sp = choose_split(blocks_cap, jtiles, K, I, block_m, flags);
     size_t off = 0;
     l.hq = off;
     off = align256(off + (size_t)sorted_cap * I);
@@ -89,18 +104,12 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block
     off = align256(off + (size_t)blocks_cap * 8 + 16);
     l.cnt = off;
     size_t ntiles = (size_t)blocks_cap * jtiles;
-    l.cnt_words = l.sp.nsplit > 1 ? ntiles : 0;
+    l.cnt_words = l.sp.nsplit > 1 ? ntiles * (block_m > 64 ? block_m / 64 : 1) : 0;
     off = align256(off + l.cnt_words * 4);
     l.part = off;
     if (l.sp.nsplit > 1) off = align256(off + ntiles * l.sp.nsplit * block_m * 256 * 4);
     l.total = off;
     return l;
-}
-
-// Large grids take the persistent pipelined kernels (both stages share the
-// row-tile list the gate/up stage builds); small grids the split-K ones.
-bool use_persistent(const WsLayout &l, int64_t K, int64_t I, uint32_t flags) {
-    return l.sp.nsplit == 1 && !(flags & MOE_F_SPLITK_MASK) && K <= 32768 && I <= 32768;
 }
 
 moe_status check_experts_shape(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
@@ -275,14 +284,10 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
         return fail(MOE_ERR_ALIGN, "x_q and w13 must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
-    st = hip_check(moe::launch_fill((uint32_t *)(ws + l.rpos), (size_t)M * top_k, 0xffffffffu, s),
-                   "moe_fp8_gate_up: clear route map");
+    st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
+                                    (uint32_t *)(ws + l.cnt), l.cnt_words, s),
+                   "moe_fp8_gate_up: clear route map and counters");
     if (st != MOE_OK) return st;
-    if (l.sp.nsplit > 1) {
-        st = hip_check(moe::launch_fill_zero((uint32_t *)(ws + l.cnt), l.cnt_words, s),
-                       "moe_fp8_gate_up: clear split-K counters");
-        if (st != MOE_OK) return st;
-    }
     moe::GateUpArgs ga;
     ga.xq = x_q;
     ga.xs = x_s;
@@ -310,7 +315,7 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.kb_per_split = l.sp.kb_per_split;
     ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
     const bool fp8 = (flags & MOE_F_FP8_GATEUP) != 0, e8 = (flags & MOE_F_MMA_E8M0) != 0;
-    if (use_persistent(l, K, I, flags))
+    if (l.sp.persistent)
         return hip_check(moe::launch_gateup_pipe(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
     return hip_check(moe::launch_gateup(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
 }
@@ -354,7 +359,7 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
     da.tiles = (const int2 *)(ws + l.tiles);
     da.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 8);
     const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
-    st = hip_check(use_persistent(l, K, I, flags) ? moe::launch_down_pipe(da, block_m, e8, s)
+    st = hip_check(l.sp.persistent ? moe::launch_down_pipe(da, block_m, e8, s)
                                                    : moe::launch_down(da, block_m, e8, s),
                    "moe_fp8_down_reduce: down launch");
     if (st != MOE_OK) return st;

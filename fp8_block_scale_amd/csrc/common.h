@@ -155,6 +155,13 @@ __device__ __forceinline__ u32x4 lds_read16(const uint8_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l of
+// the wave writes LDS bytes [lds + 16 l, lds + 16 l + 16); lds must be
+// wave-uniform.  Counted by vmcnt like any global load.
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
 // Workgroup barrier without a memory fence, so refills still in flight stay
 // in flight.  The compiler-only fences keep LDS accesses from being moved
 // across it; they emit no instructions.

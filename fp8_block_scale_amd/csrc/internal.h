@@ -64,6 +64,10 @@ struct DownArgs {
 
 // fp8_mma: FP8 MFMA instead of the exact FP16-widened product path;
 // e8m0: (with fp8_mma) power-of-two scales applied inside the MFMA.
+// Small-grid gate/up (weight stream, split-K); kb_per_split must not exceed
+// gateup_stream_kmax(block_m), and the counters hold one word per
+// (j-tile, block, row pass of 64).
+int gateup_stream_kmax(int block_m);
 hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                          hipStream_t st);
 // Large-grid gate/up (no split-K): 128-row tiles, three-stage LDS pipeline.
@@ -72,6 +76,8 @@ hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bo
 hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
 // Large-grid down GEMM: persistent, over the gate/up stage's row tiles.
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
+// rpos[0, n_rpos) = -1 and cnt[0, n_cnt) = 0 in one launch.
+hipError_t launch_prep(uint32_t *rpos, size_t n_rpos, uint32_t *cnt, size_t n_cnt, hipStream_t st);
 hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t st);
 inline hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st) {
     return launch_fill(p, n_words, 0u, st);
