@@ -107,7 +107,7 @@ gateup_stream_kernel(GateUpArgs a) {
     int r = -1;
     if (w == 0 && lane < C::RP) r = a.sorted[(int64_t)b * BM + row0 + lane];
     const int ntp = a.ntp[0];
-    const int e = a.eids[b];
+    const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors
     if (b * BM >= ntp || e < 0 || e >= a.E) return;   // padded block
 
     for (int i = tid; i < C::RP * C::KMAX; i += C::NT) sXs[i] = 0.f;
@@ -272,14 +272,21 @@ gateup_stream_kernel(GateUpArgs a) {
         }
     };
     // Stage st computes from buffer st & 1, then refills it with stage st + 2.
-    for (int st = 0; st < nst; st += 2) {
+    // (pairs of stages, then an odd last one: no exit from the middle of
+    // the loop body, which keeps the compiler's own waits at the stage
+    // boundaries)
+    int st = 0;
+    for (; st + 1 < nst; st += 2) {
         wait_vmcnt<C::LPS>();
         compute(st, std::integral_constant<int, 0>{});
         issue(st + 2, std::integral_constant<int, 0>{});
-        if (st + 1 >= nst) break;
         wait_vmcnt<C::LPS>();
         compute(st + 1, std::integral_constant<int, 1>{});
         issue(st + 3, std::integral_constant<int, 1>{});
+    }
+    if (st < nst) {
+        wait_vmcnt<C::LPS>();
+        compute(st, std::integral_constant<int, 0>{});
     }
 
     // ---- FP32 tile of the pass: sG[row][n], gate n < 128, up n >= 128

@@ -60,6 +60,7 @@ struct DownArgs {
     int njb;            // I / 128
     int ctiles;         // column tiles of 256
     int nblocks;
+    int nct;            // column tiles per workgroup (small-grid kernel; set by its launcher)
 };
 
 // fp8_mma: FP8 MFMA instead of the exact FP16-widened product path;
