@@ -100,8 +100,8 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block
     off = align256(off + R * K * 4);
     l.rpos = off;
     off = align256(off + R * 4);
-    l.tiles = off;                       // row tiles [blocks_cap] int2 + 2 ints
-    off = align256(off + (size_t)blocks_cap * 8 + 16);
+    l.tiles = off;                       // row tiles [blocks_cap] int2, then 17 ints of tile meta
+    off = align256(off + (size_t)blocks_cap * 8 + 17 * 4);
     l.cnt = off;
     size_t ntiles = (size_t)blocks_cap * jtiles;
     l.cnt_words = l.sp.nsplit > 1 ? ntiles * (block_m > 64 ? block_m / 64 : 1) : 0;

@@ -145,6 +145,29 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
     return xcd * q + (xcd < r ? xcd : r) + k;
 }
 
+// Work queues of the persistent kernels, one per XCD.  The n units (row
+// tiles) are cut into 8 contiguous ranges; XCD x hands out the items of range
+// x (units * per_unit items, unit-major, so all items of one row tile run on
+// one XCD and share its L2) through counter ctr[x].  A workgroup starts on
+// the range of the XCD it was dispatched to (workgroups go to the XCDs
+// round-robin by id) and, once that range is used up, takes items from the
+// next ranges in turn, so the work stays balanced.  Returns the next item, or
+// -1 once every range is used up; q (0 at the start) is the caller's
+// position in its sequence of ranges.  Called by one thread.
+__device__ __forceinline__ int next_xcd_item(int32_t *ctr, int n, int per_unit, int home, int &q) {
+    while (q < 8) {
+        const int x = (home + q) & 7;
+        const int lo = (int)((int64_t)x * n / 8) * per_unit;
+        const int hi = (int)((int64_t)(x + 1) * n / 8) * per_unit;
+        if (lo < hi) {
+            const int i = __hip_atomic_fetch_add(&ctr[x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lo + i < hi) return lo + i;
+        }
+        ++q;
+    }
+    return -1;
+}
+
 // ------------------------------------------------- LDS pipeline helpers
 
 // 16-byte LDS read of an MFMA operand slice.  (Kept as a typed load: the

@@ -11,8 +11,9 @@
 //
 // Work items are (row tile, 256 output columns); the row tiles are the ones
 // the gate/up prep kernel listed in the workspace (up to 128 consecutive plan
-// rows of one expert).  One workgroup (8 waves) per CU pulls items from a
-// device counter.  Per 128-deep step of the intermediate dimension a stage
+// rows of one expert).  One workgroup (8 waves) per CU pulls items from the
+// per-XCD counters (all column tiles of a row tile on one XCD, so the
+// tile's intermediate rows are fetched into its L2 once).  Per 128-deep step of the intermediate dimension a stage
 // holds the W2 tile (256 rows x 128 B), the tile's intermediate rows
 // (128 x 128 B, contiguous in plan order) and their scales; rows are
 // XOR-swizzled in LDS as in the gate/up pipeline.  FP8 MFMA
@@ -63,17 +64,17 @@ down_pipe_kernel(DownArgs a) {
     const int64_t I = a.I, K = a.K;
     const int njb = a.njb;
     const int ntiles = a.tmeta[0];
-    const int nitems = ntiles * a.ctiles;
+    const int home = blockIdx.x & 7;
+    int q = 0;                                       // position in the XCD ranges (thread 0)
 
     for (;;) {
-        if (tid == 0)
-            sItem[0] = __hip_atomic_fetch_add(&a.tmeta[2], 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) sItem[0] = next_xcd_item(a.tmeta + 9, ntiles, a.ctiles, home, q);
         __syncthreads();
         const int item = sItem[0];
-        if (item >= nitems) break;
-        const int ct = item / ntiles;
-        const int2 tl = a.tiles[item % ntiles];
+        if (item < 0) break;
+        // a row tile's column tiles are consecutive items on one XCD
+        const int ct = item % a.ctiles;
+        const int2 tl = a.tiles[item / a.ctiles];
         const int b = tl.x, nb = tl.y;
         const int e = a.eids[b];
         if (e < 0 || e >= a.E) {

@@ -14,7 +14,10 @@
 // (a list in the workspace); the gate/up kernel is persistent -- one
 // workgroup (8 waves) per CU -- and pulls items from a device-wide counter
 // until none are left, so no workgroup is launched only to exit and the
-// per-launch set-up is paid once per CU.
+// per-launch set-up is paid once per CU.  The counter is one per XCD: each
+// XCD works through its own share of the row tiles, all j-tiles of a row
+// tile back to back, so the tile's gathered activation rows come from that
+// XCD's L2 after the first fetch; idle XCDs take over the others' leftovers.
 //
 // Pipeline.  Each K-block stage holds the W13 tile (256 rows x 128 B) and the
 // gathered activation tile (128 rows x 128 B) in LDS; all waves issue
@@ -95,11 +98,8 @@ tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, 
         if (tid == 1023) carry = before + incl;
         __syncthreads();
     }
-    if (tid == 0) {
-        meta[0] = carry;      // number of row tiles
-        meta[1] = 0;          // work counter of the gate/up kernel
-        meta[2] = 0;          // work counter of the down kernel
-    }
+    if (tid == 0) meta[0] = carry;     // number of row tiles
+    if (tid >= 1 && tid <= 16) meta[tid] = 0;   // per-XCD work counters: gate/up 1..8, down 9..16
 }
 
 template <int BM, int MODE>
@@ -121,17 +121,17 @@ gateup_pipe_kernel(GateUpArgs a) {
     const int l16 = lane & 15, g = lane >> 4;
 
     const int ntiles = a.tmeta[0];
-    const int nitems = ntiles * a.jtiles;
+    const int home = blockIdx.x & 7;
+    int q = 0;                                       // position in the XCD ranges (thread 0)
     for (;;) {
-    if (tid == 0)
-        sItem[0] = __hip_atomic_fetch_add(&a.tmeta[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) sItem[0] = next_xcd_item(a.tmeta + 1, ntiles, a.jtiles, home, q);
     __syncthreads();
     const int item = sItem[0];
-    if (item >= nitems) break;                       // every workgroup ends here
-    // items run over the row tiles fastest: row tiles of one expert that
-    // share a W13 column tile are handed out together
-    const int jt = item / ntiles;
-    const int2 tl = a.tiles[item % ntiles];
+    if (item < 0) break;                             // every workgroup ends here
+    // a row tile's j-tiles are consecutive items on one XCD: its activation
+    // rows are fetched into that XCD's L2 once
+    const int jt = item % a.jtiles;
+    const int2 tl = a.tiles[item / a.jtiles];
     const int b = tl.x, nb = tl.y;
     const int e = a.eids[b];
     if (e < 0 || e >= a.E) {                         // not a plan: skip, keep in step

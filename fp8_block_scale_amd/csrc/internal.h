@@ -32,7 +32,7 @@ struct GateUpArgs {
     uint32_t *cnt;      // split-K arrival counters, one per (block, j-tile)
     int32_t *rpos;      // [R] plan row of each route (pre-filled with -1)
     int2 *tiles;        // [nblocks] row tiles (first block, blocks) of the persistent kernels
-    int32_t *tmeta;     // [3] row-tile count, gate/up and down work counters
+    int32_t *tmeta;     // [17] row-tile count, per-XCD work counters (gate/up 1..8, down 9..16)
     int64_t K, I, R;
     int E, top_k;
     int nkb;            // K / 128
