@@ -165,12 +165,16 @@ MOE_API moe_status moe_plan_capacity(int64_t M, int32_t top_k, int32_t E, int32_
     return MOE_OK;
 }
 
-MOE_API size_t moe_plan_workspace_size(int64_t, int32_t, int32_t, int32_t) { return 0; }
+MOE_API size_t moe_plan_workspace_size(int64_t M, int32_t top_k, int32_t E, int32_t) {
+    if (M <= 0 || top_k <= 0 || E <= 0) return 0;
+    return (size_t)moe::plan_groups(M * top_k, E) * (size_t)E * sizeof(int32_t);
+}
 
 MOE_API moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k,
                             int32_t E, int32_t block_m, int32_t *sorted_token_ids,
                             int64_t sorted_cap, int32_t *expert_ids, int64_t blocks_cap,
-                            int32_t *num_tokens_post_padded, void *, size_t, void *stream) {
+                            int32_t *num_tokens_post_padded, void *workspace,
+                            size_t workspace_bytes, void *stream) {
     int64_t need_sorted, need_blocks;
     moe_status st = moe_plan_capacity(M, top_k, E, block_m, &need_sorted, &need_blocks);
     if (st != MOE_OK) return st;
@@ -191,8 +195,13 @@ MOE_API moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, 
         return hip_check(moe::launch_fill_zero((uint32_t *)num_tokens_post_padded, 1, s),
                          "moe_plan: clear num_tokens_post_padded");
     }
+    // the multi-workgroup build when the caller's workspace holds it
+    const int groups = moe::plan_groups(M * top_k, E);
+    const bool multi = groups > 0 && workspace != nullptr && ((uintptr_t)workspace & 3u) == 0 &&
+                       workspace_bytes >= (size_t)groups * (size_t)E * sizeof(int32_t);
     return hip_check(moe::launch_plan(topk_ids, ids_dtype == MOE_IDS_I64, M * top_k, E, block_m,
-                                      sorted_token_ids, expert_ids, num_tokens_post_padded, s),
+                                      sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                      multi ? (int32_t *)workspace : nullptr, multi ? groups : 0, s),
                      "moe_plan: launch");
 }
 

@@ -9,8 +9,13 @@
 namespace moe {
 
 // ---- step 1: routing plan (plan.hip)
+// Workgroups of the multi-workgroup plan for R routes (0: one-workgroup
+// kernel); it needs groups * E int32 of workspace.
+int plan_groups(int64_t R, int E);
+// ws == nullptr or groups == 0: the one-workgroup kernel.
 hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
-                       int32_t *sorted, int32_t *expert_ids, int32_t *ntp, hipStream_t st);
+                       int32_t *sorted, int32_t *expert_ids, int32_t *ntp, int32_t *ws, int groups,
+                       hipStream_t st);
 
 // ---- step 2: activation quantisation (quant.hip)
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ld,

@@ -1,4 +1,5 @@
-// Step 1: the moe_align_block_size routing plan on one workgroup.
+// Step 1: the moe_align_block_size routing plan (one workgroup, or three
+// launches over many workgroups for large route counts).
 //
 // What is built (FlashInfer PR #4287, PR summary and public-contract
 // section; masked int32/int64 routes from sglang-glm53-flash-sm120 PR #13,
@@ -26,6 +27,7 @@ namespace moe {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int64_t kPlanMultiMin = 4096;      // routes from which several workgroups pay off
 
 __device__ __forceinline__ uint64_t match_mask(int key, int nbits) {
     uint64_t m = ~0ull;
@@ -142,10 +144,200 @@ plan_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwaves,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large route counts: the same plan from three launches over G workgroups.
+// Workgroup g owns the contiguous routes [g C, (g + 1) C); its four waves own
+// consecutive quarters of that range, as in the one-workgroup kernel.
+//   hist     per-workgroup expert counts -> ws[g][e]
+//   scan     one workgroup: per-expert totals, padded offsets, P, sentinels,
+//            expert ids, and in place ws[g][e] = the offset of workgroup g's
+//            first route of expert e (column prefix over g)
+//   scatter  each workgroup recounts its waves, derives per-wave bases from
+//            ws[g][e], and scatters stably (ascending r) as pass 2 above.
+constexpr int kMT = 256;                     // threads per workgroup (4 waves)
+
+constexpr int kMIt = 16;                     // 64-route rows a wave fetches at once
+
+// Expert keys of routes base + 64 i + lane, i < kMIt (E for masked routes
+// and for routes at or past end), fetched together.
+template <typename IdT>
+__device__ __forceinline__ void fetch_keys(const IdT *__restrict__ ids, int64_t base, int64_t end,
+                                           int E, int lane, int (&key)[kMIt]) {
+#pragma unroll
+    for (int i = 0; i < kMIt; ++i) {
+        const int64_t r = base + 64 * i + lane;
+        key[i] = E;
+        if (r < end) {
+            const IdT v = ids[r];
+            if (v >= 0 && v < (IdT)E) key[i] = (int)v;
+        }
+    }
+}
+
+template <typename IdT>
+__device__ __forceinline__ void wave_count(const IdT *__restrict__ ids, int64_t beg, int64_t end,
+                                           int E, int nbits, int lane, int *hrow) {
+    const uint64_t lower = (1ull << lane) - 1ull;
+    for (int64_t base = beg; base < end; base += 64 * kMIt) {
+        int key[kMIt];
+        fetch_keys(ids, base, end, E, lane, key);
+#pragma unroll
+        for (int i = 0; i < kMIt; ++i) {
+            if (base + 64 * i >= end) break;
+            const uint64_t m = match_mask(key[i], nbits);
+            if (key[i] < E && (m & lower) == 0) hrow[key[i]] += __popcll(m);
+        }
+    }
+}
+
+template <typename IdT>
+__global__ void __launch_bounds__(kMT)
+plan_hist_kernel(const IdT *__restrict__ ids, int64_t R, int E, int64_t chunk,
+                 int32_t *__restrict__ ws) {
+    extern __shared__ int hist[];            // [4][E]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nbits = 32 - __clz(E);
+    for (int i = tid; i < 4 * E; i += kMT) hist[i] = 0;
+    __syncthreads();
+    const int64_t sub = chunk / 4;
+    const int64_t beg = (int64_t)blockIdx.x * chunk + w * sub;
+    const int64_t end = beg + sub < R ? beg + sub : R;
+    wave_count(ids, beg, end, E, nbits, lane, hist + w * E);
+    __syncthreads();
+    for (int e = tid; e < E; e += kMT)
+        ws[(int64_t)blockIdx.x * E + e] = hist[e] + hist[E + e] + hist[2 * E + e] + hist[3 * E + e];
+}
+
+__global__ void __launch_bounds__(1024)
+plan_scan_kernel(int32_t *__restrict__ ws, int G, int E, int bm, int64_t R,
+                 int32_t *__restrict__ sorted, int32_t *__restrict__ expert_ids,
+                 int32_t *__restrict__ ntp) {
+    extern __shared__ int sm[];              // counts [G][E], cnt [E], wsum [16]
+    int *hist = sm, *cnt = sm + G * E, *wsum = cnt + E;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int T = blockDim.x;
+    for (int i = tid; i < G * E; i += T) hist[i] = ws[i];
+    __syncthreads();
+    const int seg = (E + T - 1) / T;
+    const int e0 = tid * seg;
+    const int e1 = e0 + seg < E ? e0 + seg : E;
+    int local = 0;
+    for (int e = e0; e < e1; ++e) {
+        int c = 0;
+        for (int g = 0; g < G; ++g) c += hist[g * E + e];
+        cnt[e] = c;
+        local += (c + bm - 1) / bm * bm;
+    }
+    int incl = local;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int q = 0; q < T / 64; ++q) {
+            const int v = wsum[q];
+            wsum[q] = run;
+            run += v;
+        }
+        ntp[0] = run;                         // P
+    }
+    __syncthreads();
+    int off = wsum[w] + incl - local;
+    for (int e = e0; e < e1; ++e) {
+        const int c = cnt[e];
+        const int pad = (c + bm - 1) / bm * bm;
+        int run = off;
+        for (int g = 0; g < G; ++g) {
+            const int h = hist[g * E + e];
+            hist[g * E + e] = run;
+            run += h;
+        }
+        for (int s = off + c; s < off + pad; ++s) sorted[s] = (int32_t)R;
+        for (int b = off / bm; b < (off + pad) / bm; ++b) expert_ids[b] = e;
+        off += pad;
+    }
+    __syncthreads();
+    for (int i = tid; i < G * E; i += T) ws[i] = hist[i];
+}
+
+template <typename IdT>
+__global__ void __launch_bounds__(kMT)
+plan_scatter_kernel(const IdT *__restrict__ ids, int64_t R, int E, int64_t chunk,
+                    const int32_t *__restrict__ ws, int32_t *__restrict__ sorted) {
+    extern __shared__ int hist[];            // [4][E]: counts, then bases
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nbits = 32 - __clz(E);
+    const uint64_t lower = (1ull << lane) - 1ull;
+    for (int i = tid; i < 4 * E; i += kMT) hist[i] = 0;
+    __syncthreads();
+    const int64_t sub = chunk / 4;
+    const int64_t beg = (int64_t)blockIdx.x * chunk + w * sub;
+    const int64_t end = beg + sub < R ? beg + sub : R;
+    wave_count(ids, beg, end, E, nbits, lane, hist + w * E);
+    __syncthreads();
+    for (int e = tid; e < E; e += kMT) {
+        int run = ws[(int64_t)blockIdx.x * E + e];
+        for (int q = 0; q < 4; ++q) {
+            const int h = hist[q * E + e];
+            hist[q * E + e] = run;
+            run += h;
+        }
+    }
+    __syncthreads();
+    int *hrow = hist + w * E;
+    for (int64_t base = beg; base < end; base += 64 * kMIt) {
+        int key[kMIt];
+        fetch_keys(ids, base, end, E, lane, key);
+#pragma unroll
+        for (int i = 0; i < kMIt; ++i) {
+            if (base + 64 * i >= end) break;
+            const uint64_t m = match_mask(key[i], nbits);
+            if (key[i] < E) sorted[hrow[key[i]] + __popcll(m & lower)] = (int32_t)(base + 64 * i + lane);
+            if (key[i] < E && (m & lower) == 0) hrow[key[i]] += __popcll(m);
+        }
+    }
+}
+
+template <typename IdT>
+hipError_t launch_plan_multi(const IdT *ids, int64_t R, int E, int bm, int G, int32_t *ws,
+                             int32_t *sorted, int32_t *expert_ids, int32_t *ntp, hipStream_t st) {
+    int64_t chunk = (R + G - 1) / G;
+    chunk = (chunk + 255) & ~int64_t(255);   // four waves x multiples of 64
+    const size_t lds = (size_t)4 * E * sizeof(int);
+    plan_hist_kernel<IdT><<<G, kMT, lds, st>>>(ids, R, E, chunk, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    plan_scan_kernel<<<1, 1024, (size_t)(G * E + E + 16) * sizeof(int), st>>>(ws, G, E, bm, R,
+                                                                             sorted, expert_ids, ntp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    plan_scatter_kernel<IdT><<<G, kMT, lds, st>>>(ids, R, E, chunk, ws, sorted);
+    return hipGetLastError();
+}
+
 }  // namespace
 
+int plan_groups(int64_t R, int E) {
+    if (R < kPlanMultiMin || E < 1) return 0;
+    int64_t g = (R + 2047) / 2048;
+    const int64_t gmax = (16384 - E - 16) / E;   // the scan holds all counts in 64 KB of LDS
+    if (g > gmax) g = gmax;
+    return g < 2 ? 0 : (int)g;
+}
+
 hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
-                       int32_t *sorted, int32_t *expert_ids, int32_t *ntp, hipStream_t st) {
+                       int32_t *sorted, int32_t *expert_ids, int32_t *ntp, int32_t *ws, int groups,
+                       hipStream_t st) {
+    if (ws != nullptr && groups > 0) {
+        if (ids_i64)
+            return launch_plan_multi((const int64_t *)ids, R, E, block_m, groups, ws, sorted,
+                                     expert_ids, ntp, st);
+        return launch_plan_multi((const int32_t *)ids, R, E, block_m, groups, ws, sorted,
+                                 expert_ids, ntp, st);
+    }
     const int T = kPlanThreads;
     const int nwaves = E <= 512 ? 16 : 8;
     size_t lds = ((size_t)nwaves * E + E + 32) * sizeof(int);

@@ -107,7 +107,9 @@ enum {
 moe_status moe_plan_capacity(int64_t M, int32_t top_k, int32_t E, int32_t block_m,
                              int64_t *sorted_cap, int64_t *blocks_cap);
 
-/* Device workspace moe_plan needs (bytes; may be 0, then workspace may be NULL). */
+/* Device workspace for the fast moe_plan build (bytes, 4-byte aligned; 0
+ * for small route counts).  moe_plan also accepts a NULL or smaller
+ * workspace and then builds the same plan with one workgroup. */
 size_t moe_plan_workspace_size(int64_t M, int32_t top_k, int32_t E, int32_t block_m);
 
 /* Build the routing plan on the device.

@@ -106,19 +106,27 @@ PLAN_CASES = [
 ]
 
 
+def _plan_ws(M, top_k, E, bm, multi):
+    """The multi-workgroup build's workspace, or None for the one-workgroup kernel."""
+    n = moe.moe_plan_workspace_size(M, top_k, E, bm) if multi else 0
+    return torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
+
+
+@pytest.mark.parametrize("multi", [False, True])
 @pytest.mark.parametrize("name,M,dt", PLAN_CASES)
-def test_plan_bit_exact(name, M, dt):
+def test_plan_bit_exact(name, M, dt, multi):
     c = CONFIGS[name]
     M = M or c["M"]
     from moe_workloads import make_routing
     ids, _ = make_routing(c["routing"], M, c["E"], c["top_k"], c["seed"], DEV)
     ids = ids.to(dt).contiguous()
-    log(f"[plan] {name} M={M} {dt}")
+    log(f"[plan] {name} M={M} {dt} multi={multi}")
     sc, bc = moe.moe_plan_capacity(M, c["top_k"], c["E"], c["block_m"])
     s = torch.full((sc,), 0x7F7F7F7F, dtype=torch.int32, device=DEV)
     x = torch.full((bc,), 0x7F7F7F7F, dtype=torch.int32, device=DEV)
     p = torch.empty(1, dtype=torch.int32, device=DEV)
-    moe.moe_plan(ids, c["E"], c["block_m"], s, x, p)
+    moe.moe_plan(ids, c["E"], c["block_m"], s, x, p,
+                 _plan_ws(M, c["top_k"], c["E"], c["block_m"], multi))
     torch.cuda.synchronize()
     rs, rx, rP = plan_ref(ids.cpu().numpy(), c["E"], c["block_m"])
     P = int(p.item())
@@ -128,9 +136,12 @@ def test_plan_bit_exact(name, M, dt):
     assert np.all(s[P:] == 0x7F7F7F7F) and np.all(x[P // c["block_m"]:] == 0x7F7F7F7F)
 
 
+@pytest.mark.parametrize("multi", [False, True])
 @pytest.mark.parametrize("M,top_k,E,bm", [(1, 1, 1, 16), (3, 5, 7, 16), (1000, 3, 1, 128),
-                                          (777, 7, 1024, 32), (5000, 13, 64, 64), (64, 1, 3, 256)])
-def test_plan_edge_shapes(M, top_k, E, bm):
+                                          (777, 7, 1024, 32), (5000, 13, 64, 64), (64, 1, 3, 256),
+                                          (4096, 1, 257, 16), (100000, 2, 3, 128),
+                                          (4099, 8, 1024, 16)])
+def test_plan_edge_shapes(M, top_k, E, bm, multi):
     g = torch.Generator(device=DEV)
     g.manual_seed(M * 31 + E)
     ids = torch.randint(-2, E + 2, (M, top_k), generator=g, device=DEV, dtype=torch.int32)
@@ -138,7 +149,8 @@ def test_plan_edge_shapes(M, top_k, E, bm):
     s = torch.full((sc,), -7, dtype=torch.int32, device=DEV)
     x = torch.full((bc,), -7, dtype=torch.int32, device=DEV)
     p = torch.empty(1, dtype=torch.int32, device=DEV)
-    moe.moe_plan(ids, E, bm, s, x, p)
+    log(f"[plan edge] M={M} top_k={top_k} E={E} bm={bm} multi={multi}")
+    moe.moe_plan(ids, E, bm, s, x, p, _plan_ws(M, top_k, E, bm, multi))
     torch.cuda.synchronize()
     rs, rx, rP = plan_ref(ids.cpu().numpy(), E, bm)
     P = int(p.item())
