@@ -58,7 +58,7 @@ typedef enum {
     MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent        */
     MOE_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned  */
     MOE_ERR_CAPACITY = 4,    /* plan buffers or workspace too small           */
-    MOE_ERR_UNSUPPORTED = 5, /* valid request this build does not implement   */
+    MOE_ERR_UNSUPPORTED = 5, /* valid request the library does not implement  */
     MOE_ERR_HIP = 6          /* a HIP runtime call failed                     */
 } moe_status;
 

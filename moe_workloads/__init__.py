@@ -6,7 +6,8 @@ produces.  Weight storage (E4M3 codes with one FP32 scale per 128x128 block)
 uses torch's own ``float8_e4m3fn`` cast after a clamp to +-448, a library
 routine that is neither the oracle's codec nor the GPU kernels' converter.
 
-Workloads (sizes as named by the method's pages and the task):
+Workloads (the sizes the method's pages measure, plus a decode, a skewed and a
+power-of-two-scale case):
   tiny    M=4,    E=8,   K=256,  I=256,  top_k=2,  block_m=16
   decode  M=1,    E=257, K=7168, I=256,  top_k=9,  block_m=16
   page1   M=4096, E=288, K=4096, I=1024, top_k=8,  block_m=64 (M sweep 1024..8192)

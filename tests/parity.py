@@ -1,7 +1,7 @@
 """Shared helpers for the GPU parity tests: run the HIP path through the C ABI
 binding, run the oracle on the same seeded inputs, and compare.
 
-Bars (the task's stated tolerances):
+Bars (the stated parity tolerances):
   * plan (sorted ids, expert ids, padded length) and activation codes and
     scales: bit-exact;
   * intermediate FP8 codes: at most 1e-4 of the codes of valid rows may
