@@ -112,7 +112,8 @@ gateup_pipe_kernel(GateUpArgs a) {
     float *sSw = sSa + kStages * kRows;                        // [2][kMaxKb] w13_s gate, up
     int *sTok = reinterpret_cast<int *>(sSw + 2 * kMaxKb);      // [128] token or -1
     float *sRed = reinterpret_cast<float *>(sTok + kRows);      // [4][128]
-    int *sItem = reinterpret_cast<int *>(sRed + 4 * kRows);      // [1]
+    int *sItem = reinterpret_cast<int *>(sRed + 4 * kRows);      // [4]
+    uint8_t *sPf = reinterpret_cast<uint8_t *>(sItem + 4);        // [8][256] prefetch sink
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -209,6 +210,22 @@ gateup_pipe_kernel(GateUpArgs a) {
             __builtin_amdgcn_global_load_lds(ssrc + kb, sSa + stage * kRows + w * 16, 4, 0, 0);
     };
 
+    // L2 prefetch of W13 rows: lane l of wave w touches tile row 32w + (l & 31)
+    // at byte 64 (l >> 5) of a K-block -- both 64-byte halves of each of the
+    // wave's 32 rows -- with a 4-byte LDS-DMA load into a per-wave sink, so
+    // there is no register result; the ring's own loads of that K-block then
+    // hit L2.
+    const uint8_t *wpf;
+    {
+        const int row = w * 32 + (lane & 31);
+        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+        wpf = a.w13 + ((int64_t)e * twoI + n) * K + 64 * (lane >> 5);
+    }
+    auto prefetch = [&](int kb) {
+        const int kc = kb < nkb ? kb : nkb - 1;
+        __builtin_amdgcn_global_load_lds(wpf + (int64_t)kc * 128, sPf + w * 256, 4, 0, 0);
+    };
+
     constexpr int NU = 4;
     const bool wave_rows = wm * 64 < nrows;
 
@@ -218,23 +235,30 @@ gateup_pipe_kernel(GateUpArgs a) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Issue groups: the prologue's two, then one per K-block step, each =
+    // [ring refill of K-block j + 2 (while one is left)] [prefetch of j + 5].
+    // Loads complete in issue order, so at step kb everything after the
+    // refill of kb is the prefetch of its group and the next group.  A
+    // prefetch must be done three steps after its issue, before the refill of
+    // the K-block it covers is issued.
     issue(0, 0);
+    prefetch(3);
     if (nkb > 1) issue(1, 1);
+    prefetch(4);
 
     for (int kb = 0; kb < nkb; ++kb) {
         const int stage = kb % kStages;
-        if (kb + 2 < nkb) {
-            issue((kb + 2) % kStages, kb + 2);
-            wait_vmcnt<2 * kPerStage>();
-        } else if (kb + 1 < nkb) {
-            wait_vmcnt<kPerStage>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        if (kb + 1 < nkb)
+            wait_vmcnt<kPerStage + 2>();
+        else
+            wait_vmcnt<2>();
         // Every wave has waited for its own part of this stage; the barrier
-        // makes the whole stage visible.  A plain s_barrier: __syncthreads()
-        // would also drain the later stages still in flight.
+        // makes the whole stage visible, and every wave is past the multiply
+        // of kb - 1, whose stage the refill below overwrites.  A plain
+        // s_barrier: __syncthreads() would also drain the loads in flight.
         stage_barrier();
+        if (kb + 2 < nkb) issue((kb + 2) % kStages, kb + 2);
+        prefetch(kb + 5);
 
         if (wave_rows) {
             const float sbg = sSw[kb];
@@ -288,10 +312,8 @@ gateup_pipe_kernel(GateUpArgs a) {
                 }
             }
         }
-        // all reads of this stage are consumed (their results fed the MFMAs)
-        // before any wave refills it two iterations later
-        stage_barrier();
     }
+    wait_vmcnt<0>();                                 // the last prefetches land in the sink
     __syncthreads();
 
     // ---- SwiGLU + per-row 128-group FP8 requantisation
@@ -340,7 +362,8 @@ gateup_pipe_kernel(GateUpArgs a) {
 }
 
 constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + kStages * kRows * 4 +
-                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16;
+                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16 + 8 * 256;
+static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 int num_cus() {
     static int cached[64] = {0};
