@@ -79,7 +79,7 @@ SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t K, int64_t 
 }
 
 struct WsLayout {
-    size_t hq, hs, y, rpos, tiles, cnt, part, total;
+    size_t hq, hs, y, ys, rpos, tiles, cnt, part, total;
     size_t cnt_words;                 // split-K counters, zeroed per call
     SplitChoice sp;
 };
@@ -96,8 +96,10 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block
     l.hs = off;
     off = align256(off + (size_t)sorted_cap * (I / 128) * 4);
     const size_t R = (size_t)M * top_k;
-    l.y = off;
-    off = align256(off + R * K * 4);
+    l.y = off;                           // FP16 [R, K], then FP32 scales [R, K / 64]
+    off = align256(off + R * K * 2);
+    l.ys = off;
+    off = align256(off + R * (size_t)(K / 64) * 4);
     l.rpos = off;
     off = align256(off + R * 4);
     l.tiles = off;                       // row tiles [blocks_cap] int2, then 17 ints of tile meta
@@ -356,7 +358,8 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
     da.sorted = sorted_token_ids;
     da.eids = expert_ids;
     da.ntp = num_tokens_post_padded;
-    da.y = (float *)(ws + l.y);
+    da.y16 = (uint16_t *)(ws + l.y);
+    da.ys = (float *)(ws + l.ys);
     da.K = K;
     da.I = I;
     da.R = M * top_k;
@@ -372,7 +375,8 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                                    : moe::launch_down(da, block_m, e8, s),
                    "moe_fp8_down_reduce: down launch");
     if (st != MOE_OK) return st;
-    return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const float *)(ws + l.y),
+    return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const uint16_t *)(ws + l.y),
+                                          (const float *)(ws + l.ys), topk_weights,
                                           (const int32_t *)(ws + l.rpos), M, K, top_k, s),
                      "moe_fp8_down_reduce: finalize launch");
 }

@@ -202,6 +202,29 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// ------------------------------------------------- per-route partial rows
+// The down stage parks each route's FP32 row as FP16 values times one FP32
+// scale per 64 columns: s = amax / 2^15, so every value / s lies in
+// [-2^15, 2^15] (inside FP16's range) and keeps 11 significant bits.
+
+__device__ __forceinline__ void y16_scale(float amax, float &s, float &inv) {
+    s = amax * (1.0f / 32768.0f);
+    inv = amax > 0.f ? 32768.0f / amax : 0.f;
+}
+
+__device__ __forceinline__ uint2 f32x4_to_f16x4(const v4f &v, float inv) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a = {(_Float16)(v[0] * inv), (_Float16)(v[1] * inv)};
+    const h2 b = {(_Float16)(v[2] * inv), (_Float16)(v[3] * inv)};
+    return uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+__device__ __forceinline__ v4f f16x4_to_f32x4(const uint2 &u) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a = __builtin_bit_cast(h2, u.x), b = __builtin_bit_cast(h2, u.y);
+    return v4f{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+}
+
 // ------------------------------------------------------------ wave utils
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

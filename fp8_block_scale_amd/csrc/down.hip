@@ -4,13 +4,15 @@
 // What is computed (FlashInfer PR #4287, PR summary and the FP32-scale note
 // of its final kernel performance section): for plan row p of block b
 // (expert e, route r, token t = r / top_k)
-//   y[p, c] = sum_jb h_s[p, jb] * w2_s[e, c / 128, jb]
+//   y[r, c] = sum_jb h_s[p, jb] * w2_s[e, c / 128, jb]
 //                    * sum_{j in jb} h_q[p, j] * W2[e, c, j]           (FP32)
-//   out[t, c] += topk_weights[r] * y[p, c]
-// Each route's weighted row goes to a route-indexed FP32 buffer y[r, :]
-// (plain stores, no atomics); the finalize kernel then adds, per token, its
-// top_k rows in route order to the caller's BF16 output and rounds once --
-// the output is an accumulator, and the reduction is deterministic.
+//   out[t, c] += topk_weights[r] * y[r, c]
+// Each route's row goes to a route-indexed buffer y[r, :] (plain stores, no
+// atomics) as FP16 values with one FP32 scale per 64 columns (amax / 2^15:
+// 2^-12 relative rounding, FP32's range, half the bytes of FP32); the
+// finalize kernel then adds, per token, its top_k rows times their router
+// weights in route order to the caller's BF16 output and rounds once -- the
+// output is an accumulator, and the reduction is deterministic.
 //
 // Tiling: one workgroup = one plan block (BM rows) x 256 output columns; four
 // waves take 64 columns each (four 16-row W2 subtiles, all inside one
@@ -173,12 +175,22 @@ down_kernel(DownArgs a) {
 #pragma unroll
     for (int u = 0; u < C::NU; ++u) {
         const int row = wm * C::TM + u * 16 + l16;
+        // the row's 64 columns of this wave: 16 values in each of 4 lanes
+        float m = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[s][u][i]));
+        m = wave_max_xor(m, 16);
+        m = wave_max_xor(m, 32);
         const int r = sRt[row];
         if (r < 0) continue;
-        const float wr = a.topk_w[r];
-        float *dst = a.y + (int64_t)r * K + col0 + 4 * g;
+        float sc, inv;
+        y16_scale(m, sc, inv);
+        uint16_t *dst = a.y16 + (int64_t)r * K + col0 + 4 * g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) *reinterpret_cast<v4f *>(dst + 16 * s) = acc[s][u] * wr;
+        for (int s = 0; s < 4; ++s) *reinterpret_cast<uint2 *>(dst + 16 * s) = f32x4_to_f16x4(acc[s][u], inv);
+        if (g == 0) a.ys[(int64_t)r * (K >> 6) + (col0 >> 6)] = sc;
     }
 }
 
@@ -414,16 +426,27 @@ down_stream_kernel(DownArgs a) {
     }
     __syncthreads();
 
-    // ---- y[r, c] = w_r * parked results, valid rows and columns only
+    // ---- y[r, c] = parked results, valid rows and columns only.  Lanes
+    // 16q .. 16q + 15 of a wave hold one row's 64-column group (the trip
+    // count is a multiple of 64, so whole waves iterate together).
     for (int idx = tid; idx < nct * nvp * 64; idx += C::NT) {
         const int c4 = idx & 63;
         const int rest = idx >> 6;
         const int row = rest % nvp, t = rest / nvp;
         const int rt = sTok[row];
         const int64_t col = (int64_t)(ct0 + t) * 256 + 4 * c4;
-        if (rt < 0 || col >= K) continue;
+        const bool ok = rt >= 0 && col < K;
         const v4f v = *reinterpret_cast<const v4f *>(sY + (t * C::RP + row) * C::YROW + 4 * c4);
-        *reinterpret_cast<v4f *>(a.y + (int64_t)rt * K + col) = v * a.topk_w[rt];
+        float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        m = wave_max_xor(m, 1);
+        m = wave_max_xor(m, 2);
+        m = wave_max_xor(m, 4);
+        m = wave_max_xor(m, 8);
+        if (!ok) continue;
+        float sc, inv;
+        y16_scale(m, sc, inv);
+        *reinterpret_cast<uint2 *>(a.y16 + (int64_t)rt * K + col) = f32x4_to_f16x4(v, inv);
+        if ((c4 & 15) == 0) a.ys[(int64_t)rt * (K >> 6) + (col >> 6)] = sc;
     }
 }
 
@@ -440,28 +463,35 @@ fill_kernel(uint32_t *__restrict__ p, size_t n, uint32_t v) {
 // multiplied), then added in route order (deterministic), then the previous
 // output, then one round to nearest even BF16.
 __global__ void __launch_bounds__(256)
-finalize_kernel(uint16_t *__restrict__ out, const float *__restrict__ y,
+finalize_kernel(uint16_t *__restrict__ out, const uint16_t *__restrict__ y16,
+                const float *__restrict__ ys, const float *__restrict__ topk_w,
                 const int32_t *__restrict__ rpos, int64_t M, int64_t K, int top_k) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element of out
     if (i >= M * K) return;
     const int64_t t = i / K;
-    const float *src = y + t * top_k * K + (i - t * K);
+    const int64_t c = i - t * K;
+    const uint16_t *src = y16 + t * top_k * K + c;
+    const float *ssrc = ys + t * top_k * (K >> 6) + (c >> 6);
     const int32_t *rp = rpos + t * top_k;
+    const float *wt = topk_w + t * top_k;
     v4f f = v4f{0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < top_k; j0 += 8) {
-        v4f v[8];
+        uint2 v[8];
+        float sw[8];
         bool ok[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             ok[q] = false;
             if (j0 + q < top_k) {
                 ok[q] = rp[j0 + q] >= 0;
-                v[q] = *reinterpret_cast<const v4f *>(src + (int64_t)(j0 + q) * K);
+                v[q] = *reinterpret_cast<const uint2 *>(src + (int64_t)(j0 + q) * K);
+                sw[q] = ssrc[(int64_t)(j0 + q) * (K >> 6)] * wt[j0 + q];
             }
         }
+        // routes that are not in the plan hold stale rows: select, not multiply
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            if (ok[q]) f += v[q];
+            if (ok[q]) f += f16x4_to_f32x4(v[q]) * sw[q];
     }
     const uint2 o = *reinterpret_cast<const uint2 *>(out + i);
     const float r0 = bf16_bits_to_f32(o.x & 0xffffu) + f[0];
@@ -528,11 +558,11 @@ hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t 
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(uint16_t *out, const float *y, const int32_t *rpos, int64_t M,
-                           int64_t K, int top_k, hipStream_t st) {
+hipError_t launch_finalize(uint16_t *out, const uint16_t *y16, const float *ys, const float *topk_w,
+                           const int32_t *rpos, int64_t M, int64_t K, int top_k, hipStream_t st) {
     int64_t blocks = (M * K / 4 + 255) / 256;
     if (blocks == 0) return hipSuccess;
-    finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(out, y, rpos, M, K, top_k);
+    finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(out, y16, ys, topk_w, rpos, M, K, top_k);
     return hipGetLastError();
 }
 

@@ -1,24 +1,35 @@
 // Step 5 for large grids: the down-projection GEMM as a persistent kernel
-// with a three-stage LDS pipeline fed by direct global->LDS loads.
+// whose three-stage LDS ring runs without a break across all of a
+// workgroup's work items.
 //
 // Same arithmetic as down.hip (FlashInfer PR #4287, PR summary and the FP32
 // scale note of its final kernel performance section): for plan row p of
 // expert e holding route r,
-//   y[r, c] = w_r * sum_jb h_s[p, jb] * w2_s[e, c / 128, jb]
-//                         * sum_{j in jb} h_q[p, j] * W2[e, c, j]     (FP32)
-// written to the route-indexed buffer y[r, :] (the finalize kernel adds a
-// token's routes in route order).
+//   y[r, c] = sum_jb h_s[p, jb] * w2_s[e, c / 128, jb]
+//                  * sum_{j in jb} h_q[p, j] * W2[e, c, j]              (FP32)
+// written to the route-indexed buffer y[r, :] as FP16 with one FP32 scale per
+// 64 columns (the finalize kernel adds a token's routes, times their router
+// weights, in route order).
 //
 // Work items are (row tile, 256 output columns); the row tiles are the ones
 // the gate/up prep kernel listed in the workspace (up to 128 consecutive plan
-// rows of one expert).  One workgroup (8 waves) per CU pulls items from the
-// per-XCD counters (all column tiles of a row tile on one XCD, so the
-// tile's intermediate rows are fetched into its L2 once).  Per 128-deep step of the intermediate dimension a stage
-// holds the W2 tile (256 rows x 128 B), the tile's intermediate rows
-// (128 x 128 B, contiguous in plan order) and their scales; rows are
-// XOR-swizzled in LDS as in the gate/up pipeline.  FP8 MFMA
-// (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per step,
-// or with power-of-two scales as E8M0 exponents inside the MFMA.
+// rows of one expert).  Items all cost about the same, so the schedule is
+// static: the item list is cut into one contiguous range per XCD (workgroup
+// i runs on XCD i mod 8), and the XCD's workgroups take its items round
+// robin -- at any moment an XCD works on two or three row tiles, whose
+// intermediate rows its L2 then holds for all their column tiles.
+//
+// Pipeline.  A workgroup's items form one sequence of 128-deep steps of the
+// intermediate dimension.  Per step a stage holds the W2 tile (256 rows x
+// 128 B), the item's intermediate rows (128 x 128 B, contiguous in plan
+// order) and a per-wave metadata slot (16 intermediate-row scales, the two
+// W2 block scales, 16 route ids), all brought by direct global->LDS loads two
+// steps ahead -- across item boundaries too, so an item's first steps are
+// already in flight while the previous item finishes.  Rows are XOR-swizzled
+// in LDS as in the gate/up pipeline.  A 4-byte load per lane five steps ahead
+// touches the W2 rows a step will need, so the ring's own loads hit L2.  FP8
+// MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per
+// step, or with power-of-two scales as E8M0 exponents inside the MFMA.
 #include <type_traits>
 
 #include "common.h"
@@ -36,7 +47,8 @@ constexpr int kHBytes = kRows * 128;
 constexpr int kWInstr = kWBytes / 1024 / 8;
 constexpr int kHInstr = kHBytes / 1024 / 8;
 constexpr int kPerStage = kWInstr + kHInstr + 1;
-constexpr int kMaxJb = 256;                   // I <= 32768
+constexpr int kMeta = 64;                     // floats per wave and stage
+constexpr int kMetaRt = 18;                   // route ids start here
 
 __device__ __forceinline__ v8i join8q(const u32x4 &lo, const u32x4 &hi) {
     v8i r;
@@ -45,190 +57,274 @@ __device__ __forceinline__ v8i join8q(const u32x4 &lo, const u32x4 &hi) {
     return r;
 }
 
+// 4-byte global -> LDS copy per lane: lane l writes LDS bytes [lds + 4 l, +4).
+__device__ __forceinline__ void lds_dma4(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
+
+// The row-tile list and the plan's expert ids do not change while the
+// kernel runs: read through the constant address space, a uniform index
+// becomes a scalar load, which does not join the vector loads' in-order
+// count (a vector load here would wait for the whole ring).
+typedef const __attribute__((address_space(4))) int32_t *const_i32_p;
+
+struct Item {
+    int b, nb, e, ct;
+    bool ok;            // expert id in range (else: loads from expert 0, nothing computed)
+};
+
 template <int BM, bool E8M0>
 __global__ void __launch_bounds__(kNT, 1)
 down_pipe_kernel(DownArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *sW = smem;                                            // [kStages][256][128]
-    uint8_t *sH = smem + kStages * kWBytes;                        // [kStages][128][128]
-    float *sHs = reinterpret_cast<float *>(sH + kStages * kHBytes); // [kStages][128]
-    float *sSw = sHs + kStages * kRows;                            // [2][kMaxJb] w2_s blocks
-    int *sRt = reinterpret_cast<int *>(sSw + 2 * kMaxJb);          // [128] route or -1
-    int *sItem = sRt + kRows;
+    uint8_t *sW = smem;                                                 // [kStages][256][128]
+    uint8_t *sH = smem + kStages * kWBytes;                             // [kStages][128][128]
+    float *sMeta = reinterpret_cast<float *>(sH + kStages * kHBytes);   // [kStages][8][kMeta]
+    uint8_t *sPf = reinterpret_cast<uint8_t *>(sMeta + kStages * 8 * kMeta);   // [8][256] sink
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = w & 3, wm = w >> 2;
     const int l16 = lane & 15, g = lane >> 4;
+    const int sub = lane >> 3, slot = lane & 7;
     const int64_t I = a.I, K = a.K;
     const int njb = a.njb;
-    const int ntiles = a.tmeta[0];
-    const int home = blockIdx.x & 7;
-    int q = 0;                                       // position in the XCD ranges (thread 0)
 
-    for (;;) {
-        if (tid == 0) sItem[0] = next_xcd_item(a.tmeta + 9, ntiles, a.ctiles, home, q);
-        __syncthreads();
-        const int item = sItem[0];
-        if (item < 0) break;
-        // a row tile's column tiles are consecutive items on one XCD
-        const int ct = item % a.ctiles;
-        const int2 tl = a.tiles[item / a.ctiles];
-        const int b = tl.x, nb = tl.y;
-        const int e = a.eids[b];
-        if (e < 0 || e >= a.E) {
-            __syncthreads();
-            continue;
-        }
-        const int nrows = nb * BM;
-        const int64_t p0 = (int64_t)b * BM;
-        const int64_t c0 = (int64_t)ct * 256;
+    // ---- static schedule: this workgroup's items are lo + j + k * nwg < hi
+    const int64_t N = (int64_t)((const_i32_p)a.tmeta)[0] * a.ctiles;
+    const int grid = (int)gridDim.x;
+    const int ndom = grid < 8 ? grid : 8;
+    const int d = (int)blockIdx.x % ndom, j = (int)blockIdx.x / ndom;
+    const int nwg = (grid - d + ndom - 1) / ndom;
+    const int64_t lo = N * d / ndom, hi = N * (d + 1) / ndom;
+    const int64_t mine = hi - lo > j ? (hi - lo - j + nwg - 1) / nwg : 0;
+    const int64_t T = mine * njb;                    // steps
+    if (T == 0) return;
+
+    auto item_at = [&](int64_t k) {
+        const int64_t item = lo + j + k * nwg;
+        const int rt = __builtin_amdgcn_readfirstlane((int)(item / a.ctiles));
+        Item it;
+        it.ct = __builtin_amdgcn_readfirstlane((int)(item - (int64_t)rt * a.ctiles));
+        const const_i32_p tl = (const_i32_p)a.tiles + 2 * (int64_t)rt;   // int2 {first block, blocks}
+        it.b = __builtin_amdgcn_readfirstlane(tl[0]);
+        it.nb = __builtin_amdgcn_readfirstlane(tl[1]);
+        const int e = __builtin_amdgcn_readfirstlane(((const_i32_p)a.eids)[it.b]);
+        it.ok = e >= 0 && e < a.E;
+        it.e = it.ok ? e : 0;
+        return it;
+    };
+
+    // ---- load side: item and step of the next refill, and this lane's sources
+    int64_t kl = 0;
+    int jl = 0;
+    Item il = item_at(0);
+    const uint8_t *wsrc[kWInstr];
+    const uint8_t *hsrc[kHInstr];
+    const uint8_t *msrc;
+    int mstep;
+    auto set_sources = [&](const Item &it) {
+        const int nrows = it.nb * BM;
+        const int64_t p0 = (int64_t)it.b * BM;
+        const int64_t c0 = (int64_t)it.ct * 256;
         const int ncols = K - c0 < 256 ? (int)(K - c0) : 256;     // 128 or 256
-
-        if (tid < kRows) {
-            int r = -1;
-            if (tid < nrows) {
-                int v = a.sorted[p0 + tid];
-                if (v >= 0 && (int64_t)v < a.R) r = v;
-            }
-            sRt[tid] = r;
-        }
-        {
-            // the two 128-column scale blocks of this column tile
-            const float *s0 = a.w2s + ((int64_t)e * (K >> 7) + (c0 >> 7)) * njb;
-            for (int i = tid; i < njb; i += kNT) {
-                sSw[i] = s0[i];
-                sSw[kMaxJb + i] = ncols > 128 ? s0[njb + i] : 0.f;
-            }
-        }
-        __syncthreads();
-
-        // DMA sources of this lane
-        const int sub = lane >> 3, slot = lane & 7;
-        const uint8_t *wsrc[kWInstr];
 #pragma unroll
         for (int i = 0; i < kWInstr; ++i) {
             const int row = (w * kWInstr + i) * 8 + sub;              // 0..255
             const int64_t c = c0 + (row < ncols ? row : 0);
-            wsrc[i] = a.w2 + ((int64_t)e * K + c) * I + (slot ^ (row & 7)) * 16;
+            wsrc[i] = a.w2 + ((int64_t)it.e * K + c) * I + (slot ^ (row & 7)) * 16;
         }
-        const uint8_t *hsrc[kHInstr];
 #pragma unroll
         for (int i = 0; i < kHInstr; ++i) {
             const int row = (w * kHInstr + i) * 8 + sub;
             const int64_t p = p0 + (row < nrows ? row : 0);
             hsrc[i] = a.hq + p * I + (slot ^ (row & 7)) * 16;
         }
-        const float *ssrc;
-        {
-            const int row = w * 16 + (lane & 15);
-            ssrc = a.hs + (p0 + (row < nrows ? row : 0)) * njb;
+        // metadata slot of wave w: [0, 16) scales of rows 16w.., [16, 18) the
+        // W2 block scales of the item's two 128-column blocks, [18, 34) route
+        // ids of rows 16w..
+        if (lane < 16) {
+            const int row = w * 16 + lane;
+            msrc = reinterpret_cast<const uint8_t *>(a.hs + (p0 + (row < nrows ? row : 0)) * njb);
+            mstep = 4;
+        } else if (lane < kMetaRt) {
+            const int64_t blk = (c0 >> 7) + (lane == 17 && ncols > 128 ? 1 : 0);
+            msrc = reinterpret_cast<const uint8_t *>(a.w2s + ((int64_t)it.e * (K >> 7) + blk) * njb);
+            mstep = 4;
+        } else {
+            const int row = w * 16 + lane - kMetaRt;                  // lanes past 33 load nothing
+            msrc = reinterpret_cast<const uint8_t *>(a.sorted + p0 + (row < nrows ? row : 0));
+            mstep = 0;
         }
-        auto issue = [&](int stage, int jb) {
-            uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
+    };
+    set_sources(il);
+    auto issue = [&](int stage) {
+        uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
 #pragma unroll
-            for (int i = 0; i < kWInstr; ++i)
-                __builtin_amdgcn_global_load_lds(wsrc[i] + (int64_t)jb * 128, dw + i * 1024, 16, 0, 0);
-            uint8_t *dh = sH + stage * kHBytes + (w * kHInstr) * 1024;
+        for (int i = 0; i < kWInstr; ++i) lds_dma16(wsrc[i] + (int64_t)jl * 128, dw + i * 1024);
+        uint8_t *dh = sH + stage * kHBytes + (w * kHInstr) * 1024;
 #pragma unroll
-            for (int i = 0; i < kHInstr; ++i)
-                __builtin_amdgcn_global_load_lds(hsrc[i] + (int64_t)jb * 128, dh + i * 1024, 16, 0, 0);
-            if (lane < 16)
-                __builtin_amdgcn_global_load_lds(ssrc + jb, sHs + stage * kRows + w * 16, 4, 0, 0);
-        };
+        for (int i = 0; i < kHInstr; ++i) lds_dma16(hsrc[i] + (int64_t)jl * 128, dh + i * 1024);
+        if (lane < kMetaRt + 16) lds_dma4(msrc + jl * mstep, sMeta + (stage * 8 + w) * kMeta);
+        if (++jl == njb && kl + 1 < mine) {
+            jl = 0;
+            il = item_at(++kl);
+            set_sources(il);
+        }
+    };
 
-        constexpr int NU = 4;
-        const bool wave_on = (wm * 64 < nrows) && (64 * wn < ncols);
-        v4f acc[4][NU];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
+    // ---- prefetch side: lane l of wave w touches W2 tile row 32w + (l & 31)
+    // at byte 64 (l >> 5) of the step five ahead of the multiply
+    int64_t kp = 0;
+    int jp = 0;
+    const uint8_t *wpf;
+    auto set_pf = [&](const Item &it) {
+        const int64_t c0 = (int64_t)it.ct * 256;
+        const int ncols = K - c0 < 256 ? (int)(K - c0) : 256;
+        const int row = w * 32 + (lane & 31);
+        const int64_t c = c0 + (row < ncols ? row : 0);
+        wpf = a.w2 + ((int64_t)it.e * K + c) * I + 64 * (lane >> 5);
+    };
+    auto pf_advance = [&]() {
+        if (jp + 1 < njb) {
+            ++jp;
+        } else if (kp + 1 < mine) {
+            jp = 0;
+            set_pf(item_at(++kp));
+        }                                            // past the last step: stay on it
+    };
+    set_pf(il);
+    for (int i = 0; i < 3; ++i) pf_advance();        // step 3
+    auto prefetch = [&]() {
+        lds_dma4(wpf + (int64_t)jp * 128, sPf + w * 256);
+        pf_advance();
+    };
 
-        // One pipeline step: wait for stage ST (step jb), refill stage
-        // (ST + 2) % 3 with step jb + 2, multiply.  The stage indices are
-        // compile-time constants so the compiler can tell the refilled and
-        // the read LDS ranges apart and keeps the refill in flight.
-        auto step = [&](auto st_c, int jb) {
-            constexpr int ST = decltype(st_c)::value;
-            if (jb + 2 < njb) {
-                issue((ST + 2) % kStages, jb + 2);
-                wait_vmcnt<2 * kPerStage>();
-            } else if (jb + 1 < njb) {
-                wait_vmcnt<kPerStage>();
-            } else {
-                wait_vmcnt<0>();
+    // ---- multiply side
+    int64_t kc = 0;
+    int jc = 0;
+    Item ic = il;
+    constexpr int NU = 4;
+    v4f acc[4][NU];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // One step: wait for its stage, barrier, refill the stage the previous
+    // step used (every wave is past that multiply), prefetch, multiply; on an
+    // item's last step store its rows.  Groups = [refill][prefetch]; loads
+    // complete in issue order, so after the refill of step t only the
+    // prefetch of its group and the next group may still be in flight.  The
+    // stage indices are compile-time constants so the compiler can tell the
+    // refilled and the read LDS ranges apart.
+    auto step = [&](auto st_c, int64_t t) {
+        constexpr int ST = decltype(st_c)::value;
+        if (t + 1 < T)
+            wait_vmcnt<kPerStage + 2>();
+        else
+            wait_vmcnt<2>();
+        stage_barrier();
+        if (t + 2 < T) issue((ST + 2) % kStages);
+        prefetch();
+
+        const int nrows = ic.nb * BM;
+        const int64_t c0 = (int64_t)ic.ct * 256;
+        const int ncols = K - c0 < 256 ? (int)(K - c0) : 256;
+        const bool wave_on = ic.ok && (wm * 64 < nrows) && (64 * wn < ncols);
+        const float *meta = sMeta + ST * 8 * kMeta;
+        if (wave_on) {
+            // this wave's 64 columns lie in one 128-column scale block
+            const float sb = meta[w * kMeta + 16 + (wn >= 2 ? 1 : 0)];
+            const uint8_t *Ws = sW + ST * kWBytes;
+            const uint8_t *Hs = sH + ST * kHBytes;
+            v8i wq[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = 64 * wn + 16 * s + l16;
+                const uint8_t *rp = Ws + row * 128;
+                const u32x4 lo4 = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                const u32x4 hi4 = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                wq[s] = join8q(lo4, hi4);
             }
-            stage_barrier();
-            if (wave_on) {
-                // this wave's 64 columns lie in one 128-column scale block
-                const float sb = sSw[(wn >= 2 ? kMaxJb : 0) + jb];
-                const uint8_t *Ws = sW + ST * kWBytes;
-                const uint8_t *Hs = sH + ST * kHBytes;
-                const float *Ss = sHs + ST * kRows;
-                v8i wq[4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int row = 64 * wn + 16 * s + l16;
-                    const uint8_t *rp = Ws + row * 128;
-                    const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
-                    const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
-                    wq[s] = join8q(lo, hi);
-                }
+            for (int u = 0; u < NU; ++u) {
+                if (wm * 64 + u * 16 >= nrows) continue;
+                const int row = wm * 64 + u * 16 + l16;
+                const uint8_t *rp = Hs + row * 128;
+                const u32x4 lo4 = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                const u32x4 hi4 = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                const v8i B = join8q(lo4, hi4);
+                const float sa = meta[(row >> 4) * kMeta + (row & 15)];
+                if constexpr (E8M0) {
+                    const int ea = e8m0_of(sb), eb = e8m0_of(sa);
 #pragma unroll
-                for (int u = 0; u < NU; ++u) {
-                    if (wm * 64 + u * 16 >= nrows) continue;
-                    const int row = wm * 64 + u * 16 + l16;
-                    const uint8_t *rp = Hs + row * 128;
-                    const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
-                    const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
-                    const v8i B = join8q(lo, hi);
-                    const float sa = Ss[row];
-                    if constexpr (E8M0) {
-                        const int ea = e8m0_of(sb), eb = e8m0_of(sa);
+                    for (int s = 0; s < 4; ++s)
+                        acc[s][u] = mfma16x16x128_e8m0(wq[s], B, acc[s][u], ea, eb);
+                } else {
+                    const float f = sa * sb;
 #pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            acc[s][u] = mfma16x16x128_e8m0(wq[s], B, acc[s][u], ea, eb);
-                    } else {
-                        const float f = sa * sb;
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            v4f t = mfma16x16x128(wq[s], B);
-                            acc[s][u] = t * f + acc[s][u];
-                        }
+                    for (int s = 0; s < 4; ++s) {
+                        v4f tt = mfma16x16x128(wq[s], B);
+                        acc[s][u] = tt * f + acc[s][u];
                     }
                 }
             }
-            stage_barrier();
-        };
-        issue(0, 0);
-        if (njb > 1) issue(1, 1);
-        for (int jb = 0; jb < njb; jb += kStages) {
-            step(std::integral_constant<int, 0>{}, jb);
-            if (jb + 1 < njb) step(std::integral_constant<int, 1>{}, jb + 1);
-            if (jb + 2 < njb) step(std::integral_constant<int, 2>{}, jb + 2);
         }
-
+        if (jc + 1 < njb) {
+            ++jc;
+            return;
+        }
+        // last step of the item: its route ids came with this stage; rows go
+        // out as FP16 with one scale per (route, this wave's 64 columns)
         if (wave_on) {
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 const int row = wm * 64 + u * 16 + l16;
-                const int r = sRt[row];
-                if (r < 0) continue;
-                const float wr = a.topk_w[r];
-                float *dst = a.y + (int64_t)r * K + c0 + 64 * wn + 4 * g;
+                float m = 0.f;
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    *reinterpret_cast<v4f *>(dst + 16 * s) = acc[s][u] * wr;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[s][u][i]));
+                m = wave_max_xor(m, 16);
+                m = wave_max_xor(m, 32);
+                if (row >= nrows) continue;
+                const int r = __float_as_int(meta[(row >> 4) * kMeta + kMetaRt + (row & 15)]);
+                if (r < 0 || (int64_t)r >= a.R) continue;
+                float sc, inv;
+                y16_scale(m, sc, inv);
+                uint16_t *dst = a.y16 + (int64_t)r * K + c0 + 64 * wn + 4 * g;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    *reinterpret_cast<uint2 *>(dst + 16 * s) = f32x4_to_f16x4(acc[s][u], inv);
+                if (g == 0) a.ys[(int64_t)r * (K >> 6) + ((c0 >> 6) + wn)] = sc;
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (kc + 1 < mine) {
+            jc = 0;
+            ic = item_at(++kc);
+        }
+    };
+
+    issue(0);
+    prefetch();
+    if (T > 1) issue(1);
+    prefetch();
+    for (int64_t t = 0; t < T; t += kStages) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < T) step(std::integral_constant<int, 1>{}, t + 1);
+        if (t + 2 < T) step(std::integral_constant<int, 2>{}, t + 2);
     }
+    wait_vmcnt<0>();                                 // no load may land after the workgroup ends
 }
 
-constexpr size_t kSmem = (size_t)kStages * (kWBytes + kHBytes) + kStages * kRows * 4 +
-                         2 * kMaxJb * 4 + kRows * 4 + 16;
+constexpr size_t kSmem = (size_t)kStages * (kWBytes + kHBytes) + kStages * 8 * kMeta * 4 + 8 * 256;
+static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 int num_cus_dn() {
     static int cached[64] = {0};
@@ -249,12 +345,14 @@ hipError_t launch_dn_pipe(const DownArgs &a, hipStream_t st) {
     int64_t grid = num_cus_dn();
     const int64_t max_items = (int64_t)a.nblocks * a.ctiles;
     if (grid > max_items) grid = max_items;
-    static bool attr_set = false;
-    if (!attr_set) {
+    static bool attr_set[64] = {false};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!attr_set[dev]) {
         hipError_t err = hipFuncSetAttribute((const void *)down_pipe_kernel<BM, E8M0>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
         if (err != hipSuccess) return err;
-        attr_set = true;
+        attr_set[dev] = true;
     }
     down_pipe_kernel<BM, E8M0><<<(unsigned)grid, kNT, kSmem, st>>>(a);
     return hipGetLastError();

@@ -57,7 +57,8 @@ struct DownArgs {
     const int32_t *sorted;
     const int32_t *eids;
     const int32_t *ntp;
-    float *y;           // FP32 [R, K]: weighted down projection of each route
+    uint16_t *y16;      // FP16 [R, K]: down projection of each route / its scale
+    float *ys;          // FP32 [R, K / 64]: scale of each 64 columns (router weight not applied)
     const int2 *tiles;  // row tiles listed by the gate/up stage (persistent path)
     int32_t *tmeta;
     int64_t K, I, R;
@@ -89,7 +90,7 @@ inline hipError_t launch_fill_zero(uint32_t *p, size_t n_words, hipStream_t st) 
     return launch_fill(p, n_words, 0u, st);
 }
 // out[t, :] = bf16(out[t, :] + sum_{j < top_k, rpos[t*top_k+j] >= 0} y[t*top_k+j, :])
-hipError_t launch_finalize(uint16_t *out, const float *y, const int32_t *rpos, int64_t M,
-                           int64_t K, int top_k, hipStream_t st);
+hipError_t launch_finalize(uint16_t *out, const uint16_t *y16, const float *ys, const float *topk_w,
+                           const int32_t *rpos, int64_t M, int64_t K, int top_k, hipStream_t st);
 
 }  // namespace moe

@@ -146,9 +146,10 @@ moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x,
 
 /* Device workspace moe_fp8_experts needs, in bytes (flags as passed to the
  * call).  Holds the intermediate FP8 rows and their scales, each route's
- * weighted FP32 down projection [M * top_k, K], the route -> plan-row map
- * and, for small grids, split-K partial sums.  The reduction over a token's
- * routes reads them in route order: results do not depend on scheduling. */
+ * down projection [M * top_k, K] (FP16 with an FP32 scale per 64 columns),
+ * the route -> plan-row map and, for small grids, split-K partial sums.  The
+ * reduction over a token's routes reads them in route order: results do not
+ * depend on scheduling. */
 size_t moe_fp8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,
                                       int32_t top_k, int32_t block_m, int64_t sorted_cap,
                                       uint32_t flags);
