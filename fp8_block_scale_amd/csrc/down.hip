@@ -462,11 +462,13 @@ fill_kernel(uint32_t *__restrict__ p, size_t n, uint32_t v) {
 // route's row is never written, so its value is selected away, not
 // multiplied), then added in route order (deterministic), then the previous
 // output, then one round to nearest even BF16.
+// One thread per 8 consecutive outputs of a token row: 16-byte loads of each
+// route's FP16 partials, one scale per route (8 | 64), 16-byte output update.
 __global__ void __launch_bounds__(256)
 finalize_kernel(uint16_t *__restrict__ out, const uint16_t *__restrict__ y16,
                 const float *__restrict__ ys, const float *__restrict__ topk_w,
                 const int32_t *__restrict__ rpos, int64_t M, int64_t K, int top_k) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element of out
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;   // element of out
     if (i >= M * K) return;
     const int64_t t = i / K;
     const int64_t c = i - t * K;
@@ -474,9 +476,9 @@ finalize_kernel(uint16_t *__restrict__ out, const uint16_t *__restrict__ y16,
     const float *ssrc = ys + t * top_k * (K >> 6) + (c >> 6);
     const int32_t *rp = rpos + t * top_k;
     const float *wt = topk_w + t * top_k;
-    v4f f = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f f0 = v4f{0.f, 0.f, 0.f, 0.f}, f1 = f0;
     for (int j0 = 0; j0 < top_k; j0 += 8) {
-        uint2 v[8];
+        u32x4 v[8];
         float sw[8];
         bool ok[8];
 #pragma unroll
@@ -484,23 +486,29 @@ finalize_kernel(uint16_t *__restrict__ out, const uint16_t *__restrict__ y16,
             ok[q] = false;
             if (j0 + q < top_k) {
                 ok[q] = rp[j0 + q] >= 0;
-                v[q] = *reinterpret_cast<const uint2 *>(src + (int64_t)(j0 + q) * K);
+                v[q] = *reinterpret_cast<const u32x4 *>(src + (int64_t)(j0 + q) * K);
                 sw[q] = ssrc[(int64_t)(j0 + q) * (K >> 6)] * wt[j0 + q];
             }
         }
         // routes that are not in the plan hold stale rows: select, not multiply
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-            if (ok[q]) f += f16x4_to_f32x4(v[q]) * sw[q];
+            if (ok[q]) {
+                f0 += f16x4_to_f32x4(uint2{v[q].x, v[q].y}) * sw[q];
+                f1 += f16x4_to_f32x4(uint2{v[q].z, v[q].w}) * sw[q];
+            }
     }
-    const uint2 o = *reinterpret_cast<const uint2 *>(out + i);
-    const float r0 = bf16_bits_to_f32(o.x & 0xffffu) + f[0];
-    const float r1 = bf16_bits_to_f32(o.x >> 16) + f[1];
-    const float r2 = bf16_bits_to_f32(o.y & 0xffffu) + f[2];
-    const float r3 = bf16_bits_to_f32(o.y >> 16) + f[3];
-    *reinterpret_cast<uint2 *>(out + i) =
-        uint2{f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16),
-              f32_to_bf16_bits(r2) | (f32_to_bf16_bits(r3) << 16)};
+    const u32x4 o = *reinterpret_cast<const u32x4 *>(out + i);
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+    const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+    uint32_t rw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_bits_to_f32(ow[k] & 0xffffu) + fv[2 * k];
+        const float hi = bf16_bits_to_f32(ow[k] >> 16) + fv[2 * k + 1];
+        rw[k] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    }
+    *reinterpret_cast<u32x4 *>(out + i) = u32x4{rw[0], rw[1], rw[2], rw[3]};
 }
 
 template <int BM, bool E8M0>
@@ -560,7 +568,7 @@ hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t 
 
 hipError_t launch_finalize(uint16_t *out, const uint16_t *y16, const float *ys, const float *topk_w,
                            const int32_t *rpos, int64_t M, int64_t K, int top_k, hipStream_t st) {
-    int64_t blocks = (M * K / 4 + 255) / 256;
+    int64_t blocks = (M * K / 8 + 255) / 256;
     if (blocks == 0) return hipSuccess;
     finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(out, y16, ys, topk_w, rpos, M, K, top_k);
     return hipGetLastError();
