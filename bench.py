@@ -4,7 +4,9 @@
 One step = the whole hot path over one batch: routing plan, activation
 quantisation, gate/up GEMM + SwiGLU + requantisation, down GEMM + weighted
 reduce-add into the BF16 output -- all HIP kernels of libmoe_fp8 through its
-C ABI, on one stream, with every input already resident in HBM.
+C ABI, on one stream, with every input already resident in HBM.  The K timed
+steps are captured in one HIP graph and replayed once (--eager: launched one
+by one); stage times come from graphs of K launches of each stage.
 
 Default workload: E=288 experts, hidden K=4096, intermediate I=1024, top-8,
 M=4096 tokens, block_m=64 (synthetic, seeded; weights N(0, 0.02^2) stored as
@@ -55,6 +57,9 @@ def parse():
                     help="power-of-two scales inside the FP8 MFMA (zipf workload)")
     ap.add_argument("--splitk", type=int, default=0,
                     help="force the small-grid gate/up split-K factor (1..255; 0 = automatic)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of HIP graph replays (the default: one "
+                         "graph of K steps and one of K launches per stage, each replayed once)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=192)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -189,22 +194,27 @@ def main():
 
     b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
     out = torch.zeros((case.M, case.K), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def stage_plan_quant(stream):
         moe.moe_plan(case.topk_ids, case.E, case.block_m, b.sorted_ids, b.expert_ids, b.ntp,
                      b.plan_ws, stream)
         moe.moe_quant_act(case.x, b.x_q, b.x_s, act_mode, stream)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def stage_gate_up(stream):
         moe.moe_fp8_gate_up(b.x_q, b.x_s, case.w13, case.w13_s, b.sorted_ids, b.expert_ids, b.ntp,
                             case.top_k, case.block_m, b.workspace, flags, stream)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def stage_down(stream):
         moe.moe_fp8_down_reduce(case.w2, case.w2_s, case.topk_weights, b.sorted_ids, b.expert_ids,
                                 b.ntp, case.top_k, case.block_m, out, b.workspace, flags, stream)
+
+    stages = (stage_plan_quant, stage_gate_up, stage_down)
+
+    def step(ev=None):
+        stream = torch.cuda.current_stream()
+        for i, fn in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            fn(stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -220,20 +230,44 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / args.steps
-    plan_quant = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    gate_up = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    down = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    if args.eager:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(evs[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / args.steps
+        plan_quant = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+        gate_up = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        down = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    else:
+        # One graph holding K steps, and one per stage holding K launches of
+        # it, each replayed once between two events on the replay stream (a
+        # graph launch per step would add its own overhead at decode sizes).
+        def capture(fns):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(args.steps):
+                    for fn in fns:
+                        fn(torch.cuda.current_stream())
+            return g
+
+        def replay_ms(g):
+            g.replay()                               # warm
+            torch.cuda.synchronize()
+            t_start.record(stream)
+            g.replay()
+            t_end.record(stream)
+            torch.cuda.synchronize()
+            return t_start.elapsed_time(t_end) / args.steps
+
+        ms = replay_ms(capture(stages))
+        plan_quant, gate_up, down = (replay_ms(capture([fn])) for fn in stages)
 
     ids = case.topk_ids
     valid = (ids >= 0) & (ids < case.E)
@@ -287,6 +321,7 @@ def main():
         },
         "stages_ms": {"plan_quant": round(plan_quant, 4), "gate_up": round(gate_up, 4),
                       "down_reduce": round(down, 4)},
+        "launch": "eager" if args.eager else "hip graph (K steps per replay)",
         "layer_GBs": round(nb["layer"] / (ms * 1e-3) / 1e9, 1),
         "roofline": roof,
     }

@@ -141,11 +141,12 @@ def make_routing(kind, M, E, top_k, seed, device):
     return ids.to(torch.int64), w.to(torch.float32).contiguous()
 
 
-def make_case(name, M=None, device="cpu", ids_dtype=torch.int32, weights=None):
+def make_case(name, M=None, device="cpu", ids_dtype=torch.int32, weights=None, config=None):
     """Build a workload.  ``weights`` may pass a previously built
     (w13, w13_s, w2, w2_s) tuple of the same geometry (M sweeps reuse the
-    parent's weights; routing and x are seeded by (seed, M))."""
-    c = dict(CONFIGS[name])
+    parent's weights; routing and x are seeded by (seed, M)).  ``config``
+    (same keys as a CONFIGS entry) builds an ad-hoc geometry under ``name``."""
+    c = dict(CONFIGS[name] if config is None else config)
     if M is not None:
         c["M"] = M
     M, E, K, I, top_k = c["M"], c["E"], c["K"], c["I"], c["top_k"]

@@ -244,6 +244,43 @@ def test_zipf_small_full(flags):
     full_parity(case_of("zipf", M=40), flags=flags, act_mode=SCALE_UE8M0, label="zipf small")
 
 
+@pytest.mark.parametrize("bm", [64, 128])
+def test_small_grid_long_intermediate_rows(bm):
+    """Small grid with I = 2048: the down stage's rows (16 K-blocks) are too
+    long for the stream kernel's LDS tile, so its fallback kernel runs."""
+    cfg = dict(CONFIGS["tiny"], M=24, E=8, K=512, I=2048, top_k=2, block_m=bm, seed=7)
+    cs = make_case("long_rows", device=DEV, config=cfg)
+    full_parity(cs, label="small grid, long intermediate rows")
+
+
+@pytest.mark.parametrize("name,M", [("decode", None), ("page1", 512)])
+def test_graph_replay_matches_eager(name, M):
+    """The whole layer captured in a HIP graph (small-grid kernels for decode,
+    the persistent ones at M=512): every replay, with eager work and
+    synchronisations between replays, gives the eager output bit for bit."""
+    cs = case_of(name, M=M)
+    log(f"[graph] {name} M={cs.M}")
+    b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, 0, DEV)
+    args = (cs.x, cs.topk_ids, cs.topk_weights, cs.w13, cs.w13_s, cs.w2, cs.w2_s)
+    ref = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
+    moe.moe_layer(b, *args, ref, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    out = torch.zeros_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_layer(b, *args, out, stream=torch.cuda.current_stream())
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager layer"
+        # eager work between replays: the layer itself into a scratch output
+        scratch = torch.zeros_like(ref)
+        moe.moe_layer(b, *args, scratch, stream=torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(scratch, ref)
+
+
 def _sample_tokens(M, n, seed, extra=()):
     rng = np.random.default_rng(seed)
     t = set(rng.choice(M, size=min(n, M), replace=False).tolist()) | set(extra)
