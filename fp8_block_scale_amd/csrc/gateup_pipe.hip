@@ -196,18 +196,26 @@ gateup_pipe_kernel(GateUpArgs a) {
         ssrc = a.xs + (int64_t)t * nkb;
     }
     // Every wave issues exactly kPerStage vector-memory instructions per stage
-    // (the waits in the main loop count on it).
-    auto issue = [&](int stage, int kb) {
-        uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
+    // (the waits in the main loop count on it), in four parts: W13 rows 0-1,
+    // W13 rows 2-3, activation rows, scales.
+    static_assert(kWInstr == 4 && kAInstr == 2, "issue parts");
+    auto issue_part = [&](int part, int stage, int kb) {
+        if (part < 2) {
+            uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
 #pragma unroll
-        for (int i = 0; i < kWInstr; ++i)
-            __builtin_amdgcn_global_load_lds(wsrc[i] + (int64_t)kb * 128, dw + i * 1024, 16, 0, 0);
-        uint8_t *da = sA + stage * kABytes + (w * kAInstr) * 1024;
+            for (int i = 2 * part; i < 2 * part + 2; ++i)
+                __builtin_amdgcn_global_load_lds(wsrc[i] + (int64_t)kb * 128, dw + i * 1024, 16, 0, 0);
+        } else if (part == 2) {
+            uint8_t *da = sA + stage * kABytes + (w * kAInstr) * 1024;
 #pragma unroll
-        for (int i = 0; i < kAInstr; ++i)
-            __builtin_amdgcn_global_load_lds(asrc[i] + (int64_t)kb * 128, da + i * 1024, 16, 0, 0);
-        if (lane < 16)
+            for (int i = 0; i < kAInstr; ++i)
+                __builtin_amdgcn_global_load_lds(asrc[i] + (int64_t)kb * 128, da + i * 1024, 16, 0, 0);
+        } else if (lane < 16) {
             __builtin_amdgcn_global_load_lds(ssrc + kb, sSa + stage * kRows + w * 16, 4, 0, 0);
+        }
+    };
+    auto issue = [&](int stage, int kb) {
+        for (int part = 0; part < 4; ++part) issue_part(part, stage, kb);
     };
 
     // L2 prefetch of W13 rows: lane l of wave w touches tile row 32w + (l & 31)
@@ -257,10 +265,29 @@ gateup_pipe_kernel(GateUpArgs a) {
         // of kb - 1, whose stage the refill below overwrites.  A plain
         // s_barrier: __syncthreads() would also drain the loads in flight.
         stage_barrier();
-        if (kb + 2 < nkb) issue((kb + 2) % kStages, kb + 2);
-        prefetch(kb + 5);
+        // The refill of kb + 2 and the prefetch go out in parts between the
+        // token subtiles of the multiply, in their usual order: all waves
+        // issuing a whole group at once would queue behind the address unit
+        // (64 bytes per clock) instead of multiplying.
+        const bool refill = kb + 2 < nkb;
+        const int rst = (kb + 2) % kStages;
+        auto part = [&](int pi) {
+            __builtin_amdgcn_sched_barrier(0);       // keep each part where it is placed
+            if (pi < 3) {
+                if (refill) issue_part(pi, rst, kb + 2);
+            } else {
+                if (refill) issue_part(3, rst, kb + 2);
+                prefetch(kb + 5);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        part(0);
 
-        if (wave_rows) {
+        if (!wave_rows) {
+            part(1);
+            part(2);
+            part(3);
+        } else {
             const float sbg = sSw[kb];
             const float sbu = sSw[kMaxKb + kb];
             const float *Ss = sSa + stage * kRows;
@@ -280,6 +307,7 @@ gateup_pipe_kernel(GateUpArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
+                if (u < 3) part(u + 1);
                 if (wm * 64 + u * 16 >= nrows) continue;
                 const int row = wm * 64 + u * 16 + l16;
                 const uint8_t *rp = As + row * 128;
