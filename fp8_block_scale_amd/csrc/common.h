@@ -168,6 +168,34 @@ __device__ __forceinline__ int next_xcd_item(int32_t *ctr, int n, int per_unit, 
     return -1;
 }
 
+// The same queue walk in two halves, so the first counter round trip can
+// overlap other work: claim_begin bumps the counter of the caller's current
+// range (also an empty one: its counter is only ever compared with the range)
+// and claim_end turns that ticket into an item, walking on from there.
+__device__ __forceinline__ int claim_begin(int32_t *ctr, int home, int q) {
+    return q < 8 ? __hip_atomic_fetch_add(&ctr[(home + q) & 7], 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                 : 0;
+}
+__device__ __forceinline__ int claim_end(int ticket, int32_t *ctr, int n, int per_unit, int home,
+                                         int &q) {
+    if (q >= 8) return -1;
+    const int x = (home + q) & 7;
+    const int lo = (int)((int64_t)x * n / 8) * per_unit;
+    const int hi = (int)((int64_t)(x + 1) * n / 8) * per_unit;
+    if (lo + ticket < hi) return lo + ticket;
+    ++q;
+    return next_xcd_item(ctr, n, per_unit, home, q);
+}
+
+// SwiGLU of one gate/up pair: silu(g) * u = g / (1 + e^-g) * u, with the
+// exp2 and reciprocal instructions (each within about one ulp); e^-g
+// overflowing to infinity gives the limit 0 for very negative g.
+__device__ __forceinline__ float swiglu(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896340736f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 // ------------------------------------------------- LDS pipeline helpers
 
 // 16-byte LDS read of an MFMA operand slice.  (Kept as a typed load: the

@@ -363,7 +363,7 @@ gateup_stream_kernel(GateUpArgs a) {
         float h[4], amax = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            h[i] = gv[i] / (1.0f + expf(-gv[i])) * uv[i];
+            h[i] = swiglu(gv[i], uv[i]);
             amax = fmaxf(amax, fabsf(h[i]));
         }
         amax = wave_max_xor(amax, 1);

@@ -124,8 +124,10 @@ gateup_pipe_kernel(GateUpArgs a) {
     const int ntiles = a.tmeta[0];
     const int home = blockIdx.x & 7;
     int q = 0;                                       // position in the XCD ranges (thread 0)
-    for (;;) {
+    // The next item is claimed by thread 0 while the previous one finishes
+    // (its epilogue); the first one here.
     if (tid == 0) sItem[0] = next_xcd_item(a.tmeta + 1, ntiles, a.jtiles, home, q);
+    for (;;) {
     __syncthreads();
     const int item = sItem[0];
     if (item < 0) break;                             // every workgroup ends here
@@ -137,6 +139,7 @@ gateup_pipe_kernel(GateUpArgs a) {
     const int e = a.eids[b];
     if (e < 0 || e >= a.E) {                         // not a plan: skip, keep in step
         __syncthreads();
+        if (tid == 0) sItem[0] = next_xcd_item(a.tmeta + 1, ntiles, a.jtiles, home, q);
         continue;
     }
     const int nrows = nb * BM;
@@ -343,6 +346,8 @@ gateup_pipe_kernel(GateUpArgs a) {
     }
     wait_vmcnt<0>();                                 // the last prefetches land in the sink
     __syncthreads();
+    // the next item's claim travels while this one's epilogue computes
+    const int ticket = tid == 0 ? claim_begin(a.tmeta + 1, home, q) : 0;
 
     // ---- SwiGLU + per-row 128-group FP8 requantisation
     float h[NU][2][4];
@@ -357,7 +362,7 @@ gateup_pipe_kernel(GateUpArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const float gt = acc[s][u][i];
                 const float up = acc[s + 2][u][i];
-                const float hv = valid ? gt / (1.0f + expf(-gt)) * up : 0.f;
+                const float hv = valid ? swiglu(gt, up) : 0.f;
                 h[u][s][i] = hv;
                 amax = fmaxf(amax, fabsf(hv));
             }
@@ -385,6 +390,7 @@ gateup_pipe_kernel(GateUpArgs a) {
         }
         if (wn == 0 && g == 0) a.hs[p * (I >> 7) + jt] = s;
     }
+    if (tid == 0) sItem[0] = claim_end(ticket, a.tmeta + 1, ntiles, a.jtiles, home, q);
     __syncthreads();                                 // LDS is reused by the next item
     }
 }
