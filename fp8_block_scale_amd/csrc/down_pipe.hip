@@ -26,8 +26,10 @@
 // W2 block scales, 16 route ids), all brought by direct global->LDS loads two
 // steps ahead -- across item boundaries too, so an item's first steps are
 // already in flight while the previous item finishes.  Rows are XOR-swizzled
-// in LDS as in the gate/up pipeline.  A 4-byte load per lane five steps ahead
-// touches the W2 rows a step will need, so the ring's own loads hit L2.  FP8
+// in LDS as in the gate/up pipeline.  A 4-byte load per lane three steps
+// ahead touches the W2 rows a step will need, so the ring's own loads find
+// them in L2 or already on their way (further ahead, the touched lines of 32
+// CUs outgrow the XCD's 4 MB L2 and are fetched twice).  FP8
 // MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per
 // step, or with power-of-two scales as E8M0 exponents inside the MFMA.
 #include <type_traits>
@@ -49,6 +51,7 @@ constexpr int kHInstr = kHBytes / 1024 / 8;
 constexpr int kPerStage = kWInstr + kHInstr + 1;
 constexpr int kMeta = 64;                     // floats per wave and stage
 constexpr int kMetaRt = 18;                   // route ids start here
+constexpr int kPfAhead = 3;                   // steps between the L2 prefetch and the multiply
 
 __device__ __forceinline__ v8i join8q(const u32x4 &lo, const u32x4 &hi) {
     v8i r;
@@ -175,7 +178,7 @@ down_pipe_kernel(DownArgs a) {
     };
 
     // ---- prefetch side: lane l of wave w touches W2 tile row 32w + (l & 31)
-    // at byte 64 (l >> 5) of the step five ahead of the multiply
+    // at byte 64 (l >> 5) of the step kPfAhead ahead of the multiply
     int64_t kp = 0;
     int jp = 0;
     const uint8_t *wpf;
@@ -195,7 +198,7 @@ down_pipe_kernel(DownArgs a) {
         }                                            // past the last step: stay on it
     };
     set_pf(il);
-    for (int i = 0; i < 3; ++i) pf_advance();        // step 3
+    for (int i = 0; i < kPfAhead - 2; ++i) pf_advance();   // the first group's prefetch step
     auto prefetch = [&]() {
         lds_dma4(wpf + (int64_t)jp * 128, sPf + w * 256);
         pf_advance();

@@ -44,6 +44,7 @@ constexpr int kAInstr = kABytes / 1024 / 8;   // (A)
 constexpr int kSInstr = 1;                    // (activation scales: 16 rows per wave)
 constexpr int kPerStage = kWInstr + kAInstr + kSInstr;
 constexpr int kMaxKb = 256;                   // K <= 32768
+constexpr int kPfAhead = 3;                   // K-blocks between the L2 prefetch and the multiply
 
 enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
 
@@ -225,7 +226,8 @@ gateup_pipe_kernel(GateUpArgs a) {
     // at byte 64 (l >> 5) of a K-block -- both 64-byte halves of each of the
     // wave's 32 rows -- with a 4-byte LDS-DMA load into a per-wave sink, so
     // there is no register result; the ring's own loads of that K-block then
-    // hit L2.
+    // find it in L2 or already on its way.  kPfAhead = 3: further ahead, the
+    // touched lines of 32 CUs outgrow the XCD's 4 MB L2 and are fetched twice.
     const uint8_t *wpf;
     {
         const int row = w * 32 + (lane & 31);
@@ -247,15 +249,15 @@ gateup_pipe_kernel(GateUpArgs a) {
         for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // Issue groups: the prologue's two, then one per K-block step, each =
-    // [ring refill of K-block j + 2 (while one is left)] [prefetch of j + 5].
+    // [ring refill of K-block j + 2 (while one is left)] [prefetch of j + kPfAhead].
     // Loads complete in issue order, so at step kb everything after the
-    // refill of kb is the prefetch of its group and the next group.  A
-    // prefetch must be done three steps after its issue, before the refill of
-    // the K-block it covers is issued.
+    // refill of kb is the prefetch of its group and the next group.  The
+    // refill of a prefetched K-block goes out kPfAhead - 2 steps after its
+    // prefetch and finds the lines in L2 or already on their way.
     issue(0, 0);
-    prefetch(3);
+    prefetch(kPfAhead - 2);
     if (nkb > 1) issue(1, 1);
-    prefetch(4);
+    prefetch(kPfAhead - 1);
 
     for (int kb = 0; kb < nkb; ++kb) {
         const int stage = kb % kStages;
@@ -280,7 +282,7 @@ gateup_pipe_kernel(GateUpArgs a) {
                 if (refill) issue_part(pi, rst, kb + 2);
             } else {
                 if (refill) issue_part(3, rst, kb + 2);
-                prefetch(kb + 5);
+                prefetch(kb + kPfAhead);
             }
             __builtin_amdgcn_sched_barrier(0);
         };
