@@ -102,8 +102,8 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block
     off = align256(off + R * (size_t)(K / 64) * 4);
     l.rpos = off;
     off = align256(off + R * 4);
-    l.tiles = off;                       // row tiles [blocks_cap] int2, then 17 ints of tile meta
-    off = align256(off + (size_t)blocks_cap * 8 + 17 * 4);
+    l.tiles = off;                       // row tiles [blocks_cap] int4, then 17 ints of tile meta
+    off = align256(off + (size_t)blocks_cap * 16 + 17 * 4);
     l.cnt = off;
     size_t ntiles = (size_t)blocks_cap * jtiles;
     l.cnt_words = l.sp.nsplit > 1 ? ntiles * (block_m > 64 ? block_m / 64 : 1) : 0;
@@ -312,8 +312,8 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.part = (float *)(ws + l.part);
     ga.cnt = (uint32_t *)(ws + l.cnt);
     ga.rpos = (int32_t *)(ws + l.rpos);
-    ga.tiles = (int2 *)(ws + l.tiles);
-    ga.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 8);
+    ga.tiles = (int4 *)(ws + l.tiles);
+    ga.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);
     ga.K = K;
     ga.I = I;
     ga.R = M * top_k;
@@ -368,8 +368,8 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
     da.njb = (int)(I / 128);
     da.ctiles = (int)((K + 255) / 256);
     da.nblocks = (int)(sorted_cap / block_m);
-    da.tiles = (const int2 *)(ws + l.tiles);
-    da.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 8);
+    da.tiles = (const int4 *)(ws + l.tiles);
+    da.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);
     const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
     st = hip_check(l.sp.persistent ? moe::launch_down_pipe(da, block_m, e8, s)
                                                    : moe::launch_down(da, block_m, e8, s),

@@ -110,10 +110,10 @@ down_pipe_kernel(DownArgs a) {
         const int rt = __builtin_amdgcn_readfirstlane((int)(item / a.ctiles));
         Item it;
         it.ct = __builtin_amdgcn_readfirstlane((int)(item - (int64_t)rt * a.ctiles));
-        const const_i32_p tl = (const_i32_p)a.tiles + 2 * (int64_t)rt;   // int2 {first block, blocks}
+        const const_i32_p tl = (const_i32_p)a.tiles + 4 * (int64_t)rt;   // {first block, blocks, expert, 0}
         it.b = __builtin_amdgcn_readfirstlane(tl[0]);
         it.nb = __builtin_amdgcn_readfirstlane(tl[1]);
-        const int e = __builtin_amdgcn_readfirstlane(((const_i32_p)a.eids)[it.b]);
+        const int e = __builtin_amdgcn_readfirstlane(tl[2]);
         it.ok = e >= 0 && e < a.E;
         it.e = it.ok ? e : 0;
         return it;
@@ -348,9 +348,11 @@ hipError_t launch_dn_pipe(const DownArgs &a, hipStream_t st) {
     int64_t grid = num_cus_dn();
     const int64_t max_items = (int64_t)a.nblocks * a.ctiles;
     if (grid > max_items) grid = max_items;
-    static bool attr_set[64] = {false};
+    static bool attr_set[64] = {false};          // once per device
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (!attr_set[dev]) {
         hipError_t err = hipFuncSetAttribute((const void *)down_pipe_kernel<BM, E8M0>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);

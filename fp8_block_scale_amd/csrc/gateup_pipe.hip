@@ -56,12 +56,13 @@ __device__ __forceinline__ v8i join8p(const u32x4 &lo, const u32x4 &hi) {
 }
 
 // Row tiles: every expert's run of blocks [first, first + len) (expert ids of
-// a plan are non-decreasing) becomes ceil(len / mb) tiles of <= mb blocks.
+// a plan are non-decreasing) becomes ceil(len / mb) tiles of <= mb blocks,
+// each listed as {first block, blocks, expert, 0}.
 // One workgroup: pass 1 marks run starts and counts their tiles, an
 // exclusive scan gives each run its first tile slot, pass 2 writes them.
 __global__ void __launch_bounds__(1024)
 tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, int bm, int mb,
-             int nblocks, int2 *__restrict__ tiles, int32_t *__restrict__ meta) {
+             int nblocks, int4 *__restrict__ tiles, int32_t *__restrict__ meta) {
     __shared__ int wsum[16];
     __shared__ int carry;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -71,9 +72,9 @@ tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, 
     __syncthreads();
     for (int base = 0; base < nb; base += 1024) {
         const int b = base + tid;
-        int cnt = 0, len = 0;
+        int cnt = 0, len = 0, e = 0;
         if (b < nb) {
-            const int e = eids[b];
+            e = eids[b];
             if (b == 0 || eids[b - 1] != e) {
                 len = 1;
                 while (b + len < nb && eids[b + len] == e) ++len;
@@ -93,14 +94,14 @@ tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, 
         for (int t = 0; t < cnt; ++t) {
             const int first = b + t * mb;
             const int rem = len - t * mb;
-            tiles[slot + t] = make_int2(first, rem < mb ? rem : mb);
+            tiles[slot + t] = make_int4(first, rem < mb ? rem : mb, e, 0);
         }
         __syncthreads();
         if (tid == 1023) carry = before + incl;
         __syncthreads();
     }
     if (tid == 0) meta[0] = carry;     // number of row tiles
-    if (tid >= 1 && tid <= 16) meta[tid] = 0;   // per-XCD work counters: gate/up 1..8, down 9..16
+    if (tid >= 1 && tid <= 8) meta[tid] = 0;    // per-XCD work counters of the gate/up queues
 }
 
 template <int BM, int MODE>
@@ -135,9 +136,9 @@ gateup_pipe_kernel(GateUpArgs a) {
     // a row tile's j-tiles are consecutive items on one XCD: its activation
     // rows are fetched into that XCD's L2 once
     const int jt = item % a.jtiles;
-    const int2 tl = a.tiles[item / a.jtiles];
+    const int4 tl = a.tiles[item / a.jtiles];       // first block, blocks, expert
     const int b = tl.x, nb = tl.y;
-    const int e = a.eids[b];
+    const int e = tl.z;
     if (e < 0 || e >= a.E) {                         // not a plan: skip, keep in step
         __syncthreads();
         if (tid == 0) sItem[0] = next_xcd_item(a.tmeta + 1, ntiles, a.jtiles, home, q);
@@ -423,12 +424,16 @@ hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
     int64_t grid = num_cus();
     const int64_t max_items = (int64_t)a.nblocks * a.jtiles;
     if (grid > max_items) grid = max_items;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gateup_pipe_kernel<BM, MODE>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
+    static bool attr_set[64] = {false};          // once per device
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!attr_set[dev]) {
+        e = hipFuncSetAttribute((const void *)gateup_pipe_kernel<BM, MODE>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set[dev] = true;
     }
     gateup_pipe_kernel<BM, MODE><<<(unsigned)grid, kNT, kSmem, st>>>(a);
     return hipGetLastError();

@@ -36,8 +36,8 @@ struct GateUpArgs {
     float *part;        // split-K partial sums (nsplit > 1)
     uint32_t *cnt;      // split-K arrival counters, one per (block, j-tile)
     int32_t *rpos;      // [R] plan row of each route (pre-filled with -1)
-    int2 *tiles;        // [nblocks] row tiles (first block, blocks) of the persistent kernels
-    int32_t *tmeta;     // [17] row-tile count, per-XCD work counters (gate/up 1..8, down 9..16)
+    int4 *tiles;        // [nblocks] row tiles {first block, blocks, expert, 0} of the persistent kernels
+    int32_t *tmeta;     // [17] row-tile count, then the gate/up per-XCD work counters (1..8)
     int64_t K, I, R;
     int E, top_k;
     int nkb;            // K / 128
@@ -59,7 +59,7 @@ struct DownArgs {
     const int32_t *ntp;
     uint16_t *y16;      // FP16 [R, K]: down projection of each route / its scale
     float *ys;          // FP32 [R, K / 64]: scale of each 64 columns (router weight not applied)
-    const int2 *tiles;  // row tiles listed by the gate/up stage (persistent path)
+    const int4 *tiles;  // row tiles listed by the gate/up stage (persistent path)
     int32_t *tmeta;
     int64_t K, I, R;
     int E, top_k;
