@@ -36,12 +36,15 @@ def _gpu():
 _WEIGHTS = {}
 
 
-def case_of(name, M=None, ids_dtype=torch.int32):
-    """Workloads generated on the GPU; weights cached per geometry."""
-    c = CONFIGS[name]
-    key = (name,)
+def case_of(name, M=None, ids_dtype=torch.int32, **override):
+    """Workloads generated on the GPU; weights cached per geometry.  Keyword
+    overrides of the workload's config that keep E, K and I (block_m, seed
+    of the routing) reuse its weights."""
+    c = dict(CONFIGS[name], **override)
+    key = (name, c["E"], c["K"], c["I"], c["pow2"])
     w = _WEIGHTS.get(key)
-    cs = make_case(name, M=M, device=DEV, ids_dtype=ids_dtype, weights=w)
+    cs = make_case(name, M=M, device=DEV, ids_dtype=ids_dtype, weights=w,
+                   config=c if override else None)
     _WEIGHTS[key] = (cs.w13, cs.w13_s, cs.w2, cs.w2_s)
     return cs
 
@@ -279,6 +282,22 @@ def test_graph_replay_matches_eager(name, M):
         moe.moe_layer(b, *args, scratch, stream=torch.cuda.current_stream())
         torch.cuda.synchronize()
         assert torch.equal(scratch, ref)
+
+
+@pytest.mark.parametrize("bm", [16, 32])
+def test_persistent_kernels_small_block_m(bm):
+    """The persistent gate/up and down kernels with block_m 16 and 32: row
+    tiles of 8 and 4 plan blocks."""
+    cs = case_of("page1", M=512, block_m=bm)
+    full_parity(cs, tokens=_sample_tokens(cs.M, 12, 20 + bm), label=f"persistent bm={bm}")
+
+
+def test_persistent_long_k_wide_i():
+    """Persistent path at K=7168 (56 K-blocks per item) and I=2048 (16
+    128-deep steps per down item, 16 j-tiles), E=32, top-8."""
+    cfg = dict(CONFIGS["page1"], M=256, E=32, K=7168, I=2048, top_k=8, block_m=64, seed=11)
+    cs = make_case("long_k", device=DEV, config=cfg)
+    full_parity(cs, tokens=_sample_tokens(cs.M, 6, 21), label="persistent K=7168 I=2048")
 
 
 def _sample_tokens(M, n, seed, extra=()):
