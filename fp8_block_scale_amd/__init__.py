@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
 EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_quant_act",
             "moe_fp8_experts_workspace_size", "moe_fp8_experts_workspace_layout",
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
-            "moe_last_error", "moe_debug_e4m3_encode")
+            "moe_last_error", "moe_debug_e4m3_encode", "moe_debug_count_non_pow2")
 
 
 class MoeError(RuntimeError):
@@ -77,6 +77,7 @@ _c = {
     "moe_status_str": _proto("moe_status_str", ctypes.c_char_p, _i32),
     "moe_last_error": _proto("moe_last_error", ctypes.c_char_p),
     "moe_debug_e4m3_encode": _proto("moe_debug_e4m3_encode", _i32, _vp, _vp, _i64, _vp),
+    "moe_debug_count_non_pow2": _proto("moe_debug_count_non_pow2", _i32, _vp, _i64, _vp, _vp),
 }
 
 
@@ -143,6 +144,15 @@ def moe_debug_e4m3_encode(inp, out, stream=None):
     assert inp.dtype == torch.float32 and out.dtype == torch.uint8 and inp.numel() == out.numel()
     _check(_c["moe_debug_e4m3_encode"](_ptr(inp), _ptr(out), inp.numel(), _stream(stream)),
            "moe_debug_e4m3_encode")
+
+
+def moe_debug_count_non_pow2(scales, count, stream=None):
+    """count[0] = how many of `scales` (FP32, device) are not powers of two in
+    [2^-126, 2^127] -- the values MOE_F_MMA_E8M0 cannot take as they are."""
+    assert scales.dtype == torch.float32 and scales.is_contiguous()
+    assert count.dtype in (torch.int32, torch.uint32) and count.numel() >= 1
+    _check(_c["moe_debug_count_non_pow2"](_ptr(scales), scales.numel(), _ptr(count), _stream(stream)),
+           "moe_debug_count_non_pow2")
 
 
 # --------------------------------------------------------------- experts --

@@ -234,6 +234,14 @@ MOE_API moe_status moe_debug_e4m3_encode(const float *in, uint8_t *out, int64_t 
                      "moe_debug_e4m3_encode: launch");
 }
 
+MOE_API moe_status moe_debug_count_non_pow2(const float *scales, int64_t n, uint32_t *count,
+                                            void *stream) {
+    if (n < 0) return fail(MOE_ERR_SHAPE, "n < 0");
+    if (!count || (n > 0 && !scales)) return fail(MOE_ERR_NULL, "scales and count are required");
+    return hip_check(moe::launch_pow2_violations(scales, n, count, (hipStream_t)stream),
+                     "moe_debug_count_non_pow2: launch");
+}
+
 // --------------------------------------------------------------- experts
 
 MOE_API size_t moe_fp8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,

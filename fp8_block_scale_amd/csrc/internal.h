@@ -21,6 +21,8 @@ hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int bloc
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
                             uint8_t *xq, float *xs, bool ue8m0, hipStream_t st);
 hipError_t launch_e4m3_encode(const float *in, uint8_t *out, int64_t n, hipStream_t st);
+// count[0] = number of scales that are not powers of two in [2^-126, 2^127]
+hipError_t launch_pow2_violations(const float *scales, int64_t n, uint32_t *count, hipStream_t st);
 
 // ---- steps 3-5 (gateup.hip, down.hip)
 struct GateUpArgs {

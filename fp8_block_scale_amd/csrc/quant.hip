@@ -77,6 +77,39 @@ hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
     return hipGetLastError();
 }
 
+// Counts scales that the E8M0 MFMA path cannot take as they are: anything
+// but a positive power of two in [2^-126, 2^127] (sign 0, mantissa 0,
+// biased exponent 1..254).  One atomic add per wave of its ballot count.
+__global__ void __launch_bounds__(256)
+pow2_violation_kernel(const uint32_t *__restrict__ bits, int64_t n, uint32_t *__restrict__ count) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    uint32_t bad = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const uint32_t b = bits[i];
+        const uint32_t ex = (b >> 23) & 0xffu;
+        bad += (b & 0x807fffffu) != 0u || ex == 0u || ex == 0xffu;
+    }
+    for (int m = 1; m < 64; m <<= 1) bad += __shfl_xor(bad, m, 64);
+    if ((threadIdx.x & 63) == 0 && bad)
+        __hip_atomic_fetch_add(count, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void __launch_bounds__(64)
+zero_word_kernel(uint32_t *p) {
+    if (threadIdx.x == 0) p[0] = 0u;
+}
+
+hipError_t launch_pow2_violations(const float *scales, int64_t n, uint32_t *count, hipStream_t st) {
+    zero_word_kernel<<<1, 64, 0, st>>>(count);           // a kernel, not a memset: graph-safe
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || n == 0) return err;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    pow2_violation_kernel<<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<const uint32_t *>(scales), n,
+                                                            count);
+    return hipGetLastError();
+}
+
 hipError_t launch_e4m3_encode(const float *in, uint8_t *out, int64_t n, hipStream_t st) {
     int64_t blocks = (n + 1023) / 1024;
     if (blocks == 0) return hipSuccess;

@@ -227,6 +227,15 @@ const char *moe_last_error(void);
  * in/out are device pointers; n >= 0. */
 moe_status moe_debug_e4m3_encode(const float *in, uint8_t *out, int64_t n, void *stream);
 
+/* Debug check of the MOE_F_MMA_E8M0 precondition (SGLang PR #43556,
+ * Motivation: scales that are not powers of two, fed to an E8M0-scaled MFMA,
+ * give wrong results without any error).  Writes to count[0] (device memory,
+ * one uint32, overwritten) the number of the n FP32 values at `scales` that
+ * are not positive powers of two in [2^-126, 2^127]; 0 means x_s, w13_s or
+ * w2_s may be used with MOE_F_MMA_E8M0.  Asynchronous on `stream`. */
+moe_status moe_debug_count_non_pow2(const float *scales, int64_t n, uint32_t *count,
+                                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

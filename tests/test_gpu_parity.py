@@ -300,6 +300,26 @@ def test_persistent_long_k_wide_i():
     full_parity(cs, tokens=_sample_tokens(cs.M, 6, 21), label="persistent K=7168 I=2048")
 
 
+def test_debug_count_non_pow2():
+    """The E8M0 precondition check against a count from the raw bits."""
+    def expect(t):
+        b = t.cpu().contiguous().view(torch.int32).numpy().astype(np.uint32)
+        ex = (b >> 23) & 0xFF
+        return int((((b & 0x807FFFFF) != 0) | (ex == 0) | (ex == 0xFF)).sum())
+    cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+    z = case_of("zipf", M=64)
+    p = case_of("page1", M=64)
+    odd = torch.tensor([1.0, 0.5, 2.0 ** -126, 2.0 ** 127, 0.0, -1.0, 3.0, float("inf"), float("nan"),
+                        2.0 ** -127, 1.5 * 2 ** 60], dtype=torch.float32, device=DEV)
+    for t, label in ((z.w13_s, "zipf w13_s"), (z.w2_s, "zipf w2_s"), (p.w13_s, "page1 w13_s"),
+                     (odd, "edge values")):
+        flat = t.reshape(-1).contiguous()
+        moe.moe_debug_count_non_pow2(flat, cnt)
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == expect(flat), label
+    assert expect(z.w13_s.reshape(-1)) == 0 and expect(odd) == 7
+
+
 def _sample_tokens(M, n, seed, extra=()):
     rng = np.random.default_rng(seed)
     t = set(rng.choice(M, size=min(n, M), replace=False).tolist()) | set(extra)
