@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP graph replays (the default: one "
                          "graph of K steps and one of K launches per stage, each replayed once)")
+    ap.add_argument("--weight-sets", type=int, default=0,
+                    help="copies of the expert weights cycled through step by step, like "
+                         "consecutive layers, so no step finds its weights in the 256 MB "
+                         "Infinity Cache (0 = enough copies for >= 1 GiB of touched weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=192)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -192,29 +196,43 @@ def main():
     if args.splitk:
         flags |= (args.splitk & 0xFF) << moe.MOE_F_SPLITK_SHIFT
 
+    # Weight copies: a step reads the touched experts' weights once; with
+    # fewer than ~1 GiB of them per step, back-to-back steps would find them
+    # in the last-level (Infinity) cache instead of HBM.
+    ids = case.topk_ids
+    valid = (ids >= 0) & (ids < case.E)
+    n_touched = int(torch.unique(ids[valid]).numel())
+    touched_w = n_touched * 3 * case.I * case.K
+    nsets = args.weight_sets or max(1, min(64, -(-(1 << 30) // max(touched_w, 1))))
+    wsets = [(case.w13, case.w13_s, case.w2, case.w2_s)]
+    for _ in range(nsets - 1):
+        wsets.append(tuple(t.clone() for t in wsets[0]))
+
     b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
     out = torch.zeros((case.M, case.K), dtype=torch.bfloat16, device=dev)
-    def stage_plan_quant(stream):
+    def stage_plan_quant(stream, k):
         moe.moe_plan(case.topk_ids, case.E, case.block_m, b.sorted_ids, b.expert_ids, b.ntp,
                      b.plan_ws, stream)
         moe.moe_quant_act(case.x, b.x_q, b.x_s, act_mode, stream)
 
-    def stage_gate_up(stream):
-        moe.moe_fp8_gate_up(b.x_q, b.x_s, case.w13, case.w13_s, b.sorted_ids, b.expert_ids, b.ntp,
+    def stage_gate_up(stream, k):
+        w13, w13_s = wsets[k % nsets][:2]
+        moe.moe_fp8_gate_up(b.x_q, b.x_s, w13, w13_s, b.sorted_ids, b.expert_ids, b.ntp,
                             case.top_k, case.block_m, b.workspace, flags, stream)
 
-    def stage_down(stream):
-        moe.moe_fp8_down_reduce(case.w2, case.w2_s, case.topk_weights, b.sorted_ids, b.expert_ids,
+    def stage_down(stream, k):
+        w2, w2_s = wsets[k % nsets][2:]
+        moe.moe_fp8_down_reduce(w2, w2_s, case.topk_weights, b.sorted_ids, b.expert_ids,
                                 b.ntp, case.top_k, case.block_m, out, b.workspace, flags, stream)
 
     stages = (stage_plan_quant, stage_gate_up, stage_down)
 
-    def step(ev=None):
+    def step(k, ev=None):
         stream = torch.cuda.current_stream()
         for i, fn in enumerate(stages):
             if ev is not None:
                 ev[i].record(stream)
-            fn(stream)
+            fn(stream, k)
         if ev is not None:
             ev[3].record(stream)
 
@@ -226,8 +244,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -238,7 +256,7 @@ def main():
         torch.cuda.synchronize()
         t_start.record(stream)
         for i in range(args.steps):
-            step(evs[i])
+            step(i, evs[i])
         t_end.record(stream)
         torch.cuda.synchronize()
         ms = t_start.elapsed_time(t_end) / args.steps
@@ -252,9 +270,9 @@ def main():
         def capture(fns):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _ in range(args.steps):
+                for k in range(args.steps):
                     for fn in fns:
-                        fn(torch.cuda.current_stream())
+                        fn(torch.cuda.current_stream(), k)
             return g
 
         def replay_ms(g):
@@ -269,10 +287,7 @@ def main():
         ms = replay_ms(capture(stages))
         plan_quant, gate_up, down = (replay_ms(capture([fn])) for fn in stages)
 
-    ids = case.topk_ids
-    valid = (ids >= 0) & (ids < case.E)
     R_valid = int(valid.sum())
-    n_touched = int(torch.unique(ids[valid]).numel())
     P = int(b.ntp.item())
     flops = 2.0 * R_valid * 3 * case.K * case.I
     nb = algorithmic_bytes(case, n_touched, R_valid, P, case.M)
@@ -322,6 +337,7 @@ def main():
         "stages_ms": {"plan_quant": round(plan_quant, 4), "gate_up": round(gate_up, 4),
                       "down_reduce": round(down, 4)},
         "launch": "eager" if args.eager else "hip graph (K steps per replay)",
+        "weight_sets": nsets,
         "layer_GBs": round(nb["layer"] / (ms * 1e-3) / 1e9, 1),
         "roofline": roof,
     }
