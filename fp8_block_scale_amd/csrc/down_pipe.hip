@@ -237,7 +237,18 @@ down_pipe_kernel(DownArgs a) {
         const int ncols = K - c0 < 256 ? (int)(K - c0) : 256;
         const bool wave_on = ic.ok && (wm * 64 < nrows) && (64 * wn < ncols);
         const float *meta = sMeta + ST * 8 * kMeta;
+        // rows of this wave up to its last valid one (route ids come with
+        // every stage): 16-row subtiles past it hold only plan padding and
+        // are not multiplied
+        int vrows = 0;
         if (wave_on) {
+            const int row = wm * 64 + lane;
+            const int r = __float_as_int(meta[(row >> 4) * kMeta + kMetaRt + (row & 15)]);
+            const uint64_t v = __ballot(row < nrows && r >= 0 && (int64_t)r < a.R);
+            vrows = v ? wm * 64 + 64 - __builtin_clzll(v) : 0;
+            vrows = __builtin_amdgcn_readfirstlane(vrows);
+        }
+        if (vrows > 0) {
             // this wave's 64 columns lie in one 128-column scale block
             const float sb = meta[w * kMeta + 16 + (wn >= 2 ? 1 : 0)];
             const uint8_t *Ws = sW + ST * kWBytes;
@@ -253,7 +264,7 @@ down_pipe_kernel(DownArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                if (wm * 64 + u * 16 >= nrows) continue;
+                if (wm * 64 + u * 16 >= vrows) continue;
                 const int row = wm * 64 + u * 16 + l16;
                 const uint8_t *rp = Hs + row * 128;
                 const u32x4 lo4 = lds_read16(rp + ((g ^ (row & 7)) * 16));

@@ -241,7 +241,16 @@ gateup_pipe_kernel(GateUpArgs a) {
     };
 
     constexpr int NU = 4;
-    const bool wave_rows = wm * 64 < nrows;
+    // Rows of this wave up to its last valid one: 16-row subtiles past it hold
+    // only plan padding (the tail of an expert's last block) and are not
+    // multiplied.
+    int vrows;
+    {
+        const uint64_t v = __ballot(sTok[wm * 64 + lane] >= 0);
+        vrows = v ? wm * 64 + 64 - __builtin_clzll(v) : 0;
+        vrows = __builtin_amdgcn_readfirstlane(vrows);
+    }
+    const bool wave_rows = vrows > 0;
 
     v4f acc[4][NU];
 #pragma unroll
@@ -314,7 +323,7 @@ gateup_pipe_kernel(GateUpArgs a) {
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 if (u < 3) part(u + 1);
-                if (wm * 64 + u * 16 >= nrows) continue;
+                if (wm * 64 + u * 16 >= vrows) continue;
                 const int row = wm * 64 + u * 16 + l16;
                 const uint8_t *rp = As + row * 128;
                 const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
