@@ -213,6 +213,11 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// 4-byte global -> LDS copy per lane: lane l writes LDS bytes [lds + 4 l, +4).
+__device__ __forceinline__ void lds_dma4(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
+
 // Workgroup barrier without a memory fence, so refills still in flight stay
 // in flight.  The compiler-only fences keep LDS accesses from being moved
 // across it; they emit no instructions.

@@ -60,10 +60,6 @@ __device__ __forceinline__ v8i join8q(const u32x4 &lo, const u32x4 &hi) {
     return r;
 }
 
-// 4-byte global -> LDS copy per lane: lane l writes LDS bytes [lds + 4 l, +4).
-__device__ __forceinline__ void lds_dma4(const void *src, void *lds) {
-    __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
-}
 
 // The row-tile list and the plan's expert ids do not change while the
 // kernel runs: read through the constant address space, a uniform index

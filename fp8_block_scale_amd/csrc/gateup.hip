@@ -15,11 +15,13 @@
 // so the kernel is a weight stream.  One workgroup = one plan block (its
 // valid rows, in passes of at most 64) x one 128-wide intermediate tile
 // (128 gate rows + 128 up rows of W13) x one K-range; eight waves take 16
-// gate and the matching 16 up rows each.  Every wave streams its 32 weight
-// rows straight into registers, four 128-byte K-blocks per row per stage
-// (512 contiguous bytes of each row, which keeps HBM pages open), with two
-// stages in flight and no barrier in the loop.  The activation rows and all
-// scales of the K-range are gathered into LDS once, up front.
+// gate and the matching 16 up rows each.  The weights go through a ring of
+// one-K-block LDS stages filled by global_load_lds_dwordx4, eight lanes per
+// 128-byte row segment: every load instruction reads whole 128-byte lines.
+// (Loading the MFMA operand slices straight into registers -- 16 rows x 64
+// bytes per instruction -- streamed the same bytes about 30% slower.)  The
+// stage also carries the pass's activation rows and the K-block's scales;
+// three or four stages are in flight per workgroup.
 //
 // The MMA is the 16x16 tile with weights as the A operand (16 rows) and
 // tokens as B (16 columns); lane (l % 16, l / 16) ends with four consecutive
@@ -50,43 +52,36 @@ struct GSCfg {
     static constexpr int NPASS = BM / RP;
     static constexpr int NU = RP / 16;             // 16-token subtiles
     static constexpr int NT = 512;                 // eight waves
-    static constexpr int S = 4;                    // K-blocks per stage
-    static constexpr int LPS = 4 * S;              // 16-byte loads per stage per lane
-    static constexpr int KMAX = 1024 / RP;         // K-blocks per workgroup (128 KB x tile)
     static constexpr int GROW = 260;               // row stride of the FP32 tile
-};
-
-// LDS carve-up, shared by the kernel and its launcher: the activation tile
-// (RP rows of KMAX K-blocks, 16-byte chunks XOR-swizzled by row & 7 within
-// each K-block), reused after the K loop as the FP32 tile [RP][GROW]; the
-// activation scales [RP][KMAX]; the weight scales [2][KMAX]; routes; flags.
-template <int BM>
-struct GSLayout {
-    using C = GSCfg<BM>;
-    static constexpr int XROWB = C::KMAX * 128;
-    static constexpr int X0 = C::RP * XROWB, G0 = C::RP * C::GROW * 4;
-    static constexpr int XS = X0 > G0 ? X0 : G0;
-    static constexpr int WS = XS + C::RP * C::KMAX * 4;
-    static constexpr int TOK = WS + 2 * C::KMAX * 4;
-    static constexpr int XT = TOK + C::RP * 4;
-    static constexpr int MISC = XT + C::RP * 4;
+    // LDS: a ring of NS stages {W13 tile 256 x 128 B, activation rows RP x
+    // 128 B, scales: a 16-float run per wave}, reused after the K loop as the
+    // FP32 tile [RP][GROW]; then routes, row tokens, a DMA sink, flags.
+    static constexpr int NS = RP <= 32 ? 4 : 3;
+    static constexpr int WB = 256 * 128;
+    static constexpr int XB = RP * 128;
+    static constexpr int SB = 8 * 16 * 4;
+    static constexpr int STB = WB + XB + SB;
+    static constexpr int RING = NS * STB;
+    static constexpr int GT = RP * GROW * 4;
+    static constexpr int TOK = RING > GT ? RING : GT;
+    static constexpr int XT = TOK + RP * 4;
+    static constexpr int SINK = XT + RP * 4;
+    static constexpr int MISC = SINK + 8 * 256;
     static constexpr int TOTAL = MISC + 16;
+    static constexpr int NPS = 6;                  // DMA instructions per wave per stage
 };
 
 template <int BM, int MODE>
 __global__ void __launch_bounds__(512)
 gateup_stream_kernel(GateUpArgs a) {
     using C = GSCfg<BM>;
+    static_assert(C::TOTAL <= 160 * 1024, "LDS budget");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    using Ld = GSLayout<BM>;
-    const int kps = a.kb_per_split;
-    uint8_t *sX = smem;
-    float *sG = reinterpret_cast<float *>(smem);    // reuses the x tile after the loop
-    float *sXs = reinterpret_cast<float *>(smem + Ld::XS);
-    float *sWs = reinterpret_cast<float *>(smem + Ld::WS);
-    int *sTok = reinterpret_cast<int *>(smem + Ld::TOK);   // route of each row, -1 if none
-    int *sXt = reinterpret_cast<int *>(smem + Ld::XT);     // token whose x row fills the row
-    int *sMisc = reinterpret_cast<int *>(smem + Ld::MISC);
+    float *sG = reinterpret_cast<float *>(smem);    // reuses the ring after the loop
+    int *sTok = reinterpret_cast<int *>(smem + C::TOK);    // route of each row, -1 if none
+    int *sXt = reinterpret_cast<int *>(smem + C::XT);      // token whose x row fills the row
+    uint8_t *sSink = smem + C::SINK;
+    int *sMisc = reinterpret_cast<int *>(smem + C::MISC);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -110,7 +105,6 @@ gateup_stream_kernel(GateUpArgs a) {
     const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors
     if (b * BM >= ntp || e < 0 || e >= a.E) return;   // padded block
 
-    for (int i = tid; i < C::RP * C::KMAX; i += C::NT) sXs[i] = 0.f;
     // this pass's routes (wave 0), the valid-row extent, the inverse plan map
     if (w == 0) {
         if (lane < C::RP) {
@@ -128,90 +122,53 @@ gateup_stream_kernel(GateUpArgs a) {
     __syncthreads();
     const int nvp = sMisc[0];                   // rows [0, nvp) hold every valid row
     if (nvp == 0) return;                       // whole pass masked (same for all splits)
+    const int nvpad = (nvp + 15) & ~15;
 
-    const int kb0 = split * kps;
-    const int kb1 = kb0 + kps < a.nkb ? kb0 + kps : a.nkb;
+    const int kb0 = split * a.kb_per_split;
+    const int kb1 = kb0 + a.kb_per_split < a.nkb ? kb0 + a.kb_per_split : a.nkb;
     const int nk = kb1 - kb0;
-    const int nst = (nk + C::S - 1) / C::S;
+    if (nk <= 0) return;
     const int64_t K = a.K, I = a.I;
 
-    // ---- weight stream: this wave's 16 gate rows and the matching up rows,
-    // through buffer descriptors over the tile's 128 gate / 128 up rows.
-    // Stages past the K-range read at an offset beyond the descriptor, which
-    // returns zeros without touching memory: every stage issues the same
-    // loads, so the loop has no branches and the waits stay exact.
-    const uint8_t *gbase = a.w13 + ((int64_t)e * 2 * I + (int64_t)jt * 128) * K;
-    const __amdgpu_buffer_rsrc_t rg =
-        __builtin_amdgcn_make_buffer_rsrc((void *)gbase, (short)0, (int)(128 * K), 0x00020000);
-    const __amdgpu_buffer_rsrc_t ru =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(gbase + I * K), (short)0, (int)(128 * K), 0x00020000);
-    const int rowoff = (16 * w + l16) * (int)K + 16 * g;
-    const int past = (int)(128 * K);            // first offset past the descriptor
-    u32x4 wb[2][C::S][4];
-    auto issue = [&](int st, auto BUF) {
-        constexpr int bf = decltype(BUF)::value;
-        const int vo = st < nst ? rowoff + (kb0 + st * C::S) * 128 : past;
+    // ---- DMA sources of this lane.  Every wave issues NPS instructions per
+    // stage (the waits count on it): four W13 segments (8 rows x 128 B each,
+    // 16-byte chunks XOR-swizzled by row & 7), one activation segment (rows
+    // 8w.., waves w < RP / 8; the others a 4-byte load into a sink), and one
+    // scale load (lanes 0-7: x_s of rows 8w..; lanes 8, 9: the gate and up
+    // weight-block scales).  Masked and padding rows read the last valid
+    // row's token (sXt); their columns are never stored.
+    const int sub = lane >> 3, slot = lane & 7;
+    const uint8_t *wsrc[4];
 #pragma unroll
-        for (int kk = 0; kk < C::S; ++kk) {
-            wb[bf][kk][0] = __builtin_amdgcn_raw_buffer_load_b128(rg, vo + kk * 128, 0, 0);
-            wb[bf][kk][1] = __builtin_amdgcn_raw_buffer_load_b128(rg, vo + kk * 128 + 64, 0, 0);
-            wb[bf][kk][2] = __builtin_amdgcn_raw_buffer_load_b128(ru, vo + kk * 128, 0, 0);
-            wb[bf][kk][3] = __builtin_amdgcn_raw_buffer_load_b128(ru, vo + kk * 128 + 64, 0, 0);
-        }
-    };
-    // ---- activation rows [0, nvpad) of the K-range (LDS DMA: lane l of an
-    // instruction fills 16-byte slot l of a 1 KB run of one row), their
-    // scales, the weight scales.  Masked and padding rows read the last
-    // valid row's token (sXt); their columns are never stored.
-    const int nvpad = (nvp + 15) & ~15;
-    {
-        constexpr int SPR = C::KMAX * 8;        // slots per row
-        constexpr int NI = C::RP * SPR / 64;    // DMA instructions for a full tile
-        const int tv = sXt[lane < C::RP ? lane : 0];   // row tokens, one per lane
-#pragma unroll
-        for (int i = 0; i < NI / 8; ++i) {
-            const int q = i * 8 + w;
-            const int row = q * 64 / SPR, slot0 = q * 64 % SPR;
-            if (row < nvpad && slot0 < nk * 8) {
-                const int t = __builtin_amdgcn_readlane(tv, row);
-                const int c = (slot0 + lane) ^ (row & 7);
-                const int kbl = (c >> 3) < nk ? (c >> 3) : 0;
-                lds_dma16(a.xq + (int64_t)t * K + (int64_t)(kb0 + kbl) * 128 + (c & 7) * 16,
-                          sX + row * Ld::XROWB + slot0 * 16);
-            }
-        }
-        // activation scales [row][KMAX] (rows < nvp, K-blocks < nk), two per thread
-        constexpr int XSPT = C::RP * C::KMAX / C::NT;
-        float xs[XSPT], wsv = 0.f;
-        int xsi[XSPT];
-#pragma unroll
-        for (int j = 0; j < XSPT; ++j) {
-            const int idx = tid + j * C::NT;
-            xs[j] = 0.f;
-            xsi[j] = -1;
-            if (idx < nvp * nk) {
-                const int srow = idx / nk, skb = idx - srow * nk;
-                if (sTok[srow] >= 0) {
-                    xs[j] = a.xs[(int64_t)sXt[srow] * a.nkb + kb0 + skb];
-                    xsi[j] = srow * C::KMAX + skb;
-                }
-            }
-        }
-        const int nb13 = (int)(2 * I / 128);
-        const int half = tid / C::KMAX, wkb = tid % C::KMAX;   // half < 2: weight scale slot
-        if (half < 2 && wkb < nk)
-            wsv = a.w13s[((int64_t)e * nb13 + (half ? (int)(I / 128) : 0) + jt) * a.nkb + kb0 + wkb];
-        // the weight stream starts behind the activation tile: waiting for
-        // the tile then leaves both weight stages in flight
-        issue(0, std::integral_constant<int, 0>{});
-        issue(1, std::integral_constant<int, 1>{});
-        wait_vmcnt<2 * C::LPS>();
-#pragma unroll
-        for (int j = 0; j < XSPT; ++j)
-            if (xsi[j] >= 0) sXs[xsi[j]] = xs[j];
-        if (half < 2) sWs[tid] = wsv;           // [half][KMAX]
+    for (int i = 0; i < 4; ++i) {
+        const int row = (w * 4 + i) * 8 + sub;                  // tile row 0..255
+        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+        wsrc[i] = a.w13 + ((int64_t)e * 2 * I + n) * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
     }
-    __syncthreads();
+    const bool xw = w < C::RP / 8;
+    const uint8_t *xsrc;
+    {
+        const int row = xw ? 8 * w + sub : 0;
+        xsrc = a.xq + (int64_t)sXt[row] * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
+    }
+    const float *ssrc;
+    if (lane < 8) {
+        const int row = 8 * w + lane < C::RP ? 8 * w + lane : 0;
+        ssrc = a.xs + (int64_t)sXt[row] * a.nkb + kb0;
+    } else {
+        const int nb13 = (int)(2 * I / 128);
+        ssrc = a.w13s + ((int64_t)e * nb13 + (lane == 9 ? (int)(I / 128) : 0) + jt) * a.nkb + kb0;
+    }
+    auto issue = [&](int st, int kbl) {
+        uint8_t *base = smem + st * C::STB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(wsrc[i] + kbl * 128, base + (w * 4 + i) * 1024);
+        if (xw)
+            lds_dma16(xsrc + kbl * 128, base + C::WB + w * 1024);
+        else
+            lds_dma4(xsrc + kbl * 128, sSink + w * 256);
+        if (lane < 10) lds_dma4(ssrc + kbl, base + C::WB + C::XB + w * 64);
+    };
 
     v4f accg[C::NU], accu[C::NU];
 #pragma unroll
@@ -220,73 +177,76 @@ gateup_stream_kernel(GateUpArgs a) {
         accu[u] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    // K-blocks past the range (the tail of the last stage, whole dummy
-    // stages) carry zero scales, so they add exact zeros: their weights are
-    // finite codes or zeros and the x tile holds finite codes up to the next
-    // multiple of 8 K-blocks.
-    auto compute = [&](int st, auto BUF) {
-        constexpr int bf = decltype(BUF)::value;
+    auto compute = [&](int st) {
+        const uint8_t *Ws = smem + st * C::STB;
+        const uint8_t *Xs = Ws + C::WB;
+        const float *Ss = reinterpret_cast<const float *>(Ws + C::WB + C::XB);
+        const float sg = Ss[8], su = Ss[9];     // wave 0's run
+        u32x4 wlo[2], whi[2];
 #pragma unroll
-        for (int kk = 0; kk < C::S; ++kk) {
-            const int kbl = st * C::S + kk;
-            const float sg = sWs[kbl], su = sWs[C::KMAX + kbl];
-            v8h Wg[4], Wu[4];
+        for (int h = 0; h < 2; ++h) {
+            const int row = 128 * h + 16 * w + l16;
+            const uint8_t *rp = Ws + row * 128;
+            wlo[h] = lds_read16(rp + ((g ^ (row & 7)) << 4));
+            whi[h] = lds_read16(rp + (((4 + g) ^ (row & 7)) << 4));
+        }
+        v8h Wg[4], Wu[4];
+        if constexpr (MODE == kExact) {
+            e4m3x32_to_f16(wlo[0], whi[0], Wg);
+            e4m3x32_to_f16(wlo[1], whi[1], Wu);
+        }
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+            if (16 * u >= nvp) break;
+            const int row = 16 * u + l16;
+            const uint8_t *xp = Xs + row * 128;
+            const u32x4 lo = lds_read16(xp + ((g ^ (row & 7)) << 4));
+            const u32x4 hi = lds_read16(xp + (((4 + g) ^ (row & 7)) << 4));
+            const float sa = Ss[(row >> 3) * 16 + (row & 7)];
             if constexpr (MODE == kExact) {
-                e4m3x32_to_f16(wb[bf][kk][0], wb[bf][kk][1], Wg);
-                e4m3x32_to_f16(wb[bf][kk][2], wb[bf][kk][3], Wu);
-            }
-#pragma unroll
-            for (int u = 0; u < C::NU; ++u) {
-                if (16 * u >= nvp) break;
-                const int row = 16 * u + l16;
-                const uint8_t *xp = sX + row * Ld::XROWB + kbl * 128;
-                const u32x4 lo = lds_read16(xp + ((g ^ (row & 7)) << 4));
-                const u32x4 hi = lds_read16(xp + (((4 + g) ^ (row & 7)) << 4));
-                const float sa = sXs[row * C::KMAX + kbl];
-                if constexpr (MODE == kExact) {
-                    v8h Bh[4];
-                    e4m3x32_to_f16(lo, hi, Bh);
-                    const v4f tg = mfma16x16x128_f16(Wg, Bh);
-                    const v4f tu = mfma16x16x128_f16(Wu, Bh);
-                    accg[u] = tg * (sa * sg) + accg[u];
-                    accu[u] = tu * (sa * su) + accu[u];
+                v8h Bh[4];
+                e4m3x32_to_f16(lo, hi, Bh);
+                const v4f tg = mfma16x16x128_f16(Wg, Bh);
+                const v4f tu = mfma16x16x128_f16(Wu, Bh);
+                accg[u] = tg * (sa * sg) + accg[u];
+                accu[u] = tu * (sa * su) + accu[u];
+            } else {
+                const v8i B = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                const v8i Ag = {(int)wlo[0].x, (int)wlo[0].y, (int)wlo[0].z, (int)wlo[0].w,
+                                (int)whi[0].x, (int)whi[0].y, (int)whi[0].z, (int)whi[0].w};
+                const v8i Au = {(int)wlo[1].x, (int)wlo[1].y, (int)wlo[1].z, (int)wlo[1].w,
+                                (int)whi[1].x, (int)whi[1].y, (int)whi[1].z, (int)whi[1].w};
+                if constexpr (MODE == kFp8E8) {
+                    const int eb = e8m0_of(sa);
+                    accg[u] = mfma16x16x128_e8m0(Ag, B, accg[u], e8m0_of(sg), eb);
+                    accu[u] = mfma16x16x128_e8m0(Au, B, accu[u], e8m0_of(su), eb);
                 } else {
-                    const v8i B = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    const u32x4 &g0 = wb[bf][kk][0], &g1 = wb[bf][kk][1];
-                    const u32x4 &u0 = wb[bf][kk][2], &u1 = wb[bf][kk][3];
-                    const v8i Ag = {(int)g0.x, (int)g0.y, (int)g0.z, (int)g0.w,
-                                    (int)g1.x, (int)g1.y, (int)g1.z, (int)g1.w};
-                    const v8i Au = {(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                                    (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                    if constexpr (MODE == kFp8E8) {
-                        const int eb = e8m0_of(sa);
-                        accg[u] = mfma16x16x128_e8m0(Ag, B, accg[u], e8m0_of(sg), eb);
-                        accu[u] = mfma16x16x128_e8m0(Au, B, accu[u], e8m0_of(su), eb);
-                    } else {
-                        accg[u] = mfma16x16x128(Ag, B) * (sa * sg) + accg[u];
-                        accu[u] = mfma16x16x128(Au, B) * (sa * su) + accu[u];
-                    }
+                    accg[u] = mfma16x16x128(Ag, B) * (sa * sg) + accg[u];
+                    accu[u] = mfma16x16x128(Au, B) * (sa * su) + accu[u];
                 }
             }
         }
     };
-    // Stage st computes from buffer st & 1, then refills it with stage st + 2.
-    // (pairs of stages, then an odd last one: no exit from the middle of
-    // the loop body, which keeps the compiler's own waits at the stage
-    // boundaries)
-    int st = 0;
-    for (; st + 1 < nst; st += 2) {
-        wait_vmcnt<C::LPS>();
-        compute(st, std::integral_constant<int, 0>{});
-        issue(st + 2, std::integral_constant<int, 0>{});
-        wait_vmcnt<C::LPS>();
-        compute(st + 1, std::integral_constant<int, 1>{});
-        issue(st + 3, std::integral_constant<int, 1>{});
-    }
-    if (st < nst) {
-        wait_vmcnt<C::LPS>();
-        compute(st, std::integral_constant<int, 0>{});
+
+    // Ring: stages 0 .. NS-2 up front; step kb waits for its stage (loads
+    // complete in issue order, so only the later stages already issued may
+    // still be in flight), then a barrier makes the stage visible and frees
+    // the slot of kb - 1 for the refill of kb + NS - 1.
+#pragma unroll
+    for (int s0 = 0; s0 < C::NS - 1; ++s0)
+        if (s0 < nk) issue(s0, s0);
+    for (int kb = 0; kb < nk; ++kb) {
+        const int ahead = nk - 1 - kb;
+        if (C::NS > 3 && ahead >= 2)
+            wait_vmcnt<(C::NS > 3 ? 2 : 1) * C::NPS>();
+        else if (ahead >= 1)
+            wait_vmcnt<C::NPS>();
+        else
+            wait_vmcnt<0>();
+        stage_barrier();
+        if (kb + C::NS - 1 < nk) issue((kb + C::NS - 1) % C::NS, kb + C::NS - 1);
+        compute(kb % C::NS);
     }
 
     // ---- FP32 tile of the pass: sG[row][n], gate n < 128, up n >= 128
@@ -387,8 +347,8 @@ hipError_t launch_gs(const GateUpArgs &a, hipStream_t st) {
     using C = GSCfg<BM>;
     const int64_t grid = (int64_t)a.nblocks * a.nsplit * a.jtiles * C::NPASS;
     if (grid == 0) return hipSuccess;
-    if (a.kb_per_split < 1 || a.kb_per_split > C::KMAX) return hipErrorInvalidValue;
-    const int lds = GSLayout<BM>::TOTAL;
+    if (a.kb_per_split < 1) return hipErrorInvalidValue;
+    const int lds = C::TOTAL;
     if (lds > 64 * 1024) {                      // once per device
         static bool attr_set[64] = {};
         int dev = 0;
@@ -429,7 +389,7 @@ prep_kernel(uint32_t *__restrict__ rpos, size_t nr, uint32_t *__restrict__ cnt, 
 
 }  // namespace
 
-int gateup_stream_kmax(int block_m) { return 1024 / (block_m < 64 ? block_m : 64); }
+int gateup_stream_kmax(int) { return 1 << 20; }   // the K-range streams through the ring
 
 hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                          hipStream_t st) {
