@@ -57,6 +57,10 @@ def parse():
                     help="power-of-two scales inside the FP8 MFMA (zipf workload)")
     ap.add_argument("--splitk", type=int, default=0,
                     help="force the small-grid gate/up split-K factor (1..255; 0 = automatic)")
+    ap.add_argument("--gateup-path", choices=("auto", "stream", "persistent"), default="auto",
+                    help="force the gate/up kernel family (tuning override)")
+    ap.add_argument("--down-path", choices=("auto", "stream", "persistent"), default="auto",
+                    help="force the down kernel family (tuning override)")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP graph replays (the default: one "
                          "graph of K steps and one of K launches per stage, each replayed once)")
@@ -97,12 +101,12 @@ GATEUP_SOURCES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
-def gateup_kernel_name(sorted_cap, block_m, I, splitk):
-    """The gate/up kernel the library picks: the persistent pipelined kernel
-    for >= 512 (block, 128-column tile) pairs unless split-K is forced, else
-    the weight-stream kernel."""
-    return ("gateup_pipe_kernel" if splitk == 0 and (sorted_cap // block_m) * (I // 128) >= 512
-            else "gateup_stream_kernel")
+def gateup_kernel_name(case, sorted_cap, flags):
+    """The gate/up kernel the library picks for these sizes and flags."""
+    import fp8_block_scale_amd as moe
+    gu_persistent = moe.moe_fp8_experts_schedule(case.M, case.K, case.I, case.E, case.top_k,
+                                                 case.block_m, sorted_cap, flags)[0]
+    return "gateup_pipe_kernel" if gu_persistent else "gateup_stream_kernel"
 
 
 def sources_sha(kernel):
@@ -195,6 +199,10 @@ def main():
         flags |= moe.MOE_F_FP8_GATEUP
     if args.splitk:
         flags |= (args.splitk & 0xFF) << moe.MOE_F_SPLITK_SHIFT
+    paths = {"auto": moe.MOE_PATH_AUTO, "stream": moe.MOE_PATH_STREAM,
+             "persistent": moe.MOE_PATH_PERSISTENT}
+    flags |= paths[args.gateup_path] << moe.MOE_F_GATEUP_PATH_SHIFT
+    flags |= paths[args.down_path] << moe.MOE_F_DOWN_PATH_SHIFT
 
     # Weight copies: a step reads the touched experts' weights once; with
     # fewer than ~1 GiB of them per step, back-to-back steps would find them
@@ -298,7 +306,7 @@ def main():
     mfma_peak = FP8_MFMA_PEAK if args.fp8_gateup else FP16_MFMA_PEAK
     t_hbm = nb["gate_up"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = gu_flops / (mfma_peak * 1e12)
-    kernel = gateup_kernel_name(b.sorted_ids.numel(), case.block_m, case.I, args.splitk)
+    kernel = gateup_kernel_name(case, b.sorted_ids.numel(), flags)
     workload = f"{case.name} M={case.M}"
     if t_mfma > t_hbm:
         achieved = gu_flops / (gate_up * 1e-3) / 1e12

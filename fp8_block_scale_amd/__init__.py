@@ -24,12 +24,16 @@ MOE_F_INTER_UE8M0 = 1
 MOE_F_MMA_E8M0 = 2
 MOE_F_FP8_GATEUP = 4
 MOE_F_SPLITK_SHIFT = 8
+MOE_F_GATEUP_PATH_SHIFT = 16
+MOE_F_DOWN_PATH_SHIFT = 18
+MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_PERSISTENT = 0, 1, 2
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
                 4: "MOE_ERR_CAPACITY", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
 
 EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_quant_act",
             "moe_fp8_experts_workspace_size", "moe_fp8_experts_workspace_layout",
+            "moe_fp8_experts_schedule",
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
             "moe_last_error", "moe_debug_e4m3_encode", "moe_debug_count_non_pow2")
 
@@ -67,6 +71,8 @@ _c = {
                                              _i64, _i32, _i32, _i32, _i64, _u32),
     "moe_fp8_experts_workspace_layout": _proto("moe_fp8_experts_workspace_layout", _i32, _i64, _i64,
                                                _i64, _i32, _i32, _i32, _i64, _u32, _psz, _psz),
+    "moe_fp8_experts_schedule": _proto("moe_fp8_experts_schedule", _i32, _i64, _i64, _i64, _i32,
+                                       _i32, _i32, _i64, _u32, _vp),
     "moe_fp8_experts": _proto("moe_fp8_experts", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp, _sz,
                               _vp),
@@ -167,6 +173,14 @@ def moe_fp8_experts_workspace_layout(M, K, I, E, top_k, block_m, sorted_cap, fla
                                                   ctypes.byref(a), ctypes.byref(b)),
            "moe_fp8_experts_workspace_layout")
     return a.value, b.value
+
+
+def moe_fp8_experts_schedule(M, K, I, E, top_k, block_m, sorted_cap, flags=0):
+    """(gate/up persistent, down persistent, split-K factor, K-blocks per split)."""
+    info = (ctypes.c_int32 * 4)()
+    _check(_c["moe_fp8_experts_schedule"](M, K, I, E, top_k, block_m, sorted_cap, flags, info),
+           "moe_fp8_experts_schedule")
+    return bool(info[0]), bool(info[1]), int(info[2]), int(info[3])
 
 
 def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,

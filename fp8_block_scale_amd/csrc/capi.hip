@@ -43,26 +43,44 @@ int64_t plan_sorted_cap(int64_t M, int32_t top_k, int32_t E, int32_t bm) {
 
 bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
-// Gate/up work split.  Large grids take the persistent pipelined kernels
-// (both stages share the row-tile list the gate/up stage builds); small grids
-// the weight-stream kernel, with K split over enough workgroups to cover the
-// chip and each K-range short enough for its LDS activation tile.
+// Kernel families and the gate/up work split.  The persistent kernels walk
+// 128-row tiles of one expert (the row-tile list, built in the gate/up
+// stage, is shared by both stages) and reuse each weight tile across all of
+// its rows; the per-block kernels stream an expert's weights once per plan
+// block (per 64-row pass), which wins while experts hold few rows each.
+// The small-grid gate/up splits K over enough workgroups to cover the chip.
 struct SplitChoice {
     int nsplit;
     int kb_per_split;
-    bool persistent;
+    bool gu_persistent;
+    bool dn_persistent;
 };
 
 constexpr int64_t kPersistentTiles = 512;   // (block, j-tile) pairs
 constexpr int64_t kStreamTarget = 256;      // workgroups of the stream kernel
 
-SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t K, int64_t I, int32_t bm,
-                         uint32_t flags) {
+SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtiles, int64_t K,
+                         int64_t I, int32_t bm, uint32_t flags) {
     const int64_t nkb = K / 128;
     const int64_t tiles = blocks_cap * jtiles;
     const int64_t forced = (flags & MOE_F_SPLITK_MASK) >> MOE_F_SPLITK_SHIFT;
-    if (forced == 0 && tiles >= kPersistentTiles && K <= 32768 && I <= 32768)
-        return {1, (int)nkb, true};
+    const uint32_t gu_path = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
+    const uint32_t dn_path = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
+    const bool fits = K <= 32768 && I <= 32768;
+    const bool big = tiles >= kPersistentTiles && fits;
+    // Measured on the page-1, skew and zipf workloads: the per-block gate/up
+    // is faster up to ~3/4 of a 64-row pass of routes per expert on average.
+    const int64_t pass_rows = bm < 64 ? bm : 64;
+    const bool dense = 4 * R > 3 * pass_rows * (int64_t)E;
+    SplitChoice c;
+    c.gu_persistent = gu_path == MOE_PATH_PERSISTENT ||
+                      (gu_path == MOE_PATH_AUTO && forced == 0 && big && dense);
+    c.dn_persistent = dn_path == MOE_PATH_PERSISTENT || (dn_path == MOE_PATH_AUTO && big);
+    if (c.gu_persistent) {
+        c.nsplit = 1;
+        c.kb_per_split = (int)nkb;
+        return c;
+    }
     const int64_t npass = bm > 64 ? bm / 64 : 1;
     int64_t s = forced;
     if (s == 0) {
@@ -75,7 +93,9 @@ SplitChoice choose_split(int64_t blocks_cap, int64_t jtiles, int64_t K, int64_t 
     if (s < 1) s = 1;
     const int64_t kps = (nkb + s - 1) / s;
     s = (nkb + kps - 1) / kps;        // no empty splits
-    return {(int)s, (int)kps, false};
+    c.nsplit = (int)s;
+    c.kb_per_split = (int)kps;
+    return c;
 }
 
 struct WsLayout {
@@ -84,12 +104,12 @@ struct WsLayout {
     SplitChoice sp;
 };
 
-WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t top_k, int32_t block_m,
+WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, int32_t block_m,
                    int64_t sorted_cap, uint32_t flags) {
     WsLayout l;
     int64_t blocks_cap = sorted_cap / block_m;
     int64_t jtiles = I / 128;
-    l.sp = choose_split(blocks_cap, jtiles, K, I, block_m, flags);
+    l.sp = choose_split(M * top_k, E, blocks_cap, jtiles, K, I, block_m, flags);
     size_t off = 0;
     l.hq = off;
     off = align256(off + (size_t)sorted_cap * I);
@@ -248,7 +268,7 @@ MOE_API size_t moe_fp8_experts_workspace_size(int64_t M, int64_t K, int64_t I, i
                                               int32_t top_k, int32_t block_m, int64_t sorted_cap,
                                               uint32_t flags) {
     if (check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap) != MOE_OK) return 0;
-    return ws_layout(M, K, I, top_k, block_m, sorted_cap, flags).total;
+    return ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags).total;
 }
 
 MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int32_t E,
@@ -258,9 +278,46 @@ MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
     if (!h_q_offset || !h_s_offset) return fail(MOE_ERR_NULL, "output pointer is NULL");
-    WsLayout l = ws_layout(M, K, I, top_k, block_m, sorted_cap, flags);
+    WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
     *h_q_offset = l.hq;
     *h_s_offset = l.hs;
+    return MOE_OK;
+}
+
+namespace {
+
+moe_status check_flags(uint32_t flags, int64_t K, int64_t I) {
+    const uint32_t known = MOE_F_INTER_UE8M0 | MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_SPLITK_MASK |
+                           MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK;
+    if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
+    const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
+    const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
+    if (gp > MOE_PATH_PERSISTENT || dp > MOE_PATH_PERSISTENT)
+        return fail(MOE_ERR_SHAPE, "kernel path override must be 0, 1 or 2");
+    if ((gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT) && (K > 32768 || I > 32768))
+        return fail(MOE_ERR_UNSUPPORTED, "the persistent kernels need K, I <= 32768");
+    if (gp == MOE_PATH_PERSISTENT && (flags & MOE_F_SPLITK_MASK))
+        return fail(MOE_ERR_SHAPE, "a forced split-K factor needs the per-block gate/up kernel");
+    if ((flags & MOE_F_MMA_E8M0) && !(flags & MOE_F_INTER_UE8M0))
+        return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
+    return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int32_t E,
+                                            int32_t top_k, int32_t block_m, int64_t sorted_cap,
+                                            uint32_t flags, int32_t *info) {
+    moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
+    if (st != MOE_OK) return st;
+    if (!info) return fail(MOE_ERR_NULL, "output pointer is NULL");
+    st = check_flags(flags, K, I);
+    if (st != MOE_OK) return st;
+    const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
+    info[0] = l.sp.gu_persistent ? 1 : 0;
+    info[1] = l.sp.dn_persistent ? 1 : 0;
+    info[2] = l.sp.nsplit;
+    info[3] = l.sp.kb_per_split;
     return MOE_OK;
 }
 
@@ -272,11 +329,9 @@ moe_status check_stage(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k
                        size_t workspace_bytes, WsLayout *l) {
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
-    const uint32_t known = MOE_F_INTER_UE8M0 | MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_SPLITK_MASK;
-    if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
-    if ((flags & MOE_F_MMA_E8M0) && !(flags & MOE_F_INTER_UE8M0))
-        return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
-    *l = ws_layout(M, K, I, top_k, block_m, sorted_cap, flags);
+    st = check_flags(flags, K, I);
+    if (st != MOE_OK) return st;
+    *l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
     if (M == 0 || sorted_cap == 0) return MOE_OK;
     if (!workspace) return fail(MOE_ERR_NULL, "workspace is required");
     if (((uintptr_t)workspace & 255u) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -334,8 +389,12 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.kb_per_split = l.sp.kb_per_split;
     ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
     const bool fp8 = (flags & MOE_F_FP8_GATEUP) != 0, e8 = (flags & MOE_F_MMA_E8M0) != 0;
-    if (l.sp.persistent)
+    if (l.sp.gu_persistent)
         return hip_check(moe::launch_gateup_pipe(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
+    if (l.sp.dn_persistent) {                  // the down stage's row tiles
+        st = hip_check(moe::launch_tiles(ga, block_m, s), "moe_fp8_gate_up: row tiles");
+        if (st != MOE_OK) return st;
+    }
     return hip_check(moe::launch_gateup(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
 }
 
@@ -379,7 +438,7 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
     da.tiles = (const int4 *)(ws + l.tiles);
     da.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);
     const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
-    st = hip_check(l.sp.persistent ? moe::launch_down_pipe(da, block_m, e8, s)
+    st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe(da, block_m, e8, s)
                                                    : moe::launch_down(da, block_m, e8, s),
                    "moe_fp8_down_reduce: down launch");
     if (st != MOE_OK) return st;

@@ -460,6 +460,14 @@ hipError_t launch_pipe_mode(const GateUpArgs &a, int mode, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st) {
+    if (a.nblocks == 0) return hipSuccess;
+    if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return hipErrorInvalidValue;
+    tiles_kernel<<<1, 1024, 0, st>>>(a.eids, a.ntp, block_m, kRows / block_m, a.nblocks, a.tiles,
+                                     a.tmeta);
+    return hipGetLastError();
+}
+
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                               hipStream_t st) {
     const int mode = !fp8_mma ? kExact : (e8m0 ? kFp8E8 : kFp8);

@@ -79,6 +79,9 @@ struct DownArgs {
 int gateup_stream_kmax(int block_m);
 hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                          hipStream_t st);
+// The row-tile list of the persistent kernels alone (when only the down
+// stage runs persistent); launch_gateup_pipe builds it itself.
+hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st);
 // Large-grid gate/up (no split-K): 128-row tiles, three-stage LDS pipeline.
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                               hipStream_t st);

@@ -97,6 +97,18 @@ enum {
  * given to moe_fp8_experts_workspace_size. */
 #define MOE_F_SPLITK_SHIFT 8
 #define MOE_F_SPLITK_MASK  0xFF00u
+/* Bits 16..17 and 18..19 optionally force the kernel family of the gate/up
+ * and of the down stage: MOE_PATH_AUTO (0), MOE_PATH_STREAM (1: per plan
+ * block, the weights streamed once per block) or MOE_PATH_PERSISTENT (2:
+ * persistent workgroups over 128-row tiles of one expert; needs
+ * K, I <= 32768 and no forced split-K).  A tuning and test override; the
+ * same value must be given to moe_fp8_experts_workspace_size.  Other
+ * values: MOE_ERR_SHAPE. */
+#define MOE_F_GATEUP_PATH_SHIFT 16
+#define MOE_F_GATEUP_PATH_MASK  0x30000u
+#define MOE_F_DOWN_PATH_SHIFT   18
+#define MOE_F_DOWN_PATH_MASK    0xC0000u
+enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_PERSISTENT = 2 };
 
 /* ---------------------------------------------------------------- plan -- */
 
@@ -161,6 +173,16 @@ moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int
                                             int32_t top_k, int32_t block_m,
                                             int64_t sorted_cap, uint32_t flags,
                                             size_t *h_q_offset, size_t *h_s_offset);
+
+/* The launch schedule moe_fp8_experts would use for these sizes and flags
+ * (host only, nothing enqueued): info[0] = 1 if the gate/up stage runs the
+ * persistent kernel, info[1] = 1 if the down stage does, info[2] = the
+ * gate/up split-K factor, info[3] = K-blocks (of 128) per split.  info is
+ * host memory of 4 int32.  Errors: as moe_fp8_experts_workspace_size's
+ * shape checks (MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED), MOE_ERR_NULL. */
+moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                                    int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                                    int32_t *info);
 
 /* Steps 3-5 over a plan built by moe_plan (or any plan of that form):
  *   out[t, :] += sum over valid routes r of token t of

@@ -256,14 +256,20 @@ def test_small_grid_long_intermediate_rows(bm):
     full_parity(cs, label="small grid, long intermediate rows")
 
 
-@pytest.mark.parametrize("name,M", [("decode", None), ("page1", 512)])
-def test_graph_replay_matches_eager(name, M):
-    """The whole layer captured in a HIP graph (small-grid kernels for decode,
-    the persistent ones at M=512): every replay, with eager work and
-    synchronisations between replays, gives the eager output bit for bit."""
+PERSIST = ((moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT)
+           | (moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT))
+
+
+@pytest.mark.parametrize("name,M,flags", [("decode", None, 0), ("page1", 512, 0),
+                                          ("page1", 512, PERSIST)])
+def test_graph_replay_matches_eager(name, M, flags):
+    """The whole layer captured in a HIP graph (small-grid kernels for decode;
+    at M=512 the per-block gate/up with the persistent down, then both
+    persistent kernels): every replay, with eager work and synchronisations
+    between replays, gives the eager output bit for bit."""
     cs = case_of(name, M=M)
-    log(f"[graph] {name} M={cs.M}")
-    b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, 0, DEV)
+    log(f"[graph] {name} M={cs.M} flags={flags:#x}")
+    b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, flags, DEV)
     args = (cs.x, cs.topk_ids, cs.topk_weights, cs.w13, cs.w13_s, cs.w2, cs.w2_s)
     ref = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
     moe.moe_layer(b, *args, ref, stream=torch.cuda.current_stream())
@@ -289,7 +295,8 @@ def test_persistent_kernels_small_block_m(bm):
     """The persistent gate/up and down kernels with block_m 16 and 32: row
     tiles of 8 and 4 plan blocks."""
     cs = case_of("page1", M=512, block_m=bm)
-    full_parity(cs, tokens=_sample_tokens(cs.M, 12, 20 + bm), label=f"persistent bm={bm}")
+    full_parity(cs, flags=PERSIST, tokens=_sample_tokens(cs.M, 12, 20 + bm),
+                label=f"persistent bm={bm}")
 
 
 def test_persistent_long_k_wide_i():
@@ -297,7 +304,22 @@ def test_persistent_long_k_wide_i():
     128-deep steps per down item, 16 j-tiles), E=32, top-8."""
     cfg = dict(CONFIGS["page1"], M=256, E=32, K=7168, I=2048, top_k=8, block_m=64, seed=11)
     cs = make_case("long_k", device=DEV, config=cfg)
-    full_parity(cs, tokens=_sample_tokens(cs.M, 6, 21), label="persistent K=7168 I=2048")
+    full_parity(cs, flags=PERSIST, tokens=_sample_tokens(cs.M, 6, 21),
+                label="persistent K=7168 I=2048")
+
+
+@pytest.mark.parametrize("gu,dn", [(1, 1), (1, 2), (2, 1), (2, 2)])
+def test_kernel_path_combinations(gu, dn):
+    """Every pairing of the per-block (1) and persistent (2) kernel families
+    of the two stages on one input: the down stage's row tiles come from the
+    gate/up stage whichever kernel it runs."""
+    cs = case_of("page1", M=256)
+    flags = (gu << moe.MOE_F_GATEUP_PATH_SHIFT) | (dn << moe.MOE_F_DOWN_PATH_SHIFT)
+    cap = moe.moe_plan_capacity(cs.M, cs.top_k, cs.E, cs.block_m)[0]
+    sched = moe.moe_fp8_experts_schedule(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, cap, flags)
+    assert sched[0] == (gu == 2) and sched[1] == (dn == 2)
+    full_parity(cs, flags=flags, tokens=_sample_tokens(cs.M, 8, 30 + 3 * gu + dn),
+                label=f"paths gate/up {gu} down {dn}")
 
 
 def test_debug_count_non_pow2():

@@ -140,3 +140,32 @@ def test_plan_workspace_size():
     assert moe.moe_plan_workspace_size(10 ** 6, 8, 64, 64) == 254 * 64 * 4
     assert moe.moe_plan_workspace_size(10 ** 6, 8, 1024, 64) == 14 * 1024 * 4
     assert moe.moe_plan_workspace_size(0, 8, 288, 64) == 0
+
+
+def test_experts_schedule():
+    """Kernel families per stage: the per-block gate/up while experts hold
+    few routes on average, the persistent kernels for large grids; overrides
+    and their validation."""
+    sched = moe.moe_fp8_experts_schedule
+    GU, DN = moe.MOE_F_GATEUP_PATH_SHIFT, moe.MOE_F_DOWN_PATH_SHIFT
+    # decode: small grid, both per-block, K split 14 ways of 4 K-blocks
+    assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, False, 14, 4)
+    # page-1 M=16 and M=1024: per-block gate/up, persistent down
+    assert sched(16, 4096, 1024, 288, 8, 64, 8192)[:2] == (False, True)
+    assert sched(1024, 4096, 1024, 288, 8, 64, 26368)[:2] == (False, True)
+    # page-1 M=4096 (the bench configuration): both persistent, no split
+    assert sched(4096, 4096, 1024, 288, 8, 64, 50944) == (True, True, 1, 32)
+    # overrides
+    assert sched(16, 4096, 1024, 288, 8, 64, 8192, 2 << GU)[:2] == (True, True)
+    assert sched(16, 4096, 1024, 288, 8, 64, 8192, 1 << DN)[:2] == (False, False)
+    assert sched(4096, 4096, 1024, 288, 8, 64, 50944, (1 << GU) | (1 << DN))[:2] == (False, False)
+    # a forced split-K factor selects the per-block gate/up
+    assert sched(4096, 4096, 1024, 288, 8, 64, 50944, 2 << moe.MOE_F_SPLITK_SHIFT)[0] is False
+    for bad, status in ((3 << GU, "MOE_ERR_SHAPE"), (3 << DN, "MOE_ERR_SHAPE"),
+                        ((2 << GU) | (2 << moe.MOE_F_SPLITK_SHIFT), "MOE_ERR_SHAPE"),
+                        (1 << 24, "MOE_ERR_SHAPE")):
+        with pytest.raises(moe.MoeError) as ei:
+            sched(16, 4096, 1024, 288, 8, 64, 8192, bad)
+        assert moe.STATUS_NAMES[ei.value.status] == status
+    with pytest.raises(moe.MoeError):       # the persistent kernels need K <= 32768
+        sched(16, 65536, 1024, 288, 8, 64, 8192, 2 << DN)
