@@ -61,6 +61,8 @@ def parse():
                     help="force the gate/up kernel family (tuning override)")
     ap.add_argument("--down-path", choices=("auto", "stream", "persistent"), default="auto",
                     help="force the down kernel family (tuning override)")
+    ap.add_argument("--separate-plan-quant", action="store_true",
+                    help="moe_plan then moe_quant_act instead of the fused moe_plan_quant")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP graph replays (the default: one "
                          "graph of K steps and one of K launches per stage, each replayed once)")
@@ -219,9 +221,13 @@ def main():
     b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
     out = torch.zeros((case.M, case.K), dtype=torch.bfloat16, device=dev)
     def stage_plan_quant(stream, k):
-        moe.moe_plan(case.topk_ids, case.E, case.block_m, b.sorted_ids, b.expert_ids, b.ntp,
-                     b.plan_ws, stream)
-        moe.moe_quant_act(case.x, b.x_q, b.x_s, act_mode, stream)
+        if args.separate_plan_quant:
+            moe.moe_plan(case.topk_ids, case.E, case.block_m, b.sorted_ids, b.expert_ids, b.ntp,
+                         b.plan_ws, stream)
+            moe.moe_quant_act(case.x, b.x_q, b.x_s, act_mode, stream)
+        else:
+            moe.moe_plan_quant(case.topk_ids, case.E, case.block_m, b.sorted_ids, b.expert_ids,
+                               b.ntp, case.x, b.x_q, b.x_s, act_mode, b.plan_ws, stream)
 
     def stage_gate_up(stream, k):
         w13, w13_s = wsets[k % nsets][:2]

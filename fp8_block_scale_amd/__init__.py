@@ -32,6 +32,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
                 4: "MOE_ERR_CAPACITY", 5: "MOE_ERR_UNSUPPORTED", 6: "MOE_ERR_HIP"}
 
 EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_quant_act",
+            "moe_plan_quant",
             "moe_fp8_experts_workspace_size", "moe_fp8_experts_workspace_layout",
             "moe_fp8_experts_schedule",
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
@@ -67,6 +68,8 @@ _c = {
     "moe_plan": _proto("moe_plan", _i32, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
                        _vp, _vp, _sz, _vp),
     "moe_quant_act": _proto("moe_quant_act", _i32, _vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp),
+    "moe_plan_quant": _proto("moe_plan_quant", _i32, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _i64, _vp,
+                             _i64, _vp, _vp, _sz, _vp, _i64, _i64, _vp, _vp, _i32, _vp),
     "moe_fp8_experts_workspace_size": _proto("moe_fp8_experts_workspace_size", _sz, _i64, _i64,
                                              _i64, _i32, _i32, _i32, _i64, _u32),
     "moe_fp8_experts_workspace_layout": _proto("moe_fp8_experts_workspace_layout", _i32, _i64, _i64,
@@ -115,9 +118,8 @@ def moe_plan_workspace_size(M, top_k, E, block_m):
     return _c["moe_plan_workspace_size"](M, top_k, E, block_m)
 
 
-def moe_plan(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded,
-             workspace=None, stream=None):
-    """topk_ids [M, top_k] int32/int64 (device); outputs are preallocated int32 tensors."""
+def _plan_args(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded,
+               workspace):
     M, top_k = topk_ids.shape
     if topk_ids.dtype == torch.int32:
         dt = MOE_IDS_I32
@@ -128,22 +130,45 @@ def moe_plan(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post
     assert topk_ids.is_contiguous() and sorted_token_ids.dtype == torch.int32
     assert expert_ids.dtype == torch.int32 and num_tokens_post_padded.dtype == torch.int32
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_c["moe_plan"](_ptr(topk_ids), dt, M, top_k, E, block_m, _ptr(sorted_token_ids),
-                          sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(),
-                          _ptr(num_tokens_post_padded), _ptr(workspace), ws_bytes, _stream(stream)),
-           "moe_plan")
+    return (_ptr(topk_ids), dt, M, top_k, E, block_m, _ptr(sorted_token_ids), sorted_token_ids.numel(),
+            _ptr(expert_ids), expert_ids.numel(), _ptr(num_tokens_post_padded), _ptr(workspace),
+            ws_bytes)
+
+
+def _quant_args(x_bf16, x_q, x_s):
+    assert x_bf16.dtype == torch.bfloat16 and x_bf16.dim() == 2 and x_bf16.stride(1) == 1
+    M, K = x_bf16.shape
+    assert x_q.dtype == torch.uint8 and x_q.is_contiguous() and tuple(x_q.shape) == (M, K)
+    assert x_s.dtype == torch.float32 and x_s.is_contiguous() and tuple(x_s.shape) == (M, K // 128)
+    return M, K, x_bf16.stride(0)
+
+
+def moe_plan(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded,
+             workspace=None, stream=None):
+    """topk_ids [M, top_k] int32/int64 (device); outputs are preallocated int32 tensors."""
+    args = _plan_args(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                      workspace)
+    _check(_c["moe_plan"](*args, _stream(stream)), "moe_plan")
+
+
+def moe_plan_quant(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                   x_bf16, x_q, x_s, scale_mode=MOE_SCALE_FP32, workspace=None, stream=None):
+    """moe_plan and moe_quant_act in one call (one launch fewer); same outputs."""
+    args = _plan_args(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                      workspace)
+    M, K, ld = _quant_args(x_bf16, x_q, x_s)
+    assert M == topk_ids.shape[0], "x_bf16 and topk_ids disagree on M"
+    _check(_c["moe_plan_quant"](*args, _ptr(x_bf16), K, ld, _ptr(x_q), _ptr(x_s), scale_mode,
+                                _stream(stream)), "moe_plan_quant")
 
 
 # ------------------------------------------------------------- quant act --
 
 def moe_quant_act(x_bf16, x_q, x_s, scale_mode=MOE_SCALE_FP32, stream=None):
     """x_bf16 [M, K] bf16 (row stride may exceed K); x_q uint8 [M, K]; x_s fp32 [M, K/128]."""
-    assert x_bf16.dtype == torch.bfloat16 and x_bf16.dim() == 2 and x_bf16.stride(1) == 1
-    M, K = x_bf16.shape
-    assert x_q.dtype == torch.uint8 and x_q.is_contiguous() and tuple(x_q.shape) == (M, K)
-    assert x_s.dtype == torch.float32 and x_s.is_contiguous() and tuple(x_s.shape) == (M, K // 128)
-    _check(_c["moe_quant_act"](_ptr(x_bf16), M, K, x_bf16.stride(0), _ptr(x_q), _ptr(x_s),
-                               scale_mode, _stream(stream)), "moe_quant_act")
+    M, K, ld = _quant_args(x_bf16, x_q, x_s)
+    _check(_c["moe_quant_act"](_ptr(x_bf16), M, K, ld, _ptr(x_q), _ptr(x_s), scale_mode,
+                               _stream(stream)), "moe_quant_act")
 
 
 def moe_debug_e4m3_encode(inp, out, stream=None):
@@ -271,10 +296,9 @@ class MoeLayerBuffers:
 
 def moe_layer(bufs, x_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s, out_bf16,
               act_scale_mode=MOE_SCALE_FP32, stream=None):
-    """All five steps on one stream: plan, activation quantisation, experts."""
-    moe_plan(topk_ids, bufs.E, bufs.block_m, bufs.sorted_ids, bufs.expert_ids, bufs.ntp,
-             bufs.plan_ws, stream)
-    moe_quant_act(x_bf16, bufs.x_q, bufs.x_s, act_scale_mode, stream)
+    """All five steps on one stream: plan with activation quantisation, experts."""
+    moe_plan_quant(topk_ids, bufs.E, bufs.block_m, bufs.sorted_ids, bufs.expert_ids, bufs.ntp,
+                   x_bf16, bufs.x_q, bufs.x_s, act_scale_mode, bufs.plan_ws, stream)
     moe_fp8_experts(bufs.x_q, bufs.x_s, w13, w13_s, w2, w2_s, topk_weights, bufs.sorted_ids,
                     bufs.expert_ids, bufs.ntp, bufs.top_k, bufs.block_m, out_bf16,
                     bufs.workspace, bufs.flags, stream)

@@ -192,11 +192,15 @@ MOE_API size_t moe_plan_workspace_size(int64_t M, int32_t top_k, int32_t E, int3
     return (size_t)moe::plan_groups(M * top_k, E) * (size_t)E * sizeof(int32_t);
 }
 
-MOE_API moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k,
-                            int32_t E, int32_t block_m, int32_t *sorted_token_ids,
-                            int64_t sorted_cap, int32_t *expert_ids, int64_t blocks_cap,
-                            int32_t *num_tokens_post_padded, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+namespace {
+
+// Validation of moe_plan's arguments; *groups = workgroups of the
+// multi-workgroup build when the workspace holds it, else 0.
+moe_status check_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k, int32_t E,
+                      int32_t block_m, const int32_t *sorted_token_ids, int64_t sorted_cap,
+                      const int32_t *expert_ids, int64_t blocks_cap,
+                      const int32_t *num_tokens_post_padded, const void *workspace,
+                      size_t workspace_bytes, int *groups) {
     int64_t need_sorted, need_blocks;
     moe_status st = moe_plan_capacity(M, top_k, E, block_m, &need_sorted, &need_blocks);
     if (st != MOE_OK) return st;
@@ -211,26 +215,16 @@ MOE_API moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, 
                     (long long)need_blocks);
     if (sorted_cap < blocks_cap * block_m)
         return fail(MOE_ERR_CAPACITY, "sorted_cap must be >= blocks_cap * block_m");
-    hipStream_t s = (hipStream_t)stream;
-    if (M == 0) {
-        // a fill kernel, not a memset node, so the call stays graph-capturable
-        return hip_check(moe::launch_fill_zero((uint32_t *)num_tokens_post_padded, 1, s),
-                         "moe_plan: clear num_tokens_post_padded");
-    }
     // the multi-workgroup build when the caller's workspace holds it
-    const int groups = moe::plan_groups(M * top_k, E);
-    const bool multi = groups > 0 && workspace != nullptr && ((uintptr_t)workspace & 3u) == 0 &&
-                       workspace_bytes >= (size_t)groups * (size_t)E * sizeof(int32_t);
-    return hip_check(moe::launch_plan(topk_ids, ids_dtype == MOE_IDS_I64, M * top_k, E, block_m,
-                                      sorted_token_ids, expert_ids, num_tokens_post_padded,
-                                      multi ? (int32_t *)workspace : nullptr, multi ? groups : 0, s),
-                     "moe_plan: launch");
+    const int g = M > 0 ? moe::plan_groups(M * top_k, E) : 0;
+    const bool multi = g > 0 && workspace != nullptr && ((uintptr_t)workspace & 3u) == 0 &&
+                       workspace_bytes >= (size_t)g * (size_t)E * sizeof(int32_t);
+    *groups = multi ? g : 0;
+    return MOE_OK;
 }
 
-// ------------------------------------------------------------- quant act
-
-MOE_API moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x,
-                                 uint8_t *x_q, float *x_s, int32_t scale_mode, void *stream) {
+moe_status check_quant(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x, const uint8_t *x_q,
+                       const float *x_s, int32_t scale_mode) {
     if (M < 0 || K <= 0 || K % 128 != 0)
         return fail(MOE_ERR_SHAPE, "need M >= 0 and K a positive multiple of 128");
     if (ld_x < K) return fail(MOE_ERR_SHAPE, "ld_x (%lld) < K (%lld)", (long long)ld_x, (long long)K);
@@ -241,6 +235,71 @@ MOE_API moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64
     if (!aligned16(x_bf16) || ld_x % 8 != 0 || !aligned16(x_q))
         return fail(MOE_ERR_ALIGN, "x_bf16 and x_q must be 16-byte aligned and ld_x a multiple of 8");
     if (((uintptr_t)x_s & 3u) != 0) return fail(MOE_ERR_ALIGN, "x_s must be 4-byte aligned");
+    return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k,
+                            int32_t E, int32_t block_m, int32_t *sorted_token_ids,
+                            int64_t sorted_cap, int32_t *expert_ids, int64_t blocks_cap,
+                            int32_t *num_tokens_post_padded, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    int groups = 0;
+    moe_status st = check_plan(topk_ids, ids_dtype, M, top_k, E, block_m, sorted_token_ids, sorted_cap,
+                               expert_ids, blocks_cap, num_tokens_post_padded, workspace,
+                               workspace_bytes, &groups);
+    if (st != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {
+        // a fill kernel, not a memset node, so the call stays graph-capturable
+        return hip_check(moe::launch_fill_zero((uint32_t *)num_tokens_post_padded, 1, s),
+                         "moe_plan: clear num_tokens_post_padded");
+    }
+    return hip_check(moe::launch_plan(topk_ids, ids_dtype == MOE_IDS_I64, M * top_k, E, block_m,
+                                      sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                      groups > 0 ? (int32_t *)workspace : nullptr, groups, s),
+                     "moe_plan: launch");
+}
+
+MOE_API moe_status moe_plan_quant(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k,
+                                  int32_t E, int32_t block_m, int32_t *sorted_token_ids,
+                                  int64_t sorted_cap, int32_t *expert_ids, int64_t blocks_cap,
+                                  int32_t *num_tokens_post_padded, void *workspace,
+                                  size_t workspace_bytes, const void *x_bf16, int64_t K,
+                                  int64_t ld_x, uint8_t *x_q, float *x_s, int32_t scale_mode,
+                                  void *stream) {
+    int groups = 0;
+    moe_status st = check_plan(topk_ids, ids_dtype, M, top_k, E, block_m, sorted_token_ids, sorted_cap,
+                               expert_ids, blocks_cap, num_tokens_post_padded, workspace,
+                               workspace_bytes, &groups);
+    if (st != MOE_OK) return st;
+    st = check_quant(x_bf16, M, K, ld_x, x_q, x_s, scale_mode);
+    if (st != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0)
+        return hip_check(moe::launch_fill_zero((uint32_t *)num_tokens_post_padded, 1, s),
+                         "moe_plan_quant: clear num_tokens_post_padded");
+    moe::QuantJob q;
+    q.x = (const uint16_t *)x_bf16;
+    q.M = M;
+    q.K = K;
+    q.ld = ld_x;
+    q.xq = x_q;
+    q.xs = x_s;
+    return hip_check(moe::launch_plan_quant(topk_ids, ids_dtype == MOE_IDS_I64, M * top_k, E, block_m,
+                                            sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                            groups > 0 ? (int32_t *)workspace : nullptr, groups, q,
+                                            scale_mode == MOE_SCALE_UE8M0, s),
+                     "moe_plan_quant: launch");
+}
+
+// ------------------------------------------------------------- quant act
+
+MOE_API moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x,
+                                 uint8_t *x_q, float *x_s, int32_t scale_mode, void *stream) {
+    const moe_status st = check_quant(x_bf16, M, K, ld_x, x_q, x_s, scale_mode);
+    if (st != MOE_OK || M == 0) return st;
     return hip_check(moe::launch_quant_act((const uint16_t *)x_bf16, M, K, ld_x, x_q, x_s,
                                            scale_mode == MOE_SCALE_UE8M0, (hipStream_t)stream),
                      "moe_quant_act: launch");

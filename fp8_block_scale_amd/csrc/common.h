@@ -264,4 +264,42 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
     return fmaxf(v, __shfl_xor(v, mask, 64));
 }
 
+// ------------------------------------------- activation quantisation group
+// One 128-column group of one token per 16 lanes (lig = lane in the group):
+// a 16-byte load of eight BF16 values per lane (fully coalesced rows), the
+// group amax by a 16-lane xor reduction, one 8-byte store of codes per lane
+// and one scale per group.  Lanes of a group past M * K / 128 return together.
+template <bool UE8M0>
+__device__ __forceinline__ void quant_act_group(const uint16_t *__restrict__ x, int64_t M, int64_t K,
+                                                int64_t ld, uint8_t *__restrict__ xq,
+                                                float *__restrict__ xs, int64_t gid, int lig) {
+    const int64_t G = K >> 7;
+    if (gid >= M * G) return;
+    const int64_t m = gid / G;
+    const int64_t g = gid - m * G;
+
+    const u32x4 raw = *reinterpret_cast<const u32x4 *>(x + m * ld + g * 128 + lig * 8);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
+        f[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = wave_max_xor(amax, 8);
+    amax = wave_max_xor(amax, 4);
+    amax = wave_max_xor(amax, 2);
+    amax = wave_max_xor(amax, 1);
+
+    float s, inv;
+    group_scale(amax, UE8M0, s, inv);
+    uint2 o;
+    o.x = pack_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    o.y = pack_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+    *reinterpret_cast<uint2 *>(xq + m * K + g * 128 + lig * 8) = o;
+    if (lig == 0) xs[m * G + g] = s;
+}
+
 }  // namespace moe

@@ -17,6 +17,20 @@ hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int bloc
                        int32_t *sorted, int32_t *expert_ids, int32_t *ntp, int32_t *ws, int groups,
                        hipStream_t st);
 
+// Activation quantisation work launched together with the plan
+// (moe_plan_quant): the arguments of launch_quant_act.
+struct QuantJob {
+    const uint16_t *x;
+    int64_t M, K, ld;
+    uint8_t *xq;
+    float *xs;
+};
+// The plan (as launch_plan) and the quantisation of q (as launch_quant_act)
+// with one launch fewer: the quantisation runs in the launch that builds the
+// plan (one-workgroup build) or counts its routes (multi-workgroup build).
+hipError_t launch_plan_quant(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
+                             int32_t *sorted, int32_t *expert_ids, int32_t *ntp, int32_t *ws,
+                             int groups, const QuantJob &q, bool ue8m0, hipStream_t st);
 // ---- step 2: activation quantisation (quant.hip)
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
                             uint8_t *xq, float *xs, bool ue8m0, hipStream_t st);

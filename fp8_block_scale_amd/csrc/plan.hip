@@ -40,11 +40,10 @@ __device__ __forceinline__ uint64_t match_mask(int key, int nbits) {
 }
 
 template <typename IdT>
-__global__ void __launch_bounds__(kPlanThreads)
-plan_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwaves,
-            int32_t *__restrict__ sorted, int32_t *__restrict__ expert_ids,
-            int32_t *__restrict__ ntp) {
-    extern __shared__ int smem[];
+__device__ __forceinline__ void plan_body(const IdT *__restrict__ ids, int64_t R, int E, int bm,
+                                          int nwaves, int32_t *__restrict__ sorted,
+                                          int32_t *__restrict__ expert_ids,
+                                          int32_t *__restrict__ ntp, int *smem) {
     int *hist = smem;                     // [nwaves][E]: counts, then bases
     int *cnt = hist + nwaves * E;         // [E] per-expert totals
     int *wsum = cnt + E;                  // [32] wave totals for the scan
@@ -144,6 +143,32 @@ plan_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwaves,
     }
 }
 
+template <typename IdT>
+__global__ void __launch_bounds__(kPlanThreads)
+plan_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwaves,
+            int32_t *__restrict__ sorted, int32_t *__restrict__ expert_ids,
+            int32_t *__restrict__ ntp) {
+    extern __shared__ int smem[];
+    plan_body(ids, R, E, bm, nwaves, sorted, expert_ids, ntp, smem);
+}
+
+// The one-workgroup plan and the activation quantisation in one launch:
+// workgroup 0 builds the plan, the others quantise 64 groups each.
+template <typename IdT, bool UE8M0>
+__global__ void __launch_bounds__(kPlanThreads)
+plan_quant_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwaves,
+                  int32_t *__restrict__ sorted, int32_t *__restrict__ expert_ids,
+                  int32_t *__restrict__ ntp, QuantJob q) {
+    extern __shared__ int smem[];
+    if (blockIdx.x == 0) {
+        plan_body(ids, R, E, bm, nwaves, sorted, expert_ids, ntp, smem);
+        return;
+    }
+    quant_act_group<UE8M0>(q.x, q.M, q.K, q.ld, q.xq, q.xs,
+                           ((int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x) >> 4,
+                           threadIdx.x & 15);
+}
+
 // ---------------------------------------------------------------------------
 // Large route counts: the same plan from three launches over G workgroups.
 // Workgroup g owns the contiguous routes [g C, (g + 1) C); its four waves own
@@ -191,10 +216,9 @@ __device__ __forceinline__ void wave_count(const IdT *__restrict__ ids, int64_t 
 }
 
 template <typename IdT>
-__global__ void __launch_bounds__(kMT)
-plan_hist_kernel(const IdT *__restrict__ ids, int64_t R, int E, int64_t chunk,
-                 int32_t *__restrict__ ws) {
-    extern __shared__ int hist[];            // [4][E]
+__device__ __forceinline__ void hist_body(const IdT *__restrict__ ids, int64_t R, int E,
+                                          int64_t chunk, int32_t *__restrict__ ws, int *hist) {
+    // hist: [4][E] in LDS
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nbits = 32 - __clz(E);
     for (int i = tid; i < 4 * E; i += kMT) hist[i] = 0;
@@ -206,6 +230,29 @@ plan_hist_kernel(const IdT *__restrict__ ids, int64_t R, int E, int64_t chunk,
     __syncthreads();
     for (int e = tid; e < E; e += kMT)
         ws[(int64_t)blockIdx.x * E + e] = hist[e] + hist[E + e] + hist[2 * E + e] + hist[3 * E + e];
+}
+
+template <typename IdT>
+__global__ void __launch_bounds__(kMT)
+plan_hist_kernel(const IdT *__restrict__ ids, int64_t R, int E, int64_t chunk,
+                 int32_t *__restrict__ ws) {
+    extern __shared__ int hist[];            // [4][E]
+    hist_body(ids, R, E, chunk, ws, hist);
+}
+
+// The histogram pass and the activation quantisation in one launch:
+// workgroups below G count routes, the others quantise 16 groups each.
+template <typename IdT, bool UE8M0>
+__global__ void __launch_bounds__(kMT)
+plan_hist_quant_kernel(const IdT *__restrict__ ids, int64_t R, int E, int64_t chunk,
+                       int32_t *__restrict__ ws, int G, QuantJob q) {
+    extern __shared__ int hist[];            // [4][E]
+    if ((int)blockIdx.x < G) {
+        hist_body(ids, R, E, chunk, ws, hist);
+        return;
+    }
+    quant_act_group<UE8M0>(q.x, q.M, q.K, q.ld, q.xq, q.xs,
+                           ((int64_t)(blockIdx.x - G) * kMT + threadIdx.x) >> 4, threadIdx.x & 15);
 }
 
 __global__ void __launch_bounds__(1024)
@@ -318,7 +365,49 @@ hipError_t launch_plan_multi(const IdT *ids, int64_t R, int E, int bm, int G, in
     return hipGetLastError();
 }
 
+template <typename IdT, bool UE8M0>
+hipError_t launch_plan_quant_t(const IdT *ids, int64_t R, int E, int bm, int32_t *sorted,
+                               int32_t *expert_ids, int32_t *ntp, int32_t *ws, int G,
+                               const QuantJob &q, hipStream_t st) {
+    const int64_t qgroups = q.M * (q.K >> 7);
+    if (ws != nullptr && G > 0) {
+        int64_t chunk = (R + G - 1) / G;
+        chunk = (chunk + 255) & ~int64_t(255);   // four waves x multiples of 64
+        const size_t lds = (size_t)4 * E * sizeof(int);
+        const int64_t qwg = (qgroups + kMT / 16 - 1) / (kMT / 16);
+        plan_hist_quant_kernel<IdT, UE8M0><<<(unsigned)(G + qwg), kMT, lds, st>>>(ids, R, E, chunk, ws, G, q);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        plan_scan_kernel<<<1, 1024, (size_t)(G * E + E + 16) * sizeof(int), st>>>(ws, G, E, bm, R, sorted,
+                                                                                 expert_ids, ntp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        plan_scatter_kernel<IdT><<<G, kMT, lds, st>>>(ids, R, E, chunk, ws, sorted);
+        return hipGetLastError();
+    }
+    const int nwaves = E <= 512 ? 16 : 8;
+    const size_t lds = ((size_t)nwaves * E + E + 32) * sizeof(int);
+    const int64_t qwg = (qgroups + kPlanThreads / 16 - 1) / (kPlanThreads / 16);
+    plan_quant_kernel<IdT, UE8M0><<<(unsigned)(1 + qwg), kPlanThreads, lds, st>>>(ids, R, E, bm, nwaves, sorted,
+                                                                                expert_ids, ntp, q);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_plan_quant(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
+                             int32_t *sorted, int32_t *expert_ids, int32_t *ntp, int32_t *ws,
+                             int groups, const QuantJob &q, bool ue8m0, hipStream_t st) {
+    if (ids_i64)
+        return ue8m0 ? launch_plan_quant_t<int64_t, true>((const int64_t *)ids, R, E, block_m, sorted,
+                                                          expert_ids, ntp, ws, groups, q, st)
+                     : launch_plan_quant_t<int64_t, false>((const int64_t *)ids, R, E, block_m, sorted,
+                                                           expert_ids, ntp, ws, groups, q, st);
+    return ue8m0 ? launch_plan_quant_t<int32_t, true>((const int32_t *)ids, R, E, block_m, sorted, expert_ids,
+                                                      ntp, ws, groups, q, st)
+                 : launch_plan_quant_t<int32_t, false>((const int32_t *)ids, R, E, block_m, sorted,
+                                                       expert_ids, ntp, ws, groups, q, st);
+}
 
 int plan_groups(int64_t R, int E) {
     if (R < kPlanMultiMin || E < 1) return 0;

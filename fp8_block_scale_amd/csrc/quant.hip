@@ -20,37 +20,8 @@ template <bool UE8M0>
 __global__ void __launch_bounds__(256)
 quant_act_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K, int64_t ld,
                  uint8_t *__restrict__ xq, float *__restrict__ xs) {
-    const int64_t G = K >> 7;
-    const int64_t gid = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
-    const int lig = threadIdx.x & 15;
-    if (gid >= M * G) return;             // whole 16-lane groups leave together
-    const int64_t m = gid / G;
-    const int64_t g = gid - m * G;
-
-    const u32x4 raw = *reinterpret_cast<const u32x4 *>(x + m * ld + g * 128 + lig * 8);
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
-        f[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = wave_max_xor(amax, 8);
-    amax = wave_max_xor(amax, 4);
-    amax = wave_max_xor(amax, 2);
-    amax = wave_max_xor(amax, 1);
-
-    float s, inv;
-    group_scale(amax, UE8M0, s, inv);
-    uint32_t lo = pack_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-    uint32_t hi = pack_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-    uint2 o;
-    o.x = lo;
-    o.y = hi;
-    *reinterpret_cast<uint2 *>(xq + m * K + g * 128 + lig * 8) = o;
-    if (lig == 0) xs[m * G + g] = s;
+    quant_act_group<UE8M0>(x, M, K, ld, xq, xs, ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4,
+                           threadIdx.x & 15);
 }
 
 __global__ void __launch_bounds__(256)

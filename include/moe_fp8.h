@@ -154,6 +154,19 @@ moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t 
 moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x,
                          uint8_t *x_q, float *x_s, int32_t scale_mode, void *stream);
 
+/* moe_plan and moe_quant_act in one call, with one kernel launch fewer (the
+ * quantisation runs inside the plan's first launch).  Arguments, outputs and
+ * errors are those of the two calls (validated in full before anything is
+ * enqueued); the results are bit-identical to calling them in turn. */
+moe_status moe_plan_quant(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t top_k,
+                          int32_t E, int32_t block_m,
+                          int32_t *sorted_token_ids, int64_t sorted_cap,
+                          int32_t *expert_ids, int64_t blocks_cap,
+                          int32_t *num_tokens_post_padded,
+                          void *workspace, size_t workspace_bytes,
+                          const void *x_bf16, int64_t K, int64_t ld_x,
+                          uint8_t *x_q, float *x_s, int32_t scale_mode, void *stream);
+
 /* --------------------------------------------------------------- experts -- */
 
 /* Device workspace moe_fp8_experts needs, in bytes (flags as passed to the

@@ -203,6 +203,46 @@ def test_quant_bit_exact(mode, M, K, ld):
     assert np.array_equal(xq.cpu().numpy(), rq)
 
 
+@pytest.mark.parametrize("multi", [False, True])
+@pytest.mark.parametrize("name,M,dt,mode,pad", [
+    ("tiny", None, torch.int32, SCALE_FP32, 0), ("decode", None, torch.int64, SCALE_FP32, 0),
+    ("decode", 16, torch.int32, SCALE_UE8M0, 64), ("page1", 4096, torch.int32, SCALE_FP32, 0),
+    ("zipf", 1024, torch.int64, SCALE_UE8M0, 8), ("skew", 333, torch.int32, SCALE_FP32, 0)])
+def test_plan_quant_matches_separate_calls(name, M, dt, mode, pad, multi):
+    """moe_plan_quant (one launch fewer) writes exactly what moe_plan then
+    moe_quant_act write: the whole plan buffers and the codes and scales."""
+    c = CONFIGS[name]
+    M = M or c["M"]
+    E, k, bm, K = c["E"], c["top_k"], c["block_m"], c["K"]
+    from moe_workloads import make_routing
+    ids, _ = make_routing(c["routing"], M, E, k, c["seed"], DEV)
+    ids = ids.to(dt).contiguous()
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M + K)
+    x = torch.randn((M, K + pad), generator=g, device=DEV).to(torch.bfloat16)[:, :K]
+    log(f"[plan_quant] {name} M={M} {dt} mode={mode} ld={K + pad} multi={multi}")
+    sc, bc = moe.moe_plan_capacity(M, k, E, bm)
+    outs = []
+    for fused in (False, True):
+        s = torch.full((sc,), 0x7F7F7F7F, dtype=torch.int32, device=DEV)
+        e = torch.full((bc,), 0x7F7F7F7F, dtype=torch.int32, device=DEV)
+        p = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        q = torch.full((M, K), 0x5A, dtype=torch.uint8, device=DEV)
+        qs = torch.full((M, K // 128), -1.0, dtype=torch.float32, device=DEV)
+        ws = _plan_ws(M, k, E, bm, multi)
+        if fused:
+            moe.moe_plan_quant(ids, E, bm, s, e, p, x, q, qs, mode, ws)
+        else:
+            moe.moe_plan(ids, E, bm, s, e, p, ws)
+            moe.moe_quant_act(x, q, qs, mode)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (s, e, p, q, qs)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    rq, rs = quant_act_ref(x.float().cpu().numpy(), mode)      # and both are the oracle's
+    assert np.array_equal(outs[1][3].numpy(), rq) and np.array_equal(outs[1][4].numpy(), rs)
+
+
 # --------------------------------------------------------- whole path
 
 def test_tiny_full():

@@ -169,3 +169,24 @@ def test_experts_schedule():
         assert moe.STATUS_NAMES[ei.value.status] == status
     with pytest.raises(moe.MoeError):       # the persistent kernels need K <= 32768
         sched(16, 65536, 1024, 288, 8, 64, 8192, 2 << DN)
+
+
+def test_plan_quant_validation():
+    """moe_plan_quant validates both halves before launching anything."""
+    f = _raw("moe_plan_quant")
+    base = dict(ids=FAKE, dt=0, M=4, k=2, E=8, bm=16, s=FAKE, sc=128, e=FAKE, bc=8, p=FAKE,
+                x=FAKE, K=256, ld=256, q=FAKE, qs=FAKE, mode=0)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["ids"], a["dt"], a["M"], a["k"], a["E"], a["bm"], a["s"], a["sc"], a["e"], a["bc"],
+                 a["p"], None, 0, a["x"], a["K"], a["ld"], a["q"], a["qs"], a["mode"], None)
+
+    assert _err(call(sc=127)) == "MOE_ERR_CAPACITY"
+    assert _err(call(dt=2)) == "MOE_ERR_SHAPE"
+    assert _err(call(K=200, ld=200)) == "MOE_ERR_SHAPE"
+    assert _err(call(ld=128)) == "MOE_ERR_SHAPE"
+    assert _err(call(mode=5)) == "MOE_ERR_SHAPE"
+    assert _err(call(x=None)) == "MOE_ERR_NULL"
+    assert _err(call(ld=260)) == "MOE_ERR_ALIGN"
+    assert _err(call(p=None)) == "MOE_ERR_NULL"
