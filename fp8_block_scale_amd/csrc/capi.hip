@@ -417,10 +417,14 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
         return fail(MOE_ERR_ALIGN, "x_q and w13 must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
-    st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
-                                    (uint32_t *)(ws + l.cnt), l.cnt_words, s),
-                   "moe_fp8_gate_up: clear route map and counters");
-    if (st != MOE_OK) return st;
+    // the route map and the split-K counters are cleared by the row-tile
+    // launch when a persistent kernel runs, else by a launch of their own
+    if (!l.sp.gu_persistent && !l.sp.dn_persistent) {
+        st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
+                                        (uint32_t *)(ws + l.cnt), l.cnt_words, s),
+                       "moe_fp8_gate_up: clear route map and counters");
+        if (st != MOE_OK) return st;
+    }
     moe::GateUpArgs ga;
     ga.xq = x_q;
     ga.xs = x_s;
@@ -433,6 +437,7 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     ga.hs = (float *)(ws + l.hs);
     ga.part = (float *)(ws + l.part);
     ga.cnt = (uint32_t *)(ws + l.cnt);
+    ga.n_cnt = (int64_t)l.cnt_words;
     ga.rpos = (int32_t *)(ws + l.rpos);
     ga.tiles = (int4 *)(ws + l.tiles);
     ga.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);

@@ -60,9 +60,10 @@ __device__ __forceinline__ v8i join8p(const u32x4 &lo, const u32x4 &hi) {
 // each listed as {first block, blocks, expert, 0}.
 // One workgroup: pass 1 marks run starts and counts their tiles, an
 // exclusive scan gives each run its first tile slot, pass 2 writes them.
-__global__ void __launch_bounds__(1024)
-tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, int bm, int mb,
-             int nblocks, int4 *__restrict__ tiles, int32_t *__restrict__ meta) {
+__device__ __forceinline__ void tiles_body(const int32_t *__restrict__ eids,
+                                           const int32_t *__restrict__ ntp, int bm, int mb,
+                                           int nblocks, int4 *__restrict__ tiles,
+                                           int32_t *__restrict__ meta) {
     __shared__ int wsum[16];
     __shared__ int carry;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -102,6 +103,30 @@ tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, 
     }
     if (tid == 0) meta[0] = carry;     // number of row tiles
     if (tid >= 1 && tid <= 8) meta[tid] = 0;    // per-XCD work counters of the gate/up queues
+}
+
+// The row tiles (workgroup 0) and the stage's set-up in the same launch
+// (workgroups 1..): the route map rpos[0, n_rpos) = -1 and the split-K
+// counters cnt[0, n_cnt) = 0.
+__global__ void __launch_bounds__(1024)
+tiles_kernel(const int32_t *__restrict__ eids, const int32_t *__restrict__ ntp, int bm, int mb,
+             int nblocks, int4 *__restrict__ tiles, int32_t *__restrict__ meta,
+             uint32_t *__restrict__ rpos, int64_t n_rpos, uint32_t *__restrict__ cnt, int64_t n_cnt) {
+    if (blockIdx.x == 0) {
+        tiles_body(eids, ntp, bm, mb, nblocks, tiles, meta);
+        return;
+    }
+    const int64_t stride = (int64_t)(gridDim.x - 1) * 1024;
+    for (int64_t i = (int64_t)(blockIdx.x - 1) * 1024 + threadIdx.x; i < n_rpos + n_cnt; i += stride) {
+        if (i < n_rpos) rpos[i] = 0xffffffffu;
+        else cnt[i - n_rpos] = 0u;
+    }
+}
+
+// workgroups of the set-up part of tiles_kernel
+unsigned prep_groups(int64_t n) {
+    int64_t g = (n + 1023) / 1024;
+    return (unsigned)(g > 256 ? 256 : g);
 }
 
 template <int BM, int MODE>
@@ -427,7 +452,9 @@ int num_cus() {
 template <int BM, int MODE>
 hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
-    tiles_kernel<<<1, 1024, 0, st>>>(a.eids, a.ntp, BM, kRows / BM, a.nblocks, a.tiles, a.tmeta);
+    tiles_kernel<<<1 + prep_groups(a.R + a.n_cnt), 1024, 0, st>>>(a.eids, a.ntp, BM, kRows / BM, a.nblocks,
+                                                                   a.tiles, a.tmeta, (uint32_t *)a.rpos,
+                                                                   a.R, a.cnt, a.n_cnt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     int64_t grid = num_cus();
@@ -463,8 +490,9 @@ hipError_t launch_pipe_mode(const GateUpArgs &a, int mode, hipStream_t st) {
 hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
     if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return hipErrorInvalidValue;
-    tiles_kernel<<<1, 1024, 0, st>>>(a.eids, a.ntp, block_m, kRows / block_m, a.nblocks, a.tiles,
-                                     a.tmeta);
+    tiles_kernel<<<1 + prep_groups(a.R + a.n_cnt), 1024, 0, st>>>(a.eids, a.ntp, block_m, kRows / block_m,
+                                                                   a.nblocks, a.tiles, a.tmeta,
+                                                                   (uint32_t *)a.rpos, a.R, a.cnt, a.n_cnt);
     return hipGetLastError();
 }
 

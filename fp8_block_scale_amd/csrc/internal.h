@@ -51,6 +51,7 @@ struct GateUpArgs {
     float *hs;
     float *part;        // split-K partial sums (nsplit > 1)
     uint32_t *cnt;      // split-K arrival counters, one per (block, j-tile)
+    int64_t n_cnt;      // counter words the row-tile launch zeroes (with rpos = -1)
     int32_t *rpos;      // [R] plan row of each route (pre-filled with -1)
     int4 *tiles;        // [nblocks] row tiles {first block, blocks, expert, 0} of the persistent kernels
     int32_t *tmeta;     // [17] row-tile count, then the gate/up per-XCD work counters (1..8)
@@ -94,7 +95,9 @@ int gateup_stream_kmax(int block_m);
 hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                          hipStream_t st);
 // The row-tile list of the persistent kernels alone (when only the down
-// stage runs persistent); launch_gateup_pipe builds it itself.
+// stage runs persistent); launch_gateup_pipe builds it itself.  Either way
+// the same launch sets rpos[0, R) = -1 and zeroes cnt[0, n_cnt) (the work of
+// launch_prep, which the stage then skips).
 hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st);
 // Large-grid gate/up (no split-K): 128-row tiles, three-stage LDS pipeline.
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
