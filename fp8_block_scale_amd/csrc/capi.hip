@@ -1,5 +1,6 @@
 // C ABI of libmoe_fp8.so: argument validation, workspace layout and the
 // launch sequence of each entry point (declared in include/moe_fp8.h).
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
@@ -57,7 +58,7 @@ struct SplitChoice {
 };
 
 constexpr int64_t kPersistentTiles = 512;   // (block, j-tile) pairs
-constexpr int64_t kStreamTarget = 256;      // workgroups of the stream kernel
+constexpr double kStreamFill = 192.0;       // workgroups the stream kernel's split aims at
 
 SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtiles, int64_t K,
                          int64_t I, int32_t bm, uint32_t flags) {
@@ -84,8 +85,18 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     const int64_t npass = bm > 64 ? bm / 64 : 1;
     int64_t s = forced;
     if (s == 0) {
-        const int64_t units = tiles * npass > 0 ? tiles * npass : 1;
-        s = (kStreamTarget + units - 1) / units;
+        // Workgroups that will have work: plan blocks expected under uniform
+        // routing (the experts hit, E (1 - (1 - 1/E)^R), or R / block_m if
+        // more), not the capacity's one block per route.  The smallest split
+        // that fills 3/4 of the chip in one round: a partial second round
+        // costs nearly a whole one (decode M=4: 37 us at 288 workgroups
+        // against 26 us at 216).
+        const double hit = (double)E * -std::expm1((double)R * std::log1p(-1.0 / (double)E));
+        double blocks = hit > (double)R / bm ? hit : (double)R / bm;
+        if (blocks > (double)blocks_cap) blocks = (double)blocks_cap;
+        double units = blocks * (double)jtiles * (double)npass;
+        if (units < 1.0) units = 1.0;
+        s = (int64_t)std::ceil(kStreamFill / units);
     }
     const int64_t kmax = moe::gateup_stream_kmax(bm);
     if (s < (nkb + kmax - 1) / kmax) s = (nkb + kmax - 1) / kmax;

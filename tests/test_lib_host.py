@@ -148,8 +148,13 @@ def test_experts_schedule():
     and their validation."""
     sched = moe.moe_fp8_experts_schedule
     GU, DN = moe.MOE_F_GATEUP_PATH_SHIFT, moe.MOE_F_DOWN_PATH_SHIFT
-    # decode: small grid, both per-block, K split 14 ways of 4 K-blocks
-    assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, False, 14, 4)
+    # decode: small grid, both per-block; the split fills ~3/4 of the chip in
+    # one round with the plan blocks expected under uniform routing: M=1
+    # (~9 blocks x 2 column tiles) 10 ways of 6 K-blocks, M=4 (~34 blocks)
+    # 3 ways, M=16 (~112 blocks) no split
+    assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, False, 10, 6)
+    assert sched(4, 7168, 256, 257, 9, 16, 576)[2:] == (3, 19)
+    assert sched(16, 7168, 256, 257, 9, 16, 2304)[2] == 1
     # page-1 M=16 and M=1024: per-block gate/up, persistent down
     assert sched(16, 4096, 1024, 288, 8, 64, 8192)[:2] == (False, True)
     assert sched(1024, 4096, 1024, 288, 8, 64, 26368)[:2] == (False, True)
