@@ -333,18 +333,61 @@ gateup_pipe_kernel(GateUpArgs a) {
             const float *Ss = sSa + stage * kRows;
             const uint8_t *Ws = sW + stage * kWBytes;
             const uint8_t *As = sA + stage * kABytes;
-            // W operands of this wave: tile rows 32wn + 16(s&1) (+128 for up)
-            v8i wq[4];
-            v8h wh[4][4];
+            // W operand rows of this wave: tile rows 32wn + 16(s&1) (+128 for up)
+            u32x4 wr[4][2];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int row = (s < 2 ? 0 : 128) + 32 * wn + 16 * (s & 1) + l16;
                 const uint8_t *rp = Ws + row * 128;
-                const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
-                const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
-                if constexpr (MODE == kExact) e4m3x32_to_f16(lo, hi, wh[s]);
-                else wq[s] = join8p(lo, hi);
+                wr[s][0] = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                wr[s][1] = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
             }
+            if constexpr (MODE == kExact) {
+            // Hand-pipelined: the activation rows of subtile u + 1 are read
+            // from LDS while subtile u multiplies; the W13 widening of s = 2, 3
+            // runs behind subtile 0's first chains; and the scale FMAs of one
+            // chain go out behind the MFMAs of the next, so the matrix pipe
+            // does not drain between chains.  Subtile 0 always has rows here
+            // (vrows > 64 wm).
+            u32x4 ar[2];
+            float sa;
+            auto read_a = [&](int u) {
+                const int row = wm * 64 + u * 16 + l16;
+                const uint8_t *rp = As + row * 128;
+                ar[0] = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                ar[1] = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                sa = Ss[row];
+            };
+            read_a(0);
+            v8h wh[4][4];
+            e4m3x32_to_f16(wr[0][0], wr[0][1], wh[0]);
+            e4m3x32_to_f16(wr[1][0], wr[1][1], wh[1]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (u < 3) part(u + 1);
+                if (wm * 64 + u * 16 >= vrows) continue;
+                if (u > 0) read_a(u);
+                v8h bh[4];
+                e4m3x32_to_f16(ar[0], ar[1], bh);
+                const float fg = sa * sbg, fu = sa * sbu;
+                v4f t0 = mfma16x16x128_f16(wh[0], bh);
+                v4f t1 = mfma16x16x128_f16(wh[1], bh);
+                __builtin_amdgcn_sched_barrier(0);
+                if (u == 0) e4m3x32_to_f16(wr[2][0], wr[2][1], wh[2]);
+                acc[0][u] = t0 * fg + acc[0][u];
+                t0 = mfma16x16x128_f16(wh[2], bh);
+                __builtin_amdgcn_sched_barrier(0);
+                if (u == 0) e4m3x32_to_f16(wr[3][0], wr[3][1], wh[3]);
+                acc[1][u] = t1 * fg + acc[1][u];
+                t1 = mfma16x16x128_f16(wh[3], bh);
+                __builtin_amdgcn_sched_barrier(0);
+                acc[2][u] = t0 * fu + acc[2][u];
+                acc[3][u] = t1 * fu + acc[3][u];
+            }
+            } else {
+            v8i wq[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wq[s] = join8p(wr[s][0], wr[s][1]);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 if (u < 3) part(u + 1);
@@ -354,16 +397,7 @@ gateup_pipe_kernel(GateUpArgs a) {
                 const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
                 const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
                 const float sa = Ss[row];
-                if constexpr (MODE == kExact) {
-                    v8h bh[4];
-                    e4m3x32_to_f16(lo, hi, bh);
-                    const float fg = sa * sbg, fu = sa * sbu;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        v4f t = mfma16x16x128_f16(wh[s], bh);
-                        acc[s][u] = t * (s < 2 ? fg : fu) + acc[s][u];
-                    }
-                } else if constexpr (MODE == kFp8E8) {
+                if constexpr (MODE == kFp8E8) {
                     const v8i B = join8p(lo, hi);
                     const int eb = e8m0_of(sa), eg = e8m0_of(sbg), eu = e8m0_of(sbu);
 #pragma unroll
@@ -378,6 +412,7 @@ gateup_pipe_kernel(GateUpArgs a) {
                         acc[s][u] = t * (s < 2 ? fg : fu) + acc[s][u];
                     }
                 }
+            }
             }
         }
     }
