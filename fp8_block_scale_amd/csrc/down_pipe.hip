@@ -26,11 +26,7 @@
 // W2 block scales, 16 route ids), all brought by direct global->LDS loads two
 // steps ahead -- across item boundaries too, so an item's first steps are
 // already in flight while the previous item finishes.  Rows are XOR-swizzled
-// in LDS as in the gate/up pipeline.  A 4-byte load per lane three steps
-// ahead touches the W2 rows a step will need, so the ring's own loads find
-// them in L2 or already on their way (further ahead, the touched lines of 32
-// CUs outgrow the XCD's 4 MB L2 and are fetched twice).  FP8
-// MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per
+// in LDS as in the gate/up pipeline.  FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per
 // step, or with power-of-two scales as E8M0 exponents inside the MFMA.
 #include <type_traits>
 
@@ -51,7 +47,6 @@ constexpr int kHInstr = kHBytes / 1024 / 8;
 constexpr int kPerStage = kWInstr + kHInstr + 1;
 constexpr int kMeta = 64;                     // floats per wave and stage
 constexpr int kMetaRt = 18;                   // route ids start here
-constexpr int kPfAhead = 3;                   // steps between the L2 prefetch and the multiply
 
 __device__ __forceinline__ v8i join8q(const u32x4 &lo, const u32x4 &hi) {
     v8i r;
@@ -79,7 +74,6 @@ down_pipe_kernel(DownArgs a) {
     uint8_t *sW = smem;                                                 // [kStages][256][128]
     uint8_t *sH = smem + kStages * kWBytes;                             // [kStages][128][128]
     float *sMeta = reinterpret_cast<float *>(sH + kStages * kHBytes);   // [kStages][8][kMeta]
-    uint8_t *sPf = reinterpret_cast<uint8_t *>(sMeta + kStages * 8 * kMeta);   // [8][256] sink
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -173,33 +167,6 @@ down_pipe_kernel(DownArgs a) {
         }
     };
 
-    // ---- prefetch side: lane l of wave w touches W2 tile row 32w + (l & 31)
-    // at byte 64 (l >> 5) of the step kPfAhead ahead of the multiply
-    int64_t kp = 0;
-    int jp = 0;
-    const uint8_t *wpf;
-    auto set_pf = [&](const Item &it) {
-        const int64_t c0 = (int64_t)it.ct * 256;
-        const int ncols = K - c0 < 256 ? (int)(K - c0) : 256;
-        const int row = w * 32 + (lane & 31);
-        const int64_t c = c0 + (row < ncols ? row : 0);
-        wpf = a.w2 + ((int64_t)it.e * K + c) * I + 64 * (lane >> 5);
-    };
-    auto pf_advance = [&]() {
-        if (jp + 1 < njb) {
-            ++jp;
-        } else if (kp + 1 < mine) {
-            jp = 0;
-            set_pf(item_at(++kp));
-        }                                            // past the last step: stay on it
-    };
-    set_pf(il);
-    for (int i = 0; i < kPfAhead - 2; ++i) pf_advance();   // the first group's prefetch step
-    auto prefetch = [&]() {
-        lds_dma4(wpf + (int64_t)jp * 128, sPf + w * 256);
-        pf_advance();
-    };
-
     // ---- multiply side
     int64_t kc = 0;
     int jc = 0;
@@ -212,21 +179,21 @@ down_pipe_kernel(DownArgs a) {
         for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // One step: wait for its stage, barrier, refill the stage the previous
-    // step used (every wave is past that multiply), prefetch, multiply; on an
-    // item's last step store its rows.  Groups = [refill][prefetch]; loads
-    // complete in issue order, so after the refill of step t only the
-    // prefetch of its group and the next group may still be in flight.  The
-    // stage indices are compile-time constants so the compiler can tell the
-    // refilled and the read LDS ranges apart.
+    // step used (every wave is past that multiply), multiply; on an item's
+    // last step store its rows.  Loads complete in issue order, so after the
+    // refill of step t only the refill of step t + 1 may still be in flight.
+    // (An L2 prefetch of the W2 lines a step ahead of the refill, with 4-byte
+    // LDS-DMA touches, made the kernel slower: each touch costs the address
+    // unit a whole cache line.)  The stage indices are compile-time constants
+    // so the compiler can tell the refilled and the read LDS ranges apart.
     auto step = [&](auto st_c, int64_t t) {
         constexpr int ST = decltype(st_c)::value;
         if (t + 1 < T)
-            wait_vmcnt<kPerStage + 2>();
+            wait_vmcnt<kPerStage>();
         else
-            wait_vmcnt<2>();
+            wait_vmcnt<0>();
         stage_barrier();
         if (t + 2 < T) issue((ST + 2) % kStages);
-        prefetch();
 
         const int nrows = ic.nb * BM;
         const int64_t c0 = (int64_t)ic.ct * 256;
@@ -322,9 +289,7 @@ down_pipe_kernel(DownArgs a) {
     };
 
     issue(0);
-    prefetch();
     if (T > 1) issue(1);
-    prefetch();
     for (int64_t t = 0; t < T; t += kStages) {
         step(std::integral_constant<int, 0>{}, t);
         if (t + 1 < T) step(std::integral_constant<int, 1>{}, t + 1);
@@ -333,7 +298,7 @@ down_pipe_kernel(DownArgs a) {
     wait_vmcnt<0>();                                 // no load may land after the workgroup ends
 }
 
-constexpr size_t kSmem = (size_t)kStages * (kWBytes + kHBytes) + kStages * 8 * kMeta * 4 + 8 * 256;
+constexpr size_t kSmem = (size_t)kStages * (kWBytes + kHBytes) + kStages * 8 * kMeta * 4;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 int num_cus_dn() {

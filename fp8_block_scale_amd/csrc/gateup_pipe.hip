@@ -44,7 +44,6 @@ constexpr int kAInstr = kABytes / 1024 / 8;   // (A)
 constexpr int kSInstr = 1;                    // (activation scales: 16 rows per wave)
 constexpr int kPerStage = kWInstr + kAInstr + kSInstr;
 constexpr int kMaxKb = 256;                   // K <= 32768
-constexpr int kPfAhead = 3;                   // K-blocks between the L2 prefetch and the multiply
 
 enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
 
@@ -140,7 +139,6 @@ gateup_pipe_kernel(GateUpArgs a) {
     int *sTok = reinterpret_cast<int *>(sSw + 2 * kMaxKb);      // [128] token or -1
     float *sRed = reinterpret_cast<float *>(sTok + kRows);      // [4][128]
     int *sItem = reinterpret_cast<int *>(sRed + 4 * kRows);      // [4]
-    uint8_t *sPf = reinterpret_cast<uint8_t *>(sItem + 4);        // [8][256] prefetch sink
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -248,23 +246,6 @@ gateup_pipe_kernel(GateUpArgs a) {
         for (int part = 0; part < 4; ++part) issue_part(part, stage, kb);
     };
 
-    // L2 prefetch of W13 rows: lane l of wave w touches tile row 32w + (l & 31)
-    // at byte 64 (l >> 5) of a K-block -- both 64-byte halves of each of the
-    // wave's 32 rows -- with a 4-byte LDS-DMA load into a per-wave sink, so
-    // there is no register result; the ring's own loads of that K-block then
-    // find it in L2 or already on its way.  kPfAhead = 3: further ahead, the
-    // touched lines of 32 CUs outgrow the XCD's 4 MB L2 and are fetched twice.
-    const uint8_t *wpf;
-    {
-        const int row = w * 32 + (lane & 31);
-        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
-        wpf = a.w13 + ((int64_t)e * twoI + n) * K + 64 * (lane >> 5);
-    }
-    auto prefetch = [&](int kb) {
-        const int kc = kb < nkb ? kb : nkb - 1;
-        __builtin_amdgcn_global_load_lds(wpf + (int64_t)kc * 128, sPf + w * 256, 4, 0, 0);
-    };
-
     constexpr int NU = 4;
     // Rows of this wave up to its last valid one: 16-row subtiles past it hold
     // only plan padding (the tail of an expert's last block) and are not
@@ -283,29 +264,27 @@ gateup_pipe_kernel(GateUpArgs a) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) acc[s][u] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Issue groups: the prologue's two, then one per K-block step, each =
-    // [ring refill of K-block j + 2 (while one is left)] [prefetch of j + kPfAhead].
-    // Loads complete in issue order, so at step kb everything after the
-    // refill of kb is the prefetch of its group and the next group.  The
-    // refill of a prefetched K-block goes out kPfAhead - 2 steps after its
-    // prefetch and finds the lines in L2 or already on their way.
+    // The prologue fills stages 0 and 1; step kb refills the stage of kb + 2
+    // (while one is left).  Loads complete in issue order, so at step kb only
+    // the refill of kb + 1 may still be in flight.  (An L2 prefetch of the
+    // W13 lines one step ahead of the refill, with 4-byte LDS-DMA touches,
+    // made the kernel slower: each touch costs the address unit a whole
+    // cache line.)
     issue(0, 0);
-    prefetch(kPfAhead - 2);
     if (nkb > 1) issue(1, 1);
-    prefetch(kPfAhead - 1);
 
     for (int kb = 0; kb < nkb; ++kb) {
         const int stage = kb % kStages;
         if (kb + 1 < nkb)
-            wait_vmcnt<kPerStage + 2>();
+            wait_vmcnt<kPerStage>();
         else
-            wait_vmcnt<2>();
+            wait_vmcnt<0>();
         // Every wave has waited for its own part of this stage; the barrier
         // makes the whole stage visible, and every wave is past the multiply
         // of kb - 1, whose stage the refill below overwrites.  A plain
         // s_barrier: __syncthreads() would also drain the loads in flight.
         stage_barrier();
-        // The refill of kb + 2 and the prefetch go out in parts between the
+        // The refill of kb + 2 goes out in parts between the
         // token subtiles of the multiply, in their usual order: all waves
         // issuing a whole group at once would queue behind the address unit
         // (64 bytes per clock) instead of multiplying.
@@ -313,12 +292,7 @@ gateup_pipe_kernel(GateUpArgs a) {
         const int rst = (kb + 2) % kStages;
         auto part = [&](int pi) {
             __builtin_amdgcn_sched_barrier(0);       // keep each part where it is placed
-            if (pi < 3) {
-                if (refill) issue_part(pi, rst, kb + 2);
-            } else {
-                if (refill) issue_part(3, rst, kb + 2);
-                prefetch(kb + kPfAhead);
-            }
+            if (refill) issue_part(pi, rst, kb + 2);
             __builtin_amdgcn_sched_barrier(0);
         };
         part(0);
@@ -416,7 +390,6 @@ gateup_pipe_kernel(GateUpArgs a) {
             }
         }
     }
-    wait_vmcnt<0>();                                 // the last prefetches land in the sink
     __syncthreads();
     // the next item's claim travels while this one's epilogue computes
     const int ticket = tid == 0 ? claim_begin(a.tmeta + 1, home, q) : 0;
@@ -468,7 +441,7 @@ gateup_pipe_kernel(GateUpArgs a) {
 }
 
 constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + kStages * kRows * 4 +
-                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16 + 8 * 256;
+                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 int num_cus() {
