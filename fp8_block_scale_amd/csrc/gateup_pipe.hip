@@ -41,8 +41,8 @@ constexpr int kWBytes = 256 * 128;            // W13 tile per stage
 constexpr int kABytes = kRows * 128;          // activation tile per stage
 constexpr int kWInstr = kWBytes / 1024 / 8;   // DMA instructions per wave per stage (W)
 constexpr int kAInstr = kABytes / 1024 / 8;   // (A)
-constexpr int kSInstr = 1;                    // (activation scales: 16 rows per wave)
-constexpr int kPerStage = kWInstr + kAInstr + kSInstr;
+constexpr int kPerStage = kWInstr + kAInstr;  // + 1 on K-blocks that start a scale group
+constexpr int kSGroup = 4;                    // K-blocks of activation scales per scale load
 constexpr int kMaxKb = 256;                   // K <= 32768
 
 enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
@@ -134,8 +134,8 @@ gateup_pipe_kernel(GateUpArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *sW = smem;                                        // [kStages][256][128]
     uint8_t *sA = smem + kStages * kWBytes;                    // [kStages][128][128]
-    float *sSa = reinterpret_cast<float *>(sA + kStages * kABytes);  // [kStages][128] x_s
-    float *sSw = sSa + kStages * kRows;                        // [2][kMaxKb] w13_s gate, up
+    float *sSa = reinterpret_cast<float *>(sA + kStages * kABytes);  // [2][128][kSGroup] x_s
+    float *sSw = sSa + 2 * kRows * kSGroup;                    // [2][kMaxKb] w13_s gate, up
     int *sTok = reinterpret_cast<int *>(sSw + 2 * kMaxKb);      // [128] token or -1
     float *sRed = reinterpret_cast<float *>(sTok + kRows);      // [4][128]
     int *sItem = reinterpret_cast<int *>(sRed + 4 * kRows);      // [4]
@@ -216,16 +216,21 @@ gateup_pipe_kernel(GateUpArgs a) {
         const int chunk = slot ^ (row & 7);
         asrc[i] = a.xq + (int64_t)t * K + chunk * 16;
     }
-    // activation scales: wave w fetches rows 16w .. 16w + 15 (lanes 0..15)
+    // Activation scales come kSGroup K-blocks at a time, with the refill of
+    // the group's first K-block, into one of two group slots: lane l of wave
+    // w fetches row 16w + l / 4, K-block l % 4 of the group (clamped to the
+    // last K-block).  One 4-byte load per row and group instead of one per
+    // row and K-block: each of those costs the address unit a cache line.
     const float *ssrc;
     {
-        const int row = w * 16 + (lane & 15);
+        const int row = w * 16 + (lane >> 2);
         const int t = sTok[row] >= 0 ? sTok[row] : fallback;
         ssrc = a.xs + (int64_t)t * nkb;
     }
-    // Every wave issues exactly kPerStage vector-memory instructions per stage
-    // (the waits in the main loop count on it), in four parts: W13 rows 0-1,
-    // W13 rows 2-3, activation rows, scales.
+    // Every wave issues kPerStage vector-memory instructions per stage, plus
+    // one on stages whose K-block starts a scale group (the waits in the main
+    // loop count on it), in four parts: W13 rows 0-1, W13 rows 2-3,
+    // activation rows, scales.
     static_assert(kWInstr == 4 && kAInstr == 2, "issue parts");
     auto issue_part = [&](int part, int stage, int kb) {
         if (part < 2) {
@@ -238,8 +243,11 @@ gateup_pipe_kernel(GateUpArgs a) {
 #pragma unroll
             for (int i = 0; i < kAInstr; ++i)
                 __builtin_amdgcn_global_load_lds(asrc[i] + (int64_t)kb * 128, da + i * 1024, 16, 0, 0);
-        } else if (lane < 16) {
-            __builtin_amdgcn_global_load_lds(ssrc + kb, sSa + stage * kRows + w * 16, 4, 0, 0);
+        } else if (kb % kSGroup == 0) {
+            const int kq = kb + (lane & (kSGroup - 1));
+            __builtin_amdgcn_global_load_lds(ssrc + (kq < nkb ? kq : nkb - 1),
+                                             sSa + ((kb / kSGroup) & 1) * (kRows * kSGroup) + w * 64,
+                                             4, 0, 0);
         }
     };
     auto issue = [&](int stage, int kb) {
@@ -275,10 +283,12 @@ gateup_pipe_kernel(GateUpArgs a) {
 
     for (int kb = 0; kb < nkb; ++kb) {
         const int stage = kb % kStages;
-        if (kb + 1 < nkb)
-            wait_vmcnt<kPerStage>();
-        else
+        if (kb + 1 >= nkb)
             wait_vmcnt<0>();
+        else if ((kb + 1) % kSGroup == 0)
+            wait_vmcnt<kPerStage + 1>();
+        else
+            wait_vmcnt<kPerStage>();
         // Every wave has waited for its own part of this stage; the barrier
         // makes the whole stage visible, and every wave is past the multiply
         // of kb - 1, whose stage the refill below overwrites.  A plain
@@ -304,7 +314,8 @@ gateup_pipe_kernel(GateUpArgs a) {
         } else {
             const float sbg = sSw[kb];
             const float sbu = sSw[kMaxKb + kb];
-            const float *Ss = sSa + stage * kRows;
+            // this K-block's activation scales: [row][kb % kSGroup] of its group slot
+            const float *Ss = sSa + ((kb / kSGroup) & 1) * (kRows * kSGroup) + kb % kSGroup;
             const uint8_t *Ws = sW + stage * kWBytes;
             const uint8_t *As = sA + stage * kABytes;
             // W operand rows of this wave: tile rows 32wn + 16(s&1) (+128 for up)
@@ -330,7 +341,7 @@ gateup_pipe_kernel(GateUpArgs a) {
                 const uint8_t *rp = As + row * 128;
                 ar[0] = lds_read16(rp + ((g ^ (row & 7)) * 16));
                 ar[1] = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
-                sa = Ss[row];
+                sa = Ss[row * kSGroup];
             };
             read_a(0);
             v8h wh[4][4];
@@ -370,7 +381,7 @@ gateup_pipe_kernel(GateUpArgs a) {
                 const uint8_t *rp = As + row * 128;
                 const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
                 const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
-                const float sa = Ss[row];
+                const float sa = Ss[row * kSGroup];
                 if constexpr (MODE == kFp8E8) {
                     const v8i B = join8p(lo, hi);
                     const int eb = e8m0_of(sa), eg = e8m0_of(sbg), eu = e8m0_of(sbu);
@@ -440,7 +451,7 @@ gateup_pipe_kernel(GateUpArgs a) {
     }
 }
 
-constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + kStages * kRows * 4 +
+constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + 2 * kRows * kSGroup * 4 +
                          2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
