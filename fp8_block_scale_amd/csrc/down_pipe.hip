@@ -26,8 +26,10 @@
 // W2 block scales, 16 route ids), all brought by direct global->LDS loads two
 // steps ahead -- across item boundaries too, so an item's first steps are
 // already in flight while the previous item finishes.  Rows are XOR-swizzled
-// in LDS as in the gate/up pipeline.  FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per
-// step, or with power-of-two scales as E8M0 exponents inside the MFMA.
+// in LDS (the intermediate rows as in the gate/up pipeline, the W2 rows by
+// w2_swizzle below).  FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32
+// scale product applied per step, or with power-of-two scales as E8M0
+// exponents inside the MFMA.
 #include <type_traits>
 
 #include "common.h"
@@ -66,6 +68,14 @@ struct Item {
     int b, nb, e, ct;
     bool ok;            // expert id in range (else: loads from expert 0, nothing computed)
 };
+
+// W2 tile rows in LDS: the eight 16-byte chunks of row r sit XOR-swizzled
+// by this value.  MFMA operand s of wave wn takes tile rows 64 wn + 16 (m / 4)
+// + 4 s + m % 4 for its 16 operand rows m, so that output lane group g holds
+// 16 consecutive columns (64 wn + 16 g ..) and a route row leaves in whole
+// 16-byte stores; over each 16-lane read phase this swizzle puts the 8 rows
+// of either parity on 8 distinct chunks (no bank conflicts).
+__device__ __forceinline__ int w2_swizzle(int r) { return (r ^ (r >> 3) ^ (r >> 4)) & 7; }
 
 template <int BM, bool E8M0>
 __global__ void __launch_bounds__(kNT, 1)
@@ -126,7 +136,7 @@ down_pipe_kernel(DownArgs a) {
         for (int i = 0; i < kWInstr; ++i) {
             const int row = (w * kWInstr + i) * 8 + sub;              // 0..255
             const int64_t c = c0 + (row < ncols ? row : 0);
-            wsrc[i] = a.w2 + ((int64_t)it.e * K + c) * I + (slot ^ (row & 7)) * 16;
+            wsrc[i] = a.w2 + ((int64_t)it.e * K + c) * I + (slot ^ w2_swizzle(row)) * 16;
         }
 #pragma unroll
         for (int i = 0; i < kHInstr; ++i) {
@@ -219,10 +229,10 @@ down_pipe_kernel(DownArgs a) {
             v8i wq[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int row = 64 * wn + 16 * s + l16;
+                const int row = 64 * wn + 16 * (l16 >> 2) + 4 * s + (l16 & 3);
                 const uint8_t *rp = Ws + row * 128;
-                const u32x4 lo4 = lds_read16(rp + ((g ^ (row & 7)) * 16));
-                const u32x4 hi4 = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                const u32x4 lo4 = lds_read16(rp + ((g ^ w2_swizzle(row)) * 16));
+                const u32x4 hi4 = lds_read16(rp + (((4 + g) ^ w2_swizzle(row)) * 16));
                 wq[s] = join8q(lo4, hi4);
             }
 #pragma unroll
@@ -271,10 +281,13 @@ down_pipe_kernel(DownArgs a) {
                 if (r < 0 || (int64_t)r >= a.R) continue;
                 float sc, inv;
                 y16_scale(m, sc, inv);
-                uint16_t *dst = a.y16 + (int64_t)r * K + c0 + 64 * wn + 4 * g;
+                // the lane's 16 columns are consecutive: two 16-byte stores
+                uint16_t *dst = a.y16 + (int64_t)r * K + c0 + 64 * wn + 16 * g;
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    *reinterpret_cast<uint2 *>(dst + 16 * s) = f32x4_to_f16x4(acc[s][u], inv);
+                for (int s = 0; s < 4; s += 2) {
+                    const uint2 lo = f32x4_to_f16x4(acc[s][u], inv), hi = f32x4_to_f16x4(acc[s + 1][u], inv);
+                    *reinterpret_cast<uint4 *>(dst + 4 * s) = uint4{lo.x, lo.y, hi.x, hi.y};
+                }
                 if (g == 0) a.ys[(int64_t)r * (K >> 6) + ((c0 >> 6) + wn)] = sc;
             }
         }
