@@ -131,11 +131,11 @@ def test_workspace_size_monotone_and_layout():
 
 def test_plan_workspace_size():
     # one-workgroup build below 4096 routes; above, one int32 per (workgroup of
-    # 2048 routes, expert)
+    # ~1024 routes, at least 16 workgroups, expert)
     assert moe.moe_plan_workspace_size(1, 9, 257, 16) == 0
     assert moe.moe_plan_workspace_size(511, 8, 288, 64) == 0
-    assert moe.moe_plan_workspace_size(512, 8, 288, 64) == 2 * 288 * 4
-    assert moe.moe_plan_workspace_size(4096, 8, 288, 64) == 16 * 288 * 4
+    assert moe.moe_plan_workspace_size(512, 8, 288, 64) == 16 * 288 * 4
+    assert moe.moe_plan_workspace_size(4096, 8, 288, 64) == 32 * 288 * 4
     # the scan keeps G * E + E + 16 ints in 64 KB of LDS
     assert moe.moe_plan_workspace_size(10 ** 6, 8, 64, 64) == 254 * 64 * 4
     assert moe.moe_plan_workspace_size(10 ** 6, 8, 1024, 64) == 14 * 1024 * 4
