@@ -348,6 +348,18 @@ def test_persistent_long_k_wide_i():
                 label="persistent K=7168 I=2048")
 
 
+@pytest.mark.parametrize("K", [128, 640, 768, 896])
+def test_persistent_ragged_scale_groups(K):
+    """The persistent gate/up loads activation scales four K-blocks at a time
+    into two alternating slots: K = 128 / 640 / 768 / 896 gives 1 / 5 / 6 / 7
+    K-blocks, so the last group is short (1-3 K-blocks, its loads clamped to
+    the last K-block) or the only one."""
+    cfg = dict(CONFIGS["page1"], M=192, E=16, K=K, I=512, top_k=4, block_m=32, seed=17)
+    cs = make_case("ragged_k", device=DEV, config=cfg)
+    full_parity(cs, flags=PERSIST, tokens=_sample_tokens(cs.M, 8, 50 + K // 128),
+                label=f"persistent K={K}")
+
+
 @pytest.mark.parametrize("gu,dn", [(1, 1), (1, 2), (2, 1), (2, 2)])
 def test_kernel_path_combinations(gu, dn):
     """Every pairing of the per-block (1) and persistent (2) kernel families
