@@ -143,8 +143,10 @@ def test_plan_bit_exact(name, M, dt, multi):
 @pytest.mark.parametrize("M,top_k,E,bm", [(1, 1, 1, 16), (3, 5, 7, 16), (1000, 3, 1, 128),
                                           (777, 7, 1024, 32), (5000, 13, 64, 64), (64, 1, 3, 256),
                                           (4096, 1, 257, 16), (100000, 2, 3, 128),
-                                          (4099, 8, 1024, 16)])
+                                          (4099, 8, 1024, 16), (4100, 1, 5, 16), (2051, 2, 300, 32)])
 def test_plan_edge_shapes(M, top_k, E, bm, multi):
+    """Ragged and extreme shapes; 4100 and 4102 routes give the multi-group
+    build 16 groups of 512 routes, the last seven of them empty."""
     g = torch.Generator(device=DEV)
     g.manual_seed(M * 31 + E)
     ids = torch.randint(-2, E + 2, (M, top_k), generator=g, device=DEV, dtype=torch.int32)
