@@ -362,6 +362,17 @@ def test_persistent_ragged_scale_groups(K):
                 label=f"persistent K={K}")
 
 
+@pytest.mark.parametrize("flags", [0, PERSIST])
+def test_max_k(flags):
+    """K = 32768, the largest hidden size the persistent kernels accept
+    (256 K-blocks of weight-block scales per column tile), on both kernel
+    families: E=4, I=256, top-2, M=64."""
+    cfg = dict(CONFIGS["tiny"], M=64, E=4, K=32768, I=256, top_k=2, block_m=16, seed=19)
+    cs = make_case("max_k", device=DEV, config=cfg)
+    full_parity(cs, flags=flags, tokens=_sample_tokens(cs.M, 6, 60 + flags % 7),
+                label=f"K=32768 flags={flags:#x}")
+
+
 @pytest.mark.parametrize("gu,dn", [(1, 1), (1, 2), (2, 1), (2, 2)])
 def test_kernel_path_combinations(gu, dn):
     """Every pairing of the per-block (1) and persistent (2) kernel families
