@@ -373,6 +373,26 @@ def test_max_k(flags):
                 label=f"K=32768 flags={flags:#x}")
 
 
+@pytest.mark.parametrize("flags", [0, PERSIST])
+def test_max_i_single_k_block(flags):
+    """I = 32768, the largest intermediate size the persistent kernels accept
+    (256 column tiles per row tile; 256 128-deep steps per down item), with
+    K = 128 (one K-block): E=2, top-1, M=32."""
+    cfg = dict(CONFIGS["tiny"], M=32, E=2, K=128, I=32768, top_k=1, block_m=16, seed=23)
+    cs = make_case("max_i", device=DEV, config=cfg)
+    full_parity(cs, flags=flags, tokens=_sample_tokens(cs.M, 4, 70 + flags % 5),
+                label=f"I=32768 K=128 flags={flags:#x}")
+
+
+@pytest.mark.parametrize("flags", [0, PERSIST])
+def test_max_experts(flags):
+    """E = 1024, the largest expert count the ABI accepts, on both kernel
+    families: top-8, M=128, K=I=256."""
+    cfg = dict(CONFIGS["tiny"], M=128, E=1024, K=256, I=256, top_k=8, block_m=16, seed=29)
+    cs = make_case("max_e", device=DEV, config=cfg)
+    full_parity(cs, flags=flags, label=f"E=1024 flags={flags:#x}")
+
+
 @pytest.mark.parametrize("gu,dn", [(1, 1), (1, 2), (2, 1), (2, 2)])
 def test_kernel_path_combinations(gu, dn):
     """Every pairing of the per-block (1) and persistent (2) kernel families
