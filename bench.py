@@ -20,7 +20,10 @@ E4M3 with 128x128 FP32 block scales).  Prints one JSON line:
                stream inside the timed region; `traffic` is the HBM bytes per
                launch from rocprofv3 counters recorded in profiles/, reported
                only while the kernel sources still hash to the ones measured
-  cpu_baseline the CPU oracle on a bounded sample of the same batch
+  steps35      steps 3-5 (gate/up through the reduce, the basis of the HBM
+               and MFMA targets) against the HBM peak and the dense FP8 peak
+  cpu_baseline the CPU oracle on a bounded sample of the same batch (median
+               of three runs, host CPU model, BLAS and thread count stated)
 
 Runs on a single GPU only; --gpus N > 1 exits with a message.
 """
@@ -71,7 +74,8 @@ def parse():
                          "consecutive layers, so no step finds its weights in the 256 MB "
                          "Infinity Cache (0 = enough copies for >= 1 GiB of touched weights)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=192)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=96)
+    ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before warm-up (a known-size "
                          "kernel to scale HBM byte counters against)")
@@ -138,35 +142,54 @@ def measured_traffic(kernel, workload, flags):
     return None
 
 
-def cpu_baseline(case, n_tokens):
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, n_tokens, runs=3):
     """The CPU oracle (plain numpy, FP64 dot products) on the first n_tokens
-    tokens of the same batch; reported in the metric's unit."""
+    tokens of the same batch, all five steps, timed `runs` times (median);
+    reported in the metric's unit with the host CPU, BLAS and thread count."""
     import numpy as np
     from oracle import experts_ref, plan_ref, quant_act_ref
+    blas, threads = "unknown", os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            threads = max(p.get("num_threads", 1) for p in info)
+            blas = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in info)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        pass
     h = dict(x=case.x[:n_tokens].float().cpu().numpy(), ids=case.topk_ids.cpu().numpy(),
              w=case.topk_weights.cpu().numpy(), w13=case.w13.cpu().numpy(),
              w13_s=case.w13_s.cpu().numpy(), w2=case.w2.cpu().numpy(), w2_s=case.w2_s.cpu().numpy())
-    t0 = time.perf_counter()
-    s, e, P = plan_ref(h["ids"], case.E, case.block_m)
-    xq, xs = quant_act_ref(h["x"])
-    xq_full = np.zeros((case.M, case.K), np.uint8)
-    xs_full = np.zeros((case.M, case.K // 128), np.float32)
-    xq_full[:n_tokens], xs_full[:n_tokens] = xq, xs
-    experts_ref(xq_full, xs_full, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"], s, e, P,
-                case.top_k, case.block_m, tokens=range(n_tokens))
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        s, e, P = plan_ref(h["ids"], case.E, case.block_m)
+        xq, xs = quant_act_ref(h["x"])
+        xq_full = np.zeros((case.M, case.K), np.uint8)
+        xs_full = np.zeros((case.M, case.K // 128), np.float32)
+        xq_full[:n_tokens], xs_full[:n_tokens] = xq, xs
+        experts_ref(xq_full, xs_full, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"], s, e, P,
+                    case.top_k, case.block_m, tokens=range(n_tokens))
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     ids = h["ids"][:n_tokens]
     routes = int(((ids >= 0) & (ids < case.E)).sum())
     flops = 2.0 * routes * 3 * case.K * case.I
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n_tokens} of {case.M} tokens ({routes} routes, all five steps, "
-                      f"{dt:.1f} s wall, numpy FP64 BLAS)",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+            "sample": f"first {n_tokens} of {case.M} tokens ({routes} routes, all five steps), "
+                      f"median of {runs} runs: {', '.join(f'{t:.2f}' for t in times)} s wall",
+            "seconds": dt, "runs_s": [round(t, 3) for t in times], "host_cpus": os.cpu_count(),
+            "cpu_model": host_cpu_model(), "blas": blas}
 
 
 def main():
@@ -324,9 +347,17 @@ def main():
         achieved = nb["gate_up"] / (gate_up * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["frac_vs_fp8_dense_peak"] = round(gu_flops / (gate_up * 1e-3) / 1e12 / FP8_MFMA_PEAK, 4)
     roof["traffic"] = measured_traffic(kernel, workload, flags)
     roof.update({"kernel": kernel, "algorithmic_bytes": nb["gate_up"], "avg_ms": round(gate_up, 4),
                  "bound_ms": {"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4)}})
+
+    t35 = gate_up + down
+    steps35 = {"ms": round(t35, 4), "algorithmic_bytes": nb["layer"],
+               "GB/s": round(nb["layer"] / (t35 * 1e-3) / 1e9, 1),
+               "frac_hbm": round(nb["layer"] / (t35 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "TFLOP/s": round(flops / (t35 * 1e-3) / 1e12, 2),
+               "frac_fp8_dense_peak": round(flops / (t35 * 1e-3) / 1e12 / FP8_MFMA_PEAK, 4)}
 
     res = {
         "metric": METRIC,
@@ -354,9 +385,11 @@ def main():
         "weight_sets": nsets,
         "layer_GBs": round(nb["layer"] / (ms * 1e-3) / 1e9, 1),
         "roofline": roof,
+        # the basis of both targets: steps 3-5 (gate/up through the reduce)
+        "steps35": steps35,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_tokens, case.M))
+        res["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_tokens, case.M), args.cpu_runs)
     print(f"# generated inputs in {t_gen:.1f} s", file=sys.stderr)
     print(json.dumps(res), flush=True)
 

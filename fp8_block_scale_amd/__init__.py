@@ -36,7 +36,8 @@ EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_qua
             "moe_fp8_experts_workspace_size", "moe_fp8_experts_workspace_layout",
             "moe_fp8_experts_schedule",
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
-            "moe_last_error", "moe_debug_e4m3_encode", "moe_debug_count_non_pow2")
+            "moe_last_hip_error", "moe_last_error", "moe_debug_e4m3_encode",
+            "moe_debug_count_non_pow2")
 
 
 class MoeError(RuntimeError):
@@ -84,6 +85,7 @@ _c = {
     "moe_fp8_down_reduce": _proto("moe_fp8_down_reduce", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                   _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp, _sz, _vp),
     "moe_status_str": _proto("moe_status_str", ctypes.c_char_p, _i32),
+    "moe_last_hip_error": _proto("moe_last_hip_error", ctypes.c_char_p),
     "moe_last_error": _proto("moe_last_error", ctypes.c_char_p),
     "moe_debug_e4m3_encode": _proto("moe_debug_e4m3_encode", _i32, _vp, _vp, _i64, _vp),
     "moe_debug_count_non_pow2": _proto("moe_debug_count_non_pow2", _i32, _vp, _i64, _vp, _vp),
@@ -92,7 +94,7 @@ _c = {
 
 def _check(st, where):
     if st != MOE_OK:
-        raise MoeError(st, where, _c["moe_last_error"]().decode())
+        raise MoeError(st, where, _c["moe_last_hip_error"]().decode())
 
 
 def _ptr(t):
@@ -219,6 +221,11 @@ def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_i
               out_bf16, workspace):
         assert t.is_contiguous()
     assert out_bf16.dtype == torch.bfloat16 and topk_weights.dtype == torch.float32
+    # the kernels read expert ids of blocks below P only; P / block_m is at
+    # most the plan's block capacity and at most sorted_cap / block_m
+    assert expert_ids.numel() >= min(moe_plan_capacity(M, top_k, E, block_m)[1],
+                                     sorted_token_ids.numel() // block_m), \
+        "expert_ids shorter than the plan can need"
     _check(_c["moe_fp8_experts"](_ptr(x_q), _ptr(x_s), _ptr(w13), _ptr(w13_s), _ptr(w2),
                                  _ptr(w2_s), _ptr(topk_weights), _ptr(sorted_token_ids),
                                  _ptr(expert_ids), _ptr(num_tokens_post_padded), M, K, I, E, top_k,
@@ -258,8 +265,11 @@ def moe_status_str(status):
     return _c["moe_status_str"](status).decode()
 
 
-def moe_last_error():
-    return _c["moe_last_error"]().decode()
+def moe_last_hip_error():
+    return _c["moe_last_hip_error"]().decode()
+
+
+moe_last_error = moe_last_hip_error
 
 
 # ------------------------------------------------------------- a layer --

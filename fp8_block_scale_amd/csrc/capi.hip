@@ -181,6 +181,7 @@ MOE_API const char *moe_status_str(moe_status s) {
     return "unknown moe_status";
 }
 
+MOE_API const char *moe_last_hip_error(void) { return g_err; }
 MOE_API const char *moe_last_error(void) { return g_err; }
 
 // ------------------------------------------------------------------ plan

@@ -265,8 +265,9 @@ down_stream_kernel(DownArgs a) {
     int r = -1;
     if (w == 0 && lane < C::RP) r = a.sorted[(int64_t)b * BM + row0 + lane];
     const int ntp = a.ntp[0];
+    if (b * BM >= ntp) return;                          // padded block
     const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors
-    if (b * BM >= ntp || e < 0 || e >= a.E) return;     // padded block
+    if (e < 0 || e >= a.E) return;
 
     const int njb = a.njb;
     const int64_t K = a.K, I = a.I;
@@ -531,17 +532,9 @@ hipError_t launch_ds(DownArgs a, hipStream_t st) {
     const int64_t grid = (int64_t)a.nblocks * ((a.ctiles + nct - 1) / nct) * C::NPASS;
     if (grid == 0) return hipSuccess;
     const int lds = DSLayout(C::RP, a.njb, nct, C::YROW).total;
-    static bool attr_set[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_stream_kernel<BM, E8M0>, 160 * 1024);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute((const void *)down_stream_kernel<BM, E8M0>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
     down_stream_kernel<BM, E8M0><<<(unsigned)grid, C::NT, lds, st>>>(a);
     return hipGetLastError();
 }

@@ -314,36 +314,15 @@ down_pipe_kernel(DownArgs a) {
 constexpr size_t kSmem = (size_t)kStages * (kWBytes + kHBytes) + kStages * 8 * kMeta * 4;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
-int num_cus_dn() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int BM, bool E8M0>
 hipError_t launch_dn_pipe(const DownArgs &a, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
-    int64_t grid = num_cus_dn();
+    int64_t grid = device_cu_count();
     const int64_t max_items = (int64_t)a.nblocks * a.ctiles;
     if (grid > max_items) grid = max_items;
-    static bool attr_set[64] = {false};          // once per device
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = raise_lds_limit(lds_set, (const void *)down_pipe_kernel<BM, E8M0>, (int)kSmem);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        hipError_t err = hipFuncSetAttribute((const void *)down_pipe_kernel<BM, E8M0>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
-        if (err != hipSuccess) return err;
-        attr_set[dev] = true;
-    }
     down_pipe_kernel<BM, E8M0><<<(unsigned)grid, kNT, kSmem, st>>>(a);
     return hipGetLastError();
 }

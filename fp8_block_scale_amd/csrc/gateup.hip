@@ -97,13 +97,15 @@ gateup_stream_kernel(GateUpArgs a) {
     const int pass = L / a.jtiles;
     const int row0 = pass * C::RP;
 
-    // the plan entries of this pass are read together with the block's
-    // expert (every entry below sorted_cap is readable)
+    // the plan entries of this pass (every entry below sorted_cap is
+    // readable); the block's expert only once the block is known to lie
+    // below P (expert_ids may be sized by the plan's blocks_cap)
     int r = -1;
     if (w == 0 && lane < C::RP) r = a.sorted[(int64_t)b * BM + row0 + lane];
     const int ntp = a.ntp[0];
+    if (b * BM >= ntp) return;                          // padded block
     const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors
-    if (b * BM >= ntp || e < 0 || e >= a.E) return;   // padded block
+    if (e < 0 || e >= a.E) return;
 
     // this pass's routes (wave 0), the valid-row extent, the inverse plan map
     if (w == 0) {
@@ -163,7 +165,8 @@ gateup_stream_kernel(GateUpArgs a) {
     // those loads take the non-temporal policy (6.6 against 5.9 TB/s on a
     // 411 MB slab stream); experts with several blocks keep theirs cacheable,
     // for the other blocks' workgroups to find in L2.
-    const bool once = (b == 0 || a.eids[b - 1] != e) && (b + 1 >= a.nblocks || a.eids[b + 1] != e);
+    const bool once = (b == 0 || a.eids[b - 1] != e) &&
+                      ((int64_t)(b + 1) * BM >= ntp || a.eids[b + 1] != e);
     auto issue = [&](int st, int kbl) {
         uint8_t *base = smem + st * C::STB;
         if (once) {
@@ -359,18 +362,10 @@ hipError_t launch_gs(const GateUpArgs &a, hipStream_t st) {
     if (grid == 0) return hipSuccess;
     if (a.kb_per_split < 1) return hipErrorInvalidValue;
     const int lds = C::TOTAL;
-    if (lds > 64 * 1024) {                      // once per device
-        static bool attr_set[64] = {};
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
+    if (lds > 64 * 1024) {
+        static std::atomic<uint64_t> lds_set{0};
+        const hipError_t e = raise_lds_limit(lds_set, (const void *)gateup_stream_kernel<BM, MODE>, lds);
         if (e != hipSuccess) return e;
-        if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-        if (!attr_set[dev]) {
-            e = hipFuncSetAttribute((const void *)gateup_stream_kernel<BM, MODE>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-            if (e != hipSuccess) return e;
-            attr_set[dev] = true;
-        }
     }
     gateup_stream_kernel<BM, MODE><<<(unsigned)grid, C::NT, lds, st>>>(a);
     return hipGetLastError();

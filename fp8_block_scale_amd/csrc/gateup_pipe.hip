@@ -455,19 +455,6 @@ constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + 2 * kRows * kSG
                          2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
-int num_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int BM, int MODE>
 hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
@@ -476,20 +463,12 @@ hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
                                                                    a.R, a.cnt, a.n_cnt);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    int64_t grid = num_cus();
+    int64_t grid = device_cu_count();
     const int64_t max_items = (int64_t)a.nblocks * a.jtiles;
     if (grid > max_items) grid = max_items;
-    static bool attr_set[64] = {false};          // once per device
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = raise_lds_limit(lds_set, (const void *)gateup_pipe_kernel<BM, MODE>, (int)kSmem);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!attr_set[dev]) {
-        e = hipFuncSetAttribute((const void *)gateup_pipe_kernel<BM, MODE>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmem);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
     gateup_pipe_kernel<BM, MODE><<<(unsigned)grid, kNT, kSmem, st>>>(a);
     return hipGetLastError();
 }

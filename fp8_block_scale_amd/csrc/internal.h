@@ -6,7 +6,41 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
+
+// ---- per-device launch set-up, safe for concurrent first calls
+// Raises a kernel's dynamic-LDS limit on the current device once: the
+// device's bit in `done` is set after the (idempotent) attribute call
+// succeeds, so threads racing on a first call may each make the call, and
+// no thread launches before its own call (or an earlier one) has returned.
+inline hipError_t raise_lds_limit(std::atomic<uint64_t> &done, const void *fn, int bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    const uint64_t bit = 1ull << dev;
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    done.fetch_or(bit, std::memory_order_release);
+    return hipSuccess;
+}
+
+// Compute units of the current device (256 if the query fails), queried once
+// per device; a racing first call queries twice and stores the same value.
+inline int device_cu_count() {
+    static std::atomic<int> cached[64];        // static storage: zero-initialised
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 // ---- step 1: routing plan (plan.hip)
 // Workgroups of the multi-workgroup plan for R routes (0: one-workgroup

@@ -23,15 +23,18 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument, unless said otherwise, is DEVICE memory owned
- *     by the caller.  The library allocates nothing, frees nothing and keeps
- *     no state between calls.
+ *     by the caller.  The library allocates nothing and frees nothing.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work; buffers must stay alive until the stream has
  *     executed it.  No call synchronises the host or copies device data to
  *     the host.
  *   - Host-checkable problems (NULL pointers, shapes, alignment, capacity,
  *     workspace size) return a status and enqueue nothing.  Launch failures
- *     return MOE_ERR_HIP and moe_last_error() holds the HIP message.
+ *     return MOE_ERR_HIP and moe_last_hip_error() holds the HIP message.
+ *   - Host-side state: none that affects results.  Each launcher raises its
+ *     kernel's dynamic-LDS limit once per device and the device's CU count
+ *     is queried once; both are kept in atomics, so concurrent first calls
+ *     from several host threads are safe.
  *   - Data conditions are not errors: ids outside [0, E) are masked routes;
  *     zero scales contribute zero.
  *   - All tensors are dense row-major with the shapes given; sizes are in
@@ -84,12 +87,15 @@ enum {
      * [2^-126, 2^127] (no zeros): a non-power-of-two scale is silently
      * truncated to its exponent. */
     MOE_F_MMA_E8M0 = 2u,
-    /* run the gate/up GEMM on the FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4)
-     * instead of the default exact path (codes widened to FP16, exact
-     * products, FP32 accumulation).  Faster, but the FP8 MFMA keeps only
-     * ~15 bits below the largest product of each instruction, so about 1e-3
-     * of the requantised SwiGLU codes move by one step relative to an
-     * exactly accumulated reference. */
+    /* EXPERIMENTAL, outside the parity contract: run the gate/up GEMM on
+     * the FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) instead of the default
+     * exact path (codes widened to FP16, exact products, FP32 accumulation).
+     * Faster, but the FP8 MFMA keeps only ~15 bits below the largest product
+     * of each instruction, so about 1e-3 of the requantised SwiGLU codes
+     * move (some by more than one step) relative to an exactly accumulated
+     * reference -- ten times the 1e-4 intermediate-code budget the default
+     * path meets.  The output stays within the output tolerance on the
+     * tested workloads, but no bar is promised. */
     MOE_F_FP8_GATEUP = 4u
 };
 /* Bits 8..15 of `flags` optionally force the gate/up split-K factor
@@ -205,9 +211,11 @@ moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int32_t E, 
  *   w13 [E, 2I, K] E4M3, w13_s [E, 2I/128, K/128] FP32
  *   w2  [E, K, I]  E4M3, w2_s  [E, K/128, I/128]  FP32
  *   topk_weights [M, top_k] FP32 (any routed scaling already folded in)
- *   sorted_token_ids [sorted_cap], expert_ids [sorted_cap / block_m],
+ *   sorted_token_ids [sorted_cap], expert_ids (at least P / block_m
+ *   entries: a buffer of moe_plan_capacity's blocks_cap suffices),
  *   num_tokens_post_padded [1]: the plan (device); blocks at or beyond P
- *   exit untouched, so worst-case buffers are fine.
+ *   exit untouched and their expert ids are never read, so worst-case
+ *   buffers are fine.
  *   out_bf16 [M, K] BF16, read and written (accumulated into).
  * Constraints: K % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128},
  * sorted_cap % block_m == 0, weights and x_q 16-byte aligned.
@@ -254,7 +262,10 @@ moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
 /* ------------------------------------------------------------ utilities -- */
 
 const char *moe_status_str(moe_status s);
-/* Text of the last MOE_ERR_HIP / validation failure on this thread. */
+/* Text of the last MOE_ERR_HIP / validation failure on this thread (a
+ * thread-local buffer, valid until this thread's next library call). */
+const char *moe_last_hip_error(void);
+/* The same text under its earlier name. */
 const char *moe_last_error(void);
 
 /* Test hook: convert n FP32 values to E4M3 codes with the exact device

@@ -9,10 +9,13 @@ Bars (the stated parity tolerances):
     (ranks of the 253 ordered E4M3 values; +0 and -0 are one value) -- or, in
     a group whose scale itself landed on the other side of a rounding
     boundary, within one value step after dequantisation;
-  * output: relative L2 <= 5e-3 and max |gpu - ref| <= 2e-2 * rms(ref), with
-    the FP64 oracle sum (before its BF16 rounding) as ref; an element whose
-    reference exceeds ~10 rms may use one BF16 ulp of ref as its bound
-    instead (the BF16 output cannot be closer); such elements are counted.
+  * output: relative L2 <= 5e-3 and, per element, |gpu - ref| <= 2e-2 *
+    rms(ref) + half a BF16 ulp of ref, with the FP64 oracle sum (before its
+    BF16 rounding) as ref: the 2e-2 * rms bound covers the arithmetic up to
+    the FP32 sum, and the BF16 output then adds its one rounding (the
+    oracle's own BF16-rounded output needs the same allowance: above ~6 rms
+    half an ulp alone can exceed 2e-2 * rms).  Elements that used the
+    rounding allowance are counted.
 """
 
 import sys
@@ -98,14 +101,20 @@ def compare_output(gpu, ref64, rows=None):
     err = g - r
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
     rel_l2 = float(np.linalg.norm(err) / max(np.linalg.norm(r), 1e-300))
-    bound = np.maximum(MAX_ABS_RMS * rms, np.where(np.abs(r) > 10 * rms, bf16_ulp(r), 0.0))
+    bound = MAX_ABS_RMS * rms + 0.5 * bf16_ulp(r)
     viol = np.abs(err) > bound
     n_floor = int(((np.abs(err) > MAX_ABS_RMS * rms) & ~viol).sum())
     max_abs_rms = float(np.abs(err).max() / rms) if rms > 0 else 0.0
     assert rel_l2 <= REL_L2_MAX, f"relative L2 {rel_l2:.3g} > {REL_L2_MAX}"
-    assert not viol.any(), (f"{int(viol.sum())} outputs exceed max(2e-2*rms, bf16 ulp); "
-                            f"max |err|/rms = {max_abs_rms:.3g}")
-    return dict(rel_l2=rel_l2, max_abs_over_rms=max_abs_rms, ulp_floor_used=n_floor, rms=rms)
+    if viol.any():
+        i = np.unravel_index(int(np.argmax(np.where(viol, np.abs(err), -1.0))), err.shape)
+        raise AssertionError(
+            f"{int(viol.sum())} outputs exceed 2e-2*rms + bf16 ulp/2; max |err|/rms = "
+            f"{max_abs_rms:.3g}; worst at {tuple(int(v) for v in i)}: ref/rms {r[i] / rms:.4g}, "
+            f"gpu/rms {g[i] / rms:.4g}, err/rms {err[i] / rms:.4g}, bf16 ulp/rms "
+            f"{bf16_ulp(r[i]) / rms:.4g}, rms {rms:.4g}")
+    return dict(rel_l2=rel_l2, max_abs_over_rms=max_abs_rms, rounding_allowance_used=n_floor,
+                rms=rms)
 
 
 # ------------------------------------------------------------------ runs

@@ -240,3 +240,45 @@ def test_output_accumulates(tiny):
     init = np.random.default_rng(5).standard_normal((c.M, c.K)).astype(np.float32)
     b, _ = _run(d, c.E, c.top_k, c.block_m, out_init=init)
     assert np.allclose(b.ref64 - init, a.ref64, rtol=1e-12, atol=1e-12 * np.abs(init).max())
+
+
+@pytest.mark.parametrize("geom", ["tiny", "page1_small"])
+def test_token_sampling_equals_full_evaluation(geom):
+    """experts_ref(tokens=S) -- the mode every full-size GPU parity case uses
+    -- equals the full evaluation restricted to S: the intermediate codes and
+    scales of S's plan rows bit for bit, S's output rows to FP64 rounding, and
+    every other output row left at out_init with zero codes and the floored
+    scale in the rows it skipped.  Checked on the tiny workload and on a
+    page-1-like geometry (E=16, K=512, I=256, top-8, block_m=64, M=96) with a
+    prefilled output."""
+    if geom == "tiny":
+        c = make_case("tiny")
+        S = [1, 3]
+    else:
+        from moe_workloads import CONFIGS
+        cfg = dict(CONFIGS["page1"], M=96, E=16, K=512, I=256, seed=31)
+        c = make_case("page1_small", config=cfg)
+        S = [0, 7, 8, 50, 95]
+    d = _np(c)
+    rng = np.random.default_rng(3)
+    init = (rng.standard_normal((c.M, c.K)) * 0.1).astype(np.float32)
+    xq, xs = quant_act_ref(d["x"])
+    s, x, P = plan_ref(d["ids"], c.E, c.block_m)
+    args = (xq, xs, d["w13"], d["w13_s"], d["w2"], d["w2_s"], d["w"], s, x, P, c.top_k, c.block_m)
+    full = experts_ref(*args, out_init=init)
+    part = experts_ref(*args, out_init=init, tokens=S)
+    R = c.M * c.top_k
+    tok_of_row = np.where(s < R, s // c.top_k, -1)
+    in_S = np.isin(tok_of_row, S) & full.row_valid
+    assert in_S.any()
+    assert np.array_equal(part.h_q[in_S], full.h_q[in_S])
+    assert np.array_equal(part.h_s[in_S], full.h_s[in_S])
+    skipped = full.row_valid & ~in_S
+    assert skipped.any()
+    assert np.all(part.h_q[skipped] == 0) and np.all(part.h_s[skipped] == FLT_MIN)
+    np.testing.assert_allclose(part.ref64[S], full.ref64[S], rtol=1e-12, atol=1e-14)
+    others = np.setdiff1d(np.arange(c.M), S)
+    assert np.array_equal(part.ref64[others], init[others].astype(np.float64))
+    assert np.array_equal(np.nonzero(part.computed_tokens)[0], np.asarray(sorted(S)))
+    # and the sampled rows really differ from out_init (the routes were added)
+    assert not np.allclose(part.ref64[S], init[S].astype(np.float64))
