@@ -37,7 +37,9 @@ EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_qua
             "moe_fp8_experts_schedule",
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
             "moe_last_hip_error", "moe_last_error", "moe_debug_e4m3_encode",
-            "moe_debug_count_non_pow2")
+            "moe_debug_count_non_pow2", "moe_fp8_experts_noalloc")
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -84,6 +86,9 @@ _c = {
                               _i64, _i32, _i32, _i32, _i64, _u32, _vp, _sz, _vp),
     "moe_fp8_down_reduce": _proto("moe_fp8_down_reduce", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                   _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp, _sz, _vp),
+    "moe_fp8_experts_noalloc": _proto("moe_fp8_experts_noalloc", _i32, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                                      _i32, _i64, _u32, _vp, _vp),
     "moe_status_str": _proto("moe_status_str", ctypes.c_char_p, _i32),
     "moe_last_hip_error": _proto("moe_last_hip_error", ctypes.c_char_p),
     "moe_last_error": _proto("moe_last_error", ctypes.c_char_p),
@@ -233,6 +238,26 @@ def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_i
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)),
            "moe_fp8_experts")
+
+
+def moe_fp8_experts_noalloc(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids,
+                            expert_ids, num_tokens_post_padded, top_k, block_m, out_bf16, flags=0,
+                            stream=None):
+    """moe_fp8_experts with the library's static per-device scratch as the
+    workspace (no allocation anywhere); raises MoeError (MOE_ERR_CAPACITY)
+    for sizes whose workspace exceeds MOE_NOALLOC_SCRATCH_BYTES."""
+    M, K = x_q.shape
+    E, twoI, _ = w13.shape
+    for t in (x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+              out_bf16):
+        assert t.is_contiguous()
+    assert out_bf16.dtype == torch.bfloat16 and topk_weights.dtype == torch.float32
+    _check(_c["moe_fp8_experts_noalloc"](_ptr(x_q), _ptr(x_s), _ptr(w13), _ptr(w13_s), _ptr(w2),
+                                         _ptr(w2_s), _ptr(topk_weights), _ptr(sorted_token_ids),
+                                         _ptr(expert_ids), _ptr(num_tokens_post_padded), M, K,
+                                         twoI // 2, E, top_k, block_m, sorted_token_ids.numel(),
+                                         flags, _ptr(out_bf16), _stream(stream)),
+           "moe_fp8_experts_noalloc")
 
 
 def moe_fp8_gate_up(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids, num_tokens_post_padded,

@@ -1,5 +1,6 @@
 // C ABI of libmoe_fp8.so: argument validation, workspace layout and the
 // launch sequence of each entry point (declared in include/moe_fp8.h).
+#include <atomic>
 #include <cmath>
 #include <hip/hip_runtime.h>
 
@@ -549,4 +550,66 @@ MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const u
     return moe_fp8_down_reduce(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
                                num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap,
                                flags, out_bf16, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------- no-allocation variant
+
+// The static workspace of moe_fp8_experts_noalloc: one copy per device,
+// allocated with the code object.  Host code never passes `scratch` itself
+// (on the host it is only a stand-in symbol): it takes the device address
+// that hipGetSymbolAddress reports for the current device, looked up once per
+// device and kept in g_scratch.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<uintptr_t> g_scratch[64];   // device address of `scratch`, per device (0: not yet)
+
+moe_status scratch_of_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_check(e, "moe_fp8_experts_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the 64 supported", dev);
+    uintptr_t p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        void *q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_check(e, "moe_fp8_experts_noalloc: hipGetSymbolAddress");
+        if (q == nullptr || ((uintptr_t)q & 255u) != 0)
+            return fail(MOE_ERR_HIP, "moe_fp8_experts_noalloc: scratch address %p unusable", q);
+        p = (uintptr_t)q;
+        g_scratch[dev].store(p, std::memory_order_release);   // a racing lookup stores the same
+    }
+    *out = (void *)p;
+    return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_fp8_experts_noalloc(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                                           const float *w13_s, const uint8_t *w2, const float *w2_s,
+                                           const float *topk_weights,
+                                           const int32_t *sorted_token_ids,
+                                           const int32_t *expert_ids,
+                                           const int32_t *num_tokens_post_padded, int64_t M,
+                                           int64_t K, int64_t I, int32_t E, int32_t top_k,
+                                           int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                                           void *out_bf16, void *stream) {
+    moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
+    if (st != MOE_OK) return st;
+    st = check_flags(flags, K, I);
+    if (st != MOE_OK) return st;
+    const size_t need = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags).total;
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_CAPACITY,
+                    "moe_fp8_experts_noalloc: these sizes need %zu bytes of workspace, above the "
+                    "%zu-byte static scratch; use moe_fp8_experts with a caller workspace",
+                    need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    if (M == 0 || sorted_cap == 0) return MOE_OK;
+    void *ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != MOE_OK) return st;
+    return moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+                           num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap, flags,
+                           out_bf16, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -259,6 +259,32 @@ moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                void *out_bf16, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* ------------------------------------------------- no-allocation variant -- */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_fp8_experts with its workspace taken from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  Arguments, results and errors are those of
+ * moe_fp8_experts (the caller still passes every input and the output);
+ * sizes whose moe_fp8_experts_workspace_size exceeds the array return
+ * MOE_ERR_CAPACITY before anything is enqueued (the decode shapes fit; the
+ * page-1 shape at M=4096 does not).  No call allocates or frees memory: the
+ * first call on a device looks up the array's device address once.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents; calls that overlap on one GPU (concurrent streams or host
+ * threads) race on it and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_fp8_experts_noalloc(const uint8_t *x_q, const float *x_s,
+                                   const uint8_t *w13, const float *w13_s,
+                                   const uint8_t *w2, const float *w2_s,
+                                   const float *topk_weights,
+                                   const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                                   const int32_t *num_tokens_post_padded,
+                                   int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                                   int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                                   void *out_bf16, void *stream);
+
 /* ------------------------------------------------------------ utilities -- */
 
 const char *moe_status_str(moe_status s);

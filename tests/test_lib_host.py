@@ -195,3 +195,27 @@ def test_plan_quant_validation():
     assert _err(call(x=None)) == "MOE_ERR_NULL"
     assert _err(call(ld=260)) == "MOE_ERR_ALIGN"
     assert _err(call(p=None)) == "MOE_ERR_NULL"
+
+
+def test_noalloc_validation_before_any_device_call():
+    """moe_fp8_experts_noalloc validates like moe_fp8_experts and rejects
+    sizes whose workspace exceeds the static scratch, all before touching the
+    device (these calls run without a GPU)."""
+    f = _raw("moe_fp8_experts_noalloc")
+
+    def call(M, K, I, E, k, bm, fl=0):
+        sc = moe.moe_plan_capacity(M, k, E, bm)[0]
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, K, I, E, k, bm, sc,
+                 fl, FAKE, None)
+
+    assert _err(call(4096, 4096, 1024, 288, 8, 64)) == "MOE_ERR_CAPACITY"     # page-1 M=4096
+    assert "static scratch" in moe.moe_last_hip_error()
+    assert _err(call(4, 200, 256, 8, 2, 16)) == "MOE_ERR_SHAPE"
+    assert _err(call(4, 256, 256, 8, 2, 48)) == "MOE_ERR_UNSUPPORTED"
+    assert _err(call(4, 256, 256, 8, 2, 16, fl=moe.MOE_F_MMA_E8M0)) == "MOE_ERR_SHAPE"
+    assert _err(call(0, 256, 256, 8, 2, 16)) == "MOE_OK"                      # M = 0: no work
+    # the decode shapes fit the scratch
+    for M in (1, 4, 16):
+        sc = moe.moe_plan_capacity(M, 9, 257, 16)[0]
+        need = moe.moe_fp8_experts_workspace_size(M, 7168, 256, 257, 9, 16, sc, 0)
+        assert 0 < need <= moe.MOE_NOALLOC_SCRATCH_BYTES, (M, need)
