@@ -64,6 +64,9 @@ def parse():
                     help="force the gate/up kernel family (tuning override)")
     ap.add_argument("--down-path", choices=("auto", "stream", "persistent"), default="auto",
                     help="force the down kernel family (tuning override)")
+    ap.add_argument("--fuse", choices=("auto", "on", "off"), default="auto",
+                    help="steps 3-5 as one launch (on), as two stages (off), or the library's "
+                         "choice (auto)")
     ap.add_argument("--separate-plan-quant", action="store_true",
                     help="moe_plan then moe_quant_act instead of the fused moe_plan_quant")
     ap.add_argument("--eager", action="store_true",
@@ -100,9 +103,10 @@ def algorithmic_bytes(case, n_touched, R_valid, P, n_tok):
 
 
 CSRC = os.path.join(ROOT, "fp8_block_scale_amd", "csrc")
-GATEUP_SOURCES = {
+KERNEL_SOURCES = {
     "gateup_pipe_kernel": ("gateup_pipe.hip", "common.h", "internal.h"),
-    "gateup_stream_kernel": ("gateup.hip", "common.h", "internal.h"),
+    "gateup_stream_kernel": ("gateup.hip", "gateup_item.h", "common.h", "internal.h"),
+    "fused_experts_kernel": ("fused.hip", "gateup_item.h", "down_item.h", "common.h", "internal.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
@@ -117,7 +121,7 @@ def gateup_kernel_name(case, sorted_cap, flags):
 
 def sources_sha(kernel):
     h = hashlib.sha256()
-    for f in GATEUP_SOURCES[kernel]:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -228,6 +232,8 @@ def main():
              "persistent": moe.MOE_PATH_PERSISTENT}
     flags |= paths[args.gateup_path] << moe.MOE_F_GATEUP_PATH_SHIFT
     flags |= paths[args.down_path] << moe.MOE_F_DOWN_PATH_SHIFT
+    fuses = {"auto": moe.MOE_FUSE_AUTO, "on": moe.MOE_FUSE_ON, "off": moe.MOE_FUSE_OFF}
+    flags |= fuses[args.fuse] << moe.MOE_F_FUSE_SHIFT
 
     # Weight copies: a step reads the touched experts' weights once; with
     # fewer than ~1 GiB of them per step, back-to-back steps would find them
@@ -262,7 +268,17 @@ def main():
         moe.moe_fp8_down_reduce(w2, w2_s, case.topk_weights, b.sorted_ids, b.expert_ids,
                                 b.ntp, case.top_k, case.block_m, out, b.workspace, flags, stream)
 
-    stages = (stage_plan_quant, stage_gate_up, stage_down)
+    def stage_experts(stream, k):
+        w13, w13_s, w2, w2_s = wsets[k % nsets]
+        moe.moe_fp8_experts(b.x_q, b.x_s, w13, w13_s, w2, w2_s, case.topk_weights, b.sorted_ids,
+                            b.expert_ids, b.ntp, case.top_k, case.block_m, out, b.workspace, flags,
+                            stream)
+
+    sched = moe.moe_fp8_experts_schedule(case.M, case.K, case.I, case.E, case.top_k, case.block_m,
+                                         b.sorted_ids.numel(), flags)
+    fused = sched[4]
+    # one step: plan + quantisation, then steps 3-5 as the library schedules them
+    stages = (stage_plan_quant, stage_experts)
 
     def step(k, ev=None):
         stream = torch.cuda.current_stream()
@@ -271,7 +287,7 @@ def main():
                 ev[i].record(stream)
             fn(stream, k)
         if ev is not None:
-            ev[3].record(stream)
+            ev[len(stages)].record(stream)
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -288,8 +304,9 @@ def main():
     stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    gate_up = down = None
     if args.eager:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t_start.record(stream)
         for i in range(args.steps):
@@ -298,8 +315,7 @@ def main():
         torch.cuda.synchronize()
         ms = t_start.elapsed_time(t_end) / args.steps
         plan_quant = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-        gate_up = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        down = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+        experts = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     else:
         # One graph holding K steps, and one per stage holding K launches of
         # it, each replayed once between two events on the replay stream (a
@@ -322,7 +338,9 @@ def main():
             return t_start.elapsed_time(t_end) / args.steps
 
         ms = replay_ms(capture(stages))
-        plan_quant, gate_up, down = (replay_ms(capture([fn])) for fn in stages)
+        plan_quant, experts = (replay_ms(capture([fn])) for fn in stages)
+        if not fused:       # the two stages of steps 3-5, each timed on its own
+            gate_up, down = (replay_ms(capture([fn])) for fn in (stage_gate_up, stage_down))
 
     R_valid = int(valid.sum())
     P = int(b.ntp.item())
@@ -330,29 +348,44 @@ def main():
     nb = algorithmic_bytes(case, n_touched, R_valid, P, case.M)
     tflops = flops / (ms * 1e-3) / 1e12
 
-    # gate/up roofline: the larger of the two lower bounds on its time binds
-    gu_flops = 2.0 * R_valid * case.K * 2 * case.I
-    mfma_peak = FP8_MFMA_PEAK if args.fp8_gateup else FP16_MFMA_PEAK
-    t_hbm = nb["gate_up"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = gu_flops / (mfma_peak * 1e12)
-    kernel = gateup_kernel_name(case, b.sorted_ids.numel(), flags)
-    workload = f"{case.name} M={case.M}"
-    if t_mfma > t_hbm:
-        achieved = gu_flops / (gate_up * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4),
-                "mfma": "fp8 16x16x128" if args.fp8_gateup else "fp16 16x16x32 (FP8 codes widened)",
-                "algorithmic_flops": gu_flops}
-    else:
-        achieved = nb["gate_up"] / (gate_up * 1e-3) / 1e9
+    if fused or gate_up is None:
+        # the single launch (or eager timing without stage graphs): the
+        # dominant kernel is steps 3-5 as a whole, HBM-bound at these sizes
+        kname = "fused_experts_kernel" if fused else "steps 3-5"
+        t_hbm = nb["layer"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = flops / (FP16_MFMA_PEAK * 1e12) * (2 / 3) + flops / (FP8_MFMA_PEAK * 1e12) / 3
+        achieved = nb["layer"] / (experts * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof["frac_vs_fp8_dense_peak"] = round(gu_flops / (gate_up * 1e-3) / 1e12 / FP8_MFMA_PEAK, 4)
-    roof["traffic"] = measured_traffic(kernel, workload, flags)
-    roof.update({"kernel": kernel, "algorithmic_bytes": nb["gate_up"], "avg_ms": round(gate_up, 4),
-                 "bound_ms": {"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4)}})
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "frac_vs_fp8_dense_peak": round(flops / (experts * 1e-3) / 1e12 / FP8_MFMA_PEAK, 4),
+                "traffic": measured_traffic(kname, f"{case.name} M={case.M}", flags)
+                if fused else None,
+                "kernel": kname, "algorithmic_bytes": nb["layer"], "avg_ms": round(experts, 4),
+                "bound_ms": {"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4)}}
+    else:
+        # gate/up roofline: the larger of the two lower bounds on its time binds
+        gu_flops = 2.0 * R_valid * case.K * 2 * case.I
+        mfma_peak = FP8_MFMA_PEAK if args.fp8_gateup else FP16_MFMA_PEAK
+        t_hbm = nb["gate_up"] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = gu_flops / (mfma_peak * 1e12)
+        kernel = gateup_kernel_name(case, b.sorted_ids.numel(), flags)
+        workload = f"{case.name} M={case.M}"
+        if t_mfma > t_hbm:
+            achieved = gu_flops / (gate_up * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4),
+                    "mfma": "fp8 16x16x128" if args.fp8_gateup else "fp16 16x16x32 (FP8 codes widened)",
+                    "algorithmic_flops": gu_flops}
+        else:
+            achieved = nb["gate_up"] / (gate_up * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        roof["frac_vs_fp8_dense_peak"] = round(gu_flops / (gate_up * 1e-3) / 1e12 / FP8_MFMA_PEAK, 4)
+        roof["traffic"] = measured_traffic(kernel, workload, flags)
+        roof.update({"kernel": kernel, "algorithmic_bytes": nb["gate_up"], "avg_ms": round(gate_up, 4),
+                     "bound_ms": {"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4)}})
 
-    t35 = gate_up + down
+    t35 = experts
     steps35 = {"ms": round(t35, 4), "algorithmic_bytes": nb["layer"],
                "GB/s": round(nb["layer"] / (t35 * 1e-3) / 1e9, 1),
                "frac_hbm": round(nb["layer"] / (t35 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -379,8 +412,10 @@ def main():
             "block_m": case.block_m, "flags": flags, "valid_routes": R_valid,
             "touched_experts": n_touched, "padded_rows": P,
         },
-        "stages_ms": {"plan_quant": round(plan_quant, 4), "gate_up": round(gate_up, 4),
-                      "down_reduce": round(down, 4)},
+        "stages_ms": {"plan_quant": round(plan_quant, 4), "experts": round(experts, 4),
+                      **({} if gate_up is None else {"gate_up": round(gate_up, 4),
+                                                     "down_reduce": round(down, 4)})},
+        "single_launch": bool(fused),
         "launch": "eager" if args.eager else "hip graph (K steps per replay)",
         "weight_sets": nsets,
         "layer_GBs": round(nb["layer"] / (ms * 1e-3) / 1e9, 1),

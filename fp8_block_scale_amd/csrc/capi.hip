@@ -56,6 +56,7 @@ struct SplitChoice {
     int kb_per_split;
     bool gu_persistent;
     bool dn_persistent;
+    bool fused;          // steps 3-5 in one launch (moe_fp8_experts only)
 };
 
 constexpr int64_t kPersistentTiles = 512;   // (block, j-tile) pairs
@@ -74,10 +75,17 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     // is faster up to ~3/4 of a 64-row pass of routes per expert on average.
     const int64_t pass_rows = bm < 64 ? bm : 64;
     const bool dense = 4 * R > 3 * pass_rows * (int64_t)E;
+    const uint32_t fuse = (flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT;
     SplitChoice c;
     c.gu_persistent = gu_path == MOE_PATH_PERSISTENT ||
                       (gu_path == MOE_PATH_AUTO && forced == 0 && big && dense);
     c.dn_persistent = dn_path == MOE_PATH_PERSISTENT || (dn_path == MOE_PATH_AUTO && big);
+    // The single launch only on request: measured on MI355X it is slower than
+    // the two stages at every size tried (decode M=1: 34 against 27 us; M=16:
+    // 155 against 120 us): every workgroup pays the larger item's LDS, so
+    // neither item kind keeps its own occupancy and ring depth.
+    if (fuse == MOE_FUSE_ON) c.gu_persistent = c.dn_persistent = false;   // (forced paths: rejected)
+    c.fused = fuse == MOE_FUSE_ON;
     if (c.gu_persistent) {
         c.nsplit = 1;
         c.kb_per_split = (int)nkb;
@@ -112,7 +120,8 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
 
 struct WsLayout {
     size_t hq, hs, y, ys, rpos, tiles, cnt, part, total;
-    size_t cnt_words;                 // split-K counters, zeroed per call
+    size_t splitk_words;              // split-K counters
+    size_t cnt_words;                 // all counters (split-K, then the single launch's), zeroed per call
     SplitChoice sp;
 };
 
@@ -138,7 +147,9 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, in
     off = align256(off + (size_t)blocks_cap * 16 + 17 * 4);
     l.cnt = off;
     size_t ntiles = (size_t)blocks_cap * jtiles;
-    l.cnt_words = l.sp.nsplit > 1 ? ntiles * (block_m > 64 ? block_m / 64 : 1) : 0;
+    l.splitk_words = l.sp.nsplit > 1 ? ntiles * (block_m > 64 ? block_m / 64 : 1) : 0;
+    l.cnt_words = l.splitk_words;
+    if (l.sp.fused) l.cnt_words += moe::fused_counter_words(blocks_cap, block_m, M, (K + 255) / 256);
     off = align256(off + l.cnt_words * 4);
     l.part = off;
     if (l.sp.nsplit > 1) off = align256(off + ntiles * l.sp.nsplit * block_m * 256 * 4);
@@ -358,9 +369,9 @@ MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_
 
 namespace {
 
-moe_status check_flags(uint32_t flags, int64_t K, int64_t I) {
+moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m) {
     const uint32_t known = MOE_F_INTER_UE8M0 | MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_SPLITK_MASK |
-                           MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK;
+                           MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK | MOE_F_FUSE_MASK;
     if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
     const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
@@ -372,6 +383,13 @@ moe_status check_flags(uint32_t flags, int64_t K, int64_t I) {
         return fail(MOE_ERR_SHAPE, "a forced split-K factor needs the per-block gate/up kernel");
     if ((flags & MOE_F_MMA_E8M0) && !(flags & MOE_F_INTER_UE8M0))
         return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
+    const uint32_t fu = (flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT;
+    if (fu > MOE_FUSE_ON) return fail(MOE_ERR_SHAPE, "fuse choice must be 0, 1 or 2");
+    if (fu == MOE_FUSE_ON && (gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT))
+        return fail(MOE_ERR_SHAPE, "MOE_FUSE_ON runs the per-block kernel family: no persistent path");
+    if (fu == MOE_FUSE_ON && I / 128 > moe::fused_max_njb(block_m))
+        return fail(MOE_ERR_UNSUPPORTED, "MOE_FUSE_ON needs I / 128 <= %d at block_m %d",
+                    moe::fused_max_njb(block_m), block_m);
     return MOE_OK;
 }
 
@@ -383,13 +401,14 @@ MOE_API moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
     if (!info) return fail(MOE_ERR_NULL, "output pointer is NULL");
-    st = check_flags(flags, K, I);
+    st = check_flags(flags, K, I, block_m);
     if (st != MOE_OK) return st;
     const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
     info[0] = l.sp.gu_persistent ? 1 : 0;
     info[1] = l.sp.dn_persistent ? 1 : 0;
     info[2] = l.sp.nsplit;
     info[3] = l.sp.kb_per_split;
+    info[4] = l.sp.fused ? 1 : 0;
     return MOE_OK;
 }
 
@@ -401,7 +420,7 @@ moe_status check_stage(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k
                        size_t workspace_bytes, WsLayout *l) {
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
-    st = check_flags(flags, K, I);
+    st = check_flags(flags, K, I, block_m);
     if (st != MOE_OK) return st;
     *l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
     if (M == 0 || sorted_cap == 0) return MOE_OK;
@@ -410,6 +429,75 @@ moe_status check_stage(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k
     if (workspace_bytes < l->total)
         return fail(MOE_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, l->total);
     return MOE_OK;
+}
+
+}  // namespace
+
+namespace {
+
+moe::GateUpArgs gateup_args(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                            const float *w13_s, const int32_t *sorted_token_ids,
+                            const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
+                            int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                            int32_t block_m, int64_t sorted_cap, uint32_t flags, uint8_t *ws,
+                            const WsLayout &l) {
+    moe::GateUpArgs ga;
+    ga.xq = x_q;
+    ga.xs = x_s;
+    ga.w13 = w13;
+    ga.w13s = w13_s;
+    ga.sorted = sorted_token_ids;
+    ga.eids = expert_ids;
+    ga.ntp = num_tokens_post_padded;
+    ga.hq = ws + l.hq;
+    ga.hs = (float *)(ws + l.hs);
+    ga.part = (float *)(ws + l.part);
+    ga.cnt = (uint32_t *)(ws + l.cnt);
+    ga.n_cnt = (int64_t)l.cnt_words;
+    ga.rpos = (int32_t *)(ws + l.rpos);
+    ga.tiles = (int4 *)(ws + l.tiles);
+    ga.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);
+    ga.K = K;
+    ga.I = I;
+    ga.R = M * top_k;
+    ga.E = E;
+    ga.top_k = top_k;
+    ga.nkb = (int)(K / 128);
+    ga.jtiles = (int)(I / 128);
+    ga.nblocks = (int)(sorted_cap / block_m);
+    ga.nsplit = l.sp.nsplit;
+    ga.kb_per_split = l.sp.kb_per_split;
+    ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
+    return ga;
+}
+
+moe::DownArgs down_args(const uint8_t *w2, const float *w2_s, const float *topk_weights,
+                        const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                        const int32_t *num_tokens_post_padded, int64_t M, int64_t K, int64_t I,
+                        int32_t E, int32_t top_k, int32_t block_m, int64_t sorted_cap, uint8_t *ws,
+                        const WsLayout &l) {
+    moe::DownArgs da;
+    da.hq = ws + l.hq;
+    da.hs = (const float *)(ws + l.hs);
+    da.w2 = w2;
+    da.w2s = w2_s;
+    da.topk_w = topk_weights;
+    da.sorted = sorted_token_ids;
+    da.eids = expert_ids;
+    da.ntp = num_tokens_post_padded;
+    da.y16 = (uint16_t *)(ws + l.y);
+    da.ys = (float *)(ws + l.ys);
+    da.K = K;
+    da.I = I;
+    da.R = M * top_k;
+    da.E = E;
+    da.top_k = top_k;
+    da.njb = (int)(I / 128);
+    da.ctiles = (int)((K + 255) / 256);
+    da.nblocks = (int)(sorted_cap / block_m);
+    da.tiles = (const int4 *)(ws + l.tiles);
+    da.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);
+    return da;
 }
 
 }  // namespace
@@ -438,33 +526,9 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
                        "moe_fp8_gate_up: clear route map and counters");
         if (st != MOE_OK) return st;
     }
-    moe::GateUpArgs ga;
-    ga.xq = x_q;
-    ga.xs = x_s;
-    ga.w13 = w13;
-    ga.w13s = w13_s;
-    ga.sorted = sorted_token_ids;
-    ga.eids = expert_ids;
-    ga.ntp = num_tokens_post_padded;
-    ga.hq = ws + l.hq;
-    ga.hs = (float *)(ws + l.hs);
-    ga.part = (float *)(ws + l.part);
-    ga.cnt = (uint32_t *)(ws + l.cnt);
-    ga.n_cnt = (int64_t)l.cnt_words;
-    ga.rpos = (int32_t *)(ws + l.rpos);
-    ga.tiles = (int4 *)(ws + l.tiles);
-    ga.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);
-    ga.K = K;
-    ga.I = I;
-    ga.R = M * top_k;
-    ga.E = E;
-    ga.top_k = top_k;
-    ga.nkb = (int)(K / 128);
-    ga.jtiles = (int)(I / 128);
-    ga.nblocks = (int)(sorted_cap / block_m);
-    ga.nsplit = l.sp.nsplit;
-    ga.kb_per_split = l.sp.kb_per_split;
-    ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
+    const moe::GateUpArgs ga = gateup_args(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids,
+                                           num_tokens_post_padded, M, K, I, E, top_k, block_m,
+                                           sorted_cap, flags, ws, l);
     const bool fp8 = (flags & MOE_F_FP8_GATEUP) != 0, e8 = (flags & MOE_F_MMA_E8M0) != 0;
     if (l.sp.gu_persistent)
         return hip_check(moe::launch_gateup_pipe(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
@@ -493,27 +557,9 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
         return fail(MOE_ERR_ALIGN, "w2 and out must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
-    moe::DownArgs da;
-    da.hq = ws + l.hq;
-    da.hs = (const float *)(ws + l.hs);
-    da.w2 = w2;
-    da.w2s = w2_s;
-    da.topk_w = topk_weights;
-    da.sorted = sorted_token_ids;
-    da.eids = expert_ids;
-    da.ntp = num_tokens_post_padded;
-    da.y16 = (uint16_t *)(ws + l.y);
-    da.ys = (float *)(ws + l.ys);
-    da.K = K;
-    da.I = I;
-    da.R = M * top_k;
-    da.E = E;
-    da.top_k = top_k;
-    da.njb = (int)(I / 128);
-    da.ctiles = (int)((K + 255) / 256);
-    da.nblocks = (int)(sorted_cap / block_m);
-    da.tiles = (const int4 *)(ws + l.tiles);
-    da.tmeta = (int32_t *)(ws + l.tiles + (size_t)(sorted_cap / block_m) * 16);
+    const moe::DownArgs da = down_args(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+                                       num_tokens_post_padded, M, K, I, E, top_k, block_m,
+                                       sorted_cap, ws, l);
     const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
     st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe(da, block_m, e8, s)
                                                    : moe::launch_down(da, block_m, e8, s),
@@ -543,6 +589,35 @@ MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const u
         return fail(MOE_ERR_NULL, "all tensor arguments and the workspace are required");
     if (!aligned16(x_q) || !aligned16(w13) || !aligned16(w2) || !aligned16(out_bf16))
         return fail(MOE_ERR_ALIGN, "x_q, w13, w2 and out must be 16-byte aligned");
+    if (l.sp.fused) {
+        hipStream_t s = (hipStream_t)stream;
+        uint8_t *ws = (uint8_t *)workspace;
+        const moe::GateUpArgs ga = gateup_args(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids,
+                                               num_tokens_post_padded, M, K, I, E, top_k, block_m,
+                                               sorted_cap, flags, ws, l);
+        const moe::DownArgs da = down_args(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+                                           num_tokens_post_padded, M, K, I, E, top_k, block_m,
+                                           sorted_cap, ws, l);
+        uint32_t *c = (uint32_t *)(ws + l.cnt) + l.splitk_words;
+        const int64_t npass = block_m > 64 ? block_m / 64 : 1;
+        moe::FusedArgs f;
+        f.tickets = c;
+        f.err = c + moe::kFusedQueues;
+        f.cnt_h = c + moe::kFusedQueues + 4;
+        f.cnt_t = f.cnt_h + (sorted_cap / block_m) * npass;
+        f.out = (uint16_t *)out_bf16;
+        f.rpos = (const int32_t *)(ws + l.rpos);
+        f.M = M;
+        f.per_queue = f.lds_ticket = 0;
+        st = hip_check(moe::launch_fused_prep((uint32_t *)(ws + l.cnt), l.cnt_words,
+                                              (int32_t *)(ws + l.rpos), M * top_k, sorted_token_ids,
+                                              num_tokens_post_padded, sorted_cap, s),
+                       "moe_fp8_experts: single-launch set-up");
+        if (st != MOE_OK) return st;
+        const bool fp8 = (flags & MOE_F_FP8_GATEUP) != 0, e8 = (flags & MOE_F_MMA_E8M0) != 0;
+        return hip_check(moe::launch_fused(ga, da, f, block_m, fp8, e8, s),
+                         "moe_fp8_experts: single-launch kernel");
+    }
     st = moe_fp8_gate_up(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids, num_tokens_post_padded,
                          M, K, I, E, top_k, block_m, sorted_cap, flags, workspace, workspace_bytes,
                          stream);
@@ -597,7 +672,7 @@ MOE_API moe_status moe_fp8_experts_noalloc(const uint8_t *x_q, const float *x_s,
                                            void *out_bf16, void *stream) {
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
-    st = check_flags(flags, K, I);
+    st = check_flags(flags, K, I, block_m);
     if (st != MOE_OK) return st;
     const size_t need = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags).total;
     if (need > MOE_NOALLOC_SCRATCH_BYTES)

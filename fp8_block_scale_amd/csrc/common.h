@@ -18,6 +18,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kCacheNT = 2;                   // cache policy bits: non-temporal
+constexpr int kCacheAgent = 16;               // cache policy bits: sc1 (agent-coherent)
 constexpr float kE4M3Max = 448.0f;
 constexpr float kFltMin = 1.17549435e-38f;  // 2^-126
 
@@ -265,6 +266,27 @@ __device__ __forceinline__ v4f f16x4_to_f32x4(const uint2 &u) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const h2 a = __builtin_bit_cast(h2, u.x), b = __builtin_bit_cast(h2, u.y);
     return v4f{(float)a[0], (float)a[1], (float)b[0], (float)b[1]};
+}
+
+// ------------------------------------------- cross-workgroup hand-offs
+// Data one workgroup hands to another inside a launch (which may run on a
+// different XCD, each XCD having its own L2) moves with relaxed atomic
+// accesses at agent scope: stores write through this XCD's L2 and loads miss
+// in it, so a producer needs only its stores' completion (vmcnt) before the
+// counter bump that publishes them, and a consumer that has seen the count
+// reads current data -- no cache-wide write-back or invalidate.
+
+__device__ __forceinline__ void store_coherent(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ wave utils

@@ -1,93 +1,20 @@
-// Steps 3 + 4 for small grids (decode, few tokens per expert): gate/up
-// grouped GEMM with 128x128 FP32 weight block scales, SwiGLU, and FP8
-// requantisation of the SwiGLU output per plan row and 128-column group.
-//
-// What is computed (FlashInfer PR #4287, PR summary and public-contract
-// section): for plan row p of block b (expert e = expert_ids[b], route
-// r = sorted[p], token t = r / top_k)
-//   g[p, n] = sum_kb x_s[t, kb] * w13_s[e, n / 128, kb]
-//                    * sum_{k in kb} x_q[t, k] * W13[e, n, k]        (FP32)
-//   h[p, j] = silu(g[p, j]) * g[p, I + j],  silu(v) = v / (1 + e^-v)
-//   h_q[p, j], h_s[p, j / 128] = FP8 group quantisation of h (FP32 or
-//   power-of-two scale rule; the FLT_MIN floor keeps all-zero rows finite).
-//
-// Here the weights are the whole cost: a block holds one or two valid rows,
-// so the kernel is a weight stream.  One workgroup = one plan block (its
-// valid rows, in passes of at most 64) x one 128-wide intermediate tile
-// (128 gate rows + 128 up rows of W13) x one K-range; eight waves take 16
-// gate and the matching 16 up rows each.  The weights go through a ring of
-// one-K-block LDS stages filled by global_load_lds_dwordx4, eight lanes per
-// 128-byte row segment: every load instruction reads whole 128-byte lines.
-// (Loading the MFMA operand slices straight into registers -- 16 rows x 64
-// bytes per instruction -- streamed the same bytes about 30% slower.)  The
-// stage also carries the pass's activation rows and the K-block's scales;
-// three or four stages are in flight per workgroup.
-//
-// The MMA is the 16x16 tile with weights as the A operand (16 rows) and
-// tokens as B (16 columns); lane (l % 16, l / 16) ends with four consecutive
-// rows of one token.  Three MMA modes:
-//   kExact  (default) E4M3 codes widened exactly to FP16 in registers and
-//           multiplied with v_mfma_f32_16x16x32_f16 (exact products, FP32
-//           accumulation);
-//   kFp8    v_mfma_f32_16x16x128_f8f6f4 on the codes directly;
-//   kFp8E8  as kFp8 with power-of-two scales applied inside the MFMA.
-//
-// K is split over workgroups; each writes the partial sums of its valid rows
-// to the workspace and the last one of a tile to arrive (atomic counter)
-// adds them in split order -- deterministic -- and finishes the tile.
+// Steps 3 + 4 for small grids (decode, few tokens per expert): one
+// workgroup per gate/up work item of gateup_item.h (plan block, row pass,
+// j-tile, K-split).
 #include <type_traits>
 
-#include "common.h"
-#include "internal.h"
+#include "gateup_item.h"
 
 namespace moe {
 
 namespace {
 
-enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
-
-template <int BM>
-struct GSCfg {
-    static constexpr int RP = BM < 64 ? BM : 64;   // plan rows per pass
-    static constexpr int NPASS = BM / RP;
-    static constexpr int NU = RP / 16;             // 16-token subtiles
-    static constexpr int NT = 512;                 // eight waves
-    static constexpr int GROW = 260;               // row stride of the FP32 tile
-    // LDS: a ring of NS stages {W13 tile 256 x 128 B, activation rows RP x
-    // 128 B, scales: a 16-float run per wave}, reused after the K loop as the
-    // FP32 tile [RP][GROW]; then routes, row tokens, a DMA sink, flags.
-    static constexpr int NS = RP <= 32 ? 4 : 3;
-    static constexpr int WB = 256 * 128;
-    static constexpr int XB = RP * 128;
-    static constexpr int SB = 8 * 16 * 4;
-    static constexpr int STB = WB + XB + SB;
-    static constexpr int RING = NS * STB;
-    static constexpr int GT = RP * GROW * 4;
-    static constexpr int TOK = RING > GT ? RING : GT;
-    static constexpr int XT = TOK + RP * 4;
-    static constexpr int SINK = XT + RP * 4;
-    static constexpr int MISC = SINK + 8 * 256;
-    static constexpr int TOTAL = MISC + 16;
-    static constexpr int NPS = 6;                  // DMA instructions per wave per stage
-};
+using namespace gs;
 
 template <int BM, int MODE>
 __global__ void __launch_bounds__(512)
 gateup_stream_kernel(GateUpArgs a) {
-    using C = GSCfg<BM>;
-    static_assert(C::TOTAL <= 160 * 1024, "LDS budget");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    float *sG = reinterpret_cast<float *>(smem);    // reuses the ring after the loop
-    int *sTok = reinterpret_cast<int *>(smem + C::TOK);    // route of each row, -1 if none
-    int *sXt = reinterpret_cast<int *>(smem + C::XT);      // token whose x row fills the row
-    uint8_t *sSink = smem + C::SINK;
-    int *sMisc = reinterpret_cast<int *>(smem + C::MISC);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, g = lane >> 4;
-
     int L = blockIdx.x;
     const int b = L % a.nblocks;
     L /= a.nblocks;
@@ -95,264 +22,7 @@ gateup_stream_kernel(GateUpArgs a) {
     L /= a.nsplit;
     const int jt = L % a.jtiles;
     const int pass = L / a.jtiles;
-    const int row0 = pass * C::RP;
-
-    // the plan entries of this pass (every entry below sorted_cap is
-    // readable); the block's expert only once the block is known to lie
-    // below P (expert_ids may be sized by the plan's blocks_cap)
-    int r = -1;
-    if (w == 0 && lane < C::RP) r = a.sorted[(int64_t)b * BM + row0 + lane];
-    const int ntp = a.ntp[0];
-    if (b * BM >= ntp) return;                          // padded block
-    const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors
-    if (e < 0 || e >= a.E) return;
-
-    // this pass's routes (wave 0), the valid-row extent, the inverse plan map
-    if (w == 0) {
-        if (lane < C::RP) {
-            r = (r >= 0 && (int64_t)r < a.R) ? r : -1;
-            sTok[lane] = r;
-            if (r >= 0 && jt == 0 && split == 0) a.rpos[r] = b * BM + row0 + lane;
-        }
-        const uint64_t m = __ballot(r >= 0);
-        const int nv = m ? 64 - __builtin_clzll(m) : 0;
-        const int t = r >= 0 ? r / a.top_k : -1;
-        const int tlast = __shfl(t, nv > 0 ? nv - 1 : 0, 64);
-        if (lane < C::RP) sXt[lane] = t >= 0 ? t : tlast;
-        if (lane == 0) sMisc[0] = nv;
-    }
-    __syncthreads();
-    const int nvp = sMisc[0];                   // rows [0, nvp) hold every valid row
-    if (nvp == 0) return;                       // whole pass masked (same for all splits)
-    const int nvpad = (nvp + 15) & ~15;
-
-    const int kb0 = split * a.kb_per_split;
-    const int kb1 = kb0 + a.kb_per_split < a.nkb ? kb0 + a.kb_per_split : a.nkb;
-    const int nk = kb1 - kb0;
-    if (nk <= 0) return;
-    const int64_t K = a.K, I = a.I;
-
-    // ---- DMA sources of this lane.  Every wave issues NPS instructions per
-    // stage (the waits count on it): four W13 segments (8 rows x 128 B each,
-    // 16-byte chunks XOR-swizzled by row & 7), one activation segment (rows
-    // 8w.., waves w < RP / 8; the others a 4-byte load into a sink), and one
-    // scale load (lanes 0-7: x_s of rows 8w..; lanes 8, 9: the gate and up
-    // weight-block scales).  Masked and padding rows read the last valid
-    // row's token (sXt); their columns are never stored.
-    const int sub = lane >> 3, slot = lane & 7;
-    const uint8_t *wsrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (w * 4 + i) * 8 + sub;                  // tile row 0..255
-        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
-        wsrc[i] = a.w13 + ((int64_t)e * 2 * I + n) * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
-    }
-    const bool xw = w < C::RP / 8;
-    const uint8_t *xsrc;
-    {
-        const int row = xw ? 8 * w + sub : 0;
-        xsrc = a.xq + (int64_t)sXt[row] * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
-    }
-    const float *ssrc;
-    if (lane < 8) {
-        const int row = 8 * w + lane < C::RP ? 8 * w + lane : 0;
-        ssrc = a.xs + (int64_t)sXt[row] * a.nkb + kb0;
-    } else {
-        const int nb13 = (int)(2 * I / 128);
-        ssrc = a.w13s + ((int64_t)e * nb13 + (lane == 9 ? (int)(I / 128) : 0) + jt) * a.nkb + kb0;
-    }
-    // An expert with this one plan block streams its W13 tile exactly once:
-    // those loads take the non-temporal policy (6.6 against 5.9 TB/s on a
-    // 411 MB slab stream); experts with several blocks keep theirs cacheable,
-    // for the other blocks' workgroups to find in L2.
-    const bool once = (b == 0 || a.eids[b - 1] != e) &&
-                      ((int64_t)(b + 1) * BM >= ntp || a.eids[b + 1] != e);
-    auto issue = [&](int st, int kbl) {
-        uint8_t *base = smem + st * C::STB;
-        if (once) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16_nt(wsrc[i] + kbl * 128, base + (w * 4 + i) * 1024);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(wsrc[i] + kbl * 128, base + (w * 4 + i) * 1024);
-        }
-        if (xw)
-            lds_dma16(xsrc + kbl * 128, base + C::WB + w * 1024);
-        else
-            lds_dma4(xsrc + kbl * 128, sSink + w * 256);
-        if (lane < 10) lds_dma4(ssrc + kbl, base + C::WB + C::XB + w * 64);
-    };
-
-    v4f accg[C::NU], accu[C::NU];
-#pragma unroll
-    for (int u = 0; u < C::NU; ++u) {
-        accg[u] = v4f{0.f, 0.f, 0.f, 0.f};
-        accu[u] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-
-    auto compute = [&](int st) {
-        const uint8_t *Ws = smem + st * C::STB;
-        const uint8_t *Xs = Ws + C::WB;
-        const float *Ss = reinterpret_cast<const float *>(Ws + C::WB + C::XB);
-        const float sg = Ss[8], su = Ss[9];     // wave 0's run
-        u32x4 wlo[2], whi[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 128 * h + 16 * w + l16;
-            const uint8_t *rp = Ws + row * 128;
-            wlo[h] = lds_read16(rp + ((g ^ (row & 7)) << 4));
-            whi[h] = lds_read16(rp + (((4 + g) ^ (row & 7)) << 4));
-        }
-        v8h Wg[4], Wu[4];
-        if constexpr (MODE == kExact) {
-            e4m3x32_to_f16(wlo[0], whi[0], Wg);
-            e4m3x32_to_f16(wlo[1], whi[1], Wu);
-        }
-#pragma unroll
-        for (int u = 0; u < C::NU; ++u) {
-            if (16 * u >= nvp) break;
-            const int row = 16 * u + l16;
-            const uint8_t *xp = Xs + row * 128;
-            const u32x4 lo = lds_read16(xp + ((g ^ (row & 7)) << 4));
-            const u32x4 hi = lds_read16(xp + (((4 + g) ^ (row & 7)) << 4));
-            const float sa = Ss[(row >> 3) * 16 + (row & 7)];
-            if constexpr (MODE == kExact) {
-                v8h Bh[4];
-                e4m3x32_to_f16(lo, hi, Bh);
-                const v4f tg = mfma16x16x128_f16(Wg, Bh);
-                const v4f tu = mfma16x16x128_f16(Wu, Bh);
-                accg[u] = tg * (sa * sg) + accg[u];
-                accu[u] = tu * (sa * su) + accu[u];
-            } else {
-                const v8i B = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                const v8i Ag = {(int)wlo[0].x, (int)wlo[0].y, (int)wlo[0].z, (int)wlo[0].w,
-                                (int)whi[0].x, (int)whi[0].y, (int)whi[0].z, (int)whi[0].w};
-                const v8i Au = {(int)wlo[1].x, (int)wlo[1].y, (int)wlo[1].z, (int)wlo[1].w,
-                                (int)whi[1].x, (int)whi[1].y, (int)whi[1].z, (int)whi[1].w};
-                if constexpr (MODE == kFp8E8) {
-                    const int eb = e8m0_of(sa);
-                    accg[u] = mfma16x16x128_e8m0(Ag, B, accg[u], e8m0_of(sg), eb);
-                    accu[u] = mfma16x16x128_e8m0(Au, B, accu[u], e8m0_of(su), eb);
-                } else {
-                    accg[u] = mfma16x16x128(Ag, B) * (sa * sg) + accg[u];
-                    accu[u] = mfma16x16x128(Au, B) * (sa * su) + accu[u];
-                }
-            }
-        }
-    };
-
-    // Ring: stages 0 .. NS-2 up front; step kb waits for its stage (loads
-    // complete in issue order, so only the later stages already issued may
-    // still be in flight), then a barrier makes the stage visible and frees
-    // the slot of kb - 1 for the refill of kb + NS - 1.
-#pragma unroll
-    for (int s0 = 0; s0 < C::NS - 1; ++s0)
-        if (s0 < nk) issue(s0, s0);
-    for (int kb = 0; kb < nk; ++kb) {
-        const int ahead = nk - 1 - kb;
-        if (C::NS > 3 && ahead >= 2)
-            wait_vmcnt<(C::NS > 3 ? 2 : 1) * C::NPS>();
-        else if (ahead >= 1)
-            wait_vmcnt<C::NPS>();
-        else
-            wait_vmcnt<0>();
-        stage_barrier();
-        if (kb + C::NS - 1 < nk) issue((kb + C::NS - 1) % C::NS, kb + C::NS - 1);
-        compute(kb % C::NS);
-    }
-
-    // ---- FP32 tile of the pass: sG[row][n], gate n < 128, up n >= 128
-    __syncthreads();                            // every wave is done with the x tile
-#pragma unroll
-    for (int u = 0; u < C::NU; ++u) {
-        if (16 * u >= nvp) break;
-        float *gp = sG + (16 * u + l16) * C::GROW + 16 * w + 4 * g;
-        *reinterpret_cast<v4f *>(gp) = accg[u];
-        *reinterpret_cast<v4f *>(gp + 128) = accu[u];
-    }
-    __syncthreads();
-
-    if (a.nsplit > 1) {
-        // Partial sums travel through memory with agent-coherent accesses
-        // (sc1: stores write through this XCD's L2, loads miss in it), so the
-        // hand-off needs only the stores' completion before the counter
-        // bump -- no cache-wide write-back or invalidate.
-        const int tile = jt * a.nblocks + b;
-        const int sstride = BM * 256 * 4;       // bytes between splits
-        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.part + (size_t)tile * a.nsplit * BM * 256 + (size_t)row0 * 256), (short)0,
-            a.nsplit * sstride, 0x00020000);
-        constexpr int kAgent = 16;              // cache policy: sc1
-        for (int idx = tid; idx < nvp * 64; idx += C::NT) {
-            const int row = idx >> 6, c4 = idx & 63;
-            if (sTok[row] >= 0)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    *reinterpret_cast<const u32x4 *>(sG + row * C::GROW + 4 * c4), rp,
-                    split * sstride + (row * 256 + 4 * c4) * 4, 0, kAgent);
-        }
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (tid == 0) {
-            const unsigned old = __hip_atomic_fetch_add(&a.cnt[tile * C::NPASS + pass], 1u,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sMisc[1] = old == (unsigned)(a.nsplit - 1);
-        }
-        __syncthreads();
-        if (!sMisc[1]) return;
-        for (int idx = tid; idx < nvp * 64; idx += C::NT) {
-            const int row = idx >> 6, c4 = idx & 63;
-            if (sTok[row] < 0) continue;
-            const int off = (row * 256 + 4 * c4) * 4;
-            v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 0; s0 < a.nsplit; s0 += 16) {
-                u32x4 v[16];
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    if (s0 + q < a.nsplit)
-                        v[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, (s0 + q) * sstride + off, 0, kAgent);
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    if (s0 + q < a.nsplit) {
-                        sum.x += __uint_as_float(v[q].x);
-                        sum.y += __uint_as_float(v[q].y);
-                        sum.z += __uint_as_float(v[q].z);
-                        sum.w += __uint_as_float(v[q].w);
-                    }
-            }
-            *reinterpret_cast<v4f *>(sG + row * C::GROW + 4 * c4) = sum;
-        }
-        __syncthreads();
-    }
-
-    // ---- SwiGLU + per-row 128-group FP8 requantisation: 32 lanes per row
-    const bool ue = a.inter_ue8m0 != 0;
-    for (int base = 0; base < nvpad * 32; base += C::NT) {
-        const int idx = base + tid;
-        const int row = idx >> 5, q = idx & 31;
-        const float *gp = sG + row * C::GROW + 4 * q;
-        const v4f gv = *reinterpret_cast<const v4f *>(gp);
-        const v4f uv = *reinterpret_cast<const v4f *>(gp + 128);
-        float h[4], amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            h[i] = swiglu(gv[i], uv[i]);
-            amax = fmaxf(amax, fabsf(h[i]));
-        }
-        amax = wave_max_xor(amax, 1);
-        amax = wave_max_xor(amax, 2);
-        amax = wave_max_xor(amax, 4);
-        amax = wave_max_xor(amax, 8);
-        amax = wave_max_xor(amax, 16);
-        float s, inv;
-        group_scale(amax, ue, s, inv);
-        if (row < nvp && sTok[row] >= 0) {
-            const int64_t p = (int64_t)b * BM + row0 + row;
-            *reinterpret_cast<uint32_t *>(a.hq + p * I + (int64_t)jt * 128 + 4 * q) =
-                pack_e4m3x4(h[0] * inv, h[1] * inv, h[2] * inv, h[3] * inv);
-            if (q == 0) a.hs[p * (I >> 7) + jt] = s;
-        }
-    }
+    gateup_item<BM, MODE, 0, false>(a, smem, b, split, jt, pass, nullptr);
 }
 
 template <int BM, int MODE>

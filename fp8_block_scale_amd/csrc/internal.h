@@ -120,6 +120,26 @@ struct DownArgs {
     int nct;            // column tiles per workgroup (small-grid kernel; set by its launcher)
 };
 
+// The single-launch expert kernel (fused.hip).  Its workgroups take tickets
+// from kFusedQueues counters: queue q owns the plan blocks b = q (mod
+// kFusedQueues) and hands out, in ticket order, their gate/up items, then
+// their down items.  A down item waits only for gate/up items of its own
+// block -- lower tickets of its own queue, held by workgroups that have
+// started and never wait -- so every wait ends.  The route map is complete
+// before the launch (launch_fused_prep), and all counters start at zero.
+constexpr int kFusedQueues = 16;
+struct FusedArgs {
+    uint32_t *tickets;     // [kFusedQueues] next ticket per queue
+    uint32_t *cnt_h;       // [nblocks * passes] j-tiles whose intermediate rows are written
+    uint32_t *cnt_t;       // [M * ctiles] route rows of (token, 256-column tile) in y
+    uint32_t *err;         // [1] set if a bounded wait gave up (never, on a valid schedule)
+    uint16_t *out;         // BF16 [M, K], accumulated into
+    const int32_t *rpos;   // route -> plan row (-1: masked), built before the launch
+    int64_t M;
+    int per_queue;         // tickets per queue (gate/up + down items of its blocks)
+    int lds_ticket;        // byte offset of the ticket slot in dynamic LDS (after the items' use)
+};
+
 // fp8_mma: FP8 MFMA instead of the exact FP16-widened product path;
 // e8m0: (with fp8_mma) power-of-two scales applied inside the MFMA.
 // Small-grid gate/up (weight stream, split-K); kb_per_split must not exceed
@@ -139,6 +159,19 @@ hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bo
 hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
 // Large-grid down GEMM: persistent, over the gate/up stage's row tiles.
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
+// The single-launch path (fused.hip): steps 3-5 over the arguments of both
+// stages.  Needs I / 128 <= fused_max_njb(block_m).
+int fused_max_njb(int block_m);
+// counter words the single-launch path needs (the queue tickets and the
+// error flag, then cnt_h, then cnt_t)
+size_t fused_counter_words(int64_t nblocks, int block_m, int64_t M, int64_t ctiles);
+// Its set-up launch (one workgroup): cnt[0, n_cnt) = 0, rpos[0, R) = -1, then
+// rpos[sorted[p]] = p for the plan's valid rows.
+hipError_t launch_fused_prep(uint32_t *cnt, size_t n_cnt, int32_t *rpos, int64_t R,
+                             const int32_t *sorted, const int32_t *ntp, int64_t sorted_cap,
+                             hipStream_t st);
+hipError_t launch_fused(const GateUpArgs &ga, const DownArgs &da, const FusedArgs &f, int block_m,
+                        bool fp8_mma, bool e8m0, hipStream_t st);
 // rpos[0, n_rpos) = -1 and cnt[0, n_cnt) = 0 in one launch.
 hipError_t launch_prep(uint32_t *rpos, size_t n_rpos, uint32_t *cnt, size_t n_cnt, hipStream_t st);
 hipError_t launch_fill(uint32_t *p, size_t n_words, uint32_t value, hipStream_t st);

@@ -115,6 +115,23 @@ enum {
 #define MOE_F_DOWN_PATH_SHIFT   18
 #define MOE_F_DOWN_PATH_MASK    0xC0000u
 enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_PERSISTENT = 2 };
+/* Bits 20..21 choose how moe_fp8_experts launches steps 3-5:
+ *   MOE_FUSE_AUTO (0) the library's choice: currently always two stages
+ *                     (the single launch measured slower on MI355X at every
+ *                     size tried);
+ *   MOE_FUSE_OFF  (1) the gate/up and the down stage as separate launches,
+ *                     exactly moe_fp8_gate_up then moe_fp8_down_reduce;
+ *   MOE_FUSE_ON   (2) one launch for gate/up, SwiGLU + requantisation, down
+ *                     and the route sum (after a small set-up fill), as in
+ *                     PR #4287's single fused expert kernel (PR summary);
+ *                     needs the per-block family for both stages and
+ *                     I / 128 <= 512 / min(block_m, 64), else
+ *                     MOE_ERR_UNSUPPORTED.
+ * The single launch computes what the two stages compute, item for item:
+ * the output is bit-identical.  The stage calls always run separately. */
+#define MOE_F_FUSE_SHIFT 20
+#define MOE_F_FUSE_MASK  0x300000u
+enum { MOE_FUSE_AUTO = 0, MOE_FUSE_OFF = 1, MOE_FUSE_ON = 2 };
 
 /* ---------------------------------------------------------------- plan -- */
 
@@ -196,8 +213,9 @@ moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int
 /* The launch schedule moe_fp8_experts would use for these sizes and flags
  * (host only, nothing enqueued): info[0] = 1 if the gate/up stage runs the
  * persistent kernel, info[1] = 1 if the down stage does, info[2] = the
- * gate/up split-K factor, info[3] = K-blocks (of 128) per split.  info is
- * host memory of 4 int32.  Errors: as moe_fp8_experts_workspace_size's
+ * gate/up split-K factor, info[3] = K-blocks (of 128) per split, info[4] =
+ * 1 if steps 3-5 run as the single launch.  info is host memory of 5
+ * int32.  Errors: as moe_fp8_experts_workspace_size's
  * shape checks (MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED), MOE_ERR_NULL. */
 moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
                                     int32_t block_m, int64_t sorted_cap, uint32_t flags,

@@ -260,7 +260,12 @@ def test_tiny_accumulates_into_prefilled_output():
     full_parity(cs, out_init=init, label="prefilled out")
 
 
-@pytest.mark.parametrize("flags", [0, 1 << moe.MOE_F_SPLITK_SHIFT, 7 << moe.MOE_F_SPLITK_SHIFT])
+FUSE_ON = moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT
+FUSE_OFF = moe.MOE_FUSE_OFF << moe.MOE_F_FUSE_SHIFT
+
+
+@pytest.mark.parametrize("flags", [0, 1 << moe.MOE_F_SPLITK_SHIFT, 7 << moe.MOE_F_SPLITK_SHIFT,
+                                   FUSE_OFF, FUSE_OFF | (7 << moe.MOE_F_SPLITK_SHIFT)])
 def test_decode_full(flags):
     full_parity(case_of("decode"), flags=flags, label="decode")
 
@@ -299,13 +304,14 @@ PERSIST = ((moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT)
            | (moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT))
 
 
-@pytest.mark.parametrize("name,M,flags", [("decode", None, 0), ("page1", 512, 0),
-                                          ("page1", 512, PERSIST)])
+@pytest.mark.parametrize("name,M,flags", [("decode", None, 0), ("decode", 16, FUSE_ON),
+                                          ("page1", 512, 0), ("page1", 512, PERSIST)])
 def test_graph_replay_matches_eager(name, M, flags):
-    """The whole layer captured in a HIP graph (small-grid kernels for decode;
-    at M=512 the per-block gate/up with the persistent down, then both
-    persistent kernels): every replay, with eager work and synchronisations
-    between replays, gives the eager output bit for bit."""
+    """The whole layer captured in a HIP graph (small-grid kernels for decode,
+    and steps 3-5 as one launch at decode M=16; at M=512 the per-block
+    gate/up with the persistent down, then both persistent kernels): every
+    replay, with eager work and synchronisations between replays, gives the
+    eager output bit for bit."""
     cs = case_of(name, M=M)
     log(f"[graph] {name} M={cs.M} flags={flags:#x}")
     b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, flags, DEV)
@@ -393,10 +399,11 @@ def test_max_experts(flags):
 @pytest.mark.parametrize("gu,dn", [(1, 1), (1, 2), (2, 1), (2, 2)])
 def test_kernel_path_combinations(gu, dn):
     """Every pairing of the per-block (1) and persistent (2) kernel families
-    of the two stages on one input: the down stage's row tiles come from the
-    gate/up stage whichever kernel it runs."""
+    of the two stages, as two launches, on one input: the down stage's row
+    tiles come from the gate/up stage whichever kernel it runs."""
     cs = case_of("page1", M=256)
-    flags = (gu << moe.MOE_F_GATEUP_PATH_SHIFT) | (dn << moe.MOE_F_DOWN_PATH_SHIFT)
+    flags = ((gu << moe.MOE_F_GATEUP_PATH_SHIFT) | (dn << moe.MOE_F_DOWN_PATH_SHIFT)
+             | (moe.MOE_FUSE_OFF << moe.MOE_F_FUSE_SHIFT))
     cap = moe.moe_plan_capacity(cs.M, cs.top_k, cs.E, cs.block_m)[0]
     sched = moe.moe_fp8_experts_schedule(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, cap, flags)
     assert sched[0] == (gu == 2) and sched[1] == (dn == 2)
@@ -485,6 +492,46 @@ def test_zipf_full_size_sampled(flags):
     cs = case_of("zipf")
     full_parity(cs, flags=flags, act_mode=SCALE_UE8M0, tokens=_cover_tokens(cs, 6, 4),
                 label="zipf full size")
+
+
+# ------------------------------------------------- steps 3-5 in one launch
+# MOE_FUSE_ON: one launch runs the per-block gate/up items, the down items
+# (which wait for their block's intermediate rows) and the route sum (by the
+# item completing a (token, tile)).  Parity against the oracle on all five
+# workloads, and the output bit-identical to the two-launch path.
+
+@pytest.mark.parametrize("name,M,flags,cover", [
+    ("tiny", None, 0, False), ("decode", None, 0, False), ("decode", 2, 0, False),
+    ("decode", 16, 7 << moe.MOE_F_SPLITK_SHIFT, False), ("page1", 24, 0, False),
+    ("page1", None, 0, True), ("skew", None, 0, True),
+    ("zipf", None, moe.MOE_F_INTER_UE8M0, True), ("zipf", None, E8, True)])
+def test_single_launch(name, M, flags, cover):
+    cs = case_of(name, M=M)
+    act = SCALE_UE8M0 if flags & moe.MOE_F_INTER_UE8M0 else SCALE_FP32
+    cap = moe.moe_plan_capacity(cs.M, cs.top_k, cs.E, cs.block_m)[0]
+    assert moe.moe_fp8_experts_schedule(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, cap,
+                                        flags | FUSE_ON)[4]
+    tokens = _cover_tokens(cs, 6, 40) if cover else None
+    g, o, _ = full_parity(cs, flags=flags | FUSE_ON, act_mode=act, tokens=tokens,
+                          label="single launch")
+    two = run_gpu(cs, flags=flags | FUSE_OFF, act_mode=act)
+    assert np.array_equal(g.out, two.out), "single launch differs from the two launches"
+    rows = o.res.row_valid if tokens is None else (two.sorted[:two.P] < cs.M * cs.top_k)
+    assert np.array_equal(g.h_q[:g.P][rows], two.h_q[:two.P][rows])
+
+
+def test_single_launch_repeat_and_masked():
+    """Bit-identical repeat runs of the single launch on the skew workload
+    (masked routes, duplicate experts in a token, a zero-scale expert), and
+    an all-masked batch leaving the output untouched."""
+    cs = case_of("skew", M=96)
+    a = run_gpu(cs, flags=FUSE_ON)
+    b = run_gpu(cs, flags=FUSE_ON)
+    assert np.array_equal(a.out, b.out)
+    cs.topk_ids = torch.full_like(cs.topk_ids, -1)
+    init = torch.randn((cs.M, cs.K), device=DEV).to(torch.bfloat16)
+    g = run_gpu(cs, out_init=init, flags=FUSE_ON)
+    assert g.P == 0 and np.array_equal(g.out, init.float().cpu().numpy())
 
 
 # ------------------------------------------------ FP8-MFMA gate/up mode

@@ -110,7 +110,8 @@ def test_experts_validation():
     assert _err(call(bm=48)) == "MOE_ERR_UNSUPPORTED"
     assert _err(call(sc=120)) == "MOE_ERR_SHAPE"
     assert _err(call(fl=moe.MOE_F_MMA_E8M0)) == "MOE_ERR_SHAPE"
-    assert _err(call(fl=1 << 20)) == "MOE_ERR_SHAPE"
+    assert _err(call(fl=1 << 24)) == "MOE_ERR_SHAPE"                          # unknown bit
+    assert _err(call(fl=3 << moe.MOE_F_FUSE_SHIFT)) == "MOE_ERR_SHAPE"        # fuse choice 3
     assert _err(call(wsb=16)) == "MOE_ERR_CAPACITY"
     assert _err(call(ws=None)) == "MOE_ERR_NULL"
     assert _err(call(ws=ctypes.c_void_p(0x10010))) == "MOE_ERR_ALIGN"
@@ -152,14 +153,22 @@ def test_experts_schedule():
     # one round with the plan blocks expected under uniform routing: M=1
     # (~9 blocks x 2 column tiles) 10 ways of 6 K-blocks, M=4 (~34 blocks)
     # 3 ways, M=16 (~112 blocks) no split
-    assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, False, 10, 6)
-    assert sched(4, 7168, 256, 257, 9, 16, 576)[2:] == (3, 19)
+    assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, False, 10, 6, False)
+    assert sched(4, 7168, 256, 257, 9, 16, 576)[2:4] == (3, 19)
     assert sched(16, 7168, 256, 257, 9, 16, 2304)[2] == 1
     # page-1 M=16 and M=1024: per-block gate/up, persistent down
     assert sched(16, 4096, 1024, 288, 8, 64, 8192)[:2] == (False, True)
     assert sched(1024, 4096, 1024, 288, 8, 64, 26368)[:2] == (False, True)
-    # page-1 M=4096 (the bench configuration): both persistent, no split
-    assert sched(4096, 4096, 1024, 288, 8, 64, 50944) == (True, True, 1, 32)
+    # page-1 M=4096 (the bench configuration): both persistent, no split, two launches
+    assert sched(4096, 4096, 1024, 288, 8, 64, 50944) == (True, True, 1, 32, False)
+    # steps 3-5 as one launch: only on request (the fuse field)
+    FU = moe.MOE_F_FUSE_SHIFT
+    assert sched(16, 7168, 256, 257, 9, 16, 2304)[4] is False
+    assert sched(16, 7168, 256, 257, 9, 16, 2304, moe.MOE_FUSE_ON << FU)[4] is True
+    assert sched(16, 7168, 256, 257, 9, 16, 2304, moe.MOE_FUSE_OFF << FU)[4] is False
+    assert sched(4096, 4096, 1024, 288, 8, 64, 50944, moe.MOE_FUSE_ON << FU)[:2] == (False, False)
+    assert sched(4096, 4096, 1024, 288, 8, 64, 50944, moe.MOE_FUSE_ON << FU)[4] is True
+    assert sched(16, 4096, 1024, 288, 8, 64, 8192)[4] is False       # persistent down stage
     # overrides
     assert sched(16, 4096, 1024, 288, 8, 64, 8192, 2 << GU)[:2] == (True, True)
     assert sched(16, 4096, 1024, 288, 8, 64, 8192, 1 << DN)[:2] == (False, False)
@@ -168,12 +177,16 @@ def test_experts_schedule():
     assert sched(4096, 4096, 1024, 288, 8, 64, 50944, 2 << moe.MOE_F_SPLITK_SHIFT)[0] is False
     for bad, status in ((3 << GU, "MOE_ERR_SHAPE"), (3 << DN, "MOE_ERR_SHAPE"),
                         ((2 << GU) | (2 << moe.MOE_F_SPLITK_SHIFT), "MOE_ERR_SHAPE"),
-                        (1 << 24, "MOE_ERR_SHAPE")):
+                        (1 << 24, "MOE_ERR_SHAPE"), (3 << FU, "MOE_ERR_SHAPE"),
+                        ((2 << FU) | (2 << DN), "MOE_ERR_SHAPE")):
         with pytest.raises(moe.MoeError) as ei:
             sched(16, 4096, 1024, 288, 8, 64, 8192, bad)
         assert moe.STATUS_NAMES[ei.value.status] == status
     with pytest.raises(moe.MoeError):       # the persistent kernels need K <= 32768
         sched(16, 65536, 1024, 288, 8, 64, 8192, 2 << DN)
+    with pytest.raises(moe.MoeError) as ei:  # the single launch's down rows fit in LDS
+        sched(16, 4096, 8192, 288, 8, 64, 8192, moe.MOE_FUSE_ON << FU)
+    assert moe.STATUS_NAMES[ei.value.status] == "MOE_ERR_UNSUPPORTED"
 
 
 def test_plan_quant_validation():
