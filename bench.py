@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--workload", default="page1",
                     choices=["tiny", "decode", "page1", "skew", "zipf"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
+    ap.add_argument("--block-m", type=int, default=None, help="override the plan block size")
     ap.add_argument("--fp8-gateup", action="store_true",
                     help="gate/up on the FP8 MFMA (MOE_F_FP8_GATEUP)")
     ap.add_argument("--e8m0", action="store_true",
@@ -213,7 +214,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.time()
-    case = make_case(args.workload, M=args.M, device=dev)
+    config = None
+    if args.block_m is not None:
+        from moe_workloads import CONFIGS
+        config = dict(CONFIGS[args.workload], block_m=args.block_m)
+    case = make_case(args.workload, M=args.M, device=dev, config=config)
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 

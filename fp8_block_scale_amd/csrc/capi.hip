@@ -43,7 +43,7 @@ int64_t plan_sorted_cap(int64_t M, int32_t top_k, int32_t E, int32_t bm) {
     return (n + bm - 1) / bm * bm;
 }
 
-bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+bool valid_block_m(int32_t bm) { return bm == 8 || bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
 // Kernel families and the gate/up work split.  The persistent kernels walk
 // 128-row tiles of one expert (the row-tile list, built in the gate/up
@@ -165,7 +165,7 @@ moe_status check_experts_shape(int64_t M, int64_t K, int64_t I, int32_t E, int32
         return fail(MOE_ERR_SHAPE, "K (%lld) and I (%lld) must be multiples of 128",
                     (long long)K, (long long)I);
     if (!valid_block_m(block_m))
-        return fail(MOE_ERR_UNSUPPORTED, "block_m %d not in {16, 32, 64, 128}", block_m);
+        return fail(MOE_ERR_UNSUPPORTED, "block_m %d not in {8, 16, 32, 64, 128}", block_m);
     if (sorted_cap < 0 || sorted_cap % block_m != 0)
         return fail(MOE_ERR_SHAPE, "sorted_cap must be a non-negative multiple of block_m");
     if (M * top_k >= (int64_t)1 << 31)

@@ -33,8 +33,9 @@ using namespace ds;
 
 template <int BM>
 struct DNCfg {
-    static constexpr int TM = BM < 64 ? BM : 64;
-    static constexpr int WM = BM / TM;
+    static constexpr int TM = BM < 16 ? 16 : (BM < 64 ? BM : 64);   // MFMA rows per wave row
+    static constexpr int WM = BM > TM ? BM / TM : 1;
+    static constexpr int ROWS = TM * WM;           // tile rows (block_m = 8: 8 masked)
     static constexpr int NW = 4 * WM;
     static constexpr int NT = 64 * NW;
     static constexpr int NU = TM / 16;
@@ -54,9 +55,9 @@ template <int BM, bool E8M0>
 __global__ void __launch_bounds__(DNCfg<BM>::NT)
 down_kernel(DownArgs a) {
     using C = DNCfg<BM>;
-    __shared__ __attribute__((aligned(16))) uint8_t sH[2][BM * C::ROWB];
-    __shared__ float sHs[2][BM];
-    __shared__ int sRt[BM];
+    __shared__ __attribute__((aligned(16))) uint8_t sH[2][C::ROWS * C::ROWB];
+    __shared__ float sHs[2][C::ROWS];
+    __shared__ int sRt[C::ROWS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,9 +73,10 @@ down_kernel(DownArgs a) {
     const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors
     if (e < 0 || e >= a.E) return;
 
-    if (tid < BM) {
-        int r = a.sorted[(int64_t)b * BM + tid];
+    if (tid < C::ROWS) {
+        int r = tid < BM ? a.sorted[(int64_t)b * BM + tid] : -1;
         sRt[tid] = (r >= 0 && (int64_t)r < a.R) ? r : -1;
+        if (tid >= BM) sHs[0][tid] = sHs[1][tid] = 0.f;   // rows past the block: scale 0
     }
     __syncthreads();
 
@@ -260,6 +262,7 @@ hipError_t launch_ds(DownArgs a, hipStream_t st) {
 
 hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st) {
     switch (block_m) {
+        case 8: return e8m0 ? launch_ds<8, true>(a, st) : launch_ds<8, false>(a, st);
         case 16: return e8m0 ? launch_ds<16, true>(a, st) : launch_ds<16, false>(a, st);
         case 32: return e8m0 ? launch_ds<32, true>(a, st) : launch_ds<32, false>(a, st);
         case 64: return e8m0 ? launch_ds<64, true>(a, st) : launch_ds<64, false>(a, st);

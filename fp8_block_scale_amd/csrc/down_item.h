@@ -109,8 +109,11 @@ __device__ __forceinline__ bool wait_count(uint32_t *c, uint32_t target, uint32_
 // the router probability, after the loop.
 template <int BM>
 struct DSCfg {
-    static constexpr int RP = BM < 64 ? BM : 64;   // plan rows per pass
-    static constexpr int NPASS = BM / RP;
+    // A pass is one MFMA row tile of RP rows (16..64) holding RPV plan rows
+    // of the block (block_m = 8: the block's 8 rows, then 8 masked rows).
+    static constexpr int RP = BM < 16 ? 16 : (BM < 64 ? BM : 64);
+    static constexpr int RPV = BM < RP ? BM : RP;
+    static constexpr int NPASS = BM > RP ? BM / RP : 1;
     static constexpr int NU = RP / 16;
     static constexpr int NT = 512;
     static constexpr int S = 2;                    // units per stage
@@ -171,7 +174,7 @@ __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int 
     const int nct = a.ctiles - ct0 < a.nct ? a.ctiles - ct0 : a.nct;
 
     int r = -1;
-    if (w == 0 && lane < C::RP) r = a.sorted[(int64_t)b * BM + row0 + lane];
+    if (w == 0 && lane < C::RPV) r = a.sorted[(int64_t)b * BM + row0 + lane];
     const int ntp = a.ntp[0];
     if (b * BM >= ntp) return;                          // padded block
     const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors
@@ -247,7 +250,10 @@ __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int 
             }
         }
         static_assert(C::RP * C::JMAX <= C::NT, "one row scale per thread");
-        for (int q = w; q < nvpad * ipr; q += C::NT / 64) {
+        // rows past the block's own (block_m = 8) are never read from the
+        // workspace: they belong to the next block, or lie past the plan
+        const int nvdma = nvpad < C::RPV ? nvpad : C::RPV;
+        for (int q = w; q < nvdma * ipr; q += C::NT / 64) {
             const int row = q / ipr, slot0 = (q - row * ipr) * 64;
             if (slot0 < njb * 8) {
                 const int c = (slot0 + lane) ^ (row & 7);

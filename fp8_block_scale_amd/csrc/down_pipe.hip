@@ -331,6 +331,7 @@ hipError_t launch_dn_pipe(const DownArgs &a, hipStream_t st) {
 
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st) {
     switch (block_m) {
+        case 8: return e8m0 ? launch_dn_pipe<8, true>(a, st) : launch_dn_pipe<8, false>(a, st);
         case 16: return e8m0 ? launch_dn_pipe<16, true>(a, st) : launch_dn_pipe<16, false>(a, st);
         case 32: return e8m0 ? launch_dn_pipe<32, true>(a, st) : launch_dn_pipe<32, false>(a, st);
         case 64: return e8m0 ? launch_dn_pipe<64, true>(a, st) : launch_dn_pipe<64, false>(a, st);

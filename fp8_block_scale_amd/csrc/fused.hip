@@ -151,6 +151,7 @@ hipError_t launch_fused_bm(const GateUpArgs &ga, const DownArgs &da, const Fused
 
 int fused_max_njb(int block_m) {
     switch (block_m) {
+        case 8: return ds::DSCfg<8>::JMAX;
         case 16: return ds::DSCfg<16>::JMAX;
         case 32: return ds::DSCfg<32>::JMAX;
         case 64: return ds::DSCfg<64>::JMAX;
@@ -174,6 +175,7 @@ hipError_t launch_fused_prep(uint32_t *cnt, size_t n_cnt, int32_t *rpos, int64_t
 hipError_t launch_fused(const GateUpArgs &ga, const DownArgs &da, const FusedArgs &f, int block_m,
                         bool fp8_mma, bool e8m0, hipStream_t st) {
     switch (block_m) {
+        case 8: return launch_fused_bm<8>(ga, da, f, fp8_mma, e8m0, st);
         case 16: return launch_fused_bm<16>(ga, da, f, fp8_mma, e8m0, st);
         case 32: return launch_fused_bm<32>(ga, da, f, fp8_mma, e8m0, st);
         case 64: return launch_fused_bm<64>(ga, da, f, fp8_mma, e8m0, st);

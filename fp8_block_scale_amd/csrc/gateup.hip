@@ -70,6 +70,7 @@ hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8
                          hipStream_t st) {
     const int mode = !fp8_mma ? kExact : (e8m0 ? kFp8E8 : kFp8);
     switch (block_m) {
+        case 8: return launch_gs_mode<8>(a, mode, st);
         case 16: return launch_gs_mode<16>(a, mode, st);
         case 32: return launch_gs_mode<32>(a, mode, st);
         case 64: return launch_gs_mode<64>(a, mode, st);

@@ -47,8 +47,11 @@ enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
 template <int BM, int NSO = 0>
 struct GSCfg {
     static_assert(NSO == 0 || (NSO >= 2 && NSO <= 4), "ring depth 2..4");
-    static constexpr int RP = BM < 64 ? BM : 64;   // plan rows per pass
-    static constexpr int NPASS = BM / RP;
+    // A pass is one MFMA row tile of RP rows (16..64); it holds RPV plan rows
+    // of the block (block_m = 8: the 8 rows of the block, then 8 masked rows).
+    static constexpr int RP = BM < 16 ? 16 : (BM < 64 ? BM : 64);
+    static constexpr int RPV = BM < RP ? BM : RP;
+    static constexpr int NPASS = BM > RP ? BM / RP : 1;
     static constexpr int NU = RP / 16;             // 16-token subtiles
     static constexpr int NT = 512;                 // eight waves
     static constexpr int GROW = 260;               // row stride of the FP32 tile
@@ -97,7 +100,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     // readable); the block's expert only once the block is known to lie
     // below P (expert_ids may be sized by the plan's blocks_cap)
     int r = -1;
-    if (w == 0 && lane < C::RP) r = a.sorted[(int64_t)b * BM + row0 + lane];
+    if (w == 0 && lane < C::RPV) r = a.sorted[(int64_t)b * BM + row0 + lane];
     const int ntp = a.ntp[0];
     if (b * BM >= ntp) return;                          // padded block
     const int e = __builtin_amdgcn_readfirstlane(a.eids[b]);   // uniform: scalar descriptors

@@ -487,7 +487,8 @@ hipError_t launch_pipe_mode(const GateUpArgs &a, int mode, hipStream_t st) {
 
 hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
-    if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return hipErrorInvalidValue;
+    if (block_m != 8 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+        return hipErrorInvalidValue;
     tiles_kernel<<<1 + prep_groups(a.R + a.n_cnt), 1024, 0, st>>>(a.eids, a.ntp, block_m, kRows / block_m,
                                                                    a.nblocks, a.tiles, a.tmeta,
                                                                    (uint32_t *)a.rpos, a.R, a.cnt, a.n_cnt);
@@ -498,6 +499,7 @@ hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bo
                               hipStream_t st) {
     const int mode = !fp8_mma ? kExact : (e8m0 ? kFp8E8 : kFp8);
     switch (block_m) {
+        case 8: return launch_pipe_mode<8>(a, mode, st);
         case 16: return launch_pipe_mode<16>(a, mode, st);
         case 32: return launch_pipe_mode<32>(a, mode, st);
         case 64: return launch_pipe_mode<64>(a, mode, st);

@@ -235,7 +235,7 @@ moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int32_t E, 
  *   exit untouched and their expert ids are never read, so worst-case
  *   buffers are fine.
  *   out_bf16 [M, K] BF16, read and written (accumulated into).
- * Constraints: K % 128 == 0, I % 128 == 0, block_m in {16, 32, 64, 128},
+ * Constraints: K % 128 == 0, I % 128 == 0, block_m in {8, 16, 32, 64, 128},
  * sorted_cap % block_m == 0, weights and x_q 16-byte aligned.
  * Errors: MOE_ERR_CAPACITY if workspace_bytes is below
  * moe_fp8_experts_workspace_size; MOE_ERR_SHAPE if MOE_F_MMA_E8M0 is set

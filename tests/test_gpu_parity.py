@@ -291,7 +291,7 @@ def test_zipf_small_full(flags):
     full_parity(case_of("zipf", M=40), flags=flags, act_mode=SCALE_UE8M0, label="zipf small")
 
 
-@pytest.mark.parametrize("bm", [64, 128])
+@pytest.mark.parametrize("bm", [8, 64, 128])
 def test_small_grid_long_intermediate_rows(bm):
     """Small grid with I = 2048: the down stage's rows (16 K-blocks) are too
     long for the stream kernel's LDS tile, so its fallback kernel runs."""
@@ -492,6 +492,27 @@ def test_zipf_full_size_sampled(flags):
     cs = case_of("zipf")
     full_parity(cs, flags=flags, act_mode=SCALE_UE8M0, tokens=_cover_tokens(cs, 6, 4),
                 label="zipf full size")
+
+
+# ------------------------------------------------------------ block_m = 8
+# Plan blocks of 8 rows: the per-block kernels run a 16-row MFMA tile whose
+# last 8 rows are masked (they belong to the next block and are never read),
+# the persistent kernels cut 16 blocks per 128-row tile.
+
+@pytest.mark.parametrize("name,M,flags", [
+    ("tiny", None, 0), ("decode", None, 0), ("decode", 4, 0), ("decode", 16, 0),
+    ("decode", 16, 7 << moe.MOE_F_SPLITK_SHIFT), ("decode", 16, FUSE_ON),
+    ("skew", 64, 0), ("skew", 64, FUSE_ON)])
+def test_block_m_8(name, M, flags):
+    full_parity(case_of(name, M=M, block_m=8), flags=flags, label="block_m=8")
+
+
+@pytest.mark.parametrize("gu,dn", [(1, 1), (2, 2), (1, 2)])
+def test_block_m_8_kernel_families(gu, dn):
+    cs = case_of("page1", M=256, block_m=8)
+    flags = ((gu << moe.MOE_F_GATEUP_PATH_SHIFT) | (dn << moe.MOE_F_DOWN_PATH_SHIFT) | FUSE_OFF)
+    full_parity(cs, flags=flags, tokens=_cover_tokens(cs, 6, 80 + gu + dn),
+                label=f"block_m=8 paths {gu}/{dn}")
 
 
 # ------------------------------------------------- steps 3-5 in one launch

@@ -106,7 +106,7 @@ def test_experts_validation():
 
     assert _err(call(K=200)) == "MOE_ERR_SHAPE"
     assert _err(call(I=100)) == "MOE_ERR_SHAPE"
-    assert _err(call(bm=8)) == "MOE_ERR_UNSUPPORTED"
+    assert _err(call(bm=4)) == "MOE_ERR_UNSUPPORTED"
     assert _err(call(bm=48)) == "MOE_ERR_UNSUPPORTED"
     assert _err(call(sc=120)) == "MOE_ERR_SHAPE"
     assert _err(call(fl=moe.MOE_F_MMA_E8M0)) == "MOE_ERR_SHAPE"
