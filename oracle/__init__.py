@@ -20,6 +20,9 @@ modifications sections):
                 by expert, each expert padded to a multiple of block_m).
 * ``quant``   -- 1x128 activation quantisation, FP32 scale mode and the
                 power-of-two (UE8M0) scale mode.
+* ``router``  -- softmax top-k routing with renormalised weights, routed
+                scaling and an optional shared expert (the router the plan
+                can be fused with).
 * ``experts`` -- gate/up GEMM with 128x128 block scales, SwiGLU, per-row
                 128-group FP8 requantisation, down GEMM, route weighting and
                 the reduce-add into the caller's output, all dot products in
@@ -41,6 +44,7 @@ from .e4m3 import (
 from .plan import plan_capacity, plan_ref
 from .quant import quant_groups_ref, quant_act_ref, ue8m0_exponent
 from .experts import experts_ref, ExpertsResult
+from .router import router_ref
 
 __all__ = [
     "E4M3_MAX",
@@ -57,4 +61,5 @@ __all__ = [
     "ue8m0_exponent",
     "experts_ref",
     "ExpertsResult",
+    "router_ref",
 ]
