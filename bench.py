@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--fuse", choices=("auto", "on", "off"), default="auto",
                     help="steps 3-5 as one launch (on), as two stages (off), or the library's "
                          "choice (auto)")
+    ap.add_argument("--router", action="store_true",
+                    help="route from FP32 logits inside the plan's launches (moe_route_plan): "
+                         "softmax top-k, routed scaling; the decode workload's expert 256 as a "
+                         "shared expert with routed scaling 2.5")
     ap.add_argument("--separate-plan-quant", action="store_true",
                     help="moe_plan then moe_quant_act instead of the fused moe_plan_quant")
     ap.add_argument("--eager", action="store_true",
@@ -254,8 +258,23 @@ def main():
 
     b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
     out = torch.zeros((case.M, case.K), dtype=torch.bfloat16, device=dev)
+    if args.router:
+        # the E=257 geometry: 256 routed experts + expert 256 shared, top-8 + shared
+        n_shared = 1 if case.E == 257 else 0
+        e_routed, k_routed = case.E - n_shared, case.top_k - n_shared
+        scaling = 2.5 if n_shared else 1.0
+        g = torch.Generator(device=dev)
+        g.manual_seed(12345)
+        logits = torch.randn((case.M, e_routed), generator=g, device=dev, dtype=torch.float32)
+        case.topk_ids = torch.empty((case.M, case.top_k), dtype=torch.int32, device=dev)
+        case.topk_weights = torch.empty((case.M, case.top_k), dtype=torch.float32, device=dev)
+
     def stage_plan_quant(stream, k):
-        if args.separate_plan_quant:
+        if args.router:
+            moe.moe_route_plan(logits, k_routed, n_shared, scaling, case.block_m, case.topk_ids,
+                               case.topk_weights, b.sorted_ids, b.expert_ids, b.ntp, b.plan_ws,
+                               case.x, b.x_q, b.x_s, act_mode, stream)
+        elif args.separate_plan_quant:
             moe.moe_plan(case.topk_ids, case.E, case.block_m, b.sorted_ids, b.expert_ids, b.ntp,
                          b.plan_ws, stream)
             moe.moe_quant_act(case.x, b.x_q, b.x_s, act_mode, stream)
@@ -305,6 +324,10 @@ def main():
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
+    if args.router:     # the routes the router chose (same count, other experts)
+        ids = case.topk_ids
+        valid = (ids >= 0) & (ids < case.E)
+        n_touched = int(torch.unique(ids[valid]).numel())
 
     stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -421,6 +444,7 @@ def main():
                       **({} if gate_up is None else {"gate_up": round(gate_up, 4),
                                                      "down_reduce": round(down, 4)})},
         "single_launch": bool(fused),
+        "router": bool(args.router),
         "launch": "eager" if args.eager else "hip graph (K steps per replay)",
         "weight_sets": nsets,
         "layer_GBs": round(nb["layer"] / (ms * 1e-3) / 1e9, 1),

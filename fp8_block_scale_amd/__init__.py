@@ -39,7 +39,7 @@ EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_qua
             "moe_fp8_experts_schedule",
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
             "moe_last_hip_error", "moe_last_error", "moe_debug_e4m3_encode",
-            "moe_debug_count_non_pow2", "moe_fp8_experts_noalloc")
+            "moe_debug_count_non_pow2", "moe_fp8_experts_noalloc", "moe_route_plan")
 
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -73,6 +73,9 @@ _c = {
     "moe_plan": _proto("moe_plan", _i32, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _i64,
                        _vp, _vp, _sz, _vp),
     "moe_quant_act": _proto("moe_quant_act", _i32, _vp, _i64, _i64, _i64, _vp, _vp, _i32, _vp),
+    "moe_route_plan": _proto("moe_route_plan", _i32, _vp, _i64, _i32, _i32, _i32, ctypes.c_float, _i32,
+                             _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _vp, _i64, _i64, _vp,
+                             _vp, _i32, _vp),
     "moe_plan_quant": _proto("moe_plan_quant", _i32, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _i64, _vp,
                              _i64, _vp, _vp, _sz, _vp, _i64, _i64, _vp, _vp, _i32, _vp),
     "moe_fp8_experts_workspace_size": _proto("moe_fp8_experts_workspace_size", _sz, _i64, _i64,
@@ -169,6 +172,36 @@ def moe_plan_quant(topk_ids, E, block_m, sorted_token_ids, expert_ids, num_token
     assert M == topk_ids.shape[0], "x_bf16 and topk_ids disagree on M"
     _check(_c["moe_plan_quant"](*args, _ptr(x_bf16), K, ld, _ptr(x_q), _ptr(x_s), scale_mode,
                                 _stream(stream)), "moe_plan_quant")
+
+
+def moe_route_plan(router_logits, top_k, n_shared, routed_scaling, block_m, topk_ids,
+                   topk_weights, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                   workspace=None, x_bf16=None, x_q=None, x_s=None, scale_mode=MOE_SCALE_FP32,
+                   stream=None):
+    """Router (softmax top-k, routed scaling, optional shared expert) and the
+    plan in the plan's launches; with x_bf16 also the activation quantisation.
+    router_logits [M, E_routed] fp32; topk_ids int32 / topk_weights fp32
+    [M, top_k + n_shared] out; the plan buffers sized for E_routed + n_shared
+    experts and top_k + n_shared routes per token."""
+    assert router_logits.dtype == torch.float32 and router_logits.is_contiguous()
+    M, Er = router_logits.shape
+    kk = top_k + n_shared
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous() and tuple(topk_ids.shape) == (M, kk)
+    assert topk_weights.dtype == torch.float32 and topk_weights.is_contiguous()
+    assert tuple(topk_weights.shape) == (M, kk)
+    assert sorted_token_ids.dtype == torch.int32 and expert_ids.dtype == torch.int32
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if x_bf16 is not None:
+        Mx, K, ld = _quant_args(x_bf16, x_q, x_s)
+        assert Mx == M, "x_bf16 and router_logits disagree on M"
+    else:
+        K, ld = 0, 0
+    _check(_c["moe_route_plan"](_ptr(router_logits), M, Er, top_k, n_shared, routed_scaling, block_m,
+                                _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_token_ids),
+                                sorted_token_ids.numel(), _ptr(expert_ids), expert_ids.numel(),
+                                _ptr(num_tokens_post_padded), _ptr(workspace), ws_bytes,
+                                _ptr(x_bf16), K, ld, _ptr(x_q), _ptr(x_s), scale_mode,
+                                _stream(stream)), "moe_route_plan")
 
 
 # ------------------------------------------------------------- quant act --

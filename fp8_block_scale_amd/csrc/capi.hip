@@ -318,6 +318,62 @@ MOE_API moe_status moe_plan_quant(const void *topk_ids, int32_t ids_dtype, int64
                      "moe_plan_quant: launch");
 }
 
+MOE_API moe_status moe_route_plan(const float *router_logits, int64_t M, int32_t E_routed,
+                                  int32_t top_k, int32_t n_shared, float routed_scaling,
+                                  int32_t block_m, int32_t *topk_ids, float *topk_weights,
+                                  int32_t *sorted_token_ids, int64_t sorted_cap,
+                                  int32_t *expert_ids, int64_t blocks_cap,
+                                  int32_t *num_tokens_post_padded, void *workspace,
+                                  size_t workspace_bytes, const void *x_bf16, int64_t K,
+                                  int64_t ld_x, uint8_t *x_q, float *x_s, int32_t scale_mode,
+                                  void *stream) {
+    if (E_routed < 1 || top_k < 1 || top_k > 32 || top_k > E_routed)
+        return fail(MOE_ERR_SHAPE, "need 1 <= top_k <= min(E_routed, 32) (top_k %d, E_routed %d)",
+                    top_k, E_routed);
+    if (n_shared != 0 && n_shared != 1) return fail(MOE_ERR_SHAPE, "n_shared must be 0 or 1");
+    if (E_routed + n_shared > kMaxE)
+        return fail(MOE_ERR_SHAPE, "E_routed + n_shared = %d exceeds %d", E_routed + n_shared, kMaxE);
+    if (!std::isfinite(routed_scaling)) return fail(MOE_ERR_SHAPE, "routed_scaling must be finite");
+    const int32_t E = E_routed + n_shared, kk = top_k + n_shared;
+    int groups = 0;
+    moe_status st = check_plan(topk_ids, MOE_IDS_I32, M, kk, E, block_m, sorted_token_ids, sorted_cap,
+                               expert_ids, blocks_cap, num_tokens_post_padded, workspace,
+                               workspace_bytes, &groups);
+    if (st != MOE_OK) return st;
+    const bool quant = x_bf16 != nullptr;
+    if (quant) {
+        st = check_quant(x_bf16, M, K, ld_x, x_q, x_s, scale_mode);
+        if (st != MOE_OK) return st;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0)
+        return hip_check(moe::launch_fill_zero((uint32_t *)num_tokens_post_padded, 1, s),
+                         "moe_route_plan: clear num_tokens_post_padded");
+    if (!router_logits || !topk_weights)
+        return fail(MOE_ERR_NULL, "router_logits and topk_weights are required");
+    if (((uintptr_t)router_logits & 3u) || ((uintptr_t)topk_weights & 3u) || ((uintptr_t)topk_ids & 3u))
+        return fail(MOE_ERR_ALIGN, "router_logits, topk_ids and topk_weights must be 4-byte aligned");
+    if (groups == 0 && moe::route_plan_single_lds(M * kk, E) > 160 * 1024)
+        return fail(MOE_ERR_CAPACITY,
+                    "%lld routes need the plan workspace (moe_plan_workspace_size bytes)",
+                    (long long)(M * kk));
+    moe::QuantJob q;
+    if (quant) {
+        q.x = (const uint16_t *)x_bf16;
+        q.M = M;
+        q.K = K;
+        q.ld = ld_x;
+        q.xq = x_q;
+        q.xs = x_s;
+    }
+    return hip_check(moe::launch_route_plan(router_logits, M, E_routed, top_k, n_shared, routed_scaling,
+                                            block_m, topk_ids, topk_weights, sorted_token_ids,
+                                            expert_ids, num_tokens_post_padded,
+                                            groups > 0 ? (int32_t *)workspace : nullptr, groups,
+                                            quant ? &q : nullptr, scale_mode == MOE_SCALE_UE8M0, s),
+                     "moe_route_plan: launch");
+}
+
 // ------------------------------------------------------------- quant act
 
 MOE_API moe_status moe_quant_act(const void *x_bf16, int64_t M, int64_t K, int64_t ld_x,

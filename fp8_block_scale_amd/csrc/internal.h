@@ -65,6 +65,15 @@ struct QuantJob {
 hipError_t launch_plan_quant(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
                              int32_t *sorted, int32_t *expert_ids, int32_t *ntp, int32_t *ws,
                              int groups, const QuantJob &q, bool ue8m0, hipStream_t st);
+// Router + plan (+ quantisation when q != nullptr) in the plan's launches
+// (plan.hip): ids/w [M, top_k + n_shared] out; ws/groups as launch_plan
+// (the multi-workgroup build needs ws).  The one-workgroup build keeps every
+// route id in LDS: route_plan_single_lds(R, E) bytes, at most 160 KB.
+size_t route_plan_single_lds(int64_t R, int E);
+hipError_t launch_route_plan(const float *logits, int64_t M, int E_routed, int top_k, int n_shared,
+                             float scale, int block_m, int32_t *ids, float *w, int32_t *sorted,
+                             int32_t *expert_ids, int32_t *ntp, int32_t *ws, int groups,
+                             const QuantJob *q, bool ue8m0, hipStream_t st);
 // ---- step 2: activation quantisation (quant.hip)
 hipError_t launch_quant_act(const uint16_t *x, int64_t M, int64_t K, int64_t ld,
                             uint8_t *xq, float *xs, bool ue8m0, hipStream_t st);

@@ -19,6 +19,8 @@
 //   pass 2  the waves walk their chunks again in the same order; a lane's
 //           slot is its wave base + the number of lower lanes in its match
 //           group, so the scatter is stable (ascending r) without atomics.
+#include <climits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -170,6 +172,173 @@ plan_quant_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwa
 }
 
 // ---------------------------------------------------------------------------
+// Router fused into the plan: softmax top-k over each token's routed experts
+// (the fixed router PR #4287 runs its expert kernel behind, real-model
+// evaluation; its retained-measurement notes give the routed scaling and the
+// shared expert of the E=257 geometry).  One wave routes one token: lane l
+// holds logits l, l + 64, ...; k rounds each take the wave's largest
+// remaining logit (equal logits: the lower expert index), so the chosen
+// experts come out largest first; weight i = exp(l_i - l_max) / sum over the
+// chosen, times the routed scaling; a shared expert (index E_routed) follows
+// in slot k with weight 1.  Softmax is increasing, so choosing on the logits
+// is choosing on the probabilities, without ties that rounding exp creates.
+
+struct RouteJob {
+    const float *logits;                  // [M, E_routed] FP32
+    int64_t M;
+    int Er, k, nshared;                   // routed experts, routed top-k, 0 or 1
+    float scale;                          // routed scaling factor
+    int32_t *ids;                         // [M, k + nshared] out
+    float *w;                             // [M, k + nshared] out
+};
+
+// Wave-wide max / min of a uint32 with DPP: within each row of 16 lanes
+// (quad swaps, half-row and row mirrors), then the four rows' results read
+// into scalar registers -- the full wave must be active.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+    return v;
+}
+__device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = row_max_u32(v);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = row_min_u32(v);
+    const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return min(min(a, b), min(c, d));
+}
+
+// FP32 -> uint32 with the same order (finite values).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Token t's logits as order keys, lane l holding experts l, l + 64, ...,
+// l + 64 (NPL - 1); key 0 marks an absent expert (every finite logit maps
+// above 0; -0 and +0 map to one key).
+template <int NPL>
+__device__ __forceinline__ void load_keys(const RouteJob &j, int64_t t, uint32_t (&key)[NPL]) {
+    const int lane = threadIdx.x & 63;
+    const float *lrow = j.logits + t * j.Er;
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < j.Er ? lrow[e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) key[i] = lane + 64 * i < j.Er ? ordered_bits(v[i] + 0.0f) : 0u;
+}
+
+// Routes token t, whose logit keys the calling wave holds (NPL per lane);
+// its k + nshared ids also go to lds_ids[0, k + nshared).  Each round takes
+// the wave's largest remaining key (one DPP max), then the lowest expert
+// index holding it (one DPP min), and clears that key.
+template <int NPL>
+__device__ __forceinline__ void route_token(const RouteJob &j, int64_t t, uint32_t (&key)[NPL],
+                                            int32_t *lds_ids) {
+    const int lane = threadIdx.x & 63;
+    float sel_v = 0.f;
+    int sel_e = 0;
+    for (int r = 0; r < j.k; ++r) {
+        // this lane's best remaining key (ascending index: ties keep the lower)
+        uint32_t bk = 0;
+        int bi = 0;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            if (key[i] > bk) {
+                bk = key[i];
+                bi = i;
+            }
+        const uint32_t top = wave_max_u32(bk);
+        const int e = (int)wave_min_u32(bk == top ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
+        if (lane == (e & 63)) {
+#pragma unroll
+            for (int i = 0; i < NPL; ++i)
+                if (i == (e >> 6)) key[i] = 0u;
+        }
+        if (lane == r) {
+            sel_e = e;
+            sel_v = __uint_as_float((top & 0x80000000u) ? (top & 0x7FFFFFFFu) : ~top);
+        }
+    }
+    const float top = __shfl(sel_v, 0, 64);
+    const float ex = lane < j.k ? expf(sel_v - top) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const int kk = j.k + j.nshared;
+    int32_t *ids = j.ids + t * kk;
+    float *w = j.w + t * kk;
+    if (lane < j.k) {
+        ids[lane] = sel_e;
+        w[lane] = __fdiv_rn(ex, sum) * j.scale;
+        lds_ids[lane] = sel_e;
+    } else if (lane < kk) {               // the shared expert
+        ids[lane] = j.Er;
+        w[lane] = 1.0f;
+        lds_ids[lane] = j.Er;
+    }
+}
+
+// The tokens [t0, t1) (stride `step`) by the calling wave, the next token's
+// logits loading while the current one is routed.
+template <int NPL>
+__device__ __forceinline__ void route_tokens(const RouteJob &j, int64_t t0, int64_t t1, int64_t step,
+                                             int32_t *lds_base, int64_t lds_t0) {
+    if (t0 >= t1) return;
+    const int kk = j.k + j.nshared;
+    uint32_t cur[NPL], nxt[NPL];
+    load_keys<NPL>(j, t0, cur);
+    for (int64_t t = t0; t < t1; t += step) {
+        if (t + step < t1) load_keys<NPL>(j, t + step, nxt);
+        route_token<NPL>(j, t, cur, lds_base + (t - lds_t0) * kk);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) cur[i] = nxt[i];
+    }
+}
+
+// Router, plan and (optionally) the activation quantisation in one launch:
+// workgroup 0 routes every token (wave w: tokens w, w + NW, ...) into LDS and
+// global memory, then builds the plan from the LDS copy; the other
+// workgroups quantise 64 groups each.
+template <int NPL, bool QUANT, bool UE8M0>
+__global__ void __launch_bounds__(kPlanThreads)
+route_plan_kernel(RouteJob j, int bm, int nwaves, int32_t *__restrict__ sorted,
+                  int32_t *__restrict__ expert_ids, int32_t *__restrict__ ntp, QuantJob q) {
+    extern __shared__ int smem[];
+    const int E = j.Er + j.nshared;
+    if (blockIdx.x == 0) {
+        int32_t *sIds = smem + nwaves * E + E + 32;       // after the plan's own LDS
+        route_tokens<NPL>(j, threadIdx.x >> 6, j.M, kPlanThreads / 64, sIds, 0);
+        __syncthreads();
+        plan_body(static_cast<const int32_t *>(sIds), j.M * (j.k + j.nshared), E, bm, nwaves, sorted,
+                  expert_ids,
+                  ntp, smem);
+        return;
+    }
+    if constexpr (QUANT)
+        quant_act_group<UE8M0>(q.x, q.M, q.K, q.ld, q.xq, q.xs,
+                               ((int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x) >> 4,
+                               threadIdx.x & 15);
+}
+
+// ---------------------------------------------------------------------------
 // Large route counts: the same plan from three launches over G workgroups.
 // Workgroup g owns the contiguous routes [g C, (g + 1) C); its four waves own
 // consecutive quarters of that range, as in the one-workgroup kernel.
@@ -253,6 +422,51 @@ plan_hist_quant_kernel(const IdT *__restrict__ ids, int64_t R, int E, int64_t ch
     }
     quant_act_group<UE8M0>(q.x, q.M, q.K, q.ld, q.xq, q.xs,
                            ((int64_t)(blockIdx.x - G) * kMT + threadIdx.x) >> 4, threadIdx.x & 15);
+}
+
+// The router in the histogram launch (1024 threads): workgroup g routes
+// tokens [g CT, (g + 1) CT) with its 16 waves (wave w: CT / 16 consecutive
+// tokens) into global memory and LDS; then waves 0-3 count its routes from
+// LDS exactly as hist_body does (a chunk of CT tokens' routes in four equal
+// quarters -- the scatter launch recounts the same quarters).  Workgroups
+// from G on quantise 64 groups each, if asked.
+constexpr int kRT = 1024;
+
+template <int NPL, bool QUANT, bool UE8M0>
+__global__ void __launch_bounds__(kRT)
+route_hist_kernel(RouteJob j, int64_t ctw, int32_t *__restrict__ ws, int G, QuantJob q) {
+    extern __shared__ int sm[];              // hist [4][E], then this group's route ids
+    if ((int)blockIdx.x >= G) {
+        if constexpr (QUANT)
+            quant_act_group<UE8M0>(q.x, q.M, q.K, q.ld, q.xq, q.xs,
+                                   ((int64_t)(blockIdx.x - G) * kRT + threadIdx.x) >> 4,
+                                   threadIdx.x & 15);
+        return;
+    }
+    const int E = j.Er + j.nshared;
+    const int kk = j.k + j.nshared;
+    int *hist = sm;
+    int32_t *sIds = sm + 4 * E;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < 4 * E; i += kRT) hist[i] = 0;
+    const int64_t g0 = (int64_t)blockIdx.x * (kRT / 64) * ctw;      // the group's first token
+    const int64_t t0 = g0 + w * ctw;
+    const int64_t t1 = t0 + ctw < j.M ? t0 + ctw : j.M;
+    route_tokens<NPL>(j, t0, t1, 1, sIds, g0);
+    __syncthreads();
+    if (w < 4) {
+        const int64_t R = j.M * kk;
+        const int64_t sub = (kRT / 64) * ctw * kk / 4;
+        const int64_t base = g0 * kk;
+        const int64_t beg = base + w * sub;
+        const int64_t end = beg + sub < R ? beg + sub : R;
+        if (beg < end)
+            wave_count(static_cast<const int32_t *>(sIds), beg - base, end - base, E, 32 - __clz(E),
+                       lane, hist + w * E);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kRT)
+        ws[(int64_t)blockIdx.x * E + e] = hist[e] + hist[E + e] + hist[2 * E + e] + hist[3 * E + e];
 }
 
 __global__ void __launch_bounds__(1024)
@@ -393,6 +607,49 @@ hipError_t launch_plan_quant_t(const IdT *ids, int64_t R, int E, int bm, int32_t
     return hipGetLastError();
 }
 
+template <int NPL, bool QUANT, bool UE8M0>
+hipError_t launch_route_plan_t(const RouteJob &j, int bm, int32_t *sorted, int32_t *expert_ids,
+                               int32_t *ntp, int32_t *ws, int G0, const QuantJob &q,
+                               hipStream_t st) {
+    const int E = j.Er + j.nshared;
+    const int kk = j.k + j.nshared;
+    const int64_t R = j.M * kk;
+    const int64_t qgroups = QUANT ? q.M * (q.K >> 7) : 0;
+    if (ws != nullptr && G0 > 0) {
+        // groups of 16 * ctw whole tokens; no more groups than the workspace holds
+        const int64_t per = kRT / 64;
+        const int64_t ctw = (j.M + per * G0 - 1) / (per * G0);
+        const int G = (int)((j.M + per * ctw - 1) / (per * ctw));
+        const int64_t chunk = per * ctw * kk;
+        const size_t lds = ((size_t)4 * E + (size_t)chunk) * sizeof(int);
+        if (lds > 64 * 1024) return hipErrorInvalidValue;
+        const int64_t qwg = (qgroups + kRT / 16 - 1) / (kRT / 16);
+        route_hist_kernel<NPL, QUANT, UE8M0><<<(unsigned)(G + qwg), kRT, lds, st>>>(j, ctw, ws, G, q);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        plan_scan_kernel<<<1, 1024, (size_t)(G * E + E + 16) * sizeof(int), st>>>(ws, G, E, bm, R, sorted,
+                                                                                 expert_ids, ntp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        plan_scatter_kernel<int32_t><<<G, kMT, (size_t)4 * E * sizeof(int), st>>>(j.ids, R, E, chunk, ws,
+                                                                                   sorted);
+        return hipGetLastError();
+    }
+    const int nwaves = E <= 512 ? 16 : 8;
+    const size_t lds = ((size_t)nwaves * E + E + 32 + (size_t)R) * sizeof(int);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const int64_t qwg = (qgroups + kPlanThreads / 16 - 1) / (kPlanThreads / 16);
+    if (lds > 64 * 1024) {
+        static std::atomic<uint64_t> lds_set{0};
+        const hipError_t e = raise_lds_limit(lds_set, (const void *)route_plan_kernel<NPL, QUANT, UE8M0>,
+                                             160 * 1024);
+        if (e != hipSuccess) return e;
+    }
+    route_plan_kernel<NPL, QUANT, UE8M0><<<(unsigned)(1 + qwg), kPlanThreads, lds, st>>>(j, bm, nwaves, sorted,
+                                                                                 expert_ids, ntp, q);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_plan_quant(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
@@ -441,6 +698,52 @@ hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int bloc
         plan_kernel<int32_t><<<1, T, lds, st>>>((const int32_t *)ids, R, E, block_m, nwaves,
                                                sorted, expert_ids, ntp);
     return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+size_t route_plan_single_lds(int64_t R, int E) {
+    const int nwaves = E <= 512 ? 16 : 8;
+    return ((size_t)nwaves * E + E + 32 + (size_t)R) * sizeof(int);
+}
+
+template <int NPL>
+hipError_t route_plan_npl(const RouteJob &j, int block_m, int32_t *sorted, int32_t *expert_ids,
+                          int32_t *ntp, int32_t *ws, int groups, const QuantJob *q, bool ue8m0,
+                          hipStream_t st) {
+    QuantJob none{};
+    if (q == nullptr)
+        return launch_route_plan_t<NPL, false, false>(j, block_m, sorted, expert_ids, ntp, ws, groups, none,
+                                                      st);
+    return ue8m0 ? launch_route_plan_t<NPL, true, true>(j, block_m, sorted, expert_ids, ntp, ws, groups, *q, st)
+                 : launch_route_plan_t<NPL, true, false>(j, block_m, sorted, expert_ids, ntp, ws, groups, *q, st);
+}
+
+hipError_t launch_route_plan(const float *logits, int64_t M, int E_routed, int top_k, int n_shared,
+                             float scale, int block_m, int32_t *ids, float *w, int32_t *sorted,
+                             int32_t *expert_ids, int32_t *ntp, int32_t *ws, int groups,
+                             const QuantJob *q, bool ue8m0, hipStream_t st) {
+    RouteJob j;
+    j.logits = logits;
+    j.M = M;
+    j.Er = E_routed;
+    j.k = top_k;
+    j.nshared = n_shared;
+    j.scale = scale;
+    j.ids = ids;
+    j.w = w;
+    // logits per lane: the fewest of 2, 4, 5, 8, 16 that hold E_routed
+    const int npl = E_routed <= 128 ? 2 : E_routed <= 256 ? 4 : E_routed <= 320 ? 5
+                  : E_routed <= 512 ? 8 : 16;
+    switch (npl) {
+        case 2: return route_plan_npl<2>(j, block_m, sorted, expert_ids, ntp, ws, groups, q, ue8m0, st);
+        case 4: return route_plan_npl<4>(j, block_m, sorted, expert_ids, ntp, ws, groups, q, ue8m0, st);
+        case 5: return route_plan_npl<5>(j, block_m, sorted, expert_ids, ntp, ws, groups, q, ue8m0, st);
+        case 8: return route_plan_npl<8>(j, block_m, sorted, expert_ids, ntp, ws, groups, q, ue8m0, st);
+        default: return route_plan_npl<16>(j, block_m, sorted, expert_ids, ntp, ws, groups, q, ue8m0, st);
+    }
 }
 
 }  // namespace moe

@@ -166,6 +166,42 @@ moe_status moe_plan(const void *topk_ids, int32_t ids_dtype, int64_t M, int32_t 
                     int32_t *num_tokens_post_padded,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Router and plan in one call, in the plan's own launches (none added):
+ * softmax top-k over each token's routed-expert logits, the chosen weights
+ * renormalised and multiplied by routed_scaling, optionally one shared
+ * expert, then the plan of moe_plan over those routes -- the fused router
+ * that PR #4287's real-model evaluation runs in front of its expert kernel
+ * (routed scaling 1.0 without a shared expert in one geometry, 2.5 with one
+ * shared expert in the E=257 geometry, its retained-measurement notes).
+ *   router_logits [M, E_routed] FP32 (finite), 4-byte aligned.
+ *   Chosen experts: the top_k largest logits (equal logits: the lower expert
+ *   index), listed largest first; weight of a chosen expert
+ *   exp(l_i - l_max) / sum over the chosen, times routed_scaling (softmax
+ *   over all experts, top-k, renormalised: the full denominator cancels).
+ *   n_shared = 1 appends expert E_routed as route slot top_k with weight 1.
+ *   topk_ids [M, top_k + n_shared] int32 out, topk_weights the same FP32 out
+ *   (ready for moe_fp8_experts).
+ *   The plan is moe_plan's for E = E_routed + n_shared experts and
+ *   top_k + n_shared routes per token (its capacity and workspace queries
+ *   take those sizes).
+ *   x_bf16 != NULL also runs moe_quant_act's quantisation in the same
+ *   launch (x_bf16, K, ld_x, x_q, x_s, scale_mode as there); x_bf16 == NULL
+ *   skips it (the other five are then ignored).
+ * Errors: those of moe_plan (and moe_quant_act); MOE_ERR_SHAPE unless
+ * 1 <= top_k <= min(E_routed, 32), n_shared in {0, 1} and
+ * E_routed + n_shared <= 1024; MOE_ERR_CAPACITY if the routes need the
+ * plan workspace (moe_plan_workspace_size, for 4096 routes and up) and it
+ * is missing or too small while they do not fit one workgroup. */
+moe_status moe_route_plan(const float *router_logits, int64_t M, int32_t E_routed, int32_t top_k,
+                          int32_t n_shared, float routed_scaling, int32_t block_m,
+                          int32_t *topk_ids, float *topk_weights,
+                          int32_t *sorted_token_ids, int64_t sorted_cap,
+                          int32_t *expert_ids, int64_t blocks_cap,
+                          int32_t *num_tokens_post_padded,
+                          void *workspace, size_t workspace_bytes,
+                          const void *x_bf16, int64_t K, int64_t ld_x,
+                          uint8_t *x_q, float *x_s, int32_t scale_mode, void *stream);
+
 /* ----------------------------------------------------------- quant act -- */
 
 /* Quantise BF16 activations per token and 128-column group.

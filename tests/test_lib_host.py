@@ -232,3 +232,28 @@ def test_noalloc_validation_before_any_device_call():
         sc = moe.moe_plan_capacity(M, 9, 257, 16)[0]
         need = moe.moe_fp8_experts_workspace_size(M, 7168, 256, 257, 9, 16, sc, 0)
         assert 0 < need <= moe.MOE_NOALLOC_SCRATCH_BYTES, (M, need)
+
+
+def test_route_plan_validation():
+    """moe_route_plan's host checks (no GPU needed: nothing is launched)."""
+    f = _raw("moe_route_plan")
+
+    def call(M=4, Er=8, k=2, ns=0, scale=1.0, bm=16, sc=None, bc=None, ws=None, wsb=0, x=None):
+        try:
+            scap, bcap = moe.moe_plan_capacity(M, k + ns, Er + ns, bm)
+        except moe.MoeError:
+            scap, bcap = 128, 8
+        return f(FAKE, M, Er, k, ns, scale, bm, FAKE, FAKE, FAKE, scap if sc is None else sc, FAKE,
+                 bcap if bc is None else bc, FAKE, ws, wsb, x, 256, 256, FAKE, FAKE, 0, None)
+
+    assert _err(call(k=0)) == "MOE_ERR_SHAPE"
+    assert _err(call(k=9)) == "MOE_ERR_SHAPE"                 # top_k > E_routed
+    assert _err(call(Er=64, k=33)) == "MOE_ERR_SHAPE"         # top_k > 32
+    assert _err(call(ns=2)) == "MOE_ERR_SHAPE"
+    assert _err(call(Er=1024, k=8, ns=1)) == "MOE_ERR_SHAPE"  # 1025 experts
+    assert _err(call(scale=float("inf"))) == "MOE_ERR_SHAPE"
+    assert _err(call(sc=8)) == "MOE_ERR_CAPACITY"
+    assert _err(call(x=ctypes.c_void_p(0x10008))) == "MOE_ERR_ALIGN"
+    # 100000 routes need the plan workspace
+    assert _err(call(M=20000, Er=256, k=4, ns=1)) == "MOE_ERR_CAPACITY"
+    assert _err(call(M=0)) in ("MOE_OK", "MOE_ERR_HIP")      # M = 0: only the P fill

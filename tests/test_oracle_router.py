@@ -89,3 +89,10 @@ def test_invariants_and_shared_expert():
     ids3, w3 = router_ref(logits[:, perm], 8)
     assert np.array_equal(perm[ids3], ids[:, :8])
     np.testing.assert_allclose(w3, w[:, :8] / 2.5, rtol=1e-12)
+
+
+def test_signed_zeros_are_one_value():
+    logits = np.array([[0.0, -0.0, -1.0, 0.0], [-0.0, 0.0, 0.0, -0.0]], dtype=np.float32)
+    ids, w = router_ref(logits, 3)
+    assert ids.tolist() == [[0, 1, 3], [0, 1, 2]]
+    np.testing.assert_allclose(w, 1.0 / 3.0, rtol=1e-15)
