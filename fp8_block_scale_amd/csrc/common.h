@@ -113,18 +113,38 @@ __device__ __forceinline__ v4f mfma16x16x128_e8m0(const v8i &a, const v8i &b, v4
 // FP32 rounding.
 
 // 32 E4M3 codes (two 16-byte halves of one lane's K-slice) -> four 8-wide
-// FP16 operands; operand q holds bytes [8q, 8q + 8).
-__device__ __forceinline__ void e4m3x32_to_f16(const u32x4 &lo, const u32x4 &hi, v8h (&out)[4]) {
+// FP16 operands; operand q holds bytes [8q, 8q + 8).  Each value is
+// multiplied by `scale` in the conversion, which rounds once to nearest even
+// FP16 (measured on gfx950 over every code and scales 2^-40 .. 2^20: exact
+// wherever the product is an FP16 value, subnormals included); with scale 1
+// or a power of two that keeps the products in range the widening is exact.
+__device__ __forceinline__ void e4m3x32_to_f16(const u32x4 &lo, const u32x4 &hi, v8h (&out)[4],
+                                               float scale = 1.0f) {
     const unsigned d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q], 1.0f, false);
-        v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q], 1.0f, true);
-        v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q + 1], 1.0f, false);
-        v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q + 1], 1.0f, true);
+        v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q], scale, false);
+        v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q], scale, true);
+        v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q + 1], scale, false);
+        v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d[2 * q + 1], scale, true);
         out[q] = v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
     }
 }
+
+// acc += A * B over one 128-deep K-block (four FP16 16x16x32 operands per
+// side), accumulated in the MFMA chain itself.
+__device__ __forceinline__ v4f mfma16x16x128_f16_acc(const v8h (&a)[4], const v8h (&b)[4], v4f acc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[q], acc, 0, 0, 0);
+    return acc;
+}
+
+// Power-of-two FP32 helpers for folded scales: the biased exponent of a
+// power of two, and 2^(e - 127) / 2^(127 - e) for a biased exponent e in
+// [1, 253].
+__device__ __forceinline__ int biased_exp(float s) { return (int)((__float_as_uint(s) >> 23) & 0xffu); }
+__device__ __forceinline__ float pow2_biased(int e) { return __uint_as_float((uint32_t)e << 23); }
+__device__ __forceinline__ float pow2_neg_biased(int e) { return __uint_as_float((uint32_t)(254 - e) << 23); }
 
 // D = A * B over one 128-deep K-block given as four FP16 16x16x32 operands
 // per side (same lane/row mapping as the FP8 16x16x128 tile).

@@ -141,7 +141,7 @@ hipError_t launch_fused_t(const GateUpArgs &ga, DownArgs da, FusedArgs f, hipStr
 template <int BM>
 hipError_t launch_fused_bm(const GateUpArgs &ga, const DownArgs &da, const FusedArgs &f, bool fp8,
                            bool e8, hipStream_t st) {
-    if (!fp8) return e8 ? launch_fused_t<BM, gs::kExact, true>(ga, da, f, st)
+    if (!fp8) return e8 ? launch_fused_t<BM, gs::kExactE8, true>(ga, da, f, st)
                         : launch_fused_t<BM, gs::kExact, false>(ga, da, f, st);
     return e8 ? launch_fused_t<BM, gs::kFp8E8, true>(ga, da, f, st)
               : launch_fused_t<BM, gs::kFp8, false>(ga, da, f, st);

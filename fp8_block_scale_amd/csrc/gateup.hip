@@ -47,6 +47,7 @@ hipError_t launch_gs_mode(const GateUpArgs &a, int mode, hipStream_t st) {
         case kExact: return launch_gs<BM, kExact>(a, st);
         case kFp8: return launch_gs<BM, kFp8>(a, st);
         case kFp8E8: return launch_gs<BM, kFp8E8>(a, st);
+        case kExactE8: return launch_gs<BM, kExactE8>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -68,7 +69,7 @@ int gateup_stream_kmax(int) { return 1 << 20; }   // the K-range streams through
 
 hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                          hipStream_t st) {
-    const int mode = !fp8_mma ? kExact : (e8m0 ? kFp8E8 : kFp8);
+    const int mode = !fp8_mma ? (e8m0 ? kExactE8 : kExact) : (e8m0 ? kFp8E8 : kFp8);
     switch (block_m) {
         case 8: return launch_gs_mode<8>(a, mode, st);
         case 16: return launch_gs_mode<16>(a, mode, st);

@@ -42,7 +42,12 @@
 namespace moe {
 namespace gs {
 
-enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
+// kExactE8: the exact path with power-of-two scales folded into the FP16
+// widening (2^(a_kb - A) on the activations, 2^(b_kb - B) on W13, A and B the
+// largest exponents over this item's K-range) and accumulated across
+// K-blocks in the MFMA chain; the sums are scaled by 2^A * 2^B once at the
+// end, so split partials share one scale and add as before.
+enum { kExact = 0, kFp8 = 1, kFp8E8 = 2, kExactE8 = 3 };
 
 template <int BM, int NSO = 0>
 struct GSCfg {
@@ -69,7 +74,8 @@ struct GSCfg {
     static constexpr int XT = TOK + RP * 4;
     static constexpr int SINK = XT + RP * 4;
     static constexpr int MISC = SINK + 8 * 256;
-    static constexpr int TOTAL = MISC + 16;
+    static constexpr int EXP = MISC + 16;          // kExactE8: [RP] row, [2] gate/up exponents
+    static constexpr int TOTAL = EXP + (RP + 4) * 4;
     static constexpr int NPS = 6;                  // DMA instructions per wave per stage
 };
 
@@ -89,6 +95,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     int *sXt = reinterpret_cast<int *>(smem + C::XT);      // token whose x row fills the row
     uint8_t *sSink = smem + C::SINK;
     int *sMisc = reinterpret_cast<int *>(smem + C::MISC);
+    int *sExp = reinterpret_cast<int *>(smem + C::EXP);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -182,6 +189,31 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         if (lane < 10) lds_dma4(ssrc + kbl, base + C::WB + C::XB + w * 64);
     };
 
+    if constexpr (MODE == kExactE8) {
+        // largest biased exponent over this item's K-range: of each row's
+        // activation scales (8 threads a row) and of the gate / up weight
+        // scales (waves 0 / 1)
+        const int row = tid >> 3, part = tid & 7;
+        if (row < C::RP) {
+            const float *xs = a.xs + (int64_t)sXt[row] * a.nkb;
+            int m = 1;
+            for (int kb = kb0 + part; kb < kb1; kb += 8) m = max(m, biased_exp(xs[kb]));
+            m = max(m, __shfl_xor(m, 1, 64));
+            m = max(m, __shfl_xor(m, 2, 64));
+            m = max(m, __shfl_xor(m, 4, 64));
+            if (part == 0) sExp[row] = m;
+        }
+        if (w < 2) {
+            const int nb13 = (int)(2 * I / 128);
+            const float *ws = a.w13s + ((int64_t)e * nb13 + (w == 1 ? (int)(I / 128) : 0) + jt) * a.nkb;
+            int mb = 1;
+            for (int kb = kb0 + lane; kb < kb1; kb += 64) mb = max(mb, biased_exp(ws[kb]));
+            for (int off = 32; off >= 1; off >>= 1) mb = max(mb, __shfl_xor(mb, off, 64));
+            if (lane == 0) sExp[C::RP + w] = mb;
+        }
+        __syncthreads();
+    }
+
     v4f accg[C::NU], accu[C::NU];
 #pragma unroll
     for (int u = 0; u < C::NU; ++u) {
@@ -206,6 +238,9 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         if constexpr (MODE == kExact) {
             e4m3x32_to_f16(wlo[0], whi[0], Wg);
             e4m3x32_to_f16(wlo[1], whi[1], Wu);
+        } else if constexpr (MODE == kExactE8) {
+            e4m3x32_to_f16(wlo[0], whi[0], Wg, sg * pow2_neg_biased(sExp[C::RP]));
+            e4m3x32_to_f16(wlo[1], whi[1], Wu, su * pow2_neg_biased(sExp[C::RP + 1]));
         }
 #pragma unroll
         for (int u = 0; u < C::NU; ++u) {
@@ -215,7 +250,12 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             const u32x4 lo = lds_read16(xp + ((g ^ (row & 7)) << 4));
             const u32x4 hi = lds_read16(xp + (((4 + g) ^ (row & 7)) << 4));
             const float sa = Ss[(row >> 3) * 16 + (row & 7)];
-            if constexpr (MODE == kExact) {
+            if constexpr (MODE == kExactE8) {
+                v8h Bh[4];
+                e4m3x32_to_f16(lo, hi, Bh, sa * pow2_neg_biased(sExp[row]));
+                accg[u] = mfma16x16x128_f16_acc(Wg, Bh, accg[u]);
+                accu[u] = mfma16x16x128_f16_acc(Wu, Bh, accu[u]);
+            } else if constexpr (MODE == kExact) {
                 v8h Bh[4];
                 e4m3x32_to_f16(lo, hi, Bh);
                 const v4f tg = mfma16x16x128_f16(Wg, Bh);
@@ -263,6 +303,15 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         compute(kb % C::NS);
     }
 
+    if constexpr (MODE == kExactE8) {
+        const float fbg = pow2_biased(sExp[C::RP]), fbu = pow2_biased(sExp[C::RP + 1]);
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+            const float fa = pow2_biased(sExp[(16 * u + l16) < C::RP ? 16 * u + l16 : 0]);
+            accg[u] = (accg[u] * fa) * fbg;
+            accu[u] = (accu[u] * fa) * fbu;
+        }
+    }
     // ---- FP32 tile of the pass: sG[row][n], gate n < 128, up n >= 128
     __syncthreads();                            // every wave is done with the x tile
 #pragma unroll

@@ -45,7 +45,11 @@ constexpr int kPerStage = kWInstr + kAInstr;  // + 1 on K-blocks that start a sc
 constexpr int kSGroup = 4;                    // K-blocks of activation scales per scale load
 constexpr int kMaxKb = 256;                   // K <= 32768
 
-enum { kExact = 0, kFp8 = 1, kFp8E8 = 2 };
+// kExactE8: the exact path with power-of-two scales folded into the FP16
+// widening (2^(a_kb - A) on the activations, 2^(b_kb - B) on W13, A and B
+// the largest exponents over K) and accumulated across K-blocks in the MFMA
+// chain; the item's sums are scaled by 2^A * 2^B once, before SwiGLU.
+enum { kExact = 0, kFp8 = 1, kFp8E8 = 2, kExactE8 = 3 };
 
 __device__ __forceinline__ v8i join8p(const u32x4 &lo, const u32x4 &hi) {
     v8i r;
@@ -139,6 +143,7 @@ gateup_pipe_kernel(GateUpArgs a) {
     int *sTok = reinterpret_cast<int *>(sSw + 2 * kMaxKb);      // [128] token or -1
     float *sRed = reinterpret_cast<float *>(sTok + kRows);      // [4][128]
     int *sItem = reinterpret_cast<int *>(sRed + 4 * kRows);      // [4]
+    int *sExp = sItem + 4;                                       // [128] row, [2] gate/up exponents
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -194,7 +199,6 @@ gateup_pipe_kernel(GateUpArgs a) {
         }
     }
     __syncthreads();
-
     // ---- DMA sources of this lane: W13 rows and gathered activation rows
     const int sub = lane >> 3, slot = lane & 7;
     const uint8_t *wsrc[kWInstr];
@@ -208,6 +212,25 @@ gateup_pipe_kernel(GateUpArgs a) {
     int fallback = sTok[0];
     for (int m = 1; fallback < 0 && m < nrows; ++m) fallback = sTok[m];
     if (fallback < 0) fallback = 0;                  // tile without valid rows: scale 0
+    if constexpr (MODE == kExactE8) {
+        // largest biased exponent of each row's activation scales (4 threads
+        // a row) and of the gate / up weight-block scales (waves 0 / 1)
+        const int row = tid >> 2, part = tid & 3;
+        const int t = sTok[row] >= 0 ? sTok[row] : fallback;    // the row the tile holds
+        int m = 1;
+        for (int kb = part; kb < nkb; kb += 4) m = max(m, biased_exp(a.xs[(int64_t)t * nkb + kb]));
+        m = max(m, __shfl_xor(m, 1, 64));
+        m = max(m, __shfl_xor(m, 2, 64));
+        if (part == 0) sExp[row] = m;
+        if (w < 2) {
+            int mb = 1;
+            for (int i = lane; i < nkb; i += 64) mb = max(mb, biased_exp(sSw[w * kMaxKb + i]));
+            for (int off = 32; off >= 1; off >>= 1) mb = max(mb, __shfl_xor(mb, off, 64));
+            if (lane == 0) sExp[kRows + w] = mb;
+        }
+        __syncthreads();
+    }
+
     const uint8_t *asrc[kAInstr];
 #pragma unroll
     for (int i = 0; i < kAInstr; ++i) {
@@ -327,7 +350,27 @@ gateup_pipe_kernel(GateUpArgs a) {
                 wr[s][0] = lds_read16(rp + ((g ^ (row & 7)) * 16));
                 wr[s][1] = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
             }
-            if constexpr (MODE == kExact) {
+            if constexpr (MODE == kExactE8) {
+            // every factor is a power of two: the widening takes it exactly
+            const float cg = sbg * pow2_neg_biased(sExp[kRows]);
+            const float cu = sbu * pow2_neg_biased(sExp[kRows + 1]);
+            v8h wh[4][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) e4m3x32_to_f16(wr[s][0], wr[s][1], wh[s], s < 2 ? cg : cu);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (u < 3) part(u + 1);
+                if (wm * 64 + u * 16 >= vrows) continue;
+                const int row = wm * 64 + u * 16 + l16;
+                const uint8_t *rp = As + row * 128;
+                const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                v8h bh[4];
+                e4m3x32_to_f16(lo, hi, bh, Ss[row * kSGroup] * pow2_neg_biased(sExp[row]));
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[s][u] = mfma16x16x128_f16_acc(wh[s], bh, acc[s][u]);
+            }
+            } else if constexpr (MODE == kExact) {
             // Hand-pipelined: the activation rows of subtile u + 1 are read
             // from LDS while subtile u multiplies; the W13 widening of s = 2, 3
             // runs behind subtile 0's first chains; and the scale FMAs of one
@@ -405,6 +448,15 @@ gateup_pipe_kernel(GateUpArgs a) {
     // the next item's claim travels while this one's epilogue computes
     const int ticket = tid == 0 ? claim_begin(a.tmeta + 1, home, q) : 0;
 
+    if constexpr (MODE == kExactE8) {
+        const float fbg = pow2_biased(sExp[kRows]), fbu = pow2_biased(sExp[kRows + 1]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const float fa = pow2_biased(sExp[wm * 64 + u * 16 + l16]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc[s][u] = (acc[s][u] * fa) * (s < 2 ? fbg : fbu);
+        }
+    }
     // ---- SwiGLU + per-row 128-group FP8 requantisation
     float h[NU][2][4];
 #pragma unroll
@@ -452,7 +504,7 @@ gateup_pipe_kernel(GateUpArgs a) {
 }
 
 constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + 2 * kRows * kSGroup * 4 +
-                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16;
+                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16 + (kRows + 4) * 4;
 static_assert(kSmem <= 160 * 1024, "LDS budget");
 
 template <int BM, int MODE>
@@ -479,6 +531,7 @@ hipError_t launch_pipe_mode(const GateUpArgs &a, int mode, hipStream_t st) {
         case kExact: return launch_pipe<BM, kExact>(a, st);
         case kFp8: return launch_pipe<BM, kFp8>(a, st);
         case kFp8E8: return launch_pipe<BM, kFp8E8>(a, st);
+        case kExactE8: return launch_pipe<BM, kExactE8>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -497,7 +550,7 @@ hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st) {
 
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                               hipStream_t st) {
-    const int mode = !fp8_mma ? kExact : (e8m0 ? kFp8E8 : kFp8);
+    const int mode = !fp8_mma ? (e8m0 ? kExactE8 : kExact) : (e8m0 ? kFp8E8 : kFp8);
     switch (block_m) {
         case 8: return launch_pipe_mode<8>(a, mode, st);
         case 16: return launch_pipe_mode<16>(a, mode, st);

@@ -80,12 +80,16 @@ enum { MOE_SCALE_FP32 = 0, MOE_SCALE_UE8M0 = 1 };
 enum {
     /* requantise the SwiGLU output with MOE_SCALE_UE8M0 scales */
     MOE_F_INTER_UE8M0 = 1u,
-    /* apply block scales inside the FP8 MFMA as E8M0 exponents instead of
-     * FP32 multiplies (the down GEMM, and the gate/up GEMM when
-     * MOE_F_FP8_GATEUP is set).  Requires MOE_F_INTER_UE8M0, and the caller
+    /* apply the block scales as powers of two inside the multiply instead
+     * of FP32 multiplies per K-block (SGLang PR #43556, motivation): in the
+     * down GEMM as E8M0 scale operands of the FP8 MFMA; in the exact gate/up
+     * GEMM folded into the FP16 widening (codes times their scale's ratio to
+     * the largest over K, exact) with the sums accumulated across K-blocks
+     * in the MFMA and scaled once at the end; with MOE_F_FP8_GATEUP as E8M0
+     * operands of the FP8 MFMA.  Requires MOE_F_INTER_UE8M0, and the caller
      * guarantees that x_s, w13_s and w2_s hold only powers of two in
-     * [2^-126, 2^127] (no zeros): a non-power-of-two scale is silently
-     * truncated to its exponent. */
+     * [2^-126, 2^126] (no zeros): a non-power-of-two scale is silently
+     * truncated to its exponent (moe_debug_count_non_pow2 checks). */
     MOE_F_MMA_E8M0 = 2u,
     /* EXPERIMENTAL, outside the parity contract: run the gate/up GEMM on
      * the FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) instead of the default

@@ -584,6 +584,22 @@ def test_fp8_mfma_gate_up_exceeds_the_code_budget():
 
 # ------------------------------------------------------------ contracts
 
+@pytest.mark.parametrize("flags", [E8, E8 | PERSIST | FUSE_OFF])
+def test_e8m0_wide_scale_spread(flags):
+    """Power-of-two scales folded into the gate/up widening on activations
+    whose 128-column groups differ by up to 2^24 in magnitude within a row,
+    so the folded ratios reach deep into the FP16 subnormal range: codes,
+    scales and output still meet the bars against the oracle (both kernel
+    families)."""
+    cfg = dict(CONFIGS["zipf"], M=96, E=16, K=1024, I=256, top_k=4, block_m=32, seed=41)
+    cs = make_case("spread", device=DEV, config=cfg)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    k = torch.randint(-12, 13, (cs.M, cs.K // 128), generator=g, device=DEV).float()
+    cs.x = (cs.x.float() * torch.repeat_interleave(torch.exp2(k), 128, dim=1)).to(torch.bfloat16)
+    full_parity(cs, flags=flags, act_mode=SCALE_UE8M0, label=f"e8m0 spread {flags:#x}")
+
+
 def test_e8m0_matches_fp32_scale_kernels():
     """Power-of-two scales: the E8M0-scaled kernels and the FP32-scale
     kernels see identical inputs and must agree to the parity bars."""
