@@ -14,6 +14,14 @@ power-of-two-scale case):
   skew    M=2048, E=512, K=2048, I=512,  top_k=10, block_m=64
   zipf    M=8192, E=288, K=4096, I=1024, top_k=8,  block_m=128, power-of-two scales
 
+W4A8 variant (``make_case(..., fmt="w4a8")``): the same masters stored as
+E2M1 codes, two per byte (even K index in the low nibble), with one
+power-of-two scale per 32 consecutive K -- 2^e, e the least integer with
+6 * 2^e >= amax of the 32 values, kept as its biased exponent byte e + 127.
+Codes round to nearest with ties to the even code, by comparison against the
+seven midpoints of the E2M1 grid.  For ``skew`` the zero-scale expert cannot
+be expressed (a power-of-two scale is never zero): its codes are all zero.
+
 Recipe (every random draw from one ``torch.Generator`` per tensor kind,
 seeded from the workload seed):
   x        bf16(N(0, 1))                                        [M, K]
@@ -63,10 +71,10 @@ class Case:
     x: torch.Tensor            # bf16 [M, K]
     topk_ids: torch.Tensor     # int32 or int64 [M, top_k]
     topk_weights: torch.Tensor # fp32 [M, top_k]
-    w13: torch.Tensor          # uint8 [E, 2I, K]
-    w13_s: torch.Tensor        # fp32 [E, 2I/128, K/128]
-    w2: torch.Tensor           # uint8 [E, K, I]
-    w2_s: torch.Tensor         # fp32 [E, K/128, I/128]
+    w13: torch.Tensor          # uint8 [E, 2I, K]           (w4a8: [E, 2I, K/2])
+    w13_s: torch.Tensor        # fp32 [E, 2I/128, K/128]   (w4a8: uint8 [E, 2I, K/32])
+    w2: torch.Tensor           # uint8 [E, K, I]            (w4a8: [E, K, I/2])
+    w2_s: torch.Tensor         # fp32 [E, K/128, I/128]    (w4a8: uint8 [E, K, I/32])
     meta: dict = field(default_factory=dict)
 
 
@@ -91,6 +99,50 @@ def _block_quant(w, pow2):
     q = (blk / s[:, None, :, None]).clamp(-448.0, 448.0)
     codes = q.reshape(rows, cols).to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, s.to(torch.float32)
+
+
+# E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6: the midpoints between
+# neighbours, and whether a value exactly on one goes to the upper neighbour
+# (the neighbour with an even code wins a tie)
+_E2M1_MID = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+_E2M1_TIE_UP = (False, True, False, True, False, True, False)
+
+
+def _k32_quant(w):
+    """Store FP32 masters [rows, cols] as packed E2M1 [rows, cols/2] plus one
+    biased-exponent byte per 32 columns [rows, cols/32]."""
+    rows, cols = w.shape
+    grp = w.reshape(rows, cols // 32, 32).to(torch.float64)
+    amax = grp.abs().amax(dim=-1)
+    e = torch.ceil(torch.log2(torch.where(amax > 0, amax / 6.0, torch.ones_like(amax))))
+    e = torch.where(6.0 * torch.exp2(e) < amax, e + 1, e)          # guard log2 rounding
+    e = torch.where(6.0 * torch.exp2(e - 1) >= amax, e - 1, e)
+    e = torch.where(amax == 0, torch.full_like(e, -126.0), e).clamp(-126, 126)
+    q = grp / torch.exp2(e)[..., None]
+    a = q.abs().clamp_max(6.0)
+    m = torch.zeros_like(a, dtype=torch.int64)
+    for mid, up in zip(_E2M1_MID, _E2M1_TIE_UP):
+        m += (a >= mid) if up else (a > mid)
+    codes = (m | (torch.signbit(q).to(torch.int64) << 3)).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
+def make_weights_w4(E, K, I, seed, device, std=0.02):
+    """The W4A8 variant's weights, from the same seeded masters as
+    make_weights: (w13 [E, 2I, K/2], w13_e [E, 2I, K/32], w2 [E, K, I/2],
+    w2_e [E, K, I/32]), all uint8."""
+    g = _gen(device, seed, 1)
+    w13 = torch.empty((E, 2 * I, K // 2), dtype=torch.uint8, device=device)
+    w13_e = torch.empty((E, 2 * I, K // 32), dtype=torch.uint8, device=device)
+    w2 = torch.empty((E, K, I // 2), dtype=torch.uint8, device=device)
+    w2_e = torch.empty((E, K, I // 32), dtype=torch.uint8, device=device)
+    for e in range(E):
+        m13 = torch.randn((2 * I, K), generator=g, device=device, dtype=torch.float32) * std
+        w13[e], w13_e[e] = _k32_quant(m13)
+        m2 = torch.randn((K, I), generator=g, device=device, dtype=torch.float32) * std
+        w2[e], w2_e[e] = _k32_quant(m2)
+    return w13, w13_e, w2, w2_e
 
 
 def make_weights(E, K, I, seed, pow2, device, std=0.02):
@@ -141,29 +193,38 @@ def make_routing(kind, M, E, top_k, seed, device):
     return ids.to(torch.int64), w.to(torch.float32).contiguous()
 
 
-def make_case(name, M=None, device="cpu", ids_dtype=torch.int32, weights=None, config=None):
+def make_case(name, M=None, device="cpu", ids_dtype=torch.int32, weights=None, config=None,
+              fmt="w8a8"):
     """Build a workload.  ``weights`` may pass a previously built
-    (w13, w13_s, w2, w2_s) tuple of the same geometry (M sweeps reuse the
-    parent's weights; routing and x are seeded by (seed, M)).  ``config``
-    (same keys as a CONFIGS entry) builds an ad-hoc geometry under ``name``."""
+    (w13, w13_s, w2, w2_s) tuple of the same geometry and format (M sweeps
+    reuse the parent's weights; routing and x are seeded by (seed, M)).
+    ``config`` (same keys as a CONFIGS entry) builds an ad-hoc geometry under
+    ``name``.  fmt "w4a8": E2M1 weights with K32 exponent bytes in the
+    w13 / w13_s / w2 / w2_s fields (shapes in make_weights_w4)."""
+    assert fmt in ("w8a8", "w4a8")
     c = dict(CONFIGS[name] if config is None else config)
     if M is not None:
         c["M"] = M
     M, E, K, I, top_k = c["M"], c["E"], c["K"], c["I"], c["top_k"]
     seed = c["seed"]
     if weights is None:
-        weights = make_weights(E, K, I, seed, c["pow2"], device)
+        weights = make_weights(E, K, I, seed, c["pow2"], device) if fmt == "w8a8" \
+            else make_weights_w4(E, K, I, seed, device)
     w13, w13_s, w2, w2_s = weights
     if c["routing"] == "skew":
-        w13_s[SKEW_ZERO_SCALE_EXPERT].zero_()
-        w2_s[SKEW_ZERO_SCALE_EXPERT].zero_()
+        if fmt == "w8a8":
+            w13_s[SKEW_ZERO_SCALE_EXPERT].zero_()
+            w2_s[SKEW_ZERO_SCALE_EXPERT].zero_()
+        else:
+            w13[SKEW_ZERO_SCALE_EXPERT].zero_()
+            w2[SKEW_ZERO_SCALE_EXPERT].zero_()
     gx = _gen(device, seed, 3 + 1000 * M)
     x = torch.randn((M, K), generator=gx, device=device, dtype=torch.float32).to(torch.bfloat16)
     ids, w = make_routing(c["routing"], M, E, top_k, seed, device)
     return Case(name=name, M=M, E=E, K=K, I=I, top_k=top_k, block_m=c["block_m"],
                 pow2=c["pow2"], x=x, topk_ids=ids.to(ids_dtype).contiguous(),
                 topk_weights=w, w13=w13, w13_s=w13_s, w2=w2, w2_s=w2_s,
-                meta=dict(seed=seed, routing=c["routing"]))
+                meta=dict(seed=seed, routing=c["routing"], fmt=fmt))
 
 
 def flops(case, n_valid_routes=None):

@@ -20,6 +20,8 @@ modifications sections):
                 by expert, each expert padded to a multiple of block_m).
 * ``quant``   -- 1x128 activation quantisation, FP32 scale mode and the
                 power-of-two (UE8M0) scale mode.
+* ``e2m1``    -- E2M1 (FP4) codec and K32 power-of-two block dequantisation
+                of the W4A8 variant's weights.
 * ``router``  -- softmax top-k routing with renormalised weights, routed
                 scaling and an optional shared expert (the router the plan
                 can be fused with).
@@ -43,7 +45,8 @@ from .e4m3 import (
 )
 from .plan import plan_capacity, plan_ref
 from .quant import quant_groups_ref, quant_act_ref, ue8m0_exponent
-from .experts import experts_ref, ExpertsResult
+from .experts import experts_ref, experts_w4a8_ref, ExpertsResult
+from .e2m1 import E2M1_MAX, dequant_k32, e2m1_decode, e2m1_encode, unpack_e2m1
 from .router import router_ref
 
 __all__ = [
@@ -60,6 +63,12 @@ __all__ = [
     "quant_act_ref",
     "ue8m0_exponent",
     "experts_ref",
+    "experts_w4a8_ref",
     "ExpertsResult",
+    "E2M1_MAX",
+    "dequant_k32",
+    "e2m1_decode",
+    "e2m1_encode",
+    "unpack_e2m1",
     "router_ref",
 ]

@@ -31,6 +31,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from .e2m1 import dequant_k32
 from .e4m3 import bf16_round_f64, e4m3_decode
 from .quant import SCALE_FP32, quant_groups_ref
 
@@ -63,7 +64,8 @@ def silu_mul(gate, up):
 def experts_ref(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_ids,
                 expert_ids, P, top_k, block_m, out_init=None,
                 inter_mode=SCALE_FP32, tokens=None, debug=None):
-    """Evaluate the expert path over a given plan.
+    """Evaluate the expert path over a given plan (W8A8: E4M3 weights with
+    128x128 FP32 block scales).
 
     tokens: optional iterable of token indices; when given, only routes of
     those tokens are evaluated (same arithmetic, used to sample very large
@@ -71,12 +73,40 @@ def experts_ref(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_ids,
     debug: optional dict; receives the FP64 gate/up sums ``g`` and the FP64
     down-projection rows ``y`` keyed by plan row.
     """
-    x_q = np.asarray(x_q)
-    M, K = x_q.shape
-    E, twoI, K2 = w13.shape
-    assert K2 == K and twoI % 256 == 0 and K % 128 == 0
+    E, twoI, K = w13.shape
     I = twoI // 2
     assert w2.shape == (E, K, I)
+    return _experts_core(x_q, x_s, lambda e: dequant_blocks(w13[e], w13_s[e]),
+                         lambda e: dequant_blocks(w2[e], w2_s[e]), E, I, topk_weights,
+                         sorted_ids, expert_ids, P, top_k, block_m, out_init, inter_mode, tokens,
+                         debug)
+
+
+def experts_w4a8_ref(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_ids,
+                     expert_ids, P, top_k, block_m, out_init=None,
+                     inter_mode=SCALE_FP32, tokens=None, debug=None):
+    """The same expert path with E2M1 weights and K32 power-of-two scales
+    (sglang-glm53-flash-sm120 PR #13, description: FP8 activations against
+    E2M1-K32 weights, the weight scales applied in FP32):
+      w13 uint8 [E, 2I, K/2] packed E2M1 (even K in the low nibble),
+      w13_s uint8 [E, 2I, K/32] UE8M0 scale bytes; w2 [E, K, I/2], w2_s
+      [E, K, I/32] likewise.  Activations and the intermediate keep their
+    1x128 FP8 quantisation, so only the weight dequantisation differs."""
+    E, twoI, half = w13.shape
+    K, I = 2 * half, twoI // 2
+    assert w2.shape == (E, K, I // 2) and w13_s.shape == (E, twoI, K // 32)
+    return _experts_core(x_q, x_s, lambda e: dequant_k32(w13[e], w13_s[e]),
+                         lambda e: dequant_k32(w2[e], w2_s[e]), E, I, topk_weights, sorted_ids,
+                         expert_ids, P, top_k, block_m, out_init, inter_mode, tokens, debug)
+
+
+def _experts_core(x_q, x_s, deq13, deq2, E, I, topk_weights, sorted_ids, expert_ids, P, top_k,
+                  block_m, out_init, inter_mode, tokens, debug):
+    """The expert path with the weights of expert e given dequantised by
+    deq13(e) -> FP64 [2I, K] and deq2(e) -> FP64 [K, I]."""
+    x_q = np.asarray(x_q)
+    M, K = x_q.shape
+    assert I % 128 == 0 and K % 128 == 0
     R = M * top_k
     wflat = np.asarray(topk_weights, dtype=np.float32).reshape(-1).astype(np.float64)
     sorted_ids = np.asarray(sorted_ids, dtype=np.int64)[:P]
@@ -113,7 +143,7 @@ def experts_ref(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_ids,
             continue
         # gathered activation rows, dequantised
         A = e4m3_decode(x_q[t]) * np.repeat(x_s[t].astype(np.float64), 128, axis=1)
-        W13d = dequant_blocks(w13[e], w13_s[e])
+        W13d = deq13(e)
         g = A @ W13d.T                                  # [n, 2I] FP64
         del W13d
         if debug is not None:
@@ -124,7 +154,7 @@ def experts_ref(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_ids,
         h_q[rows] = codes
         h_s[rows] = scales
         Hd = e4m3_decode(codes) * np.repeat(scales.astype(np.float64), 128, axis=1)
-        W2d = dequant_blocks(w2[e], w2_s[e])
+        W2d = deq2(e)
         y = Hd @ W2d.T                                  # [n, K] FP64
         del W2d
         if debug is not None:
