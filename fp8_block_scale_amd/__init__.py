@@ -18,6 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
 
 MOE_OK = 0
+MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_CAPACITY, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = \
+    1, 2, 3, 4, 5, 6
 MOE_IDS_I32, MOE_IDS_I64 = 0, 1
 MOE_SCALE_FP32, MOE_SCALE_UE8M0 = 0, 1
 MOE_F_INTER_UE8M0 = 1
@@ -39,7 +41,8 @@ EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_qua
             "moe_fp8_experts_schedule",
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
             "moe_last_hip_error", "moe_last_error", "moe_debug_e4m3_encode",
-            "moe_debug_count_non_pow2", "moe_fp8_experts_noalloc", "moe_route_plan")
+            "moe_debug_count_non_pow2", "moe_fp8_experts_noalloc", "moe_route_plan",
+            "moe_w4a8_experts_workspace_size", "moe_w4a8_experts")
 
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -94,6 +97,11 @@ _c = {
     "moe_fp8_experts_noalloc": _proto("moe_fp8_experts_noalloc", _i32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
                                       _i32, _i64, _u32, _vp, _vp),
+    "moe_w4a8_experts_workspace_size": _proto("moe_w4a8_experts_workspace_size", _sz, _i64, _i64,
+                                              _i64, _i32, _i32, _i32, _i64, _u32),
+    "moe_w4a8_experts": _proto("moe_w4a8_experts", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp,
+                               _sz, _vp),
     "moe_status_str": _proto("moe_status_str", ctypes.c_char_p, _i32),
     "moe_last_hip_error": _proto("moe_last_hip_error", ctypes.c_char_p),
     "moe_last_error": _proto("moe_last_error", ctypes.c_char_p),
@@ -276,6 +284,38 @@ def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_i
            "moe_fp8_experts")
 
 
+def moe_w4a8_experts_workspace_size(M, K, I, E, top_k, block_m, sorted_cap, flags=0):
+    return _c["moe_w4a8_experts_workspace_size"](M, K, I, E, top_k, block_m, sorted_cap, flags)
+
+
+def moe_w4a8_experts(x_q, x_s, w13, w13_e, w2, w2_e, topk_weights, sorted_token_ids, expert_ids,
+                     num_tokens_post_padded, top_k, block_m, out_bf16, workspace, flags=0,
+                     stream=None):
+    """Steps 3-5 with E2M1 weights (w13 [E, 2I, K/2], w13_e [E, 2I, K/32],
+    w2 [E, K, I/2], w2_e [E, K, I/32], all uint8); accumulates into
+    out_bf16 [M, K]."""
+    M, K = x_q.shape
+    E, twoI, half = w13.shape
+    I = twoI // 2
+    assert 2 * half == K and w2.shape == (E, K, I // 2)
+    assert w13_e.shape == (E, twoI, K // 32) and w2_e.shape == (E, K, I // 32)
+    for t in (x_q, x_s, w13, w13_e, w2, w2_e, topk_weights, sorted_token_ids, expert_ids,
+              out_bf16, workspace):
+        assert t.is_contiguous()
+    assert w13.dtype == w13_e.dtype == w2.dtype == w2_e.dtype == torch.uint8
+    assert out_bf16.dtype == torch.bfloat16 and topk_weights.dtype == torch.float32
+    assert expert_ids.numel() >= min(moe_plan_capacity(M, top_k, E, block_m)[1],
+                                     sorted_token_ids.numel() // block_m), \
+        "expert_ids shorter than the plan can need"
+    _check(_c["moe_w4a8_experts"](_ptr(x_q), _ptr(x_s), _ptr(w13), _ptr(w13_e), _ptr(w2),
+                                  _ptr(w2_e), _ptr(topk_weights), _ptr(sorted_token_ids),
+                                  _ptr(expert_ids), _ptr(num_tokens_post_padded), M, K, I, E, top_k,
+                                  block_m, sorted_token_ids.numel(), flags, _ptr(out_bf16),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)),
+           "moe_w4a8_experts")
+
+
 def moe_fp8_experts_noalloc(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids,
                             expert_ids, num_tokens_post_padded, top_k, block_m, out_bf16, flags=0,
                             stream=None):
@@ -339,9 +379,10 @@ class MoeLayerBuffers:
     """Device buffers for one call of the whole path at a given geometry
     (allocated once with torch; reused across calls)."""
 
-    def __init__(self, M, K, I, E, top_k, block_m, flags=0, device="cuda"):
+    def __init__(self, M, K, I, E, top_k, block_m, flags=0, device="cuda", w4a8=False):
         self.M, self.K, self.I, self.E, self.top_k, self.block_m = M, K, I, E, top_k, block_m
         self.flags = flags
+        self.w4a8 = w4a8
         self.sorted_cap, self.blocks_cap = moe_plan_capacity(M, top_k, E, block_m)
         dev = torch.device(device)
         self.sorted_ids = torch.empty(self.sorted_cap, dtype=torch.int32, device=dev)
@@ -349,7 +390,10 @@ class MoeLayerBuffers:
         self.ntp = torch.empty(1, dtype=torch.int32, device=dev)
         self.x_q = torch.empty((M, K), dtype=torch.uint8, device=dev)
         self.x_s = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
-        ws = moe_fp8_experts_workspace_size(M, K, I, E, top_k, block_m, self.sorted_cap, flags)
+        size = moe_w4a8_experts_workspace_size if w4a8 else moe_fp8_experts_workspace_size
+        ws = size(M, K, I, E, top_k, block_m, self.sorted_cap, flags)
+        if w4a8 and M > 0 and ws == 0:
+            raise MoeError(MOE_ERR_SHAPE, "moe_w4a8_experts_workspace_size", moe_last_hip_error())
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         pws = moe_plan_workspace_size(M, top_k, E, block_m)
         self.plan_ws = torch.empty(pws, dtype=torch.uint8, device=dev) if pws else None

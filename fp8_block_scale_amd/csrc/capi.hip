@@ -502,6 +502,7 @@ moe::GateUpArgs gateup_args(const uint8_t *x_q, const float *x_s, const uint8_t 
     ga.xs = x_s;
     ga.w13 = w13;
     ga.w13s = w13_s;
+    ga.w13e = nullptr;
     ga.sorted = sorted_token_ids;
     ga.eids = expert_ids;
     ga.ntp = num_tokens_post_padded;
@@ -537,6 +538,7 @@ moe::DownArgs down_args(const uint8_t *w2, const float *w2_s, const float *topk_
     da.hs = (const float *)(ws + l.hs);
     da.w2 = w2;
     da.w2s = w2_s;
+    da.w2e = nullptr;
     da.topk_w = topk_weights;
     da.sorted = sorted_token_ids;
     da.eids = expert_ids;
@@ -681,6 +683,92 @@ MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const u
     return moe_fp8_down_reduce(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
                                num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap,
                                flags, out_bf16, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------- W4A8 variant
+
+namespace {
+
+// The W4A8 variant runs on the per-block kernels: its flags are those of
+// moe_fp8_experts with both stage paths resolved to MOE_PATH_STREAM.
+uint32_t w4_flags(uint32_t flags) {
+    return (flags & ~(MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK)) |
+           ((uint32_t)MOE_PATH_STREAM << MOE_F_GATEUP_PATH_SHIFT) |
+           ((uint32_t)MOE_PATH_STREAM << MOE_F_DOWN_PATH_SHIFT);
+}
+
+moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, int32_t block_m,
+                    int64_t sorted_cap, uint32_t flags) {
+    moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
+    if (st != MOE_OK) return st;
+    if (flags & (MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP))
+        return fail(MOE_ERR_UNSUPPORTED, "W4A8: MOE_F_MMA_E8M0 and MOE_F_FP8_GATEUP do not apply");
+    const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
+    const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
+    if (gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT)
+        return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs the per-block kernels only");
+    if (((flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT) == MOE_FUSE_ON)
+        return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs as two stages (no MOE_FUSE_ON)");
+    if (I / 128 > moe::down_w4_max_njb(block_m))
+        return fail(MOE_ERR_UNSUPPORTED, "W4A8 needs I / 128 <= %d at block_m %d",
+                    moe::down_w4_max_njb(block_m), block_m);
+    return check_flags(w4_flags(flags), K, I, block_m);
+}
+
+}  // namespace
+
+MOE_API size_t moe_w4a8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,
+                                               int32_t top_k, int32_t block_m, int64_t sorted_cap,
+                                               uint32_t flags) {
+    if (check_w4(M, K, I, E, top_k, block_m, sorted_cap, flags) != MOE_OK) return 0;
+    return ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags)).total;
+}
+
+MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                                    const uint8_t *w13_e, const uint8_t *w2, const uint8_t *w2_e,
+                                    const float *topk_weights, const int32_t *sorted_token_ids,
+                                    const int32_t *expert_ids,
+                                    const int32_t *num_tokens_post_padded, int64_t M, int64_t K,
+                                    int64_t I, int32_t E, int32_t top_k, int32_t block_m,
+                                    int64_t sorted_cap, uint32_t flags, void *out_bf16,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    moe_status st = check_w4(M, K, I, E, top_k, block_m, sorted_cap, flags);
+    if (st != MOE_OK) return st;
+    const uint32_t fl = w4_flags(flags);
+    const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, fl);
+    if (M == 0 || sorted_cap == 0) return MOE_OK;
+    if (!workspace) return fail(MOE_ERR_NULL, "workspace is required");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < l.total)
+        return fail(MOE_ERR_CAPACITY, "workspace %zu bytes < required %zu", workspace_bytes, l.total);
+    if (!x_q || !x_s || !w13 || !w13_e || !w2 || !w2_e || !topk_weights || !sorted_token_ids ||
+        !expert_ids || !num_tokens_post_padded || !out_bf16)
+        return fail(MOE_ERR_NULL, "all tensor arguments and the workspace are required");
+    if (!aligned16(x_q) || !aligned16(w13) || !aligned16(w2) || !aligned16(out_bf16))
+        return fail(MOE_ERR_ALIGN, "x_q, w13, w2 and out must be 16-byte aligned");
+    if (((uintptr_t)w13_e & 3u) || ((uintptr_t)w2_e & 3u))
+        return fail(MOE_ERR_ALIGN, "w13_e and w2_e must be 4-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = (uint8_t *)workspace;
+    st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
+                                    (uint32_t *)(ws + l.cnt), l.cnt_words, s),
+                   "moe_w4a8_experts: clear route map and counters");
+    if (st != MOE_OK) return st;
+    moe::GateUpArgs ga = gateup_args(x_q, x_s, w13, nullptr, sorted_token_ids, expert_ids,
+                                     num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap,
+                                     fl, ws, l);
+    ga.w13e = w13_e;
+    st = hip_check(moe::launch_gateup_w4(ga, block_m, s), "moe_w4a8_experts: gate/up launch");
+    if (st != MOE_OK) return st;
+    moe::DownArgs da = down_args(w2, nullptr, topk_weights, sorted_token_ids, expert_ids,
+                                 num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap, ws, l);
+    da.w2e = w2_e;
+    st = hip_check(moe::launch_down_w4(da, block_m, s), "moe_w4a8_experts: down launch");
+    if (st != MOE_OK) return st;
+    return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const uint16_t *)(ws + l.y),
+                                          (const float *)(ws + l.ys), topk_weights,
+                                          (const int32_t *)(ws + l.rpos), M, K, top_k, s),
+                     "moe_w4a8_experts: finalize launch");
 }
 
 // ------------------------------------------------- no-allocation variant

@@ -131,6 +131,36 @@ __device__ __forceinline__ void e4m3x32_to_f16(const u32x4 &lo, const u32x4 &hi,
     }
 }
 
+// 8 E2M1 codes (one dword, the even index in each byte's low nibble) -> one
+// 8-wide FP16 operand, each value multiplied by `scale` in the conversion
+// (one rounding to nearest even FP16; measured on gfx950 for every byte and
+// scales 2^-30 .. 2^10: exact wherever the product is an FP16 value).
+__device__ __forceinline__ v8h e2m1x8_to_f16(uint32_t d, float scale) {
+    const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 0);
+    const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 1);
+    const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 2);
+    const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, scale, 3);
+    return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
+// Largest of the four bytes of a dword.
+__device__ __forceinline__ int max_byte4(uint32_t v) {
+    const uint32_t m = max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24));
+    return (int)m;
+}
+
+// D = 2^(ea - 127) * (A * B) over a 16x16x128 tile with A = E2M1 codes (lane
+// l: 32 codes of row l % 16 at K [32 (l / 16), +32) in its first four
+// dwords, the even index in each byte's low nibble; ea the E8M0 scale of
+// exactly those 32 codes) and B = E4M3 codes in the FP8 tile's layout (lane
+// l: column l % 16, bytes 0-15 K [16 (l / 16), +16), bytes 16-31
+// K [64 + 16 (l / 16), +16)), fresh accumulator.  (Pairing measured on
+// gfx950 with one-hot operands.)
+__device__ __forceinline__ v4f mfma16x16x128_e2m1_e4m3(const v8i &a, const v8i &b, int ea) {
+    v4f z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 0, 0, ea, 0, 127);
+}
+
 // acc += A * B over one 128-deep K-block (four FP16 16x16x32 operands per
 // side), accumulated in the MFMA chain itself.
 __device__ __forceinline__ v4f mfma16x16x128_f16_acc(const v8h (&a)[4], const v8h (&b)[4], v4f acc) {

@@ -199,7 +199,7 @@ down_kernel(DownArgs a) {
     }
 }
 
-template <int BM, bool E8M0>
+template <int BM, bool E8M0, bool W4 = false>
 __global__ void __launch_bounds__(512)
 down_stream_kernel(DownArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -209,7 +209,7 @@ down_stream_kernel(DownArgs a) {
     L /= a.nblocks;
     const int cw = L % ncw;
     const int pass = L / ncw;
-    down_item<BM, E8M0, false>(a, smem, b, cw, pass, nullptr);
+    down_item<BM, E8M0, false, W4>(a, smem, b, cw, pass, nullptr);
 }
 
 __global__ void __launch_bounds__(256)
@@ -239,10 +239,13 @@ hipError_t launch_dn(const DownArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BM, bool E8M0>
+template <int BM, bool E8M0, bool W4 = false>
 hipError_t launch_ds(DownArgs a, hipStream_t st) {
     using C = DSCfg<BM>;
-    if (a.njb > C::JMAX) return launch_dn<BM, E8M0>(a, st);   // rows too long for the LDS tile
+    if (a.njb > C::JMAX) {                           // rows too long for the LDS tile
+        if constexpr (W4) return hipErrorInvalidValue;
+        else return launch_dn<BM, E8M0>(a, st);
+    }
     // column tiles per workgroup: enough workgroups to cover the chip first
     const int64_t units = (int64_t)a.nblocks * a.ctiles * C::NPASS;
     int nct = (int)(units / 1024);
@@ -252,9 +255,10 @@ hipError_t launch_ds(DownArgs a, hipStream_t st) {
     if (grid == 0) return hipSuccess;
     const int lds = DSLayout(C::RP, a.njb, nct, C::YROW).total;
     static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_stream_kernel<BM, E8M0>, 160 * 1024);
+    const hipError_t e =
+        raise_lds_limit(lds_set, (const void *)down_stream_kernel<BM, E8M0, W4>, 160 * 1024);
     if (e != hipSuccess) return e;
-    down_stream_kernel<BM, E8M0><<<(unsigned)grid, C::NT, lds, st>>>(a);
+    down_stream_kernel<BM, E8M0, W4><<<(unsigned)grid, C::NT, lds, st>>>(a);
     return hipGetLastError();
 }
 
@@ -267,6 +271,28 @@ hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st
         case 32: return e8m0 ? launch_ds<32, true>(a, st) : launch_ds<32, false>(a, st);
         case 64: return e8m0 ? launch_ds<64, true>(a, st) : launch_ds<64, false>(a, st);
         case 128: return e8m0 ? launch_ds<128, true>(a, st) : launch_ds<128, false>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int down_w4_max_njb(int block_m) {
+    switch (block_m) {
+        case 8: return DSCfg<8>::JMAX;
+        case 16: return DSCfg<16>::JMAX;
+        case 32: return DSCfg<32>::JMAX;
+        case 64: return DSCfg<64>::JMAX;
+        case 128: return DSCfg<128>::JMAX;
+        default: return 0;
+    }
+}
+
+hipError_t launch_down_w4(const DownArgs &a, int block_m, hipStream_t st) {
+    switch (block_m) {
+        case 8: return launch_ds<8, false, true>(a, st);
+        case 16: return launch_ds<16, false, true>(a, st);
+        case 32: return launch_ds<32, false, true>(a, st);
+        case 64: return launch_ds<64, false, true>(a, st);
+        case 128: return launch_ds<128, false, true>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

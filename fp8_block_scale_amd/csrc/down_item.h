@@ -144,6 +144,14 @@ struct DSLayout {
     }
 };
 
+// W4 (the W4A8 variant): W2 rows are E2M1 codes with one exponent byte per
+// 32 K.  In the mixed-format MFMA an E2M1 A operand holds K [32 g, 32 g + 32)
+// in lane group g (one 16-byte load of the row), whose E8M0 scale is that
+// lane's byte g of the K-block's exponent dword; the E4M3 B operand keeps
+// the layout of the FP8 tile (bytes 0-15: K [16 g, +16), bytes 16-31:
+// K [64 + 16 g, +16); measured on gfx950 with one-hot operands), so the
+// intermediate rows are read exactly as in the FP8 path, and h_s is
+// applied per K-block in FP32 as before.
 // One work item: plan block b, row pass `pass`, column group cw (nct tiles
 // of 256 output columns).  Every early return is taken by the whole
 // workgroup.  FUSED (the single-launch path, f != nullptr): the W2 stream
@@ -152,9 +160,10 @@ struct DSLayout {
 // workgroups are read agent-coherent, y is written through, and the item
 // that brings a (token, tile)'s count of written route rows to the token's
 // valid routes adds them into the output (finalize8, route order).
-template <int BM, bool E8M0, bool FUSED>
+template <int BM, bool E8M0, bool FUSED, bool W4 = false>
 __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int b, int cw, int pass,
                                           const FusedArgs *f) {
+    static_assert(!(W4 && (E8M0 || FUSED)), "W4 runs on the two-stage FP32-scale path");
     using C = DSCfg<BM>;
     const DSLayout Ld(C::RP, a.njb, a.nct, C::YROW);
     uint8_t *sH = smem;
@@ -200,13 +209,23 @@ __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int 
     // ---- W2 stream: units (tile t, K-block jb), jb fastest
     const int nunits = nct * njb;
     const int nst = (nunits + C::S - 1) / C::S;
-    const uint8_t *wbase = a.w2 + ((int64_t)e * K + (int64_t)ct0 * 256) * I;
     const int64_t rows_here = K - (int64_t)ct0 * 256 < (int64_t)nct * 256 ? K - (int64_t)ct0 * 256
                                                                            : (int64_t)nct * 256;
+    // bytes per W2 row (E2M1: two codes a byte) and per exponent row (W4)
+    const int wrb = W4 ? (int)(I >> 1) : (int)I, erb = (int)(I >> 5);
+    const uint8_t *wbase = a.w2 + ((int64_t)e * K + (int64_t)ct0 * 256) * wrb;
     const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc((void *)wbase, (short)0, (int)(rows_here * I), 0x00020000);
-    const int past = (int)(rows_here * I);
-    const int rowoff0 = (32 * w + l16) * (int)I + 16 * g;   // subtile 0; subtile 1 is 16 rows on
+        __builtin_amdgcn_make_buffer_rsrc((void *)wbase, (short)0, (int)(rows_here * wrb), 0x00020000);
+    const int past = (int)(rows_here * wrb);
+    __amdgpu_buffer_rsrc_t re = rw;
+    if constexpr (W4)
+        re = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.w2e + ((int64_t)e * K + (int64_t)ct0 * 256) * erb), (short)0,
+            (int)(rows_here * erb), 0x00020000);
+    const int epast = (int)(rows_here * erb);
+    // subtile 0 of this lane; subtile 1 is 16 rows on
+    const int rowoff0 = (32 * w + l16) * wrb + 16 * g;
+    const int eoff0 = (32 * w + l16) * erb;
     u32x4 wb[2][C::S][4];
     auto issue = [&](int st, auto BUF) {
         constexpr int bf = decltype(BUF)::value;
@@ -214,11 +233,22 @@ __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int 
         for (int kk = 0; kk < C::S; ++kk) {
             const int u = st * C::S + kk;
             const int t = u / njb, jb = u - t * njb;
-            const int vo = u < nunits ? rowoff0 + (t * 256) * (int)I + jb * 128 : past;
-            wb[bf][kk][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo, 0, 0);
-            wb[bf][kk][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 64, 0, 0);
-            wb[bf][kk][2] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 16 * (int)I, 0, 0);
-            wb[bf][kk][3] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 16 * (int)I + 64, 0, 0);
+            if constexpr (W4) {
+                // 64 bytes of codes per row and K-block; the exponent dword
+                // of the K-block (four K32 groups) in .x
+                const int vo = u < nunits ? rowoff0 + (t * 256) * wrb + jb * 64 : past;
+                const int eo = u < nunits ? eoff0 + (t * 256) * erb + jb * 4 : epast;
+                wb[bf][kk][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo, 0, 0);
+                wb[bf][kk][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 16 * wrb, 0, 0);
+                wb[bf][kk][2].x = __builtin_amdgcn_raw_buffer_load_b32(re, eo, 0, 0);
+                wb[bf][kk][3].x = __builtin_amdgcn_raw_buffer_load_b32(re, eo + 16 * erb, 0, 0);
+            } else {
+                const int vo = u < nunits ? rowoff0 + (t * 256) * wrb + jb * 128 : past;
+                wb[bf][kk][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo, 0, 0);
+                wb[bf][kk][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 64, 0, 0);
+                wb[bf][kk][2] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 16 * wrb, 0, 0);
+                wb[bf][kk][3] = __builtin_amdgcn_raw_buffer_load_b128(rw, vo + 16 * wrb + 64, 0, 0);
+            }
         }
     };
 
@@ -229,7 +259,7 @@ __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int 
         const uint8_t *hrow0 = a.hq + ((int64_t)b * BM + row0) * I;
         float ws = 0.f;
         int wsi = -1;
-        const int nwb = nct * 2 * njb;                    // (tile, 128-col block, jb)
+        const int nwb = W4 ? 0 : nct * 2 * njb;           // (tile, 128-col block, jb)
         if (tid < nwb) {
             const int tb = tid / njb, jb = tid - tb * njb;     // tb = 2 * tile + col block
             const int64_t cb = (int64_t)ct0 * 2 + tb;
@@ -303,6 +333,26 @@ __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int 
             const int un = st * C::S + kk;
             const int t = un / njb, jb = un - t * njb;
             const bool live = un < nunits;
+            if constexpr (W4) {
+                const u32x4 &a0 = wb[bf][kk][0], &a1 = wb[bf][kk][1];
+                const v8i A0 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+                const v8i A1 = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w, 0, 0, 0, 0};
+                const int ea0 = (int)((wb[bf][kk][2].x >> (8 * g)) & 0xffu);
+                const int ea1 = (int)((wb[bf][kk][3].x >> (8 * g)) & 0xffu);
+#pragma unroll
+                for (int u = 0; u < C::NU; ++u) {
+                    if (16 * u >= nvp) break;
+                    const int row = 16 * u + l16;
+                    const uint8_t *hp = sH + row * Ld.hrowb + jb * 128;
+                    const u32x4 lo = lds_read16(hp + ((g ^ (row & 7)) << 4));
+                    const u32x4 hi = lds_read16(hp + (((4 + g) ^ (row & 7)) << 4));
+                    const v8i B = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    const float sa = live ? sHs[row * njb + jb] : 0.f;
+                    acc[0][u] = mfma16x16x128_e2m1_e4m3(A0, B, ea0) * sa + acc[0][u];
+                    acc[1][u] = mfma16x16x128_e2m1_e4m3(A1, B, ea1) * sa + acc[1][u];
+                }
+            } else {
             const float sb = live ? sWs[(2 * (live ? t : 0) + (w >> 2)) * njb + jb] : 0.f;
             const u32x4 &a0 = wb[bf][kk][0], &a1 = wb[bf][kk][1];
             const u32x4 &b0 = wb[bf][kk][2], &b1 = wb[bf][kk][3];
@@ -329,6 +379,7 @@ __device__ __forceinline__ void down_item(const DownArgs &a, uint8_t *smem, int 
                     acc[0][u] = mfma16x16x128(A0, B) * f + acc[0][u];
                     acc[1][u] = mfma16x16x128(A1, B) * f + acc[1][u];
                 }
+            }
             }
             if (live && jb == njb - 1) {                // tile t finished: park it
 #pragma unroll

@@ -27,7 +27,7 @@ gateup_stream_kernel(GateUpArgs a) {
 
 template <int BM, int MODE>
 hipError_t launch_gs(const GateUpArgs &a, hipStream_t st) {
-    using C = GSCfg<BM>;
+    using C = GSCfg<BM, 0, MODE == kW4>;
     const int64_t grid = (int64_t)a.nblocks * a.nsplit * a.jtiles * C::NPASS;
     if (grid == 0) return hipSuccess;
     if (a.kb_per_split < 1) return hipErrorInvalidValue;
@@ -76,6 +76,17 @@ hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8
         case 32: return launch_gs_mode<32>(a, mode, st);
         case 64: return launch_gs_mode<64>(a, mode, st);
         case 128: return launch_gs_mode<128>(a, mode, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gateup_w4(const GateUpArgs &a, int block_m, hipStream_t st) {
+    switch (block_m) {
+        case 8: return launch_gs<8, kW4>(a, st);
+        case 16: return launch_gs<16, kW4>(a, st);
+        case 32: return launch_gs<32, kW4>(a, st);
+        case 64: return launch_gs<64, kW4>(a, st);
+        case 128: return launch_gs<128, kW4>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

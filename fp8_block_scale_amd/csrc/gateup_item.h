@@ -29,7 +29,14 @@
 //           multiplied with v_mfma_f32_16x16x32_f16 (exact products, FP32
 //           accumulation);
 //   kFp8    v_mfma_f32_16x16x128_f8f6f4 on the codes directly;
-//   kFp8E8  as kFp8 with power-of-two scales applied inside the MFMA.
+//   kFp8E8  as kFp8 with power-of-two scales applied inside the MFMA;
+//   kW4     E2M1 weights with one power-of-two scale per 32 K (the W4A8
+//           variant): each weight row's four K32 exponents of a K-block are
+//           taken relative to their largest, R; the codes are widened to
+//           FP16 with 2^(s - R) folded into the conversion (exact while the
+//           four exponents span at most 23 binades: every E2M1 value has two
+//           significant bits), multiplied as in kExact, and the K-block's
+//           sum is scaled by x_s * 2^(R - 127) per weight row.
 //
 // K is split over items; each writes the partial sums of its valid rows to
 // the workspace and the last one of a tile to arrive (atomic counter) adds
@@ -47,9 +54,9 @@ namespace gs {
 // largest exponents over this item's K-range) and accumulated across
 // K-blocks in the MFMA chain; the sums are scaled by 2^A * 2^B once at the
 // end, so split partials share one scale and add as before.
-enum { kExact = 0, kFp8 = 1, kFp8E8 = 2, kExactE8 = 3 };
+enum { kExact = 0, kFp8 = 1, kFp8E8 = 2, kExactE8 = 3, kW4 = 4 };
 
-template <int BM, int NSO = 0>
+template <int BM, int NSO = 0, bool W4 = false>
 struct GSCfg {
     static_assert(NSO == 0 || (NSO >= 2 && NSO <= 4), "ring depth 2..4");
     // A pass is one MFMA row tile of RP rows (16..64); it holds RPV plan rows
@@ -63,10 +70,12 @@ struct GSCfg {
     // LDS: a ring of NS stages {W13 tile 256 x 128 B, activation rows RP x
     // 128 B, scales: a 16-float run per wave}, reused after the K loop as the
     // FP32 tile [RP][GROW]; then routes, row tokens, a DMA sink, flags.
+    // W4: the W13 tile is 256 x 64 B of E2M1 codes and each wave's scale run
+    // is 256 B: the K32 exponent dwords of 32 weight rows, then 8 x_s.
     static constexpr int NS = NSO ? NSO : (RP <= 32 ? 4 : 3);
-    static constexpr int WB = 256 * 128;
+    static constexpr int WB = 256 * (W4 ? 64 : 128);
     static constexpr int XB = RP * 128;
-    static constexpr int SB = 8 * 16 * 4;
+    static constexpr int SB = W4 ? 8 * 256 : 8 * 16 * 4;
     static constexpr int STB = WB + XB + SB;
     static constexpr int RING = NS * STB;
     static constexpr int GT = RP * GROW * 4;
@@ -76,7 +85,7 @@ struct GSCfg {
     static constexpr int MISC = SINK + 8 * 256;
     static constexpr int EXP = MISC + 16;          // kExactE8: [RP] row, [2] gate/up exponents
     static constexpr int TOTAL = EXP + (RP + 4) * 4;
-    static constexpr int NPS = 6;                  // DMA instructions per wave per stage
+    static constexpr int NPS = W4 ? 4 : 6;         // DMA instructions per wave per stage
 };
 
 // One work item: plan block b, pass `pass` of its rows, j-tile jt, K-split
@@ -88,7 +97,8 @@ struct GSCfg {
 template <int BM, int MODE, int NSO, bool FUSED>
 __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, int b, int split,
                                             int jt, int pass, uint32_t *cnt_h) {
-    using C = GSCfg<BM, NSO>;
+    constexpr bool W4 = MODE == kW4;
+    using C = GSCfg<BM, NSO, W4>;
     static_assert(C::TOTAL <= 160 * 1024, "LDS budget");
     float *sG = reinterpret_cast<float *>(smem);    // reuses the ring after the loop
     int *sTok = reinterpret_cast<int *>(smem + C::TOK);    // route of each row, -1 if none
@@ -145,13 +155,27 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     // scale load (lanes 0-7: x_s of rows 8w..; lanes 8, 9: the gate and up
     // weight-block scales).  Masked and padding rows read the last valid
     // row's token (sXt); their columns are never stored.
+    // W4: two W13 segments (16 rows x 64 B each, 16-byte chunks XOR-swizzled
+    // by row & 3), the activation segment, and one 4-byte load: lanes 0-31
+    // the K32 exponent dword of weight rows 32w.., lanes 32-39 x_s of rows 8w...
     const int sub = lane >> 3, slot = lane & 7;
     const uint8_t *wsrc[4];
+    if constexpr (W4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (w * 4 + i) * 8 + sub;                  // tile row 0..255
-        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
-        wsrc[i] = a.w13 + ((int64_t)e * 2 * I + n) * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
+        for (int i = 0; i < 2; ++i) {
+            const int row = (w * 2 + i) * 16 + (lane >> 2);          // tile row 0..255
+            const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+            wsrc[i] = a.w13 + ((int64_t)e * 2 * I + n) * (K >> 1) + (int64_t)kb0 * 64 +
+                      ((lane & 3) ^ (row & 3)) * 16;
+        }
+        wsrc[2] = wsrc[3] = nullptr;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (w * 4 + i) * 8 + sub;                  // tile row 0..255
+            const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+            wsrc[i] = a.w13 + ((int64_t)e * 2 * I + n) * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
+        }
     }
     const bool xw = w < C::RP / 8;
     const uint8_t *xsrc;
@@ -159,13 +183,24 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         const int row = xw ? 8 * w + sub : 0;
         xsrc = a.xq + (int64_t)sXt[row] * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
     }
-    const float *ssrc;
-    if (lane < 8) {
+    // 4-byte scale source of this lane, advanced by 4 bytes per K-block
+    const uint8_t *ssrc;
+    if constexpr (W4) {
+        if (lane < 32) {
+            const int row = 32 * w + lane;
+            const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+            ssrc = a.w13e + ((int64_t)e * 2 * I + n) * (K >> 5) + (int64_t)kb0 * 4;
+        } else {
+            const int row = 8 * w + (lane & 7) < C::RP ? 8 * w + (lane & 7) : 0;
+            ssrc = reinterpret_cast<const uint8_t *>(a.xs + (int64_t)sXt[row] * a.nkb + kb0);
+        }
+    } else if (lane < 8) {
         const int row = 8 * w + lane < C::RP ? 8 * w + lane : 0;
-        ssrc = a.xs + (int64_t)sXt[row] * a.nkb + kb0;
+        ssrc = reinterpret_cast<const uint8_t *>(a.xs + (int64_t)sXt[row] * a.nkb + kb0);
     } else {
         const int nb13 = (int)(2 * I / 128);
-        ssrc = a.w13s + ((int64_t)e * nb13 + (lane == 9 ? (int)(I / 128) : 0) + jt) * a.nkb + kb0;
+        ssrc = reinterpret_cast<const uint8_t *>(
+            a.w13s + ((int64_t)e * nb13 + (lane == 9 ? (int)(I / 128) : 0) + jt) * a.nkb + kb0);
     }
     // An expert with this one plan block streams its W13 tile exactly once:
     // those loads take the non-temporal policy (6.6 against 5.9 TB/s on a
@@ -175,18 +210,19 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
                       ((int64_t)(b + 1) * BM >= ntp || a.eids[b + 1] != e);
     auto issue = [&](int st, int kbl) {
         uint8_t *base = smem + st * C::STB;
+        constexpr int NW = W4 ? 2 : 4, WSTEP = W4 ? 64 : 128;
         if (once) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16_nt(wsrc[i] + kbl * 128, base + (w * 4 + i) * 1024);
+            for (int i = 0; i < NW; ++i) lds_dma16_nt(wsrc[i] + kbl * WSTEP, base + (w * NW + i) * 1024);
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(wsrc[i] + kbl * 128, base + (w * 4 + i) * 1024);
+            for (int i = 0; i < NW; ++i) lds_dma16(wsrc[i] + kbl * WSTEP, base + (w * NW + i) * 1024);
         }
         if (xw)
             lds_dma16(xsrc + kbl * 128, base + C::WB + w * 1024);
         else
             lds_dma4(xsrc + kbl * 128, sSink + w * 256);
-        if (lane < 10) lds_dma4(ssrc + kbl, base + C::WB + C::XB + w * 64);
+        if (lane < (W4 ? 40 : 10)) lds_dma4(ssrc + kbl * 4, base + C::WB + C::XB + w * (C::SB / 8));
     };
 
     if constexpr (MODE == kExactE8) {
@@ -220,6 +256,56 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         accg[u] = v4f{0.f, 0.f, 0.f, 0.f};
         accu[u] = v4f{0.f, 0.f, 0.f, 0.f};
     }
+
+    auto compute_w4 = [&](int st) {
+        const uint8_t *Ws = smem + st * C::STB;
+        const uint8_t *Xs = Ws + C::WB;
+        const uint8_t *Sb = Ws + C::WB + C::XB;
+        // weight rows: this lane's A rows (gate / up), widened with their
+        // K32 scales relative to the row's largest exponent R of the K-block
+        v8h W[2][4];
+        v4f F[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 128 * h + 16 * w + l16;
+            const uint8_t *rp = Ws + row * 64 + ((g & 1) << 3);
+            const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ (row & 3)) << 4));
+            const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ (row & 3)) << 4));
+            const uint32_t sw = *reinterpret_cast<const uint32_t *>(Sb + (row >> 5) * 256 + (row & 31) * 4);
+            const int R = max_byte4(sw);
+            const int dlo = (int)((sw >> (8 * (g >> 1))) & 0xffu) - R;
+            const int dhi = (int)((sw >> (8 * (2 + (g >> 1)))) & 0xffu) - R;
+            // below 2^-30 every product rounds to zero in FP16 either way
+            const float flo = __uint_as_float((uint32_t)(127 + (dlo < -30 ? -30 : dlo)) << 23);
+            const float fhi = __uint_as_float((uint32_t)(127 + (dhi < -30 ? -30 : dhi)) << 23);
+            W[h][0] = e2m1x8_to_f16(d01.x, flo);
+            W[h][1] = e2m1x8_to_f16(d01.y, flo);
+            W[h][2] = e2m1x8_to_f16(d23.x, fhi);
+            W[h][3] = e2m1x8_to_f16(d23.y, fhi);
+            // the four output rows of this lane: 2^(R - 127) of each
+            const int orow = 128 * h + 16 * w + 4 * g;
+            const u32x4 so = lds_read16(Sb + (orow >> 5) * 256 + (orow & 31) * 4);
+            F[h] = v4f{__builtin_amdgcn_ldexpf(1.0f, max_byte4(so.x) - 127),
+                       __builtin_amdgcn_ldexpf(1.0f, max_byte4(so.y) - 127),
+                       __builtin_amdgcn_ldexpf(1.0f, max_byte4(so.z) - 127),
+                       __builtin_amdgcn_ldexpf(1.0f, max_byte4(so.w) - 127)};
+        }
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+            if (16 * u >= nvp) break;
+            const int row = 16 * u + l16;
+            const uint8_t *xp = Xs + row * 128;
+            const u32x4 lo = lds_read16(xp + ((g ^ (row & 7)) << 4));
+            const u32x4 hi = lds_read16(xp + (((4 + g) ^ (row & 7)) << 4));
+            const float sa = *reinterpret_cast<const float *>(Sb + (row >> 3) * 256 + 128 + (row & 7) * 4);
+            v8h Bh[4];
+            e4m3x32_to_f16(lo, hi, Bh);
+            const v4f tg = mfma16x16x128_f16(W[0], Bh);
+            const v4f tu = mfma16x16x128_f16(W[1], Bh);
+            accg[u] = tg * (F[0] * sa) + accg[u];
+            accu[u] = tu * (F[1] * sa) + accu[u];
+        }
+    };
 
     auto compute = [&](int st) {
         const uint8_t *Ws = smem + st * C::STB;
@@ -300,7 +386,10 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             wait_vmcnt<0>();
         stage_barrier();
         if (kb + C::NS - 1 < nk) issue((kb + C::NS - 1) % C::NS, kb + C::NS - 1);
-        compute(kb % C::NS);
+        if constexpr (W4)
+            compute_w4(kb % C::NS);
+        else
+            compute(kb % C::NS);
     }
 
     if constexpr (MODE == kExactE8) {

@@ -87,6 +87,7 @@ struct GateUpArgs {
     const float *xs;
     const uint8_t *w13;
     const float *w13s;
+    const uint8_t *w13e;  // W4A8: K32 exponent bytes [E, 2I, K / 32] (w13 then holds E2M1 pairs)
     const int32_t *sorted;
     const int32_t *eids;
     const int32_t *ntp;
@@ -113,6 +114,7 @@ struct DownArgs {
     const float *hs;
     const uint8_t *w2;
     const float *w2s;
+    const uint8_t *w2e;   // W4A8: K32 exponent bytes [E, K, I / 32] (w2 then holds E2M1 pairs)
     const float *topk_w;
     const int32_t *sorted;
     const int32_t *eids;
@@ -166,6 +168,12 @@ hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st);
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                               hipStream_t st);
 hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
+// The W4A8 variant (E2M1 weights, K32 exponent bytes in w13e / w2e) on the
+// small-grid kernels: gate/up as above (exact FP16 products); the down stage
+// needs I / 128 <= down_w4_max_njb(block_m).
+hipError_t launch_gateup_w4(const GateUpArgs &a, int block_m, hipStream_t st);
+int down_w4_max_njb(int block_m);
+hipError_t launch_down_w4(const DownArgs &a, int block_m, hipStream_t st);
 // Large-grid down GEMM: persistent, over the gate/up stage's row tiles.
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
 // The single-launch path (fused.hip): steps 3-5 over the arguments of both

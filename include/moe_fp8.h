@@ -317,6 +317,46 @@ moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                void *out_bf16, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* ------------------------------------------------------- W4A8 variant -- */
+
+/* Steps 3-5 with E2M1 (FP4) expert weights: FP8 activations against E2M1
+ * weights with one power-of-two scale per 32 elements along K, the weight
+ * scales applied in FP32 (sglang-glm53-flash-sm120 PR #13, description of
+ * its FP8-activation path for E2M1-K32 weights).  Everything else -- the
+ * plan, the activation and intermediate FP8 quantisation, SwiGLU, the route
+ * sum into out_bf16 -- is that of moe_fp8_experts.
+ *   w13   [E, 2I, K/2] uint8: E2M1 codes, two per byte, the even K index in
+ *         the low nibble (sign bit 3, exponent bits 2-1 with bias 1, mantissa
+ *         bit 0: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6);
+ *   w13_e [E, 2I, K/32] uint8: the K32 scales as E8M0 bytes, scale =
+ *         2^(byte - 127); 255 (E8M0 NaN) is not accepted and gives
+ *         undefined results;
+ *   w2 [E, K, I/2], w2_e [E, K, I/32]: the same for the down projection.
+ * Gate/up products are exact (FP16 MFMA on widened codes, FP32 sums) while
+ * the four K32 exponents of a weight row within each 128-wide K-block span
+ * at most 23; beyond that the smaller groups' products round to FP16.
+ * Runs the per-block kernels only.  Constraints: those of moe_fp8_experts,
+ * I / 128 <= 512 / min(max(block_m, 16), 64), w13 / w2 16-byte and w13_e /
+ * w2_e 4-byte aligned; flags MOE_F_INTER_UE8M0 and a forced split-K apply;
+ * MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP, MOE_PATH_PERSISTENT and MOE_FUSE_ON
+ * give MOE_ERR_UNSUPPORTED.  The workspace is sized by
+ * moe_w4a8_experts_workspace_size (0 if the arguments are rejected); the
+ * intermediate rows sit where moe_fp8_experts_workspace_layout says. */
+size_t moe_w4a8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,
+                                       int32_t top_k, int32_t block_m, int64_t sorted_cap,
+                                       uint32_t flags);
+
+moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s,
+                            const uint8_t *w13, const uint8_t *w13_e,
+                            const uint8_t *w2, const uint8_t *w2_e,
+                            const float *topk_weights,
+                            const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                            const int32_t *num_tokens_post_padded,
+                            int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                            int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                            void *out_bf16, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
 /* ------------------------------------------------- no-allocation variant -- */
 
 /* For callers that cannot allocate device memory (code under HIP graph

@@ -25,7 +25,8 @@ import numpy as np
 import torch
 
 import fp8_block_scale_amd as moe
-from oracle import (e4m3_decode, e4m3_decode_table, experts_ref, plan_ref, quant_act_ref)
+from oracle import (e4m3_decode, e4m3_decode_table, experts_ref, experts_w4a8_ref, plan_ref,
+                    quant_act_ref)
 from oracle.quant import SCALE_FP32, SCALE_UE8M0
 
 REL_L2_MAX = 5e-3
@@ -128,7 +129,9 @@ def run_gpu(case, out_init=None, flags=0, act_mode=moe.MOE_SCALE_FP32, ntp_overr
     """Whole path on the GPU through the C ABI binding."""
     dev = case.x.device
     assert dev.type == "cuda"
-    b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
+    w4 = is_w4a8(case)
+    b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev,
+                            w4a8=w4)
     if garbage_plan:
         b.sorted_ids.fill_(0x7F7F7F7F)
         b.expert_ids.fill_(0x7F7F7F7F)
@@ -141,9 +144,10 @@ def run_gpu(case, out_init=None, flags=0, act_mode=moe.MOE_SCALE_FP32, ntp_overr
     ntp = b.ntp
     if ntp_override is not None:
         ntp = torch.tensor([ntp_override], dtype=torch.int32, device=dev)
-    moe.moe_fp8_experts(b.x_q, b.x_s, case.w13, case.w13_s, case.w2, case.w2_s, case.topk_weights,
-                        b.sorted_ids, b.expert_ids, ntp, case.top_k, case.block_m, out,
-                        b.workspace, flags, stream)
+    experts = moe.moe_w4a8_experts if w4 else moe.moe_fp8_experts
+    experts(b.x_q, b.x_s, case.w13, case.w13_s, case.w2, case.w2_s, case.topk_weights,
+            b.sorted_ids, b.expert_ids, ntp, case.top_k, case.block_m, out, b.workspace, flags,
+            stream)
     torch.cuda.synchronize()
     r = GpuRun()
     r.bufs = b
@@ -163,6 +167,11 @@ class OracleRun:
     pass
 
 
+def is_w4a8(case):
+    """Cases whose weights are E2M1 with K32 exponent bytes."""
+    return case.meta.get("fmt") == "w4a8"
+
+
 def host_inputs(case):
     """Copy a case's inputs to host numpy arrays (byte-identical)."""
     h = dict(x=case.x.float().cpu().numpy(), ids=case.topk_ids.cpu().numpy(),
@@ -180,9 +189,10 @@ def run_oracle(case, h=None, out_init=None, act_mode=SCALE_FP32, inter_mode=SCAL
     P = o.P if P_override is None else min(P_override, o.P)
     init = None if out_init is None else out_init.float().cpu().numpy()
     t0 = time.time()
-    o.res = experts_ref(o.x_q, o.x_s, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"],
-                        o.sorted, o.expert_ids, P, case.top_k, case.block_m, out_init=init,
-                        inter_mode=inter_mode, tokens=tokens)
+    ref = experts_w4a8_ref if is_w4a8(case) else experts_ref
+    o.res = ref(o.x_q, o.x_s, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"], o.sorted,
+                o.expert_ids, P, case.top_k, case.block_m, out_init=init, inter_mode=inter_mode,
+                tokens=tokens)
     o.seconds = time.time() - t0
     return o
 

@@ -1,0 +1,160 @@
+"""GPU parity of the W4A8 variant (moe_w4a8_experts: FP8 activations, E2M1
+weights with K32 exponent bytes) against the oracle's W4A8 path, on the
+bars of the FP8 path (tests/parity.py): plan and activation codes
+bit-exact, intermediate codes within 1e-4 and one value step, outputs at
+relative L2 <= 5e-3 and max abs <= 2e-2 * rms.  Full-size workloads compare
+sampled tokens that reach every expert the batch touches.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scale_amd as moe
+from moe_workloads import CONFIGS, SKEW_ZERO_SCALE_EXPERT, make_case
+from oracle.quant import SCALE_FP32, SCALE_UE8M0
+
+from parity import (check_plan, check_tail_untouched, compare_intermediate, compare_output,
+                    host_inputs, log, run_gpu, run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+_WEIGHTS = {}
+
+
+def case_of(name, M=None, ids_dtype=torch.int32, **override):
+    c = dict(CONFIGS[name], **override)
+    key = (name, c["E"], c["K"], c["I"], c["seed"])
+    cs = make_case(name, M=M, device=DEV, ids_dtype=ids_dtype, weights=_WEIGHTS.get(key),
+                   config=c if override else None, fmt="w4a8")
+    _WEIGHTS[key] = (cs.w13, cs.w13_s, cs.w2, cs.w2_s)
+    return cs
+
+
+def parity(cs, flags=0, out_init=None, tokens=None, label=""):
+    log(f"[w4a8] {label} {cs.name} M={cs.M} E={cs.E} K={cs.K} I={cs.I} top_k={cs.top_k} "
+        f"bm={cs.block_m} flags={flags:#x} tokens={'all' if tokens is None else len(tokens)}")
+    g = run_gpu(cs, out_init=out_init, flags=flags)
+    inter = SCALE_UE8M0 if flags & moe.MOE_F_INTER_UE8M0 else SCALE_FP32
+    o = run_oracle(cs, h=host_inputs(cs), out_init=out_init, inter_mode=inter, tokens=tokens)
+    check_plan(g, o)
+    check_tail_untouched(g, o, cs.block_m)
+    assert np.array_equal(g.x_q, o.x_q) and np.array_equal(g.x_s, o.x_s)
+    rows = o.res.row_valid.copy()
+    if tokens is not None:
+        t_of_row = np.where(rows, o.sorted[:o.P] // cs.top_k, -1)
+        rows &= np.isin(t_of_row, np.asarray(tokens))
+    ic = compare_intermediate(g.h_q[:o.P], g.h_s[:o.P], o.res.h_q, o.res.h_s, rows)
+    trows = np.nonzero(o.res.computed_tokens)[0]
+    oc = compare_output(g.out[trows], o.res.ref64[trows])
+    log(f"[w4a8]   ok: P={o.P} inter={ic} out={oc} oracle_s={o.seconds:.2f}")
+    return g, o
+
+
+def cover_tokens(cs, n, seed, extra=()):
+    """n random tokens plus the first, the last and `extra`, then greedily
+    tokens that reach experts not yet reached, until every expert the batch
+    touches feeds a compared row."""
+    rng = np.random.default_rng(seed)
+    t = set(rng.choice(cs.M, size=min(n, cs.M), replace=False).tolist()) | set(extra)
+    t |= {0, cs.M - 1}
+    ids = cs.topk_ids.cpu().numpy()
+    valid = (ids >= 0) & (ids < cs.E)
+    onehot = np.zeros((cs.M, cs.E), dtype=bool)
+    rr, cc = np.nonzero(valid)
+    onehot[rr, ids[rr, cc]] = True
+    covered = onehot[sorted(t)].any(0)
+    touched = onehot.any(0)
+    while (touched & ~covered).any():
+        best = int(np.argmax(onehot[:, ~covered].sum(1)))
+        t.add(best)
+        covered |= onehot[best]
+    return sorted(t)
+
+
+SPLIT1 = 1 << moe.MOE_F_SPLITK_SHIFT
+
+
+@pytest.mark.parametrize("flags", [0, SPLIT1, moe.MOE_F_INTER_UE8M0])
+def test_tiny(flags):
+    parity(case_of("tiny"), flags=flags, label="tiny")
+
+
+@pytest.mark.parametrize("bm", [8, 32, 64, 128])
+def test_tiny_block_m(bm):
+    parity(case_of("tiny", M=24, block_m=bm), label="tiny block_m")
+
+
+def test_accumulates_into_prefilled_output():
+    cs = case_of("tiny")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    init = (torch.randn((cs.M, cs.K), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    parity(cs, out_init=init, label="prefilled")
+
+
+def test_scale_spread_within_k_blocks():
+    """K32 exponents spread over 23 binades inside each 128-wide K-block (the
+    exactness limit of the gate/up widening) and over the rows; the weights
+    keep their codes."""
+    cs = case_of("tiny", M=16)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    w13e = torch.randint(104, 128, cs.w13_s.shape, generator=g, device=DEV, dtype=torch.int32)
+    w2e = torch.randint(110, 134, cs.w2_s.shape, generator=g, device=DEV, dtype=torch.int32)
+    cs.w13_s = w13e.to(torch.uint8)
+    cs.w2_s = w2e.to(torch.uint8)
+    parity(cs, label="scale spread")
+
+
+@pytest.mark.parametrize("M,flags", [(1, 0), (1, SPLIT1), (1, 7 << moe.MOE_F_SPLITK_SHIFT), (4, 0),
+                                     (16, 0)])
+def test_decode(M, flags):
+    parity(case_of("decode", M=M), flags=flags, label="decode")
+
+
+def test_page1_small():
+    parity(case_of("page1", M=24), label="page1 small")
+
+
+@pytest.mark.parametrize("M", [1024, 4096])
+def test_page1_sampled(M):
+    """Page 1's W4A8 workload (E=288, K=4096, I=1024, top-8) at two of its
+    token counts; the sampled tokens reach every expert."""
+    cs = case_of("page1", M=M)
+    parity(cs, tokens=cover_tokens(cs, 6, M), label="page1")
+
+
+@pytest.mark.parametrize("dt", [torch.int32, torch.int64])
+def test_skew_masked_routes_and_zero_expert(dt):
+    """Masked routes (-1), int32 and int64 ids, an expert whose codes are all
+    zero, hot experts with several plan blocks."""
+    cs = case_of("skew", M=256, ids_dtype=dt)
+    ids = cs.topk_ids.cpu().numpy()
+    masked = int(np.nonzero((ids < 0).any(1))[0][0])
+    zero = int(np.nonzero((ids == SKEW_ZERO_SCALE_EXPERT).any(1))[0][0])
+    parity(cs, tokens=cover_tokens(cs, 8, 3, extra=(masked, zero)), label="skew")
+
+
+def test_rejects_what_does_not_apply():
+    cs = case_of("tiny")
+    b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, 0, DEV, w4a8=True)
+    out = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
+    fuse_on = moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT
+    persist = moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT
+    for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0, fuse_on, persist):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_w4a8_experts(b.x_q, b.x_s, cs.w13, cs.w13_s, cs.w2, cs.w2_s, cs.topk_weights,
+                                 b.sorted_ids, b.expert_ids, b.ntp, cs.top_k, cs.block_m, out,
+                                 b.workspace, fl)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED

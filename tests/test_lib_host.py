@@ -257,3 +257,34 @@ def test_route_plan_validation():
     # 100000 routes need the plan workspace
     assert _err(call(M=20000, Er=256, k=4, ns=1)) == "MOE_ERR_CAPACITY"
     assert _err(call(M=0)) in ("MOE_OK", "MOE_ERR_HIP")      # M = 0: only the P fill
+
+
+def test_w4a8_validation_before_any_device_call():
+    """moe_w4a8_experts rejects what does not apply to E2M1 weights and bad
+    shapes before touching the device (these calls run without a GPU)."""
+    f = _raw("moe_w4a8_experts")
+    base = dict(M=4, K=256, I=256, E=8, k=2, bm=16, sc=128, fl=0, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["M"], a["K"], a["I"],
+                 a["E"], a["k"], a["bm"], a["sc"], a["fl"], FAKE, a["ws"], a["wsb"], None)
+
+    persist = moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT
+    for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0, persist,
+               moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT):
+        assert _err(call(fl=fl)) == "MOE_ERR_UNSUPPORTED", fl
+        assert moe.moe_w4a8_experts_workspace_size(4, 256, 256, 8, 2, 16, 128, fl) == 0
+    # the down stage keeps a block's intermediate rows in LDS: I / 128 <= 512 / 64 at block_m 64
+    assert _err(call(I=2048, bm=64, sc=128)) == "MOE_ERR_UNSUPPORTED"
+    assert _err(call(I=1024, bm=64, sc=128, wsb=16)) == "MOE_ERR_CAPACITY"
+    assert _err(call(K=200)) == "MOE_ERR_SHAPE"
+    assert _err(call(wsb=16)) == "MOE_ERR_CAPACITY"
+    assert _err(call(ws=None)) == "MOE_ERR_NULL"
+    assert _err(call(M=0)) == "MOE_OK"
+    # explicit stream paths are accepted; the workspace is that of those paths
+    stream = (moe.MOE_PATH_STREAM << moe.MOE_F_GATEUP_PATH_SHIFT) | \
+             (moe.MOE_PATH_STREAM << moe.MOE_F_DOWN_PATH_SHIFT)
+    w4 = moe.moe_w4a8_experts_workspace_size(4096, 4096, 1024, 288, 8, 64, 50944)
+    assert w4 == moe.moe_w4a8_experts_workspace_size(4096, 4096, 1024, 288, 8, 64, 50944, stream)
+    assert w4 == moe.moe_fp8_experts_workspace_size(4096, 4096, 1024, 288, 8, 64, 50944, stream)
