@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--fuse", choices=("auto", "on", "off"), default="auto",
                     help="steps 3-5 as one launch (on), as two stages (off), or the library's "
                          "choice (auto)")
+    ap.add_argument("--w4a8", action="store_true",
+                    help="the W4A8 variant: E2M1 weights with K32 exponent bytes "
+                         "(moe_w4a8_experts, per-block kernels)")
     ap.add_argument("--router", action="store_true",
                     help="route from FP32 logits inside the plan's launches (moe_route_plan): "
                          "softmax top-k, routed scaling; the decode workload's expert 256 as a "
@@ -90,14 +93,19 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(case, n_touched, R_valid, P, n_tok):
+def algorithmic_bytes(case, n_touched, R_valid, P, n_tok, w4a8=False):
     """Bytes each stage must move at least once (see the layout notes of the
     library): touched expert weights and scales, activations once per token,
     intermediate rows once per valid route, the plan, and the BF16 output
-    read-modify-write."""
+    read-modify-write.  W4A8 weights: half a byte per element plus one
+    exponent byte per 32."""
     K, I, M = case.K, case.I, case.M
-    w13 = n_touched * (2 * I * K + (2 * I // 128) * (K // 128) * 4)
-    w2 = n_touched * (K * I + (K // 128) * (I // 128) * 4)
+    if w4a8:
+        w13 = n_touched * (I * K + 2 * I * (K // 32))
+        w2 = n_touched * (K * I // 2 + K * (I // 32))
+    else:
+        w13 = n_touched * (2 * I * K + (2 * I // 128) * (K // 128) * 4)
+        w2 = n_touched * (K * I + (K // 128) * (I // 128) * 4)
     xq = n_tok * (K + (K // 128) * 4)
     h = R_valid * (I + (I // 128) * 4)
     plan = P * 4 + (P // case.block_m) * 4
@@ -161,12 +169,13 @@ def host_cpu_model():
     return "unknown"
 
 
-def cpu_baseline(case, n_tokens, runs=3):
+def cpu_baseline(case, n_tokens, runs=3, w4a8=False):
     """The CPU oracle (plain numpy, FP64 dot products) on the first n_tokens
     tokens of the same batch, all five steps, timed `runs` times (median);
     reported in the metric's unit with the host CPU, BLAS and thread count."""
     import numpy as np
-    from oracle import experts_ref, plan_ref, quant_act_ref
+    from oracle import experts_ref, experts_w4a8_ref, plan_ref, quant_act_ref
+    ref = experts_w4a8_ref if w4a8 else experts_ref
     blas, threads = "unknown", os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
@@ -187,8 +196,8 @@ def cpu_baseline(case, n_tokens, runs=3):
         xq_full = np.zeros((case.M, case.K), np.uint8)
         xs_full = np.zeros((case.M, case.K // 128), np.float32)
         xq_full[:n_tokens], xs_full[:n_tokens] = xq, xs
-        experts_ref(xq_full, xs_full, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"], s, e, P,
-                    case.top_k, case.block_m, tokens=range(n_tokens))
+        ref(xq_full, xs_full, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"], s, e, P,
+            case.top_k, case.block_m, tokens=range(n_tokens))
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     ids = h["ids"][:n_tokens]
@@ -222,7 +231,8 @@ def main():
     if args.block_m is not None:
         from moe_workloads import CONFIGS
         config = dict(CONFIGS[args.workload], block_m=args.block_m)
-    case = make_case(args.workload, M=args.M, device=dev, config=config)
+    case = make_case(args.workload, M=args.M, device=dev, config=config,
+                     fmt="w4a8" if args.w4a8 else "w8a8")
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
@@ -250,13 +260,14 @@ def main():
     ids = case.topk_ids
     valid = (ids >= 0) & (ids < case.E)
     n_touched = int(torch.unique(ids[valid]).numel())
-    touched_w = n_touched * 3 * case.I * case.K
+    touched_w = n_touched * 3 * case.I * case.K // (2 if args.w4a8 else 1)
     nsets = args.weight_sets or max(1, min(64, -(-(1 << 30) // max(touched_w, 1))))
     wsets = [(case.w13, case.w13_s, case.w2, case.w2_s)]
     for _ in range(nsets - 1):
         wsets.append(tuple(t.clone() for t in wsets[0]))
 
-    b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev)
+    b = moe.MoeLayerBuffers(case.M, case.K, case.I, case.E, case.top_k, case.block_m, flags, dev,
+                            w4a8=args.w4a8)
     out = torch.zeros((case.M, case.K), dtype=torch.bfloat16, device=dev)
     if args.router:
         # the E=257 geometry: 256 routed experts + expert 256 shared, top-8 + shared
@@ -292,15 +303,19 @@ def main():
         moe.moe_fp8_down_reduce(w2, w2_s, case.topk_weights, b.sorted_ids, b.expert_ids,
                                 b.ntp, case.top_k, case.block_m, out, b.workspace, flags, stream)
 
+    experts_fn = moe.moe_w4a8_experts if args.w4a8 else moe.moe_fp8_experts
+
     def stage_experts(stream, k):
         w13, w13_s, w2, w2_s = wsets[k % nsets]
-        moe.moe_fp8_experts(b.x_q, b.x_s, w13, w13_s, w2, w2_s, case.topk_weights, b.sorted_ids,
-                            b.expert_ids, b.ntp, case.top_k, case.block_m, out, b.workspace, flags,
-                            stream)
+        experts_fn(b.x_q, b.x_s, w13, w13_s, w2, w2_s, case.topk_weights, b.sorted_ids,
+                   b.expert_ids, b.ntp, case.top_k, case.block_m, out, b.workspace, flags, stream)
 
-    sched = moe.moe_fp8_experts_schedule(case.M, case.K, case.I, case.E, case.top_k, case.block_m,
-                                         b.sorted_ids.numel(), flags)
-    fused = sched[4]
+    if args.w4a8:
+        fused = False
+    else:
+        sched = moe.moe_fp8_experts_schedule(case.M, case.K, case.I, case.E, case.top_k,
+                                             case.block_m, b.sorted_ids.numel(), flags)
+        fused = sched[4]
     # one step: plan + quantisation, then steps 3-5 as the library schedules them
     stages = (stage_plan_quant, stage_experts)
 
@@ -367,29 +382,39 @@ def main():
 
         ms = replay_ms(capture(stages))
         plan_quant, experts = (replay_ms(capture([fn])) for fn in stages)
-        if not fused:       # the two stages of steps 3-5, each timed on its own
+        if not fused and not args.w4a8:   # the two stages of steps 3-5, each timed alone
             gate_up, down = (replay_ms(capture([fn])) for fn in (stage_gate_up, stage_down))
 
     R_valid = int(valid.sum())
     P = int(b.ntp.item())
     flops = 2.0 * R_valid * 3 * case.K * case.I
-    nb = algorithmic_bytes(case, n_touched, R_valid, P, case.M)
+    nb = algorithmic_bytes(case, n_touched, R_valid, P, case.M, args.w4a8)
     tflops = flops / (ms * 1e-3) / 1e12
 
     if fused or gate_up is None:
         # the single launch (or eager timing without stage graphs): the
         # dominant kernel is steps 3-5 as a whole, HBM-bound at these sizes
-        kname = "fused_experts_kernel" if fused else "steps 3-5"
+        kname = "fused_experts_kernel" if fused else ("steps 3-5 (W4A8)" if args.w4a8
+                                                       else "steps 3-5")
         t_hbm = nb["layer"] / (HBM_PEAK_GBS * 1e9)
+        # gate/up (2/3 of the flops) on the FP16 MFMA, down on the FP8 one
         t_mfma = flops / (FP16_MFMA_PEAK * 1e12) * (2 / 3) + flops / (FP8_MFMA_PEAK * 1e12) / 3
-        achieved = nb["layer"] / (experts * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "frac_vs_fp8_dense_peak": round(flops / (experts * 1e-3) / 1e12 / FP8_MFMA_PEAK, 4),
-                "traffic": measured_traffic(kname, f"{case.name} M={case.M}", flags)
-                if fused else None,
-                "kernel": kname, "algorithmic_bytes": nb["layer"], "avg_ms": round(experts, 4),
-                "bound_ms": {"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4)}}
+        if t_mfma > t_hbm:
+            peak = flops / t_mfma / 1e12            # the blend of the two dense peaks
+            achieved = flops / (experts * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": round(peak, 1),
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "mfma": "blend: 2/3 of the flops at the fp16 and 1/3 at the fp8 dense peak",
+                    "algorithmic_flops": flops}
+        else:
+            achieved = nb["layer"] / (experts * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        roof.update({"frac_vs_fp8_dense_peak": round(flops / (experts * 1e-3) / 1e12 / FP8_MFMA_PEAK, 4),
+                     "traffic": measured_traffic(kname, f"{case.name} M={case.M}", flags)
+                     if fused else None,
+                     "kernel": kname, "algorithmic_bytes": nb["layer"], "avg_ms": round(experts, 4),
+                     "bound_ms": {"hbm": round(t_hbm * 1e3, 4), "mfma": round(t_mfma * 1e3, 4)}})
     else:
         # gate/up roofline: the larger of the two lower bounds on its time binds
         gu_flops = 2.0 * R_valid * case.K * 2 * case.I
@@ -431,7 +456,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": "fp8 x e2m1" if args.w4a8 else "fp8",
         "data": "synthetic",
         "config": {
             "workload": f"{case.name}: E={case.E} K={case.K} I={case.I} top_k={case.top_k} "
@@ -444,6 +469,7 @@ def main():
                       **({} if gate_up is None else {"gate_up": round(gate_up, 4),
                                                      "down_reduce": round(down, 4)})},
         "single_launch": bool(fused),
+        "weights": "e2m1 + K32 exponent bytes" if args.w4a8 else "e4m3 + 128x128 fp32 scales",
         "router": bool(args.router),
         "launch": "eager" if args.eager else "hip graph (K steps per replay)",
         "weight_sets": nsets,
@@ -453,7 +479,8 @@ def main():
         "steps35": steps35,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_tokens, case.M), args.cpu_runs)
+        res["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_tokens, case.M), args.cpu_runs,
+                                           args.w4a8)
     print(f"# generated inputs in {t_gen:.1f} s", file=sys.stderr)
     print(json.dumps(res), flush=True)
 
