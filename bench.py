@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--w4a8", action="store_true",
                     help="the W4A8 variant: E2M1 weights with K32 exponent bytes "
                          "(moe_w4a8_experts, per-block kernels)")
+    ap.add_argument("--prepack", action="store_true",
+                    help="W13 in the packed tile layout (moe_prepack_w13, done before timing)")
     ap.add_argument("--router", action="store_true",
                     help="route from FP32 logits inside the plan's launches (moe_route_plan): "
                          "softmax top-k, routed scaling; the decode workload's expert 256 as a "
@@ -262,6 +264,10 @@ def main():
     n_touched = int(torch.unique(ids[valid]).numel())
     touched_w = n_touched * 3 * case.I * case.K // (2 if args.w4a8 else 1)
     nsets = args.weight_sets or max(1, min(64, -(-(1 << 30) // max(touched_w, 1))))
+    if args.prepack:        # offline: not part of a step
+        assert not args.w4a8, "the packed layout is for E4M3 W13"
+        case.w13 = moe.moe_prepack_w13(case.w13)
+        flags |= moe.MOE_F_W13_PACKED
     wsets = [(case.w13, case.w13_s, case.w2, case.w2_s)]
     for _ in range(nsets - 1):
         wsets.append(tuple(t.clone() for t in wsets[0]))
@@ -469,6 +475,7 @@ def main():
                       **({} if gate_up is None else {"gate_up": round(gate_up, 4),
                                                      "down_reduce": round(down, 4)})},
         "single_launch": bool(fused),
+        "w13_packed": bool(args.prepack),
         "weights": "e2m1 + K32 exponent bytes" if args.w4a8 else "e4m3 + 128x128 fp32 scales",
         "router": bool(args.router),
         "launch": "eager" if args.eager else "hip graph (K steps per replay)",

@@ -30,6 +30,7 @@ MOE_F_GATEUP_PATH_SHIFT = 16
 MOE_F_DOWN_PATH_SHIFT = 18
 MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_PERSISTENT = 0, 1, 2
 MOE_F_FUSE_SHIFT = 20
+MOE_F_W13_PACKED = 0x400000
 MOE_FUSE_AUTO, MOE_FUSE_OFF, MOE_FUSE_ON = 0, 1, 2
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
@@ -42,7 +43,8 @@ EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_qua
             "moe_fp8_experts", "moe_fp8_gate_up", "moe_fp8_down_reduce", "moe_status_str",
             "moe_last_hip_error", "moe_last_error", "moe_debug_e4m3_encode",
             "moe_debug_count_non_pow2", "moe_fp8_experts_noalloc", "moe_route_plan",
-            "moe_w4a8_experts_workspace_size", "moe_w4a8_experts")
+            "moe_w4a8_experts_workspace_size", "moe_w4a8_experts", "moe_prepack_w13_size",
+            "moe_prepack_w13")
 
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -102,6 +104,8 @@ _c = {
     "moe_w4a8_experts": _proto("moe_w4a8_experts", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp,
                                _sz, _vp),
+    "moe_prepack_w13_size": _proto("moe_prepack_w13_size", _sz, _i64, _i64, _i64),
+    "moe_prepack_w13": _proto("moe_prepack_w13", _i32, _vp, _i64, _i64, _i64, _vp, _vp),
     "moe_status_str": _proto("moe_status_str", ctypes.c_char_p, _i32),
     "moe_last_hip_error": _proto("moe_last_hip_error", ctypes.c_char_p),
     "moe_last_error": _proto("moe_last_error", ctypes.c_char_p),
@@ -282,6 +286,24 @@ def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_i
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream)),
            "moe_fp8_experts")
+
+
+def moe_prepack_w13_size(E, I, K):
+    return _c["moe_prepack_w13_size"](E, I, K)
+
+
+def moe_prepack_w13(w13, out=None, stream=None):
+    """W13 [E, 2I, K] uint8 -> its packed tile layout (a new uint8 tensor of
+    the same size unless `out` is given); pass MOE_F_W13_PACKED with it."""
+    E, twoI, K = w13.shape
+    assert w13.dtype == torch.uint8 and w13.is_contiguous()
+    if out is None:
+        out = torch.empty(moe_prepack_w13_size(E, twoI // 2, K), dtype=torch.uint8,
+                          device=w13.device)
+    assert out.is_contiguous() and out.numel() == moe_prepack_w13_size(E, twoI // 2, K)
+    _check(_c["moe_prepack_w13"](_ptr(w13), E, twoI // 2, K, _ptr(out), _stream(stream)),
+           "moe_prepack_w13")
+    return out.view(E, twoI, K)
 
 
 def moe_w4a8_experts_workspace_size(M, K, I, E, top_k, block_m, sorted_cap, flags=0):

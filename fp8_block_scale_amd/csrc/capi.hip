@@ -427,7 +427,8 @@ namespace {
 
 moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m) {
     const uint32_t known = MOE_F_INTER_UE8M0 | MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_SPLITK_MASK |
-                           MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK | MOE_F_FUSE_MASK;
+                           MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK | MOE_F_FUSE_MASK |
+                           MOE_F_W13_PACKED;
     if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
     const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
@@ -525,6 +526,7 @@ moe::GateUpArgs gateup_args(const uint8_t *x_q, const float *x_s, const uint8_t 
     ga.nsplit = l.sp.nsplit;
     ga.kb_per_split = l.sp.kb_per_split;
     ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
+    ga.w13_packed = (flags & MOE_F_W13_PACKED) ? 1 : 0;
     return ga;
 }
 
@@ -685,6 +687,30 @@ MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const u
                                flags, out_bf16, workspace, workspace_bytes, stream);
 }
 
+// ------------------------------------------------------- weight prepack
+
+MOE_API size_t moe_prepack_w13_size(int64_t E, int64_t I, int64_t K) {
+    if (E < 1 || I <= 0 || K <= 0 || I % 128 || K % 128) return 0;
+    return (size_t)E * 2 * I * K;
+}
+
+MOE_API moe_status moe_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int64_t K,
+                                   uint8_t *w13_packed, void *stream) {
+    if (E < 1 || I <= 0 || K <= 0)
+        return fail(MOE_ERR_SHAPE, "need E >= 1, I > 0, K > 0");
+    if (I % 128 || K % 128)
+        return fail(MOE_ERR_SHAPE, "I (%lld) and K (%lld) must be multiples of 128", (long long)I,
+                    (long long)K);
+    if (!w13 || !w13_packed) return fail(MOE_ERR_NULL, "w13 and w13_packed are required");
+    if (!aligned16(w13) || !aligned16(w13_packed))
+        return fail(MOE_ERR_ALIGN, "w13 and w13_packed must be 16-byte aligned");
+    const uintptr_t a0 = (uintptr_t)w13, b0 = (uintptr_t)w13_packed;
+    const uintptr_t n = (uintptr_t)moe_prepack_w13_size(E, I, K);
+    if (a0 < b0 + n && b0 < a0 + n) return fail(MOE_ERR_SHAPE, "w13 and w13_packed overlap");
+    return hip_check(moe::launch_prepack_w13(w13, E, I, K, w13_packed, (hipStream_t)stream),
+                     "moe_prepack_w13: launch");
+}
+
 // ------------------------------------------------------- W4A8 variant
 
 namespace {
@@ -701,8 +727,9 @@ moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, i
                     int64_t sorted_cap, uint32_t flags) {
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
-    if (flags & (MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP))
-        return fail(MOE_ERR_UNSUPPORTED, "W4A8: MOE_F_MMA_E8M0 and MOE_F_FP8_GATEUP do not apply");
+    if (flags & (MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_W13_PACKED))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "W4A8: MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP and MOE_F_W13_PACKED do not apply");
     const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
     const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
     if (gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT)

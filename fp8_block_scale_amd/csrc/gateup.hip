@@ -63,7 +63,38 @@ prep_kernel(uint32_t *__restrict__ rpos, size_t nr, uint32_t *__restrict__ cnt, 
     }
 }
 
+// One thread per 16-byte chunk of the packed layout (coalesced stores,
+// gathered 16-byte loads): chunk q of tile (e, jt, kb) sits at tile row
+// r = q / 8, position q % 8, and holds the row's chunk (q % 8) ^ (r & 7).
+__global__ void __launch_bounds__(256)
+prepack_w13_kernel(const uint8_t *__restrict__ w13, int64_t I, int64_t K, int64_t nchunks,
+                   uint8_t *__restrict__ out) {
+    const int64_t nkb = K >> 7, jtiles = I >> 7;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < nchunks;
+         idx += (int64_t)gridDim.x * 256) {
+        const int q = (int)(idx & 2047);
+        int64_t t = idx >> 11;
+        const int64_t kb = t % nkb;
+        t /= nkb;
+        const int64_t jt = t % jtiles, e = t / jtiles;
+        const int r = q >> 3, c = (q & 7) ^ (r & 7);
+        const int64_t n = (r < 128 ? jt * 128 + r : I + jt * 128 + (r - 128));
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(w13 + (e * 2 * I + n) * K + kb * 128 + c * 16);
+        *reinterpret_cast<u32x4 *>(out + idx * 16) = v;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int64_t K, uint8_t *out,
+                              hipStream_t st) {
+    const int64_t nchunks = E * 2 * I * K / 16;
+    if (nchunks == 0) return hipSuccess;
+    int64_t blocks = (nchunks + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    prepack_w13_kernel<<<(unsigned)blocks, 256, 0, st>>>(w13, I, K, nchunks, out);
+    return hipGetLastError();
+}
 
 int gateup_stream_kmax(int) { return 1 << 20; }   // the K-range streams through the ring
 

@@ -169,6 +169,11 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
                       ((lane & 3) ^ (row & 3)) * 16;
         }
         wsrc[2] = wsrc[3] = nullptr;
+    } else if (a.w13_packed) {
+        // the packed tile is the stage image: each instruction copies 1 KB
+        const uint8_t *tile = a.w13 + (((int64_t)e * a.jtiles + jt) * a.nkb + kb0) * kPackedTile;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsrc[i] = tile + (w * 4 + i) * 1024 + lane * 16;
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -177,6 +182,8 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             wsrc[i] = a.w13 + ((int64_t)e * 2 * I + n) * K + (int64_t)kb0 * 128 + (slot ^ (row & 7)) * 16;
         }
     }
+    // bytes between consecutive K-blocks of a weight source
+    const int64_t wstep = W4 ? 64 : (a.w13_packed ? kPackedTile : 128);
     const bool xw = w < C::RP / 8;
     const uint8_t *xsrc;
     {
@@ -210,13 +217,13 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
                       ((int64_t)(b + 1) * BM >= ntp || a.eids[b + 1] != e);
     auto issue = [&](int st, int kbl) {
         uint8_t *base = smem + st * C::STB;
-        constexpr int NW = W4 ? 2 : 4, WSTEP = W4 ? 64 : 128;
+        constexpr int NW = W4 ? 2 : 4;
         if (once) {
 #pragma unroll
-            for (int i = 0; i < NW; ++i) lds_dma16_nt(wsrc[i] + kbl * WSTEP, base + (w * NW + i) * 1024);
+            for (int i = 0; i < NW; ++i) lds_dma16_nt(wsrc[i] + kbl * wstep, base + (w * NW + i) * 1024);
         } else {
 #pragma unroll
-            for (int i = 0; i < NW; ++i) lds_dma16(wsrc[i] + kbl * WSTEP, base + (w * NW + i) * 1024);
+            for (int i = 0; i < NW; ++i) lds_dma16(wsrc[i] + kbl * wstep, base + (w * NW + i) * 1024);
         }
         if (xw)
             lds_dma16(xsrc + kbl * 128, base + C::WB + w * 1024);

@@ -202,13 +202,20 @@ gateup_pipe_kernel(GateUpArgs a) {
     // ---- DMA sources of this lane: W13 rows and gathered activation rows
     const int sub = lane >> 3, slot = lane & 7;
     const uint8_t *wsrc[kWInstr];
+    if (a.w13_packed) {         // the packed tile is the stage image: 1 KB per instruction
+        const uint8_t *tile = a.w13 + ((int64_t)e * a.jtiles + jt) * nkb * (int64_t)kPackedTile;
 #pragma unroll
-    for (int i = 0; i < kWInstr; ++i) {
-        const int row = (w * kWInstr + i) * 8 + sub;                  // tile row 0..255
-        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
-        const int chunk = slot ^ (row & 7);
-        wsrc[i] = a.w13 + ((int64_t)e * twoI + n) * K + chunk * 16;
+        for (int i = 0; i < kWInstr; ++i) wsrc[i] = tile + (w * kWInstr + i) * 1024 + lane * 16;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kWInstr; ++i) {
+            const int row = (w * kWInstr + i) * 8 + sub;                  // tile row 0..255
+            const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+            const int chunk = slot ^ (row & 7);
+            wsrc[i] = a.w13 + ((int64_t)e * twoI + n) * K + chunk * 16;
+        }
     }
+    const int64_t wstep = a.w13_packed ? kPackedTile : 128;     // bytes per K-block
     int fallback = sTok[0];
     for (int m = 1; fallback < 0 && m < nrows; ++m) fallback = sTok[m];
     if (fallback < 0) fallback = 0;                  // tile without valid rows: scale 0
@@ -260,7 +267,7 @@ gateup_pipe_kernel(GateUpArgs a) {
             uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
 #pragma unroll
             for (int i = 2 * part; i < 2 * part + 2; ++i)
-                __builtin_amdgcn_global_load_lds(wsrc[i] + (int64_t)kb * 128, dw + i * 1024, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(wsrc[i] + kb * wstep, dw + i * 1024, 16, 0, 0);
         } else if (part == 2) {
             uint8_t *da = sA + stage * kABytes + (w * kAInstr) * 1024;
 #pragma unroll

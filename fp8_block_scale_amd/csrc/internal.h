@@ -107,7 +107,16 @@ struct GateUpArgs {
     int nsplit;         // split-K factor
     int kb_per_split;
     int inter_ue8m0;
+    int w13_packed;     // w13 in the tile layout of moe_prepack_w13 (kPackedTile bytes per K-block)
 };
+
+// The packed W13 layout (moe_prepack_w13): per (expert, 128-column tile,
+// K-block) one contiguous tile of 256 rows x 128 B -- the 128 gate rows, then
+// the 128 up rows -- whose bytes are exactly the gate/up kernels' LDS stage
+// image (row r's 16-byte chunk c at r * 128 + 16 (c ^ (r & 7))).
+constexpr int kPackedTile = 256 * 128;
+hipError_t launch_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int64_t K, uint8_t *out,
+                              hipStream_t st);
 
 struct DownArgs {
     const uint8_t *hq;

@@ -136,6 +136,10 @@ enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_PERSISTENT = 2 };
 #define MOE_F_FUSE_SHIFT 20
 #define MOE_F_FUSE_MASK  0x300000u
 enum { MOE_FUSE_AUTO = 0, MOE_FUSE_OFF = 1, MOE_FUSE_ON = 2 };
+/* Bit 22: w13 holds the packed layout written by moe_prepack_w13 (the same
+ * bytes, reordered); w13_s keeps its layout.  Every gate/up kernel family
+ * reads it.  Not accepted by moe_w4a8_experts (MOE_ERR_UNSUPPORTED). */
+#define MOE_F_W13_PACKED 0x400000u
 
 /* ---------------------------------------------------------------- plan -- */
 
@@ -317,6 +321,30 @@ moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                void *out_bf16, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* ------------------------------------------------------ weight prepack -- */
+
+/* Offline reordering of W13 into the order the gate/up kernels consume it,
+ * the analogue of the private eight-row gate/up interleave of FlashInfer PR
+ * #4287 (public contract and review fixes section): for expert e, 128-column
+ * tile jt < I/128 and K-block kb < K/128, one contiguous 32 KiB tile at byte
+ * ((e * (I/128) + jt) * (K/128) + kb) * 32768 holds 256 rows of 128 bytes --
+ * rows 0-127 are gate rows jt*128 + r of w13, rows 128-255 up rows
+ * I + jt*128 + r - 128 -- with 16-byte chunk c of row r (bytes
+ * kb*128 + 16c .. of the row) stored at r * 128 + 16 * (c ^ (r & 7)).  That is
+ * the gate/up kernels' LDS stage image, so each of their load instructions
+ * reads 1 KiB of consecutive bytes instead of 128-byte pieces of 256 rows K
+ * bytes apart.  Pass MOE_F_W13_PACKED with the result; w13_s is unchanged.
+ *   w13        [E, 2I, K] E4M3 (device), unchanged
+ *   w13_packed moe_prepack_w13_size(E, I, K) bytes (= E * 2I * K; device),
+ *              written; must not overlap w13
+ * Both 16-byte aligned; I % 128 == 0, K % 128 == 0.  Asynchronous on
+ * `stream`.  Errors: MOE_ERR_SHAPE (sizes, overlap), MOE_ERR_NULL,
+ * MOE_ERR_ALIGN, MOE_ERR_HIP.  moe_prepack_w13_size returns 0 for sizes it
+ * rejects. */
+size_t moe_prepack_w13_size(int64_t E, int64_t I, int64_t K);
+moe_status moe_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int64_t K,
+                           uint8_t *w13_packed, void *stream);
+
 /* ------------------------------------------------------- W4A8 variant -- */
 
 /* Steps 3-5 with E2M1 (FP4) expert weights: FP8 activations against E2M1
@@ -338,8 +366,8 @@ moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
  * Runs the per-block kernels only.  Constraints: those of moe_fp8_experts,
  * I / 128 <= 512 / min(max(block_m, 16), 64), w13 / w2 16-byte and w13_e /
  * w2_e 4-byte aligned; flags MOE_F_INTER_UE8M0 and a forced split-K apply;
- * MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP, MOE_PATH_PERSISTENT and MOE_FUSE_ON
- * give MOE_ERR_UNSUPPORTED.  The workspace is sized by
+ * MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP, MOE_PATH_PERSISTENT, MOE_FUSE_ON
+ * and MOE_F_W13_PACKED give MOE_ERR_UNSUPPORTED.  The workspace is sized by
  * moe_w4a8_experts_workspace_size (0 if the arguments are rejected); the
  * intermediate rows sit where moe_fp8_experts_workspace_layout says. */
 size_t moe_w4a8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,

@@ -288,3 +288,20 @@ def test_w4a8_validation_before_any_device_call():
     w4 = moe.moe_w4a8_experts_workspace_size(4096, 4096, 1024, 288, 8, 64, 50944)
     assert w4 == moe.moe_w4a8_experts_workspace_size(4096, 4096, 1024, 288, 8, 64, 50944, stream)
     assert w4 == moe.moe_fp8_experts_workspace_size(4096, 4096, 1024, 288, 8, 64, 50944, stream)
+
+
+def test_prepack_validation_before_any_device_call():
+    f = _raw("moe_prepack_w13")
+    assert moe.moe_prepack_w13_size(2, 256, 384) == 2 * 512 * 384
+    assert moe.moe_prepack_w13_size(2, 100, 384) == 0
+    assert moe.moe_prepack_w13_size(0, 256, 384) == 0
+    assert _err(f(FAKE, 2, 100, 384, ctypes.c_void_p(0x20000000), None)) == "MOE_ERR_SHAPE"
+    assert _err(f(None, 2, 256, 384, FAKE, None)) == "MOE_ERR_NULL"
+    assert _err(f(ctypes.c_void_p(0x10008), 2, 256, 384, FAKE, None)) == "MOE_ERR_ALIGN"
+    # overlapping source and destination
+    assert _err(f(ctypes.c_void_p(0x10000000), 2, 256, 384, ctypes.c_void_p(0x10000100),
+                  None)) == "MOE_ERR_SHAPE"
+    # the W4A8 entry point does not take packed FP8 weights
+    w4 = _raw("moe_w4a8_experts")
+    assert _err(w4(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 8, 2, 16,
+                   128, moe.MOE_F_W13_PACKED, FAKE, FAKE, 1 << 30, None)) == "MOE_ERR_UNSUPPORTED"
