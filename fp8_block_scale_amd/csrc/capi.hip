@@ -715,12 +715,11 @@ MOE_API moe_status moe_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int
 
 namespace {
 
-// The W4A8 variant runs on the per-block kernels: its flags are those of
-// moe_fp8_experts with both stage paths resolved to MOE_PATH_STREAM.
+// The W4A8 variant's down stage runs on the per-block kernel: its flags are
+// those of moe_fp8_experts with the down path resolved to MOE_PATH_STREAM
+// (the gate/up path is chosen, or forced, as for moe_fp8_experts).
 uint32_t w4_flags(uint32_t flags) {
-    return (flags & ~(MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK)) |
-           ((uint32_t)MOE_PATH_STREAM << MOE_F_GATEUP_PATH_SHIFT) |
-           ((uint32_t)MOE_PATH_STREAM << MOE_F_DOWN_PATH_SHIFT);
+    return (flags & ~MOE_F_DOWN_PATH_MASK) | ((uint32_t)MOE_PATH_STREAM << MOE_F_DOWN_PATH_SHIFT);
 }
 
 moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, int32_t block_m,
@@ -732,8 +731,9 @@ moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, i
                     "W4A8: MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP and MOE_F_W13_PACKED do not apply");
     const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
     const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
-    if (gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT)
-        return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs the per-block kernels only");
+    (void)gp;
+    if (dp == MOE_PATH_PERSISTENT)
+        return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs the per-block down kernel only");
     if (((flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT) == MOE_FUSE_ON)
         return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs as two stages (no MOE_FUSE_ON)");
     if (I / 128 > moe::down_w4_max_njb(block_m))
@@ -777,15 +777,19 @@ MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const 
         return fail(MOE_ERR_ALIGN, "w13_e and w2_e must be 4-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
-    st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
-                                    (uint32_t *)(ws + l.cnt), l.cnt_words, s),
-                   "moe_w4a8_experts: clear route map and counters");
-    if (st != MOE_OK) return st;
     moe::GateUpArgs ga = gateup_args(x_q, x_s, w13, nullptr, sorted_token_ids, expert_ids,
                                      num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap,
                                      fl, ws, l);
     ga.w13e = w13_e;
-    st = hip_check(moe::launch_gateup_w4(ga, block_m, s), "moe_w4a8_experts: gate/up launch");
+    if (l.sp.gu_persistent) {       // its row-tile launch clears the route map and counters
+        st = hip_check(moe::launch_gateup_pipe_w4(ga, block_m, s), "moe_w4a8_experts: gate/up launch");
+    } else {
+        st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
+                                        (uint32_t *)(ws + l.cnt), l.cnt_words, s),
+                       "moe_w4a8_experts: clear route map and counters");
+        if (st != MOE_OK) return st;
+        st = hip_check(moe::launch_gateup_w4(ga, block_m, s), "moe_w4a8_experts: gate/up launch");
+    }
     if (st != MOE_OK) return st;
     moe::DownArgs da = down_args(w2, nullptr, topk_weights, sorted_token_ids, expert_ids,
                                  num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap, ws, l);

@@ -143,6 +143,9 @@ __device__ __forceinline__ v8h e2m1x8_to_f16(uint32_t d, float scale) {
     return v8h{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
+// 2^e as an FP32 value for any e in [-149, 127] (subnormal results included).
+__device__ __forceinline__ float pow2_int(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
+
 // Largest of the four bytes of a dword.
 __device__ __forceinline__ int max_byte4(uint32_t v) {
     const uint32_t m = max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24));

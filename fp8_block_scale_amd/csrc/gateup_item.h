@@ -31,12 +31,13 @@
 //   kFp8    v_mfma_f32_16x16x128_f8f6f4 on the codes directly;
 //   kFp8E8  as kFp8 with power-of-two scales applied inside the MFMA;
 //   kW4     E2M1 weights with one power-of-two scale per 32 K (the W4A8
-//           variant): each weight row's four K32 exponents of a K-block are
-//           taken relative to their largest, R; the codes are widened to
-//           FP16 with 2^(s - R) folded into the conversion (exact while the
-//           four exponents span at most 23 binades: every E2M1 value has two
-//           significant bits), multiplied as in kExact, and the K-block's
-//           sum is scaled by x_s * 2^(R - 127) per weight row.
+//           variant): each weight row's K32 exponents are taken relative to
+//           their largest over the item's K-range, R (found in a prologue);
+//           the codes are widened to FP16 with 2^(s - R) folded into the
+//           conversion (exact while the row's exponents span at most 23
+//           binades: every E2M1 value has two significant bits), multiplied
+//           as in kExact with x_s per K-block, and each output row is scaled
+//           by 2^(R - 127) once at the end (split partials included).
 //
 // K is split over items; each writes the partial sums of its valid rows to
 // the workspace and the last one of a tile to arrive (atomic counter) adds
@@ -84,7 +85,8 @@ struct GSCfg {
     static constexpr int SINK = XT + RP * 4;
     static constexpr int MISC = SINK + 8 * 256;
     static constexpr int EXP = MISC + 16;          // kExactE8: [RP] row, [2] gate/up exponents
-    static constexpr int TOTAL = EXP + (RP + 4) * 4;
+    static constexpr int RW = EXP + (RP + 4) * 4;  // kW4: [256] weight-row exponents
+    static constexpr int TOTAL = RW + (W4 ? 256 * 4 : 0);
     static constexpr int NPS = W4 ? 4 : 6;         // DMA instructions per wave per stage
 };
 
@@ -106,6 +108,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     uint8_t *sSink = smem + C::SINK;
     int *sMisc = reinterpret_cast<int *>(smem + C::MISC);
     int *sExp = reinterpret_cast<int *>(smem + C::EXP);
+    int *sRw = reinterpret_cast<int *>(smem + C::RW);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -256,7 +259,25 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         }
         __syncthreads();
     }
+    if constexpr (W4) {
+        // largest exponent byte of each W13 row of the tile over [kb0, kb1)
+        // (two threads a row, one dword = one K-block's four K32 groups)
+        const int row = tid >> 1, half = tid & 1;
+        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+        const uint32_t *ep = reinterpret_cast<const uint32_t *>(a.w13e + ((int64_t)e * 2 * I + n) * (K >> 5));
+        int m = 0;
+        for (int kb = kb0 + half; kb < kb1; kb += 2) m = max(m, max_byte4(ep[kb]));
+        m = max(m, __shfl_xor(m, 1, 64));
+        if (half == 0) sRw[row] = m;
+        __syncthreads();
+    }
 
+    // kW4: the reference exponents of this lane's gate and up operand rows
+    int rwa[2] = {0, 0};
+    if constexpr (W4) {
+        rwa[0] = sRw[16 * w + l16];
+        rwa[1] = sRw[128 + 16 * w + l16];
+    }
     v4f accg[C::NU], accu[C::NU];
 #pragma unroll
     for (int u = 0; u < C::NU; ++u) {
@@ -269,9 +290,8 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         const uint8_t *Xs = Ws + C::WB;
         const uint8_t *Sb = Ws + C::WB + C::XB;
         // weight rows: this lane's A rows (gate / up), widened with their
-        // K32 scales relative to the row's largest exponent R of the K-block
+        // K32 scales relative to the row's reference exponent
         v8h W[2][4];
-        v4f F[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int row = 128 * h + 16 * w + l16;
@@ -279,7 +299,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ (row & 3)) << 4));
             const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ (row & 3)) << 4));
             const uint32_t sw = *reinterpret_cast<const uint32_t *>(Sb + (row >> 5) * 256 + (row & 31) * 4);
-            const int R = max_byte4(sw);
+            const int R = rwa[h];
             const int dlo = (int)((sw >> (8 * (g >> 1))) & 0xffu) - R;
             const int dhi = (int)((sw >> (8 * (2 + (g >> 1)))) & 0xffu) - R;
             // below 2^-30 every product rounds to zero in FP16 either way
@@ -289,13 +309,6 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             W[h][1] = e2m1x8_to_f16(d01.y, flo);
             W[h][2] = e2m1x8_to_f16(d23.x, fhi);
             W[h][3] = e2m1x8_to_f16(d23.y, fhi);
-            // the four output rows of this lane: 2^(R - 127) of each
-            const int orow = 128 * h + 16 * w + 4 * g;
-            const u32x4 so = lds_read16(Sb + (orow >> 5) * 256 + (orow & 31) * 4);
-            F[h] = v4f{__builtin_amdgcn_ldexpf(1.0f, max_byte4(so.x) - 127),
-                       __builtin_amdgcn_ldexpf(1.0f, max_byte4(so.y) - 127),
-                       __builtin_amdgcn_ldexpf(1.0f, max_byte4(so.z) - 127),
-                       __builtin_amdgcn_ldexpf(1.0f, max_byte4(so.w) - 127)};
         }
 #pragma unroll
         for (int u = 0; u < C::NU; ++u) {
@@ -309,8 +322,8 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             e4m3x32_to_f16(lo, hi, Bh);
             const v4f tg = mfma16x16x128_f16(W[0], Bh);
             const v4f tu = mfma16x16x128_f16(W[1], Bh);
-            accg[u] = tg * (F[0] * sa) + accg[u];
-            accu[u] = tu * (F[1] * sa) + accu[u];
+            accg[u] = tg * sa + accg[u];
+            accu[u] = tu * sa + accu[u];
         }
     };
 
@@ -399,6 +412,19 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             compute(kb % C::NS);
     }
 
+    if constexpr (W4) {
+        // 2^(R - 127) of the four output rows of this lane (gate, up)
+        const int og = 16 * w + 4 * g;
+        const v4f Fg = v4f{pow2_int(sRw[og] - 127), pow2_int(sRw[og + 1] - 127),
+                           pow2_int(sRw[og + 2] - 127), pow2_int(sRw[og + 3] - 127)};
+        const v4f Fu = v4f{pow2_int(sRw[128 + og] - 127), pow2_int(sRw[129 + og] - 127),
+                           pow2_int(sRw[130 + og] - 127), pow2_int(sRw[131 + og] - 127)};
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+            accg[u] = accg[u] * Fg;
+            accu[u] = accu[u] * Fu;
+        }
+    }
     if constexpr (MODE == kExactE8) {
         const float fbg = pow2_biased(sExp[C::RP]), fbu = pow2_biased(sExp[C::RP + 1]);
 #pragma unroll

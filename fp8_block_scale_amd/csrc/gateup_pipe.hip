@@ -37,11 +37,8 @@ namespace {
 constexpr int kRows = 128;        // tile rows
 constexpr int kNT = 512;          // threads (8 waves)
 constexpr int kStages = 3;
-constexpr int kWBytes = 256 * 128;            // W13 tile per stage
 constexpr int kABytes = kRows * 128;          // activation tile per stage
-constexpr int kWInstr = kWBytes / 1024 / 8;   // DMA instructions per wave per stage (W)
-constexpr int kAInstr = kABytes / 1024 / 8;   // (A)
-constexpr int kPerStage = kWInstr + kAInstr;  // + 1 on K-blocks that start a scale group
+constexpr int kAInstr = kABytes / 1024 / 8;   // DMA instructions per wave per stage (A)
 constexpr int kSGroup = 4;                    // K-blocks of activation scales per scale load
 constexpr int kMaxKb = 256;                   // K <= 32768
 
@@ -49,7 +46,28 @@ constexpr int kMaxKb = 256;                   // K <= 32768
 // widening (2^(a_kb - A) on the activations, 2^(b_kb - B) on W13, A and B
 // the largest exponents over K) and accumulated across K-blocks in the MFMA
 // chain; the item's sums are scaled by 2^A * 2^B once, before SwiGLU.
-enum { kExact = 0, kFp8 = 1, kFp8E8 = 2, kExactE8 = 3 };
+// kW4 (the W4A8 variant): E2M1 W13 with K32 exponent bytes; a stage holds
+// 256 rows x 64 B of codes (chunks XOR-swizzled by row & 3) and the rows'
+// exponent dwords.  Each weight row's largest exponent R over K is found
+// once per item; the codes are widened to FP16 with 2^(s - R) folded in
+// (exact while a row's exponents span at most 23 binades), the K-block sums
+// take x_s as in kExact, and each output row is scaled by 2^(R - 127) once,
+// before SwiGLU.
+enum { kExact = 0, kFp8 = 1, kFp8E8 = 2, kExactE8 = 3, kW4 = 4 };
+
+template <int MODE>
+struct PCfg {
+    static constexpr bool W4 = MODE == kW4;
+    static constexpr int WBytes = 256 * (W4 ? 64 : 128);    // W13 tile per stage
+    static constexpr int EBytes = W4 ? 256 * 4 : 0;          // exponent dwords per stage
+    static constexpr int WInstr = WBytes / 1024 / 8;         // DMA instructions per wave per stage (W)
+    // + 1 on K-blocks that start a scale group
+    static constexpr int PerStage = WInstr + kAInstr + (W4 ? 1 : 0);
+    static constexpr size_t Smem = (size_t)kStages * (WBytes + kABytes + EBytes) +
+                                   2 * kRows * kSGroup * 4 + 2 * kMaxKb * 4 + kRows * 4 +
+                                   4 * kRows * 4 + 16 + (kRows + 4) * 4 + (W4 ? 256 * 4 : 0);
+    static_assert(Smem <= 160 * 1024, "LDS budget");
+};
 
 __device__ __forceinline__ v8i join8p(const u32x4 &lo, const u32x4 &hi) {
     v8i r;
@@ -135,15 +153,18 @@ unsigned prep_groups(int64_t n) {
 template <int BM, int MODE>
 __global__ void __launch_bounds__(kNT, 1)
 gateup_pipe_kernel(GateUpArgs a) {
+    using C = PCfg<MODE>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *sW = smem;                                        // [kStages][256][128]
-    uint8_t *sA = smem + kStages * kWBytes;                    // [kStages][128][128]
-    float *sSa = reinterpret_cast<float *>(sA + kStages * kABytes);  // [2][128][kSGroup] x_s
+    uint8_t *sW = smem;                                        // [kStages][256][128 or 64]
+    uint8_t *sA = smem + kStages * C::WBytes;                  // [kStages][128][128]
+    uint8_t *sE = sA + kStages * kABytes;                      // kW4: [kStages][256] exponent dwords
+    float *sSa = reinterpret_cast<float *>(sE + kStages * C::EBytes);  // [2][128][kSGroup] x_s
     float *sSw = sSa + 2 * kRows * kSGroup;                    // [2][kMaxKb] w13_s gate, up
     int *sTok = reinterpret_cast<int *>(sSw + 2 * kMaxKb);      // [128] token or -1
     float *sRed = reinterpret_cast<float *>(sTok + kRows);      // [4][128]
     int *sItem = reinterpret_cast<int *>(sRed + 4 * kRows);      // [4]
     int *sExp = sItem + 4;                                       // [128] row, [2] gate/up exponents
+    int *sRw = sExp + kRows + 4;                                 // kW4: [256] weight-row exponents R
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -190,7 +211,7 @@ gateup_pipe_kernel(GateUpArgs a) {
     const int64_t twoI = 2 * I;
     const int nkb = a.nkb;
     const int nb13 = (int)(twoI >> 7);
-    {
+    if constexpr (!C::W4) {
         const float *sg = a.w13s + ((int64_t)e * nb13 + jt) * nkb;
         const float *su = a.w13s + ((int64_t)e * nb13 + (I >> 7) + jt) * nkb;
         for (int i = tid; i < nkb; i += kNT) {
@@ -201,21 +222,35 @@ gateup_pipe_kernel(GateUpArgs a) {
     __syncthreads();
     // ---- DMA sources of this lane: W13 rows and gathered activation rows
     const int sub = lane >> 3, slot = lane & 7;
-    const uint8_t *wsrc[kWInstr];
-    if (a.w13_packed) {         // the packed tile is the stage image: 1 KB per instruction
+    // (a fixed size: a local array whose size depends on the template
+    // parameters keeps hipcc's host pass from emitting the kernel's stub)
+    const uint8_t *wsrc[4];
+    const uint8_t *esrc = nullptr;                   // kW4: this lane's exponent dword (lanes < 32)
+    if constexpr (C::W4) {
+#pragma unroll
+        for (int i = 0; i < C::WInstr; ++i) {
+            const int row = (w * C::WInstr + i) * 16 + (lane >> 2);       // tile row 0..255
+            const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+            wsrc[i] = a.w13 + ((int64_t)e * twoI + n) * (K >> 1) + ((lane & 3) ^ (row & 3)) * 16;
+        }
+        const int row = 32 * w + (lane & 31);
+        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+        esrc = a.w13e + ((int64_t)e * twoI + n) * (K >> 5);
+    } else if (a.w13_packed) {  // the packed tile is the stage image: 1 KB per instruction
         const uint8_t *tile = a.w13 + ((int64_t)e * a.jtiles + jt) * nkb * (int64_t)kPackedTile;
 #pragma unroll
-        for (int i = 0; i < kWInstr; ++i) wsrc[i] = tile + (w * kWInstr + i) * 1024 + lane * 16;
+        for (int i = 0; i < C::WInstr; ++i) wsrc[i] = tile + (w * C::WInstr + i) * 1024 + lane * 16;
     } else {
 #pragma unroll
-        for (int i = 0; i < kWInstr; ++i) {
-            const int row = (w * kWInstr + i) * 8 + sub;                  // tile row 0..255
+        for (int i = 0; i < C::WInstr; ++i) {
+            const int row = (w * C::WInstr + i) * 8 + sub;                // tile row 0..255
             const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
             const int chunk = slot ^ (row & 7);
             wsrc[i] = a.w13 + ((int64_t)e * twoI + n) * K + chunk * 16;
         }
     }
-    const int64_t wstep = a.w13_packed ? kPackedTile : 128;     // bytes per K-block
+    // bytes per K-block
+    const int64_t wstep = C::W4 ? 64 : (a.w13_packed ? kPackedTile : 128);
     int fallback = sTok[0];
     for (int m = 1; fallback < 0 && m < nrows; ++m) fallback = sTok[m];
     if (fallback < 0) fallback = 0;                  // tile without valid rows: scale 0
@@ -235,6 +270,18 @@ gateup_pipe_kernel(GateUpArgs a) {
             for (int off = 32; off >= 1; off >>= 1) mb = max(mb, __shfl_xor(mb, off, 64));
             if (lane == 0) sExp[kRows + w] = mb;
         }
+        __syncthreads();
+    }
+    if constexpr (C::W4) {
+        // largest exponent byte of each W13 row of the tile over all of K
+        // (two threads a row, one dword = four K32 groups at a time)
+        const int row = tid >> 1, half = tid & 1;
+        const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
+        const uint32_t *ep = reinterpret_cast<const uint32_t *>(a.w13e + ((int64_t)e * twoI + n) * (K >> 5));
+        int m = 0;
+        for (int q = half; q < nkb; q += 2) m = max(m, max_byte4(ep[q]));
+        m = max(m, __shfl_xor(m, 1, 64));
+        if (half == 0) sRw[row] = m;
         __syncthreads();
     }
 
@@ -257,16 +304,20 @@ gateup_pipe_kernel(GateUpArgs a) {
         const int t = sTok[row] >= 0 ? sTok[row] : fallback;
         ssrc = a.xs + (int64_t)t * nkb;
     }
-    // Every wave issues kPerStage vector-memory instructions per stage, plus
+    // Every wave issues PerStage vector-memory instructions per stage, plus
     // one on stages whose K-block starts a scale group (the waits in the main
-    // loop count on it), in four parts: W13 rows 0-1, W13 rows 2-3,
-    // activation rows, scales.
-    static_assert(kWInstr == 4 && kAInstr == 2, "issue parts");
+    // loop count on it), in four parts: W13 rows 0-1, W13 rows 2-3 (kW4: all
+    // W13 rows, then the exponent dwords), activation rows, scales.
+    static_assert((C::W4 ? C::WInstr == 2 : C::WInstr == 4) && kAInstr == 2, "issue parts");
     auto issue_part = [&](int part, int stage, int kb) {
-        if (part < 2) {
-            uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
+        if (C::W4 && part == 1) {
+            if (lane < 32)
+                __builtin_amdgcn_global_load_lds(esrc + kb * 4, sE + stage * C::EBytes + w * 128, 4, 0, 0);
+        } else if (part < 2) {
+            uint8_t *dw = sW + stage * C::WBytes + (w * C::WInstr) * 1024;
+            constexpr int per = C::W4 ? 2 : 2;
 #pragma unroll
-            for (int i = 2 * part; i < 2 * part + 2; ++i)
+            for (int i = per * part; i < per * part + per; ++i)
                 __builtin_amdgcn_global_load_lds(wsrc[i] + kb * wstep, dw + i * 1024, 16, 0, 0);
         } else if (part == 2) {
             uint8_t *da = sA + stage * kABytes + (w * kAInstr) * 1024;
@@ -296,6 +347,13 @@ gateup_pipe_kernel(GateUpArgs a) {
     }
     const bool wave_rows = vrows > 0;
 
+    // kW4: the reference exponent of this lane's four W13 operand rows
+    int rw[4] = {0, 0, 0, 0};
+    if constexpr (C::W4) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rw[s] = sRw[(s < 2 ? 0 : 128) + 32 * wn + 16 * (s & 1) + l16];
+    }
+
     v4f acc[4][NU];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -316,9 +374,9 @@ gateup_pipe_kernel(GateUpArgs a) {
         if (kb + 1 >= nkb)
             wait_vmcnt<0>();
         else if ((kb + 1) % kSGroup == 0)
-            wait_vmcnt<kPerStage + 1>();
+            wait_vmcnt<C::PerStage + 1>();
         else
-            wait_vmcnt<kPerStage>();
+            wait_vmcnt<C::PerStage>();
         // Every wave has waited for its own part of this stage; the barrier
         // makes the whole stage visible, and every wave is past the multiply
         // of kb - 1, whose stage the refill below overwrites.  A plain
@@ -341,12 +399,54 @@ gateup_pipe_kernel(GateUpArgs a) {
             part(1);
             part(2);
             part(3);
+        } else if constexpr (C::W4) {
+            const float *Ss = sSa + ((kb / kSGroup) & 1) * (kRows * kSGroup) + kb % kSGroup;
+            const uint8_t *Ws = sW + stage * C::WBytes;
+            const uint8_t *As = sA + stage * kABytes;
+            const uint8_t *Es = sE + stage * C::EBytes;
+            // W13 rows of this wave (tile rows 32wn + 16(s&1), +128 for up),
+            // widened with their K32 scales relative to the row's R
+            v8h wh[4][4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = (s < 2 ? 0 : 128) + 32 * wn + 16 * (s & 1) + l16;
+                const uint8_t *rp = Ws + row * 64 + ((g & 1) << 3);
+                const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ (row & 3)) << 4));
+                const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ (row & 3)) << 4));
+                const uint32_t sw = *reinterpret_cast<const uint32_t *>(Es + row * 4);
+                const int dlo = (int)((sw >> (8 * (g >> 1))) & 0xffu) - rw[s];
+                const int dhi = (int)((sw >> (8 * (2 + (g >> 1)))) & 0xffu) - rw[s];
+                // below 2^-30 every product rounds to zero in FP16 either way
+                const float flo = __uint_as_float((uint32_t)(127 + (dlo < -30 ? -30 : dlo)) << 23);
+                const float fhi = __uint_as_float((uint32_t)(127 + (dhi < -30 ? -30 : dhi)) << 23);
+                wh[s][0] = e2m1x8_to_f16(d01.x, flo);
+                wh[s][1] = e2m1x8_to_f16(d01.y, flo);
+                wh[s][2] = e2m1x8_to_f16(d23.x, fhi);
+                wh[s][3] = e2m1x8_to_f16(d23.y, fhi);
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (u < 3) part(u + 1);
+                if (wm * 64 + u * 16 >= vrows) continue;
+                const int row = wm * 64 + u * 16 + l16;
+                const uint8_t *rp = As + row * 128;
+                const u32x4 lo = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                const u32x4 hi = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                const float sa = Ss[row * kSGroup];
+                v8h bh[4];
+                e4m3x32_to_f16(lo, hi, bh);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const v4f t = mfma16x16x128_f16(wh[s], bh);
+                    acc[s][u] = t * sa + acc[s][u];
+                }
+            }
         } else {
             const float sbg = sSw[kb];
             const float sbu = sSw[kMaxKb + kb];
             // this K-block's activation scales: [row][kb % kSGroup] of its group slot
             const float *Ss = sSa + ((kb / kSGroup) & 1) * (kRows * kSGroup) + kb % kSGroup;
-            const uint8_t *Ws = sW + stage * kWBytes;
+            const uint8_t *Ws = sW + stage * C::WBytes;
             const uint8_t *As = sA + stage * kABytes;
             // W operand rows of this wave: tile rows 32wn + 16(s&1) (+128 for up)
             u32x4 wr[4][2];
@@ -455,6 +555,17 @@ gateup_pipe_kernel(GateUpArgs a) {
     // the next item's claim travels while this one's epilogue computes
     const int ticket = tid == 0 ? claim_begin(a.tmeta + 1, home, q) : 0;
 
+    if constexpr (C::W4) {
+        // 2^(R - 127) of each output row (rows 4g..4g+3 of every operand s)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int orow = (s < 2 ? 0 : 128) + 32 * wn + 16 * (s & 1) + 4 * g;
+            const v4f F = v4f{pow2_int(sRw[orow] - 127), pow2_int(sRw[orow + 1] - 127),
+                              pow2_int(sRw[orow + 2] - 127), pow2_int(sRw[orow + 3] - 127)};
+#pragma unroll
+            for (int u = 0; u < NU; ++u) acc[s][u] = acc[s][u] * F;
+        }
+    }
     if constexpr (MODE == kExactE8) {
         const float fbg = pow2_biased(sExp[kRows]), fbu = pow2_biased(sExp[kRows + 1]);
 #pragma unroll
@@ -510,10 +621,6 @@ gateup_pipe_kernel(GateUpArgs a) {
     }
 }
 
-constexpr size_t kSmem = (size_t)kStages * (kWBytes + kABytes) + 2 * kRows * kSGroup * 4 +
-                         2 * kMaxKb * 4 + kRows * 4 + 4 * kRows * 4 + 16 + (kRows + 4) * 4;
-static_assert(kSmem <= 160 * 1024, "LDS budget");
-
 template <int BM, int MODE>
 hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
@@ -526,9 +633,10 @@ hipError_t launch_pipe(const GateUpArgs &a, hipStream_t st) {
     const int64_t max_items = (int64_t)a.nblocks * a.jtiles;
     if (grid > max_items) grid = max_items;
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = raise_lds_limit(lds_set, (const void *)gateup_pipe_kernel<BM, MODE>, (int)kSmem);
+    constexpr size_t smem = PCfg<MODE>::Smem;
+    hipError_t e = raise_lds_limit(lds_set, (const void *)gateup_pipe_kernel<BM, MODE>, (int)smem);
     if (e != hipSuccess) return e;
-    gateup_pipe_kernel<BM, MODE><<<(unsigned)grid, kNT, kSmem, st>>>(a);
+    gateup_pipe_kernel<BM, MODE><<<(unsigned)grid, kNT, smem, st>>>(a);
     return hipGetLastError();
 }
 
@@ -553,6 +661,17 @@ hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st) {
                                                                    a.nblocks, a.tiles, a.tmeta,
                                                                    (uint32_t *)a.rpos, a.R, a.cnt, a.n_cnt);
     return hipGetLastError();
+}
+
+hipError_t launch_gateup_pipe_w4(const GateUpArgs &a, int block_m, hipStream_t st) {
+    switch (block_m) {
+        case 8: return launch_pipe<8, kW4>(a, st);
+        case 16: return launch_pipe<16, kW4>(a, st);
+        case 32: return launch_pipe<32, kW4>(a, st);
+        case 64: return launch_pipe<64, kW4>(a, st);
+        case 128: return launch_pipe<128, kW4>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,

@@ -181,6 +181,9 @@ hipError_t launch_down(const DownArgs &a, int block_m, bool e8m0, hipStream_t st
 // small-grid kernels: gate/up as above (exact FP16 products); the down stage
 // needs I / 128 <= down_w4_max_njb(block_m).
 hipError_t launch_gateup_w4(const GateUpArgs &a, int block_m, hipStream_t st);
+// The W4A8 gate/up on the persistent kernel (builds the row tiles and clears
+// rpos and the counters itself, as launch_gateup_pipe does).
+hipError_t launch_gateup_pipe_w4(const GateUpArgs &a, int block_m, hipStream_t st);
 int down_w4_max_njb(int block_m);
 hipError_t launch_down_w4(const DownArgs &a, int block_m, hipStream_t st);
 // Large-grid down GEMM: persistent, over the gate/up stage's row tiles.

@@ -127,12 +127,39 @@ def test_page1_small():
     parity(case_of("page1", M=24), label="page1 small")
 
 
-@pytest.mark.parametrize("M", [1024, 4096])
+@pytest.mark.parametrize("M", [1024, 2048, 4096, 8192])
 def test_page1_sampled(M):
-    """Page 1's W4A8 workload (E=288, K=4096, I=1024, top-8) at two of its
-    token counts; the sampled tokens reach every expert."""
+    """Page 1's W4A8 workload (E=288, K=4096, I=1024, top-8) at its four
+    token counts (the per-block gate/up at 1024, the persistent one above);
+    the sampled tokens reach every expert."""
     cs = case_of("page1", M=M)
     parity(cs, tokens=cover_tokens(cs, 6, M), label="page1")
+
+
+GU_PERSIST = moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT
+GU_STREAM = moe.MOE_PATH_STREAM << moe.MOE_F_GATEUP_PATH_SHIFT
+
+
+@pytest.mark.parametrize("name,M,bm", [("tiny", 24, 8), ("tiny", 24, 16), ("tiny", 40, 128),
+                                       ("page1", 300, 32), ("skew", 96, 64)])
+def test_persistent_gate_up(name, M, bm):
+    """The W4A8 gate/up on the persistent kernel (forced: at these sizes the
+    schedule would pick the per-block one), block_m 8..128."""
+    cs = case_of(name, M=M, block_m=bm)
+    parity(cs, flags=GU_PERSIST, tokens=cover_tokens(cs, 6, M + bm) if cs.M > 64 else None,
+           label="persistent gate/up")
+
+
+def test_both_gate_up_families_agree_closely():
+    """Same layer through both gate/up families: intermediates within the
+    one-step budget of each other, outputs within the output bar."""
+    cs = case_of("page1", M=512)
+    g1 = run_gpu(cs, flags=GU_PERSIST)
+    g2 = run_gpu(cs, flags=GU_STREAM)
+    assert g1.P == g2.P
+    rows = (g1.sorted[:g1.P] >= 0) & (g1.sorted[:g1.P] < cs.M * cs.top_k)
+    compare_intermediate(g1.h_q[:g1.P], g1.h_s[:g1.P], g2.h_q[:g2.P], g2.h_s[:g2.P], rows)
+    compare_output(g1.out, g2.out)
 
 
 @pytest.mark.parametrize("dt", [torch.int32, torch.int64])
@@ -151,7 +178,7 @@ def test_rejects_what_does_not_apply():
     b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, 0, DEV, w4a8=True)
     out = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
     fuse_on = moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT
-    persist = moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT
+    persist = moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT
     for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0, fuse_on, persist):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_w4a8_experts(b.x_q, b.x_s, cs.w13, cs.w13_s, cs.w2, cs.w2_s, cs.topk_weights,
