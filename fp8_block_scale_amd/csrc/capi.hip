@@ -715,12 +715,9 @@ MOE_API moe_status moe_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int
 
 namespace {
 
-// The W4A8 variant's down stage runs on the per-block kernel: its flags are
-// those of moe_fp8_experts with the down path resolved to MOE_PATH_STREAM
-// (the gate/up path is chosen, or forced, as for moe_fp8_experts).
-uint32_t w4_flags(uint32_t flags) {
-    return (flags & ~MOE_F_DOWN_PATH_MASK) | ((uint32_t)MOE_PATH_STREAM << MOE_F_DOWN_PATH_SHIFT);
-}
+// The W4A8 variant schedules like moe_fp8_experts (two stages, each on the
+// per-block or the persistent kernel family).
+uint32_t w4_flags(uint32_t flags) { return flags; }
 
 moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, int32_t block_m,
                     int64_t sorted_cap, uint32_t flags) {
@@ -729,17 +726,17 @@ moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, i
     if (flags & (MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_W13_PACKED))
         return fail(MOE_ERR_UNSUPPORTED,
                     "W4A8: MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP and MOE_F_W13_PACKED do not apply");
-    const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
-    const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
-    (void)gp;
-    if (dp == MOE_PATH_PERSISTENT)
-        return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs the per-block down kernel only");
     if (((flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT) == MOE_FUSE_ON)
         return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs as two stages (no MOE_FUSE_ON)");
-    if (I / 128 > moe::down_w4_max_njb(block_m))
-        return fail(MOE_ERR_UNSUPPORTED, "W4A8 needs I / 128 <= %d at block_m %d",
+    st = check_flags(w4_flags(flags), K, I, block_m);
+    if (st != MOE_OK) return st;
+    // the per-block down kernel keeps a block's intermediate rows in LDS
+    const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags));
+    if (!l.sp.dn_persistent && I / 128 > moe::down_w4_max_njb(block_m))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "W4A8 on the per-block down kernel needs I / 128 <= %d at block_m %d",
                     moe::down_w4_max_njb(block_m), block_m);
-    return check_flags(w4_flags(flags), K, I, block_m);
+    return MOE_OK;
 }
 
 }  // namespace
@@ -781,12 +778,16 @@ MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const 
                                      num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap,
                                      fl, ws, l);
     ga.w13e = w13_e;
-    if (l.sp.gu_persistent) {       // its row-tile launch clears the route map and counters
+    // the row-tile launch (persistent gate/up, or alone for a persistent
+    // down stage) also clears the route map and the counters
+    if (l.sp.gu_persistent) {
         st = hip_check(moe::launch_gateup_pipe_w4(ga, block_m, s), "moe_w4a8_experts: gate/up launch");
     } else {
-        st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
-                                        (uint32_t *)(ws + l.cnt), l.cnt_words, s),
-                       "moe_w4a8_experts: clear route map and counters");
+        st = l.sp.dn_persistent
+                 ? hip_check(moe::launch_tiles(ga, block_m, s), "moe_w4a8_experts: row tiles")
+                 : hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
+                                              (uint32_t *)(ws + l.cnt), l.cnt_words, s),
+                             "moe_w4a8_experts: clear route map and counters");
         if (st != MOE_OK) return st;
         st = hip_check(moe::launch_gateup_w4(ga, block_m, s), "moe_w4a8_experts: gate/up launch");
     }
@@ -794,7 +795,9 @@ MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const 
     moe::DownArgs da = down_args(w2, nullptr, topk_weights, sorted_token_ids, expert_ids,
                                  num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap, ws, l);
     da.w2e = w2_e;
-    st = hip_check(moe::launch_down_w4(da, block_m, s), "moe_w4a8_experts: down launch");
+    st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe_w4(da, block_m, s)
+                                      : moe::launch_down_w4(da, block_m, s),
+                   "moe_w4a8_experts: down launch");
     if (st != MOE_OK) return st;
     return hip_check(moe::launch_finalize((uint16_t *)out_bf16, (const uint16_t *)(ws + l.y),
                                           (const float *)(ws + l.ys), topk_weights,

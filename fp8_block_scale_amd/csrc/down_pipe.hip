@@ -42,13 +42,26 @@ namespace {
 constexpr int kRows = 128;
 constexpr int kNT = 512;
 constexpr int kStages = 3;
-constexpr int kWBytes = 256 * 128;
 constexpr int kHBytes = kRows * 128;
-constexpr int kWInstr = kWBytes / 1024 / 8;
 constexpr int kHInstr = kHBytes / 1024 / 8;
-constexpr int kPerStage = kWInstr + kHInstr + 1;
 constexpr int kMeta = 64;                     // floats per wave and stage
 constexpr int kMetaRt = 18;                   // route ids start here
+
+// W4 (the W4A8 variant): a stage's W2 tile is 256 rows x 64 B of E2M1 codes
+// (four 16-byte chunks, one per K32 group, stored at chunk c ^ ((r >> 4) & 3)
+// so that the 16 rows of an operand read phase hit distinct banks) plus the
+// rows' exponent dwords; lane group g of an operand takes chunk g of its row
+// and byte g of the row's dword as the E8M0 A scale of the mixed-format MFMA.
+template <bool W4>
+struct DPCfg {
+    static constexpr int WBytes = 256 * (W4 ? 64 : 128);
+    static constexpr int EBytes = W4 ? 256 * 4 : 0;
+    static constexpr int WInstr = WBytes / 1024 / 8;
+    static constexpr int PerStage = WInstr + kHInstr + 1 + (W4 ? 1 : 0);
+    static constexpr size_t Smem = (size_t)kStages * (WBytes + kHBytes + EBytes) +
+                                   kStages * 8 * kMeta * 4;
+    static_assert(Smem <= 160 * 1024, "LDS budget");
+};
 
 __device__ __forceinline__ v8i join8q(const u32x4 &lo, const u32x4 &hi) {
     v8i r;
@@ -77,13 +90,16 @@ struct Item {
 // of either parity on 8 distinct chunks (no bank conflicts).
 __device__ __forceinline__ int w2_swizzle(int r) { return (r ^ (r >> 3) ^ (r >> 4)) & 7; }
 
-template <int BM, bool E8M0>
+template <int BM, bool E8M0, bool W4>
 __global__ void __launch_bounds__(kNT, 1)
 down_pipe_kernel(DownArgs a) {
+    using C = DPCfg<W4>;
+    static_assert(!(W4 && E8M0), "W4 takes FP32 intermediate scales");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *sW = smem;                                                 // [kStages][256][128]
-    uint8_t *sH = smem + kStages * kWBytes;                             // [kStages][128][128]
-    float *sMeta = reinterpret_cast<float *>(sH + kStages * kHBytes);   // [kStages][8][kMeta]
+    uint8_t *sW = smem;                                                 // [kStages][256][128 or 64]
+    uint8_t *sH = smem + kStages * C::WBytes;                           // [kStages][128][128]
+    uint8_t *sE = sH + kStages * kHBytes;                               // W4: [kStages][256] dwords
+    float *sMeta = reinterpret_cast<float *>(sE + kStages * C::EBytes); // [kStages][8][kMeta]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -123,20 +139,35 @@ down_pipe_kernel(DownArgs a) {
     int64_t kl = 0;
     int jl = 0;
     Item il = item_at(0);
-    const uint8_t *wsrc[kWInstr];
+    // (fixed sizes: a local array whose size depends on the template
+    // parameters keeps hipcc's host pass from emitting the kernel's stub)
+    const uint8_t *wsrc[4];
     const uint8_t *hsrc[kHInstr];
     const uint8_t *msrc;
+    const uint8_t *esrc = nullptr;                  // W4: exponent dword of row 32w + lane (lanes < 32)
     int mstep;
     auto set_sources = [&](const Item &it) {
         const int nrows = it.nb * BM;
         const int64_t p0 = (int64_t)it.b * BM;
         const int64_t c0 = (int64_t)it.ct * 256;
         const int ncols = K - c0 < 256 ? (int)(K - c0) : 256;     // 128 or 256
+        if constexpr (W4) {
 #pragma unroll
-        for (int i = 0; i < kWInstr; ++i) {
-            const int row = (w * kWInstr + i) * 8 + sub;              // 0..255
+            for (int i = 0; i < C::WInstr; ++i) {
+                const int row = (w * C::WInstr + i) * 16 + (lane >> 2);   // 0..255
+                const int64_t c = c0 + (row < ncols ? row : 0);
+                wsrc[i] = a.w2 + ((int64_t)it.e * K + c) * (I >> 1) + ((lane & 3) ^ ((row >> 4) & 3)) * 16;
+            }
+            const int row = 32 * w + (lane & 31);
             const int64_t c = c0 + (row < ncols ? row : 0);
-            wsrc[i] = a.w2 + ((int64_t)it.e * K + c) * I + (slot ^ w2_swizzle(row)) * 16;
+            esrc = a.w2e + ((int64_t)it.e * K + c) * (I >> 5);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::WInstr; ++i) {
+                const int row = (w * C::WInstr + i) * 8 + sub;              // 0..255
+                const int64_t c = c0 + (row < ncols ? row : 0);
+                wsrc[i] = a.w2 + ((int64_t)it.e * K + c) * I + (slot ^ w2_swizzle(row)) * 16;
+            }
         }
 #pragma unroll
         for (int i = 0; i < kHInstr; ++i) {
@@ -152,8 +183,10 @@ down_pipe_kernel(DownArgs a) {
             msrc = reinterpret_cast<const uint8_t *>(a.hs + (p0 + (row < nrows ? row : 0)) * njb);
             mstep = 4;
         } else if (lane < kMetaRt) {
+            // the W2 block scales (W4: none; the slot re-reads a row scale)
             const int64_t blk = (c0 >> 7) + (lane == 17 && ncols > 128 ? 1 : 0);
-            msrc = reinterpret_cast<const uint8_t *>(a.w2s + ((int64_t)it.e * (K >> 7) + blk) * njb);
+            msrc = W4 ? reinterpret_cast<const uint8_t *>(a.hs + p0 * njb)
+                      : reinterpret_cast<const uint8_t *>(a.w2s + ((int64_t)it.e * (K >> 7) + blk) * njb);
             mstep = 4;
         } else {
             const int row = w * 16 + lane - kMetaRt;                  // lanes past 33 load nothing
@@ -163,9 +196,11 @@ down_pipe_kernel(DownArgs a) {
     };
     set_sources(il);
     auto issue = [&](int stage) {
-        uint8_t *dw = sW + stage * kWBytes + (w * kWInstr) * 1024;
+        uint8_t *dw = sW + stage * C::WBytes + (w * C::WInstr) * 1024;
 #pragma unroll
-        for (int i = 0; i < kWInstr; ++i) lds_dma16(wsrc[i] + (int64_t)jl * 128, dw + i * 1024);
+        for (int i = 0; i < C::WInstr; ++i) lds_dma16(wsrc[i] + (int64_t)jl * (W4 ? 64 : 128), dw + i * 1024);
+        if constexpr (W4)
+            if (lane < 32) lds_dma4(esrc + jl * 4, sE + stage * C::EBytes + w * 128);
         uint8_t *dh = sH + stage * kHBytes + (w * kHInstr) * 1024;
 #pragma unroll
         for (int i = 0; i < kHInstr; ++i) lds_dma16(hsrc[i] + (int64_t)jl * 128, dh + i * 1024);
@@ -199,7 +234,7 @@ down_pipe_kernel(DownArgs a) {
     auto step = [&](auto st_c, int64_t t) {
         constexpr int ST = decltype(st_c)::value;
         if (t + 1 < T)
-            wait_vmcnt<kPerStage>();
+            wait_vmcnt<C::PerStage>();
         else
             wait_vmcnt<0>();
         stage_barrier();
@@ -221,10 +256,36 @@ down_pipe_kernel(DownArgs a) {
             vrows = v ? wm * 64 + 64 - __builtin_clzll(v) : 0;
             vrows = __builtin_amdgcn_readfirstlane(vrows);
         }
-        if (vrows > 0) {
+        if (W4 && vrows > 0) {
+            const uint8_t *Ws = sW + ST * C::WBytes;
+            const uint8_t *Hs = sH + ST * kHBytes;
+            const uint8_t *Es = sE + ST * C::EBytes;
+            v8i wq[4];
+            int ea[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = 64 * wn + 16 * (l16 >> 2) + 4 * s + (l16 & 3);
+                const u32x4 c4 = lds_read16(Ws + row * 64 + ((g ^ ((row >> 4) & 3)) * 16));
+                wq[s] = v8i{(int)c4.x, (int)c4.y, (int)c4.z, (int)c4.w, 0, 0, 0, 0};
+                ea[s] = (int)((*reinterpret_cast<const uint32_t *>(Es + row * 4) >> (8 * g)) & 0xffu);
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (wm * 64 + u * 16 >= vrows) continue;
+                const int row = wm * 64 + u * 16 + l16;
+                const uint8_t *rp = Hs + row * 128;
+                const u32x4 lo4 = lds_read16(rp + ((g ^ (row & 7)) * 16));
+                const u32x4 hi4 = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
+                const v8i B = join8q(lo4, hi4);
+                const float sa = meta[(row >> 4) * kMeta + (row & 15)];
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc[s][u] = mfma16x16x128_e2m1_e4m3(wq[s], B, ea[s]) * sa + acc[s][u];
+            }
+        } else if (vrows > 0) {
             // this wave's 64 columns lie in one 128-column scale block
             const float sb = meta[w * kMeta + 16 + (wn >= 2 ? 1 : 0)];
-            const uint8_t *Ws = sW + ST * kWBytes;
+            const uint8_t *Ws = sW + ST * C::WBytes;
             const uint8_t *Hs = sH + ST * kHBytes;
             v8i wq[4];
 #pragma unroll
@@ -311,23 +372,32 @@ down_pipe_kernel(DownArgs a) {
     wait_vmcnt<0>();                                 // no load may land after the workgroup ends
 }
 
-constexpr size_t kSmem = (size_t)kStages * (kWBytes + kHBytes) + kStages * 8 * kMeta * 4;
-static_assert(kSmem <= 160 * 1024, "LDS budget");
-
-template <int BM, bool E8M0>
+template <int BM, bool E8M0, bool W4 = false>
 hipError_t launch_dn_pipe(const DownArgs &a, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
     int64_t grid = device_cu_count();
     const int64_t max_items = (int64_t)a.nblocks * a.ctiles;
     if (grid > max_items) grid = max_items;
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = raise_lds_limit(lds_set, (const void *)down_pipe_kernel<BM, E8M0>, (int)kSmem);
+    constexpr size_t smem = DPCfg<W4>::Smem;
+    hipError_t e = raise_lds_limit(lds_set, (const void *)down_pipe_kernel<BM, E8M0, W4>, (int)smem);
     if (e != hipSuccess) return e;
-    down_pipe_kernel<BM, E8M0><<<(unsigned)grid, kNT, kSmem, st>>>(a);
+    down_pipe_kernel<BM, E8M0, W4><<<(unsigned)grid, kNT, smem, st>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, hipStream_t st) {
+    switch (block_m) {
+        case 8: return launch_dn_pipe<8, false, true>(a, st);
+        case 16: return launch_dn_pipe<16, false, true>(a, st);
+        case 32: return launch_dn_pipe<32, false, true>(a, st);
+        case 64: return launch_dn_pipe<64, false, true>(a, st);
+        case 128: return launch_dn_pipe<128, false, true>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st) {
     switch (block_m) {

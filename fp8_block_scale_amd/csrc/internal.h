@@ -186,6 +186,9 @@ hipError_t launch_gateup_w4(const GateUpArgs &a, int block_m, hipStream_t st);
 hipError_t launch_gateup_pipe_w4(const GateUpArgs &a, int block_m, hipStream_t st);
 int down_w4_max_njb(int block_m);
 hipError_t launch_down_w4(const DownArgs &a, int block_m, hipStream_t st);
+// The W4A8 down stage on the persistent kernel (over the gate/up stage's row
+// tiles: the gate/up stage must have listed them).
+hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, hipStream_t st);
 // Large-grid down GEMM: persistent, over the gate/up stage's row tiles.
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
 // The single-launch path (fused.hip): steps 3-5 over the arguments of both

@@ -363,12 +363,12 @@ moe_status moe_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int64_t K,
  * Gate/up products are exact (FP16 MFMA on widened codes, FP32 sums) while
  * the four K32 exponents of a weight row within each 128-wide K-block span
  * at most 23; beyond that the smaller groups' products round to FP16.
- * The gate/up stage runs the per-block or the persistent kernel (chosen,
- * or forced by flag bits 16-17, as for moe_fp8_experts); the down stage
- * runs the per-block kernel.  Constraints: those of moe_fp8_experts,
- * I / 128 <= 512 / min(max(block_m, 16), 64), w13 / w2 16-byte and w13_e /
- * w2_e 4-byte aligned; flags MOE_F_INTER_UE8M0 and a forced split-K apply;
- * MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP, MOE_PATH_PERSISTENT for the down stage,
+ * Each stage runs the per-block or the persistent kernel family, chosen
+ * (or forced by flag bits 16-19) as for moe_fp8_experts.  Constraints:
+ * those of moe_fp8_experts; w13 / w2 16-byte and w13_e / w2_e 4-byte
+ * aligned; when the down stage runs the per-block kernel, I / 128 <=
+ * 512 / min(max(block_m, 16), 64).  Flags MOE_F_INTER_UE8M0, a forced
+ * split-K and the path bits apply; MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP,
  * MOE_FUSE_ON and MOE_F_W13_PACKED give MOE_ERR_UNSUPPORTED.  The workspace is sized by
  * moe_w4a8_experts_workspace_size (0 if the arguments are rejected); the
  * intermediate rows sit where moe_fp8_experts_workspace_layout says. */

@@ -130,7 +130,7 @@ def test_page1_small():
 @pytest.mark.parametrize("M", [1024, 2048, 4096, 8192])
 def test_page1_sampled(M):
     """Page 1's W4A8 workload (E=288, K=4096, I=1024, top-8) at its four
-    token counts (the per-block gate/up at 1024, the persistent one above);
+    token counts (the per-block gate/up at 1024, the persistent kernels above);
     the sampled tokens reach every expert."""
     cs = case_of("page1", M=M)
     parity(cs, tokens=cover_tokens(cs, 6, M), label="page1")
@@ -138,16 +138,28 @@ def test_page1_sampled(M):
 
 GU_PERSIST = moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT
 GU_STREAM = moe.MOE_PATH_STREAM << moe.MOE_F_GATEUP_PATH_SHIFT
+DN_PERSIST = moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT
+DN_STREAM = moe.MOE_PATH_STREAM << moe.MOE_F_DOWN_PATH_SHIFT
 
 
+@pytest.mark.parametrize("gu,dn", [(GU_PERSIST, DN_STREAM), (GU_STREAM, DN_PERSIST),
+                                   (GU_PERSIST, DN_PERSIST)])
 @pytest.mark.parametrize("name,M,bm", [("tiny", 24, 8), ("tiny", 24, 16), ("tiny", 40, 128),
                                        ("page1", 300, 32), ("skew", 96, 64)])
-def test_persistent_gate_up(name, M, bm):
-    """The W4A8 gate/up on the persistent kernel (forced: at these sizes the
-    schedule would pick the per-block one), block_m 8..128."""
+def test_persistent_kernels(name, M, bm, gu, dn):
+    """The W4A8 stages on the persistent kernels, forced (at these sizes the
+    schedule would pick the per-block ones), every pairing, block_m 8..128."""
     cs = case_of(name, M=M, block_m=bm)
-    parity(cs, flags=GU_PERSIST, tokens=cover_tokens(cs, 6, M + bm) if cs.M > 64 else None,
-           label="persistent gate/up")
+    parity(cs, flags=gu | dn, tokens=cover_tokens(cs, 6, M + bm) if cs.M > 64 else None,
+           label="persistent")
+
+
+def test_persistent_down_long_intermediate_rows():
+    """I = 2048: rows too long for the per-block down kernel's LDS tile; the
+    persistent down kernel takes them."""
+    cfg = dict(CONFIGS["tiny"], M=24, E=8, K=512, I=2048, top_k=2, block_m=64, seed=7)
+    cs = make_case("long_rows_w4", device=DEV, config=cfg, fmt="w4a8")
+    parity(cs, flags=DN_PERSIST, label="persistent down, I=2048")
 
 
 def test_both_gate_up_families_agree_closely():
@@ -178,8 +190,8 @@ def test_rejects_what_does_not_apply():
     b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, 0, DEV, w4a8=True)
     out = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
     fuse_on = moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT
-    persist = moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT
-    for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0, fuse_on, persist):
+    for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0, fuse_on,
+               moe.MOE_F_W13_PACKED):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_w4a8_experts(b.x_q, b.x_s, cs.w13, cs.w13_s, cs.w2, cs.w2_s, cs.topk_weights,
                                  b.sorted_ids, b.expert_ids, b.ntp, cs.top_k, cs.block_m, out,

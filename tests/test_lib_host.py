@@ -270,13 +270,15 @@ def test_w4a8_validation_before_any_device_call():
         return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["M"], a["K"], a["I"],
                  a["E"], a["k"], a["bm"], a["sc"], a["fl"], FAKE, a["ws"], a["wsb"], None)
 
-    persist = moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT
-    for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0, persist,
-               moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT):
+    for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0,
+               moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT, moe.MOE_F_W13_PACKED):
         assert _err(call(fl=fl)) == "MOE_ERR_UNSUPPORTED", fl
         assert moe.moe_w4a8_experts_workspace_size(4, 256, 256, 8, 2, 16, 128, fl) == 0
-    # the down stage keeps a block's intermediate rows in LDS: I / 128 <= 512 / 64 at block_m 64
+    # the per-block down kernel keeps a block's intermediate rows in LDS:
+    # I / 128 <= 512 / 64 at block_m 64 (unless the down stage is persistent)
     assert _err(call(I=2048, bm=64, sc=128)) == "MOE_ERR_UNSUPPORTED"
+    persist_dn = moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT
+    assert moe.moe_w4a8_experts_workspace_size(4, 256, 2048, 8, 2, 64, 128, persist_dn) > 0
     assert _err(call(I=1024, bm=64, sc=128, wsb=16)) == "MOE_ERR_CAPACITY"
     assert _err(call(K=200)) == "MOE_ERR_SHAPE"
     assert _err(call(wsb=16)) == "MOE_ERR_CAPACITY"
