@@ -146,6 +146,32 @@ __device__ __forceinline__ v8h e2m1x8_to_f16(uint32_t d, float scale) {
 // 2^e as an FP32 value for any e in [-149, 127] (subnormal results included).
 __device__ __forceinline__ float pow2_int(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
 
+// 16-byte chunk swizzle of a 64-byte row (E2M1 K-block slice) in LDS: the
+// chunk c of row r sits at c ^ w4_swizzle(r).  Sixteen consecutive rows read
+// at one logical chunk then cover all 64 banks ((r & 3) alone repeats every
+// four rows: a 4-way conflict).
+__device__ __forceinline__ int w4_swizzle(int r) { return (r ^ (r >> 2)) & 3; }
+
+// Largest byte of the dwords p[i], i = first, first + step, ... < end, with
+// eight loads in flight per round trip (a plain loop waits on each load).
+__device__ __forceinline__ int max_byte_strided(const uint32_t *p, int first, int end, int step) {
+    uint32_t m = 0;
+    for (int i0 = first; i0 < end; i0 += 8 * step) {
+        uint32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = i0 + j * step;
+            v[j] = i < end ? p[i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t x = v[j];
+            m = max(m, max(max(x & 0xffu, (x >> 8) & 0xffu), max((x >> 16) & 0xffu, x >> 24)));
+        }
+    }
+    return (int)m;
+}
+
 // Largest of the four bytes of a dword.
 __device__ __forceinline__ int max_byte4(uint32_t v) {
     const uint32_t m = max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24));

@@ -159,7 +159,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     // weight-block scales).  Masked and padding rows read the last valid
     // row's token (sXt); their columns are never stored.
     // W4: two W13 segments (16 rows x 64 B each, 16-byte chunks XOR-swizzled
-    // by row & 3), the activation segment, and one 4-byte load: lanes 0-31
+    // by w4_swizzle(row)), the activation segment, and one 4-byte load: lanes 0-31
     // the K32 exponent dword of weight rows 32w.., lanes 32-39 x_s of rows 8w...
     const int sub = lane >> 3, slot = lane & 7;
     const uint8_t *wsrc[4];
@@ -169,7 +169,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             const int row = (w * 2 + i) * 16 + (lane >> 2);          // tile row 0..255
             const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
             wsrc[i] = a.w13 + ((int64_t)e * 2 * I + n) * (K >> 1) + (int64_t)kb0 * 64 +
-                      ((lane & 3) ^ (row & 3)) * 16;
+                      ((lane & 3) ^ w4_swizzle(row)) * 16;
         }
         wsrc[2] = wsrc[3] = nullptr;
     } else if (a.w13_packed) {
@@ -265,8 +265,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         const int row = tid >> 1, half = tid & 1;
         const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
         const uint32_t *ep = reinterpret_cast<const uint32_t *>(a.w13e + ((int64_t)e * 2 * I + n) * (K >> 5));
-        int m = 0;
-        for (int kb = kb0 + half; kb < kb1; kb += 2) m = max(m, max_byte4(ep[kb]));
+        int m = max_byte_strided(ep, kb0 + half, kb1, 2);
         m = max(m, __shfl_xor(m, 1, 64));
         if (half == 0) sRw[row] = m;
         __syncthreads();
@@ -296,8 +295,8 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         for (int h = 0; h < 2; ++h) {
             const int row = 128 * h + 16 * w + l16;
             const uint8_t *rp = Ws + row * 64 + ((g & 1) << 3);
-            const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ (row & 3)) << 4));
-            const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ (row & 3)) << 4));
+            const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ w4_swizzle(row)) << 4));
+            const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ w4_swizzle(row)) << 4));
             const uint32_t sw = *reinterpret_cast<const uint32_t *>(Sb + (row >> 5) * 256 + (row & 31) * 4);
             const int R = rwa[h];
             const int dlo = (int)((sw >> (8 * (g >> 1))) & 0xffu) - R;

@@ -47,8 +47,8 @@ constexpr int kMaxKb = 256;                   // K <= 32768
 // the largest exponents over K) and accumulated across K-blocks in the MFMA
 // chain; the item's sums are scaled by 2^A * 2^B once, before SwiGLU.
 // kW4 (the W4A8 variant): E2M1 W13 with K32 exponent bytes; a stage holds
-// 256 rows x 64 B of codes (chunks XOR-swizzled by row & 3) and the rows'
-// exponent dwords.  Each weight row's largest exponent R over K is found
+// 256 rows x 64 B of codes (16-byte chunks XOR-swizzled by w4_swizzle(row))
+// and the rows' exponent dwords.  Each weight row's largest exponent R over K is found
 // once per item; the codes are widened to FP16 with 2^(s - R) folded in
 // (exact while a row's exponents span at most 23 binades), the K-block sums
 // take x_s as in kExact, and each output row is scaled by 2^(R - 127) once,
@@ -231,7 +231,7 @@ gateup_pipe_kernel(GateUpArgs a) {
         for (int i = 0; i < C::WInstr; ++i) {
             const int row = (w * C::WInstr + i) * 16 + (lane >> 2);       // tile row 0..255
             const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
-            wsrc[i] = a.w13 + ((int64_t)e * twoI + n) * (K >> 1) + ((lane & 3) ^ (row & 3)) * 16;
+            wsrc[i] = a.w13 + ((int64_t)e * twoI + n) * (K >> 1) + ((lane & 3) ^ w4_swizzle(row)) * 16;
         }
         const int row = 32 * w + (lane & 31);
         const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
@@ -278,8 +278,7 @@ gateup_pipe_kernel(GateUpArgs a) {
         const int row = tid >> 1, half = tid & 1;
         const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
         const uint32_t *ep = reinterpret_cast<const uint32_t *>(a.w13e + ((int64_t)e * twoI + n) * (K >> 5));
-        int m = 0;
-        for (int q = half; q < nkb; q += 2) m = max(m, max_byte4(ep[q]));
+        int m = max_byte_strided(ep, half, nkb, 2);
         m = max(m, __shfl_xor(m, 1, 64));
         if (half == 0) sRw[row] = m;
         __syncthreads();
@@ -411,8 +410,8 @@ gateup_pipe_kernel(GateUpArgs a) {
             for (int s = 0; s < 4; ++s) {
                 const int row = (s < 2 ? 0 : 128) + 32 * wn + 16 * (s & 1) + l16;
                 const uint8_t *rp = Ws + row * 64 + ((g & 1) << 3);
-                const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ (row & 3)) << 4));
-                const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ (row & 3)) << 4));
+                const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ w4_swizzle(row)) << 4));
+                const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ w4_swizzle(row)) << 4));
                 const uint32_t sw = *reinterpret_cast<const uint32_t *>(Es + row * 4);
                 const int dlo = (int)((sw >> (8 * (g >> 1))) & 0xffu) - rw[s];
                 const int dhi = (int)((sw >> (8 * (2 + (g >> 1)))) & 0xffu) - rw[s];
