@@ -162,6 +162,24 @@ def test_persistent_down_long_intermediate_rows():
     parity(cs, flags=DN_PERSIST, label="persistent down, I=2048")
 
 
+@pytest.mark.parametrize("K,I,M,E,top_k,bm,flags", [
+    (384, 128, 37, 5, 3, 16, 0),                    # three K-blocks, one intermediate block
+    (384, 128, 37, 5, 3, 16, GU_PERSIST | DN_PERSIST),
+    (640, 384, 19, 7, 2, 8, 0),                     # five K-blocks, three intermediate blocks
+    (640, 384, 19, 7, 2, 8, GU_PERSIST | DN_PERSIST),
+    (128, 256, 64, 3, 3, 32, 3 << moe.MOE_F_SPLITK_SHIFT),   # one K-block (split 3 -> 1)
+    # nine K-blocks in five splits (64 tokens: at 9 tokens the 1e-4 code
+    # budget admits no rounding tie at all among 9216 codes)
+    (1152, 256, 64, 4, 4, 16, 5 << moe.MOE_F_SPLITK_SHIFT),
+])
+def test_ragged_shapes(K, I, M, E, top_k, bm, flags):
+    """Odd K-block counts, one- and three-block intermediate widths, ragged
+    token counts, forced splits, both kernel families."""
+    cfg = dict(CONFIGS["tiny"], M=M, E=E, K=K, I=I, top_k=top_k, block_m=bm, seed=K + I + M)
+    cs = make_case("ragged_w4", device=DEV, config=cfg, fmt="w4a8")
+    parity(cs, flags=flags, label="ragged")
+
+
 def test_both_gate_up_families_agree_closely():
     """Same layer through both gate/up families: intermediates within the
     one-step budget of each other, outputs within the output bar."""
