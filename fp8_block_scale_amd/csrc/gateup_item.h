@@ -294,9 +294,15 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int row = 128 * h + 16 * w + l16;
-            const uint8_t *rp = Ws + row * 64 + ((g & 1) << 3);
-            const uint2 d01 = *reinterpret_cast<const uint2 *>(rp + (((g >> 1) ^ w4_swizzle(row)) << 4));
-            const uint2 d23 = *reinterpret_cast<const uint2 *>(rp + (((2 + (g >> 1)) ^ w4_swizzle(row)) << 4));
+            // whole 16-byte chunks through lds_read16 (typed 16-byte reads
+            // are what lets the compiler keep these reads clear of the
+            // in-flight LDS refills; 8-byte reads drew a full vmcnt(0) wait
+            // every K-block), then this lane group's half of each
+            const uint8_t *rp = Ws + row * 64;
+            const u32x4 c01 = lds_read16(rp + (((g >> 1) ^ w4_swizzle(row)) << 4));
+            const u32x4 c23 = lds_read16(rp + (((2 + (g >> 1)) ^ w4_swizzle(row)) << 4));
+            const uint2 d01 = (g & 1) ? uint2{c01.z, c01.w} : uint2{c01.x, c01.y};
+            const uint2 d23 = (g & 1) ? uint2{c23.z, c23.w} : uint2{c23.x, c23.y};
             const uint32_t sw = *reinterpret_cast<const uint32_t *>(Sb + (row >> 5) * 256 + (row & 31) * 4);
             const int R = rwa[h];
             const int dlo = (int)((sw >> (8 * (g >> 1))) & 0xffu) - R;
