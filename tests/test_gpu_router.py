@@ -121,3 +121,41 @@ def test_decode_layer_behind_the_router(M):
                       cs.w2_s.cpu().numpy(), rw.astype(np.float32), rs, rx, rP, kk, cs.block_m)
     st = compare_output(out.float().cpu().numpy().astype(np.float64), res.ref64)
     log(f"[router layer] M={M} {st}")
+
+
+def test_graph_replay_matches_eager():
+    """Routing + plan + quantisation (moe_route_plan, both builders) captured
+    in a HIP graph: every replay writes the eager ids, weights, plan and codes
+    bit for bit."""
+    for M, multi in ((16, False), (4096, True)):
+        logits = _logits(M, 256, 77 + M)
+        g0 = torch.Generator(device=DEV)
+        g0.manual_seed(M)
+        x = torch.randn((M, 7168), generator=g0, device=DEV).to(torch.bfloat16)
+        log(f"[router graph] M={M} multi={multi}")
+        ref = _route(logits, 8, 1, 2.5, 16, multi, x)
+        E, kk = 257, 9
+        sc, bc = moe.moe_plan_capacity(M, kk, E, 16)
+        ids = torch.empty((M, kk), dtype=torch.int32, device=DEV)
+        w = torch.empty((M, kk), dtype=torch.float32, device=DEV)
+        s = torch.empty(sc, dtype=torch.int32, device=DEV)
+        e = torch.empty(bc, dtype=torch.int32, device=DEV)
+        p = torch.empty(1, dtype=torch.int32, device=DEV)
+        n = moe.moe_plan_workspace_size(M, kk, E, 16) if multi else 0
+        ws = torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
+        q = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+        qs = torch.empty((M, x.shape[1] // 128), dtype=torch.float32, device=DEV)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.moe_route_plan(logits, 8, 1, 2.5, 16, ids, w, s, e, p, ws, x, q, qs,
+                               stream=torch.cuda.current_stream())
+        for rep in range(3):
+            for t in (ids, s, e, p):
+                t.fill_(-3)
+            graph.replay()
+            torch.cuda.synchronize()
+            P = int(p.item())
+            assert P == ref[4], rep
+            assert torch.equal(ids, ref[0]) and torch.equal(w, ref[1])
+            assert torch.equal(s[:P], ref[2][:P]) and torch.equal(e[:P // 16], ref[3][:P // 16])
+            assert torch.equal(q, ref[5]) and torch.equal(qs, ref[6])

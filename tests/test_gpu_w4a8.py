@@ -215,3 +215,39 @@ def test_rejects_what_does_not_apply():
                                  b.sorted_ids, b.expert_ids, b.ntp, cs.top_k, cs.block_m, out,
                                  b.workspace, fl)
         assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name,M,flags", [("decode", 16, 0), ("page1", 512, 0),
+                                          ("page1", 512, GU_PERSIST | DN_PERSIST)])
+def test_graph_replay_matches_eager(name, M, flags):
+    """The W4A8 layer (plan + quantisation + moe_w4a8_experts, per-block and
+    persistent kernels) captured in a HIP graph: every replay, with eager
+    work and synchronisations between replays, gives the eager output bit
+    for bit."""
+    cs = case_of(name, M=M)
+    log(f"[w4a8 graph] {name} M={cs.M} flags={flags:#x}")
+    b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, flags, DEV, w4a8=True)
+
+    def layer(out, stream):
+        moe.moe_plan_quant(cs.topk_ids, cs.E, cs.block_m, b.sorted_ids, b.expert_ids, b.ntp, cs.x,
+                           b.x_q, b.x_s, moe.MOE_SCALE_FP32, b.plan_ws, stream)
+        moe.moe_w4a8_experts(b.x_q, b.x_s, cs.w13, cs.w13_s, cs.w2, cs.w2_s, cs.topk_weights,
+                             b.sorted_ids, b.expert_ids, b.ntp, cs.top_k, cs.block_m, out,
+                             b.workspace, flags, stream)
+
+    ref = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
+    layer(ref, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    out = torch.zeros_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(out, torch.cuda.current_stream())
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager layer"
+        scratch = torch.zeros_like(ref)             # eager work between replays
+        layer(scratch, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(scratch, ref)
