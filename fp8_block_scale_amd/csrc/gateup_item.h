@@ -72,8 +72,13 @@ struct GSCfg {
     // 128 B, scales: a 16-float run per wave}, reused after the K loop as the
     // FP32 tile [RP][GROW]; then routes, row tokens, a DMA sink, flags.
     // W4: the W13 tile is 256 x 64 B of E2M1 codes and each wave's scale run
-    // is 256 B: the K32 exponent dwords of 32 weight rows, then 8 x_s.
+    // is 256 B: the K32 exponent dwords of 32 weight rows, then 8 x_s.  With
+    // passes of up to 32 rows (EGRP) the exponent dwords instead come four
+    // K-blocks at a time into one of two group slots [256 rows][4 K-blocks]
+    // outside the ring (decode M=16 steps 3-5 10% faster; with 64-row passes
+    // 2.6% slower at page-1 M=1024, so those keep one load per K-block).
     static constexpr int NS = NSO ? NSO : (RP <= 32 ? 4 : 3);
+    static constexpr bool EGRP = W4 && RP <= 32;    // exponents in groups of four K-blocks
     static constexpr int WB = 256 * (W4 ? 64 : 128);
     static constexpr int XB = RP * 128;
     static constexpr int SB = W4 ? 8 * 256 : 8 * 16 * 4;
@@ -86,8 +91,10 @@ struct GSCfg {
     static constexpr int MISC = SINK + 8 * 256;
     static constexpr int EXP = MISC + 16;          // kExactE8: [RP] row, [2] gate/up exponents
     static constexpr int RW = EXP + (RP + 4) * 4;  // kW4: [256] weight-row exponents
-    static constexpr int TOTAL = RW + (W4 ? 256 * 4 : 0);
+    static constexpr int EG = RW + (W4 ? 256 * 4 : 0);  // EGRP: [2][256][4] exponent dwords
+    static constexpr int TOTAL = EG + (EGRP ? 2 * 256 * 16 : 0);
     static constexpr int NPS = W4 ? 4 : 6;         // DMA instructions per wave per stage
+    static constexpr int NPE = EGRP ? 2 : 0;       // more on stages that start an exponent group
 };
 
 // One work item: plan block b, pass `pass` of its rows, j-tile jt, K-split
@@ -109,6 +116,7 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     int *sMisc = reinterpret_cast<int *>(smem + C::MISC);
     int *sExp = reinterpret_cast<int *>(smem + C::EXP);
     int *sRw = reinterpret_cast<int *>(smem + C::RW);
+    uint8_t *sEg = smem + C::EG;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -159,8 +167,13 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     // weight-block scales).  Masked and padding rows read the last valid
     // row's token (sXt); their columns are never stored.
     // W4: two W13 segments (16 rows x 64 B each, 16-byte chunks XOR-swizzled
-    // by w4_swizzle(row)), the activation segment, and one 4-byte load: lanes 0-31
-    // the K32 exponent dword of weight rows 32w.., lanes 32-39 x_s of rows 8w...
+    // by w4_swizzle(row)), the activation segment, and one 4-byte load: lanes
+    // 0-31 the K32 exponent dword of weight rows 32w.., lanes 32-39 x_s of rows
+    // 8w...  EGRP: lanes 0-31 idle in that load; instead, on stages whose
+    // K-block starts a group of four, two more 4-byte loads bring the
+    // exponent dwords of weight rows 32w.. for the group's four K-blocks, a
+    // row's four dwords from consecutive lanes (one cache line), so a row's
+    // exponents cost one line request per four K-blocks.
     const int sub = lane >> 3, slot = lane & 7;
     const uint8_t *wsrc[4];
     if constexpr (W4) {
@@ -195,14 +208,23 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     }
     // 4-byte scale source of this lane, advanced by 4 bytes per K-block
     const uint8_t *ssrc;
+    const uint8_t *esrc[2] = {nullptr, nullptr};   // W4: exponent rows 32w + 16i + lane / 4
     if constexpr (W4) {
-        if (lane < 32) {
+        if (!C::EGRP && lane < 32) {
             const int row = 32 * w + lane;
             const int64_t n = (row < 128 ? 0 : I - 128) + (int64_t)jt * 128 + row;
             ssrc = a.w13e + ((int64_t)e * 2 * I + n) * (K >> 5) + (int64_t)kb0 * 4;
         } else {
             const int row = 8 * w + (lane & 7) < C::RP ? 8 * w + (lane & 7) : 0;
             ssrc = reinterpret_cast<const uint8_t *>(a.xs + (int64_t)sXt[row] * a.nkb + kb0);
+        }
+        if constexpr (C::EGRP) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int er = 32 * w + 16 * i + (lane >> 2);
+                const int64_t n = (er < 128 ? 0 : I - 128) + (int64_t)jt * 128 + er;
+                esrc[i] = a.w13e + ((int64_t)e * 2 * I + n) * (K >> 5) + (int64_t)kb0 * 4;
+            }
         }
     } else if (lane < 8) {
         const int row = 8 * w + lane < C::RP ? 8 * w + lane : 0;
@@ -232,7 +254,15 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             lds_dma16(xsrc + kbl * 128, base + C::WB + w * 1024);
         else
             lds_dma4(xsrc + kbl * 128, sSink + w * 256);
-        if (lane < (W4 ? 40 : 10)) lds_dma4(ssrc + kbl * 4, base + C::WB + C::XB + w * (C::SB / 8));
+        if (C::EGRP ? (lane >= 32 && lane < 40) : lane < (W4 ? 40 : 10))
+            lds_dma4(ssrc + kbl * 4, base + C::WB + C::XB + w * (C::SB / 8));
+        if (C::EGRP && (kbl & 3) == 0) {
+            // the group's K-blocks, the last one repeated past the item's range
+            const int kq = kbl + (lane & 3) < nk ? kbl + (lane & 3) : nk - 1;
+            uint8_t *eg = sEg + ((kbl >> 2) & 1) * (256 * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) lds_dma4(esrc[i] + kq * 4, eg + (32 * w + 16 * i) * 16);
+        }
     };
 
     if constexpr (MODE == kExactE8) {
@@ -284,8 +314,9 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
         accu[u] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto compute_w4 = [&](int st) {
+    auto compute_w4 = [&](int st, int kbl) {
         const uint8_t *Ws = smem + st * C::STB;
+        const uint8_t *Eg = sEg + ((kbl >> 2) & 1) * (256 * 16) + (kbl & 3) * 4;
         const uint8_t *Xs = Ws + C::WB;
         const uint8_t *Sb = Ws + C::WB + C::XB;
         // weight rows: this lane's A rows (gate / up), widened with their
@@ -303,7 +334,9 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
             const u32x4 c23 = lds_read16(rp + (((2 + (g >> 1)) ^ w4_swizzle(row)) << 4));
             const uint2 d01 = (g & 1) ? uint2{c01.z, c01.w} : uint2{c01.x, c01.y};
             const uint2 d23 = (g & 1) ? uint2{c23.z, c23.w} : uint2{c23.x, c23.y};
-            const uint32_t sw = *reinterpret_cast<const uint32_t *>(Sb + (row >> 5) * 256 + (row & 31) * 4);
+            const uint32_t sw = C::EGRP
+                ? *reinterpret_cast<const uint32_t *>(Eg + row * 16)
+                : *reinterpret_cast<const uint32_t *>(Sb + (row >> 5) * 256 + (row & 31) * 4);
             const int R = rwa[h];
             const int dlo = (int)((sw >> (8 * (g >> 1))) & 0xffu) - R;
             const int dhi = (int)((sw >> (8 * (2 + (g >> 1)))) & 0xffu) - R;
@@ -402,17 +435,27 @@ __device__ __forceinline__ void gateup_item(const GateUpArgs &a, uint8_t *smem, 
     for (int kb = 0; kb < nk; ++kb) {
         // stages kb .. kb + min(NS - 2, ahead) are in flight; all but the
         // later min(NS - 2, ahead) of them must have landed
+        // (EGRP: a stage whose K-block starts an exponent group carries NPE
+        // more; of two consecutive stages at most one does)
         const int ahead = nk - 1 - kb;
-        if (C::NS > 3 && ahead >= 2)
-            wait_vmcnt<(C::NS > 3 ? 2 : 1) * C::NPS>();
-        else if (C::NS > 2 && ahead >= 1)
-            wait_vmcnt<C::NPS>();
-        else
+        const bool eg1 = C::EGRP && ((kb + 1) & 3) == 0, eg2 = C::EGRP && ((kb + 2) & 3) == 0;
+        if (C::NS > 3 && ahead >= 2) {
+            if (eg1 || eg2)
+                wait_vmcnt<(C::NS > 3 ? 2 : 1) * C::NPS + C::NPE>();
+            else
+                wait_vmcnt<(C::NS > 3 ? 2 : 1) * C::NPS>();
+        } else if (C::NS > 2 && ahead >= 1) {
+            if (eg1)
+                wait_vmcnt<C::NPS + C::NPE>();
+            else
+                wait_vmcnt<C::NPS>();
+        } else {
             wait_vmcnt<0>();
+        }
         stage_barrier();
         if (kb + C::NS - 1 < nk) issue((kb + C::NS - 1) % C::NS, kb + C::NS - 1);
         if constexpr (W4)
-            compute_w4(kb % C::NS);
+            compute_w4(kb % C::NS, kb);
         else
             compute(kb % C::NS);
     }
