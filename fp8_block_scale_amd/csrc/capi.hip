@@ -56,6 +56,7 @@ struct SplitChoice {
     int kb_per_split;
     bool gu_persistent;
     bool dn_persistent;
+    bool dn_small;       // the persistent down on row tiles of 32 rows (deeper W2 ring)
     bool fused;          // steps 3-5 in one launch (moe_fp8_experts only)
 };
 
@@ -63,7 +64,7 @@ constexpr int64_t kPersistentTiles = 512;   // (block, j-tile) pairs
 constexpr double kStreamFill = 192.0;       // workgroups the stream kernel's split aims at
 
 SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtiles, int64_t K,
-                         int64_t I, int32_t bm, uint32_t flags) {
+                         int64_t I, int32_t bm, uint32_t flags, bool w4) {
     const int64_t nkb = K / 128;
     const int64_t tiles = blocks_cap * jtiles;
     const int64_t forced = (flags & MOE_F_SPLITK_MASK) >> MOE_F_SPLITK_SHIFT;
@@ -76,16 +77,32 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     const int64_t pass_rows = bm < 64 ? bm : 64;
     const bool dense = 4 * R > 3 * pass_rows * (int64_t)E;
     const uint32_t fuse = (flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT;
+    // Plan blocks expected to hold routes under uniform routing: the experts
+    // hit, E (1 - (1 - 1/E)^R), or R / block_m if more, at most the capacity.
+    const double hit = (double)E * -std::expm1((double)R * std::log1p(-1.0 / (double)E));
+    double blocks = hit > (double)R / bm ? hit : (double)R / bm;
+    if (blocks > (double)blocks_cap) blocks = (double)blocks_cap;
+    // The persistent down kernel streams W2 without a break across its items;
+    // with FP8 weights it wins once the (block, 256-column) items outnumber
+    // the CUs twice over (measured at the decode shape: M=4, 8, 16 faster,
+    // M=1 with 252 items slower).  With E2M1 weights (half the bytes per
+    // item) the per-block down kernel stayed 2-4% faster at M=4-16.
+    const bool dn_many = !w4 && blocks * (double)((K + 255) / 256) >= 512.0 && fits;
     SplitChoice c;
     c.gu_persistent = gu_path == MOE_PATH_PERSISTENT ||
                       (gu_path == MOE_PATH_AUTO && forced == 0 && big && dense);
-    c.dn_persistent = dn_path == MOE_PATH_PERSISTENT || (dn_path == MOE_PATH_AUTO && big);
+    c.dn_persistent = dn_path == MOE_PATH_PERSISTENT || (dn_path == MOE_PATH_AUTO && (big || dn_many));
     // The single launch only on request: measured on MI355X it is slower than
     // the two stages at every size tried (decode M=1: 34 against 27 us; M=16:
     // 155 against 120 us): every workgroup pays the larger item's LDS, so
     // neither item kind keeps its own occupancy and ring depth.
     if (fuse == MOE_FUSE_ON) c.gu_persistent = c.dn_persistent = false;   // (forced paths: rejected)
     c.fused = fuse == MOE_FUSE_ON;
+    // Without the persistent gate/up (whose row tiles hold up to 128 rows) the
+    // down stage's row tiles are cut at 32 rows when blocks allow: experts
+    // then hold a block or two each, and the 32-row tile leaves LDS for four
+    // W2 stages in flight instead of three.
+    c.dn_small = c.dn_persistent && !c.gu_persistent && bm <= 32;
     if (c.gu_persistent) {
         c.nsplit = 1;
         c.kb_per_split = (int)nkb;
@@ -94,15 +111,11 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     const int64_t npass = bm > 64 ? bm / 64 : 1;
     int64_t s = forced;
     if (s == 0) {
-        // Workgroups that will have work: plan blocks expected under uniform
-        // routing (the experts hit, E (1 - (1 - 1/E)^R), or R / block_m if
-        // more), not the capacity's one block per route.  The smallest split
-        // that fills 3/4 of the chip in one round: a partial second round
-        // costs nearly a whole one (decode M=4: 37 us at 288 workgroups
-        // against 26 us at 216).
-        const double hit = (double)E * -std::expm1((double)R * std::log1p(-1.0 / (double)E));
-        double blocks = hit > (double)R / bm ? hit : (double)R / bm;
-        if (blocks > (double)blocks_cap) blocks = (double)blocks_cap;
+        // Workgroups that will have work: the plan blocks expected above, not
+        // the capacity's one block per route.  The smallest split that fills
+        // 3/4 of the chip in one round: a partial second round costs nearly
+        // a whole one (decode M=4: 37 us at 288 workgroups against 26 us at
+        // 216).
         double units = blocks * (double)jtiles * (double)npass;
         if (units < 1.0) units = 1.0;
         s = (int64_t)std::ceil(kStreamFill / units);
@@ -126,11 +139,11 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, int32_t block_m,
-                   int64_t sorted_cap, uint32_t flags) {
+                   int64_t sorted_cap, uint32_t flags, bool w4 = false) {
     WsLayout l;
     int64_t blocks_cap = sorted_cap / block_m;
     int64_t jtiles = I / 128;
-    l.sp = choose_split(M * top_k, E, blocks_cap, jtiles, K, I, block_m, flags);
+    l.sp = choose_split(M * top_k, E, blocks_cap, jtiles, K, I, block_m, flags, w4);
     size_t off = 0;
     l.hq = off;
     off = align256(off + (size_t)sorted_cap * I);
@@ -593,7 +606,8 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     if (l.sp.gu_persistent)
         return hip_check(moe::launch_gateup_pipe(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
     if (l.sp.dn_persistent) {                  // the down stage's row tiles
-        st = hip_check(moe::launch_tiles(ga, block_m, s), "moe_fp8_gate_up: row tiles");
+        st = hip_check(moe::launch_tiles(ga, block_m, l.sp.dn_small ? 32 : 128, s),
+                       "moe_fp8_gate_up: row tiles");
         if (st != MOE_OK) return st;
     }
     return hip_check(moe::launch_gateup(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
@@ -621,7 +635,7 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                        num_tokens_post_padded, M, K, I, E, top_k, block_m,
                                        sorted_cap, ws, l);
     const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
-    st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe(da, block_m, e8, s)
+    st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe(da, block_m, e8, l.sp.dn_small, s)
                                                    : moe::launch_down(da, block_m, e8, s),
                    "moe_fp8_down_reduce: down launch");
     if (st != MOE_OK) return st;
@@ -731,7 +745,7 @@ moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, i
     st = check_flags(w4_flags(flags), K, I, block_m);
     if (st != MOE_OK) return st;
     // the per-block down kernel keeps a block's intermediate rows in LDS
-    const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags));
+    const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags), true);
     if (!l.sp.dn_persistent && I / 128 > moe::down_w4_max_njb(block_m))
         return fail(MOE_ERR_UNSUPPORTED,
                     "W4A8 on the per-block down kernel needs I / 128 <= %d at block_m %d",
@@ -745,7 +759,7 @@ MOE_API size_t moe_w4a8_experts_workspace_size(int64_t M, int64_t K, int64_t I, 
                                                int32_t top_k, int32_t block_m, int64_t sorted_cap,
                                                uint32_t flags) {
     if (check_w4(M, K, I, E, top_k, block_m, sorted_cap, flags) != MOE_OK) return 0;
-    return ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags)).total;
+    return ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags), true).total;
 }
 
 MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
@@ -759,7 +773,7 @@ MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const 
     moe_status st = check_w4(M, K, I, E, top_k, block_m, sorted_cap, flags);
     if (st != MOE_OK) return st;
     const uint32_t fl = w4_flags(flags);
-    const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, fl);
+    const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, fl, true);
     if (M == 0 || sorted_cap == 0) return MOE_OK;
     if (!workspace) return fail(MOE_ERR_NULL, "workspace is required");
     if (((uintptr_t)workspace & 255u) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -784,7 +798,8 @@ MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const 
         st = hip_check(moe::launch_gateup_pipe_w4(ga, block_m, s), "moe_w4a8_experts: gate/up launch");
     } else {
         st = l.sp.dn_persistent
-                 ? hip_check(moe::launch_tiles(ga, block_m, s), "moe_w4a8_experts: row tiles")
+                 ? hip_check(moe::launch_tiles(ga, block_m, l.sp.dn_small ? 32 : 128, s),
+                             "moe_w4a8_experts: row tiles")
                  : hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
                                               (uint32_t *)(ws + l.cnt), l.cnt_words, s),
                              "moe_w4a8_experts: clear route map and counters");
@@ -795,7 +810,7 @@ MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const 
     moe::DownArgs da = down_args(w2, nullptr, topk_weights, sorted_token_ids, expert_ids,
                                  num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap, ws, l);
     da.w2e = w2_e;
-    st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe_w4(da, block_m, s)
+    st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe_w4(da, block_m, l.sp.dn_small, s)
                                       : moe::launch_down_w4(da, block_m, s),
                    "moe_w4a8_experts: down launch");
     if (st != MOE_OK) return st;

@@ -1,6 +1,6 @@
 // Step 5 for large grids: the down-projection GEMM as a persistent kernel
-// whose three-stage LDS ring runs without a break across all of a
-// workgroup's work items.
+// whose LDS ring (three stages, four with 32-row tiles) runs without a break
+// across all of a workgroup's work items.
 //
 // Same arithmetic as down.hip (FlashInfer PR #4287, PR summary and the FP32
 // scale note of its final kernel performance section): for plan row p of
@@ -13,7 +13,8 @@
 //
 // Work items are (row tile, 256 output columns); the row tiles are the ones
 // the gate/up prep kernel listed in the workspace (up to 128 consecutive plan
-// rows of one expert).  Items all cost about the same, so the schedule is
+// rows of one expert, or up to 32 when the gate/up stage runs per plan block
+// and block_m <= 32).  Items all cost about the same, so the schedule is
 // static: the item list is cut into one contiguous range per XCD (workgroup
 // i runs on XCD i mod 8), and the XCD's workgroups take its items round
 // robin -- at any moment an XCD works on two or three row tiles, whose
@@ -24,8 +25,11 @@
 // 128 B), the item's intermediate rows (128 x 128 B, contiguous in plan
 // order) and a per-wave metadata slot (16 intermediate-row scales, the two
 // W2 block scales, 16 route ids), all brought by direct global->LDS loads two
-// steps ahead -- across item boundaries too, so an item's first steps are
-// already in flight while the previous item finishes.  Rows are XOR-swizzled
+// steps ahead (three with 32-row tiles) -- across item boundaries too, so an
+// item's first steps are already in flight while the previous item finishes.
+// The W2 tile loads carry the non-temporal cache policy: each W2 tile is read
+// by one item (measured at the decode shape, M=16: down stage 49.6 -> 43.8 us
+// with 128-row tiles, 40.7 us with 32-row tiles; page-1 M=4096 unchanged).  Rows are XOR-swizzled
 // in LDS (the intermediate rows as in the gate/up pipeline, the W2 rows by
 // w2_swizzle below).  FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32
 // scale product applied per step, or with power-of-two scales as E8M0
@@ -39,11 +43,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kRows = 128;
 constexpr int kNT = 512;
-constexpr int kStages = 3;
-constexpr int kHBytes = kRows * 128;
-constexpr int kHInstr = kHBytes / 1024 / 8;
 constexpr int kMeta = 64;                     // floats per wave and stage
 constexpr int kMetaRt = 18;                   // route ids start here
 
@@ -52,14 +52,26 @@ constexpr int kMetaRt = 18;                   // route ids start here
 // so that the 16 rows of an operand read phase hit distinct banks) plus the
 // rows' exponent dwords; lane group g of an operand takes chunk g of its row
 // and byte g of the row's dword as the E8M0 A scale of the mixed-format MFMA.
-template <bool W4>
+// RT: rows of a row tile, 128 or (for row tiles of at most 32 rows, cut
+// when the gate/up stage runs per plan block) 32.  The small tile leaves LDS
+// for more stages in flight: four of W2 (FP8) instead of three.  With RT = 32
+// a stage's 4 KB of intermediate rows is one DMA instruction per wave over
+// its first 32 lanes.
+template <bool W4, int RT>
 struct DPCfg {
+    static constexpr int Rows = RT;
     static constexpr int WBytes = 256 * (W4 ? 64 : 128);
     static constexpr int EBytes = W4 ? 256 * 4 : 0;
+    static constexpr int HBytes = RT * 128;
     static constexpr int WInstr = WBytes / 1024 / 8;
-    static constexpr int PerStage = WInstr + kHInstr + 1 + (W4 ? 1 : 0);
-    static constexpr size_t Smem = (size_t)kStages * (WBytes + kHBytes + EBytes) +
-                                   kStages * 8 * kMeta * 4;
+    static constexpr int HInstr = RT == 32 ? 1 : HBytes / 1024 / 8;
+    static constexpr int HRowsPerWave = HBytes / 8 / 128;     // 16 (RT 128) or 4 (RT 32)
+    static constexpr int NU = RT / 32;                        // 16-row subtiles per wave
+    static constexpr int PerStage = WInstr + HInstr + 1 + (W4 ? 1 : 0);
+    static constexpr size_t StageBytes = (size_t)WBytes + HBytes + EBytes + 8 * kMeta * 4;
+    static constexpr int Stages = RT == 32 ? 4 : 3;
+    static constexpr size_t Smem = (size_t)Stages * StageBytes;
+    static_assert(RT == 32 || RT == 128, "row tiles of 32 or 128 rows");
     static_assert(Smem <= 160 * 1024, "LDS budget");
 };
 
@@ -90,16 +102,18 @@ struct Item {
 // of either parity on 8 distinct chunks (no bank conflicts).
 __device__ __forceinline__ int w2_swizzle(int r) { return (r ^ (r >> 3) ^ (r >> 4)) & 7; }
 
-template <int BM, bool E8M0, bool W4>
+template <int BM, bool E8M0, bool W4, int RT>
 __global__ void __launch_bounds__(kNT, 1)
 down_pipe_kernel(DownArgs a) {
-    using C = DPCfg<W4>;
+    using C = DPCfg<W4, RT>;
+    constexpr int NS = C::Stages;
+    constexpr int HALF = RT / 2;                  // rows of a wm half
     static_assert(!(W4 && E8M0), "W4 takes FP32 intermediate scales");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *sW = smem;                                                 // [kStages][256][128 or 64]
-    uint8_t *sH = smem + kStages * C::WBytes;                           // [kStages][128][128]
-    uint8_t *sE = sH + kStages * kHBytes;                               // W4: [kStages][256] dwords
-    float *sMeta = reinterpret_cast<float *>(sE + kStages * C::EBytes); // [kStages][8][kMeta]
+    uint8_t *sW = smem;                                            // [NS][256][128 or 64]
+    uint8_t *sH = smem + NS * C::WBytes;                           // [NS][RT][128]
+    uint8_t *sE = sH + NS * C::HBytes;                             // W4: [NS][256] dwords
+    float *sMeta = reinterpret_cast<float *>(sE + NS * C::EBytes); // [NS][8][kMeta]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -142,7 +156,7 @@ down_pipe_kernel(DownArgs a) {
     // (fixed sizes: a local array whose size depends on the template
     // parameters keeps hipcc's host pass from emitting the kernel's stub)
     const uint8_t *wsrc[4];
-    const uint8_t *hsrc[kHInstr];
+    const uint8_t *hsrc[2];
     const uint8_t *msrc;
     const uint8_t *esrc = nullptr;                  // W4: exponent dword of row 32w + lane (lanes < 32)
     int mstep;
@@ -170,8 +184,8 @@ down_pipe_kernel(DownArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < kHInstr; ++i) {
-            const int row = (w * kHInstr + i) * 8 + sub;
+        for (int i = 0; i < C::HInstr; ++i) {
+            const int row = w * C::HRowsPerWave + i * 8 + sub;      // RT 32: lanes < 32 only
             const int64_t p = p0 + (row < nrows ? row : 0);
             hsrc[i] = a.hq + p * I + (slot ^ (row & 7)) * 16;
         }
@@ -198,12 +212,17 @@ down_pipe_kernel(DownArgs a) {
     auto issue = [&](int stage) {
         uint8_t *dw = sW + stage * C::WBytes + (w * C::WInstr) * 1024;
 #pragma unroll
-        for (int i = 0; i < C::WInstr; ++i) lds_dma16(wsrc[i] + (int64_t)jl * (W4 ? 64 : 128), dw + i * 1024);
+        for (int i = 0; i < C::WInstr; ++i)
+            lds_dma16_nt(wsrc[i] + (int64_t)jl * (W4 ? 64 : 128), dw + i * 1024);
         if constexpr (W4)
             if (lane < 32) lds_dma4(esrc + jl * 4, sE + stage * C::EBytes + w * 128);
-        uint8_t *dh = sH + stage * kHBytes + (w * kHInstr) * 1024;
+        uint8_t *dh = sH + stage * C::HBytes + w * C::HRowsPerWave * 128;
+        if constexpr (RT == 32) {
+            if (lane < 32) lds_dma16(hsrc[0] + (int64_t)jl * 128, dh);
+        } else {
 #pragma unroll
-        for (int i = 0; i < kHInstr; ++i) lds_dma16(hsrc[i] + (int64_t)jl * 128, dh + i * 1024);
+            for (int i = 0; i < C::HInstr; ++i) lds_dma16(hsrc[i] + (int64_t)jl * 128, dh + i * 1024);
+        }
         if (lane < kMetaRt + 16) lds_dma4(msrc + jl * mstep, sMeta + (stage * 8 + w) * kMeta);
         if (++jl == njb && kl + 1 < mine) {
             jl = 0;
@@ -216,7 +235,7 @@ down_pipe_kernel(DownArgs a) {
     int64_t kc = 0;
     int jc = 0;
     Item ic = il;
-    constexpr int NU = 4;
+    constexpr int NU = C::NU;
     v4f acc[4][NU];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -233,32 +252,38 @@ down_pipe_kernel(DownArgs a) {
     // so the compiler can tell the refilled and the read LDS ranges apart.
     auto step = [&](auto st_c, int64_t t) {
         constexpr int ST = decltype(st_c)::value;
-        if (t + 1 < T)
+        // stages t + 1 .. t + NS - 2 (those issued) may still be in flight
+        const int64_t ahead = T - 1 - t;
+        if (ahead >= NS - 2)
+            wait_vmcnt<(NS - 2) * C::PerStage>();
+        else if (ahead == 2)
+            wait_vmcnt<2 * C::PerStage>();
+        else if (ahead == 1)
             wait_vmcnt<C::PerStage>();
         else
             wait_vmcnt<0>();
         stage_barrier();
-        if (t + 2 < T) issue((ST + 2) % kStages);
+        if (t + NS - 1 < T) issue((ST + NS - 1) % NS);
 
         const int nrows = ic.nb * BM;
         const int64_t c0 = (int64_t)ic.ct * 256;
         const int ncols = K - c0 < 256 ? (int)(K - c0) : 256;
-        const bool wave_on = ic.ok && (wm * 64 < nrows) && (64 * wn < ncols);
+        const bool wave_on = ic.ok && (wm * HALF < nrows) && (64 * wn < ncols);
         const float *meta = sMeta + ST * 8 * kMeta;
         // rows of this wave up to its last valid one (route ids come with
         // every stage): 16-row subtiles past it hold only plan padding and
         // are not multiplied
         int vrows = 0;
         if (wave_on) {
-            const int row = wm * 64 + lane;
+            const int row = wm * HALF + lane;
             const int r = __float_as_int(meta[(row >> 4) * kMeta + kMetaRt + (row & 15)]);
-            const uint64_t v = __ballot(row < nrows && r >= 0 && (int64_t)r < a.R);
-            vrows = v ? wm * 64 + 64 - __builtin_clzll(v) : 0;
+            const uint64_t v = __ballot(lane < HALF && row < nrows && r >= 0 && (int64_t)r < a.R);
+            vrows = v ? wm * HALF + 64 - __builtin_clzll(v) : 0;
             vrows = __builtin_amdgcn_readfirstlane(vrows);
         }
         if (W4 && vrows > 0) {
             const uint8_t *Ws = sW + ST * C::WBytes;
-            const uint8_t *Hs = sH + ST * kHBytes;
+            const uint8_t *Hs = sH + ST * C::HBytes;
             const uint8_t *Es = sE + ST * C::EBytes;
             v8i wq[4];
             int ea[4];
@@ -271,8 +296,8 @@ down_pipe_kernel(DownArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                if (wm * 64 + u * 16 >= vrows) continue;
-                const int row = wm * 64 + u * 16 + l16;
+                if (wm * HALF + u * 16 >= vrows) continue;
+                const int row = wm * HALF + u * 16 + l16;
                 const uint8_t *rp = Hs + row * 128;
                 const u32x4 lo4 = lds_read16(rp + ((g ^ (row & 7)) * 16));
                 const u32x4 hi4 = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
@@ -286,7 +311,7 @@ down_pipe_kernel(DownArgs a) {
             // this wave's 64 columns lie in one 128-column scale block
             const float sb = meta[w * kMeta + 16 + (wn >= 2 ? 1 : 0)];
             const uint8_t *Ws = sW + ST * C::WBytes;
-            const uint8_t *Hs = sH + ST * kHBytes;
+            const uint8_t *Hs = sH + ST * C::HBytes;
             v8i wq[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -298,8 +323,8 @@ down_pipe_kernel(DownArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                if (wm * 64 + u * 16 >= vrows) continue;
-                const int row = wm * 64 + u * 16 + l16;
+                if (wm * HALF + u * 16 >= vrows) continue;
+                const int row = wm * HALF + u * 16 + l16;
                 const uint8_t *rp = Hs + row * 128;
                 const u32x4 lo4 = lds_read16(rp + ((g ^ (row & 7)) * 16));
                 const u32x4 hi4 = lds_read16(rp + (((4 + g) ^ (row & 7)) * 16));
@@ -329,7 +354,7 @@ down_pipe_kernel(DownArgs a) {
         if (wave_on) {
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                const int row = wm * 64 + u * 16 + l16;
+                const int row = wm * HALF + u * 16 + l16;
                 float m = 0.f;
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
@@ -362,50 +387,68 @@ down_pipe_kernel(DownArgs a) {
         }
     };
 
-    issue(0);
-    if (T > 1) issue(1);
-    for (int64_t t = 0; t < T; t += kStages) {
+    for (int q = 0; q < NS - 1; ++q)
+        if (q < T) issue(q);
+    for (int64_t t = 0; t < T; t += NS) {
         step(std::integral_constant<int, 0>{}, t);
         if (t + 1 < T) step(std::integral_constant<int, 1>{}, t + 1);
         if (t + 2 < T) step(std::integral_constant<int, 2>{}, t + 2);
+        if constexpr (NS > 3)
+            if (t + 3 < T) step(std::integral_constant<int, 3>{}, t + 3);
     }
     wait_vmcnt<0>();                                 // no load may land after the workgroup ends
 }
 
-template <int BM, bool E8M0, bool W4 = false>
+template <int BM, bool E8M0, bool W4, int RT>
 hipError_t launch_dn_pipe(const DownArgs &a, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
     int64_t grid = device_cu_count();
     const int64_t max_items = (int64_t)a.nblocks * a.ctiles;
     if (grid > max_items) grid = max_items;
     static std::atomic<uint64_t> lds_set{0};
-    constexpr size_t smem = DPCfg<W4>::Smem;
-    hipError_t e = raise_lds_limit(lds_set, (const void *)down_pipe_kernel<BM, E8M0, W4>, (int)smem);
+    constexpr size_t smem = DPCfg<W4, RT>::Smem;
+    hipError_t e = raise_lds_limit(lds_set, (const void *)down_pipe_kernel<BM, E8M0, W4, RT>, (int)smem);
     if (e != hipSuccess) return e;
-    down_pipe_kernel<BM, E8M0, W4><<<(unsigned)grid, kNT, smem, st>>>(a);
+    down_pipe_kernel<BM, E8M0, W4, RT><<<(unsigned)grid, kNT, smem, st>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, hipStream_t st) {
+hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, bool small, hipStream_t st) {
+    if (small) {
+        switch (block_m) {
+            case 8: return launch_dn_pipe<8, false, true, 32>(a, st);
+            case 16: return launch_dn_pipe<16, false, true, 32>(a, st);
+            case 32: return launch_dn_pipe<32, false, true, 32>(a, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (block_m) {
-        case 8: return launch_dn_pipe<8, false, true>(a, st);
-        case 16: return launch_dn_pipe<16, false, true>(a, st);
-        case 32: return launch_dn_pipe<32, false, true>(a, st);
-        case 64: return launch_dn_pipe<64, false, true>(a, st);
-        case 128: return launch_dn_pipe<128, false, true>(a, st);
+        case 8: return launch_dn_pipe<8, false, true, 128>(a, st);
+        case 16: return launch_dn_pipe<16, false, true, 128>(a, st);
+        case 32: return launch_dn_pipe<32, false, true, 128>(a, st);
+        case 64: return launch_dn_pipe<64, false, true, 128>(a, st);
+        case 128: return launch_dn_pipe<128, false, true, 128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st) {
+hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, bool small, hipStream_t st) {
+    if (small) {
+        switch (block_m) {
+            case 8: return e8m0 ? launch_dn_pipe<8, true, false, 32>(a, st) : launch_dn_pipe<8, false, false, 32>(a, st);
+            case 16: return e8m0 ? launch_dn_pipe<16, true, false, 32>(a, st) : launch_dn_pipe<16, false, false, 32>(a, st);
+            case 32: return e8m0 ? launch_dn_pipe<32, true, false, 32>(a, st) : launch_dn_pipe<32, false, false, 32>(a, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (block_m) {
-        case 8: return e8m0 ? launch_dn_pipe<8, true>(a, st) : launch_dn_pipe<8, false>(a, st);
-        case 16: return e8m0 ? launch_dn_pipe<16, true>(a, st) : launch_dn_pipe<16, false>(a, st);
-        case 32: return e8m0 ? launch_dn_pipe<32, true>(a, st) : launch_dn_pipe<32, false>(a, st);
-        case 64: return e8m0 ? launch_dn_pipe<64, true>(a, st) : launch_dn_pipe<64, false>(a, st);
-        case 128: return e8m0 ? launch_dn_pipe<128, true>(a, st) : launch_dn_pipe<128, false>(a, st);
+        case 8: return e8m0 ? launch_dn_pipe<8, true, false, 128>(a, st) : launch_dn_pipe<8, false, false, 128>(a, st);
+        case 16: return e8m0 ? launch_dn_pipe<16, true, false, 128>(a, st) : launch_dn_pipe<16, false, false, 128>(a, st);
+        case 32: return e8m0 ? launch_dn_pipe<32, true, false, 128>(a, st) : launch_dn_pipe<32, false, false, 128>(a, st);
+        case 64: return e8m0 ? launch_dn_pipe<64, true, false, 128>(a, st) : launch_dn_pipe<64, false, false, 128>(a, st);
+        case 128: return e8m0 ? launch_dn_pipe<128, true, false, 128>(a, st) : launch_dn_pipe<128, false, false, 128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

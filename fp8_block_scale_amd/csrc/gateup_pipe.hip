@@ -658,11 +658,12 @@ hipError_t launch_pipe_mode(const GateUpArgs &a, int mode, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st) {
+hipError_t launch_tiles(const GateUpArgs &a, int block_m, int tile_rows, hipStream_t st) {
     if (a.nblocks == 0) return hipSuccess;
     if (block_m != 8 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
         return hipErrorInvalidValue;
-    tiles_kernel<<<1 + prep_groups(a.R + a.n_cnt), 1024, 0, st>>>(a.eids, a.ntp, block_m, kRows / block_m,
+    if ((tile_rows != 32 && tile_rows != kRows) || block_m > tile_rows) return hipErrorInvalidValue;
+    tiles_kernel<<<1 + prep_groups(a.R + a.n_cnt), 1024, 0, st>>>(a.eids, a.ntp, block_m, tile_rows / block_m,
                                                                    a.nblocks, a.tiles, a.tmeta,
                                                                    (uint32_t *)a.rpos, a.R, a.cnt, a.n_cnt);
     return hipGetLastError();

@@ -171,8 +171,9 @@ hipError_t launch_gateup(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8
 // The row-tile list of the persistent kernels alone (when only the down
 // stage runs persistent); launch_gateup_pipe builds it itself.  Either way
 // the same launch sets rpos[0, R) = -1 and zeroes cnt[0, n_cnt) (the work of
-// launch_prep, which the stage then skips).
-hipError_t launch_tiles(const GateUpArgs &a, int block_m, hipStream_t st);
+// launch_prep, which the stage then skips).  tile_rows: 128, or 32 for the
+// down kernel's small-tile form (block_m <= 32).
+hipError_t launch_tiles(const GateUpArgs &a, int block_m, int tile_rows, hipStream_t st);
 // Large-grid gate/up (no split-K): 128-row tiles, three-stage LDS pipeline.
 hipError_t launch_gateup_pipe(const GateUpArgs &a, int block_m, bool fp8_mma, bool e8m0,
                               hipStream_t st);
@@ -188,9 +189,11 @@ int down_w4_max_njb(int block_m);
 hipError_t launch_down_w4(const DownArgs &a, int block_m, hipStream_t st);
 // The W4A8 down stage on the persistent kernel (over the gate/up stage's row
 // tiles: the gate/up stage must have listed them).
-hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, hipStream_t st);
-// Large-grid down GEMM: persistent, over the gate/up stage's row tiles.
-hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, hipStream_t st);
+hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, bool small, hipStream_t st);
+// Large-grid down GEMM: persistent, over the gate/up stage's row tiles --
+// of 128 rows, or (small: block_m <= 32, tiles listed by launch_tiles with
+// tile_rows 32) of 32 rows with a deeper W2 ring.
+hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, bool small, hipStream_t st);
 // The single-launch path (fused.hip): steps 3-5 over the arguments of both
 // stages.  Needs I / 128 <= fused_max_njb(block_m).
 int fused_max_njb(int block_m);

@@ -499,6 +499,21 @@ def test_zipf_full_size_sampled(flags):
 # last 8 rows are masked (they belong to the next block and are never read),
 # the persistent kernels cut 16 blocks per 128-row tile.
 
+# The persistent down stage behind the per-block gate/up works on row tiles of
+# at most 32 rows (a deeper W2 ring); experts with many blocks span several
+# such tiles (skew's hot experts, page-1 at M=256), masked routes and the
+# zero-scale expert included; power-of-two scales through the E8M0 MFMA.
+@pytest.mark.parametrize("name,M,bm,flags", [
+    ("page1", 256, 16, 0), ("page1", 256, 32, 0), ("skew", 512, 32, 0),
+    ("zipf", 256, 32, E8), ("decode", 16, 8, 0)])
+def test_small_tile_down(name, M, bm, flags):
+    cs = case_of(name, M=M, block_m=bm)
+    fl = (flags | (moe.MOE_PATH_STREAM << moe.MOE_F_GATEUP_PATH_SHIFT)
+          | (moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT) | FUSE_OFF)
+    act = SCALE_UE8M0 if flags & moe.MOE_F_INTER_UE8M0 else SCALE_FP32
+    tokens = None if cs.M <= 16 else _cover_tokens(cs, 6, 60 + bm)
+    full_parity(cs, flags=fl, act_mode=act, tokens=tokens, label=f"small-tile down bm={bm}")
+
 @pytest.mark.parametrize("name,M,flags", [
     ("tiny", None, 0), ("decode", None, 0), ("decode", 4, 0), ("decode", 16, 0),
     ("decode", 16, 7 << moe.MOE_F_SPLITK_SHIFT), ("decode", 16, FUSE_ON),

@@ -156,6 +156,13 @@ def test_experts_schedule():
     assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, False, 10, 6, False)
     assert sched(4, 7168, 256, 257, 9, 16, 576)[2:4] == (3, 19)
     assert sched(16, 7168, 256, 257, 9, 16, 2304)[2] == 1
+    # the down stage goes persistent once its expected (block, 256-column)
+    # items reach twice the CU count: decode M=1 has ~9 x 28 = 252, M=4
+    # ~34 x 28, M=16 ~112 x 28
+    assert sched(4, 7168, 256, 257, 9, 16, 576)[:2] == (False, True)
+    assert sched(16, 7168, 256, 257, 9, 16, 2304)[:2] == (False, True)
+    # the tiny workload (~5 blocks x 1 item): per-block down
+    assert sched(4, 256, 256, 8, 2, 16, 128)[:2] == (False, False)
     # page-1 M=16 and M=1024: per-block gate/up, persistent down
     assert sched(16, 4096, 1024, 288, 8, 64, 8192)[:2] == (False, True)
     assert sched(1024, 4096, 1024, 288, 8, 64, 26368)[:2] == (False, True)
