@@ -63,7 +63,7 @@ def parse():
                     help="force the small-grid gate/up split-K factor (1..255; 0 = automatic)")
     ap.add_argument("--gateup-path", choices=("auto", "stream", "persistent"), default="auto",
                     help="force the gate/up kernel family (tuning override)")
-    ap.add_argument("--down-path", choices=("auto", "stream", "persistent"), default="auto",
+    ap.add_argument("--down-path", choices=("auto", "stream", "persistent", "columns"), default="auto",
                     help="force the down kernel family (tuning override)")
     ap.add_argument("--fuse", choices=("auto", "on", "off"), default="auto",
                     help="steps 3-5 as one launch (on), as two stages (off), or the library's "
@@ -250,7 +250,7 @@ def main():
     if args.splitk:
         flags |= (args.splitk & 0xFF) << moe.MOE_F_SPLITK_SHIFT
     paths = {"auto": moe.MOE_PATH_AUTO, "stream": moe.MOE_PATH_STREAM,
-             "persistent": moe.MOE_PATH_PERSISTENT}
+             "persistent": moe.MOE_PATH_PERSISTENT, "columns": moe.MOE_PATH_COLUMNS}
     flags |= paths[args.gateup_path] << moe.MOE_F_GATEUP_PATH_SHIFT
     flags |= paths[args.down_path] << moe.MOE_F_DOWN_PATH_SHIFT
     fuses = {"auto": moe.MOE_FUSE_AUTO, "on": moe.MOE_FUSE_ON, "off": moe.MOE_FUSE_OFF}

@@ -28,7 +28,7 @@ MOE_F_FP8_GATEUP = 4
 MOE_F_SPLITK_SHIFT = 8
 MOE_F_GATEUP_PATH_SHIFT = 16
 MOE_F_DOWN_PATH_SHIFT = 18
-MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_PERSISTENT = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_STREAM, MOE_PATH_PERSISTENT, MOE_PATH_COLUMNS = 0, 1, 2, 3
 MOE_F_FUSE_SHIFT = 20
 MOE_F_W13_PACKED = 0x400000
 MOE_FUSE_AUTO, MOE_FUSE_OFF, MOE_FUSE_ON = 0, 1, 2
@@ -255,12 +255,12 @@ def moe_fp8_experts_workspace_layout(M, K, I, E, top_k, block_m, sorted_cap, fla
 
 
 def moe_fp8_experts_schedule(M, K, I, E, top_k, block_m, sorted_cap, flags=0):
-    """(gate/up persistent, down persistent, split-K factor, K-blocks per split,
-    steps 3-5 as one launch)."""
+    """(gate/up persistent, down kernel (0 per block, 1 persistent, 2 split over
+    output columns), split-K factor, K-blocks per split, steps 3-5 as one launch)."""
     info = (ctypes.c_int32 * 5)()
     _check(_c["moe_fp8_experts_schedule"](M, K, I, E, top_k, block_m, sorted_cap, flags, info),
            "moe_fp8_experts_schedule")
-    return bool(info[0]), bool(info[1]), int(info[2]), int(info[3]), bool(info[4])
+    return bool(info[0]), int(info[1]), int(info[2]), int(info[3]), bool(info[4])
 
 
 def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,

@@ -57,6 +57,7 @@ struct SplitChoice {
     bool gu_persistent;
     bool dn_persistent;
     bool dn_small;       // the persistent down on row tiles of 32 rows (deeper W2 ring)
+    bool dn_cols;        // the down stage split over output columns, route sum included
     bool fused;          // steps 3-5 in one launch (moe_fp8_experts only)
 };
 
@@ -103,6 +104,14 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     // then hold a block or two each, and the 32-row tile leaves LDS for four
     // W2 stages in flight instead of three.
     c.dn_small = c.dn_persistent && !c.gu_persistent && bm <= 32;
+    // The column-split down with its own route sum (no per-route buffer, no
+    // route-sum launch) where it applies; chosen by itself up to 24 routes
+    // (measured at the decode shape: faster than the per-block down at M=1
+    // and M=2, slower than the persistent one from M=4 on, where each of its
+    // one-wave workgroups walks too many blocks).
+    c.dn_cols = !w4 && fuse != MOE_FUSE_ON && moe::down_cols_fits(R, I, bm) &&
+                (dn_path == MOE_PATH_COLUMNS || (dn_path == MOE_PATH_AUTO && R <= 24));
+    if (c.dn_cols) c.dn_persistent = c.dn_small = false;
     if (c.gu_persistent) {
         c.nsplit = 1;
         c.kb_per_split = (int)nkb;
@@ -438,15 +447,18 @@ MOE_API moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_
 
 namespace {
 
-moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m) {
+moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m, int64_t R) {
     const uint32_t known = MOE_F_INTER_UE8M0 | MOE_F_MMA_E8M0 | MOE_F_FP8_GATEUP | MOE_F_SPLITK_MASK |
                            MOE_F_GATEUP_PATH_MASK | MOE_F_DOWN_PATH_MASK | MOE_F_FUSE_MASK |
                            MOE_F_W13_PACKED;
     if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
     const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
-    if (gp > MOE_PATH_PERSISTENT || dp > MOE_PATH_PERSISTENT)
-        return fail(MOE_ERR_SHAPE, "kernel path override must be 0, 1 or 2");
+    if (gp > MOE_PATH_PERSISTENT || dp > MOE_PATH_COLUMNS)
+        return fail(MOE_ERR_SHAPE, "kernel path override must be 0, 1 or 2 (3: down stage only)");
+    if (dp == MOE_PATH_COLUMNS && R > 0 && !moe::down_cols_fits(R, I, block_m))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "the column-split down needs I = 256, block_m 8 or 16 and M * top_k <= 192");
     if ((gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT) && (K > 32768 || I > 32768))
         return fail(MOE_ERR_UNSUPPORTED, "the persistent kernels need K, I <= 32768");
     if (gp == MOE_PATH_PERSISTENT && (flags & MOE_F_SPLITK_MASK))
@@ -455,8 +467,9 @@ moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m) {
         return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
     const uint32_t fu = (flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT;
     if (fu > MOE_FUSE_ON) return fail(MOE_ERR_SHAPE, "fuse choice must be 0, 1 or 2");
-    if (fu == MOE_FUSE_ON && (gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT))
-        return fail(MOE_ERR_SHAPE, "MOE_FUSE_ON runs the per-block kernel family: no persistent path");
+    if (fu == MOE_FUSE_ON && (gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT ||
+                              dp == MOE_PATH_COLUMNS))
+        return fail(MOE_ERR_SHAPE, "MOE_FUSE_ON runs the per-block kernel family: no other path");
     if (fu == MOE_FUSE_ON && I / 128 > moe::fused_max_njb(block_m))
         return fail(MOE_ERR_UNSUPPORTED, "MOE_FUSE_ON needs I / 128 <= %d at block_m %d",
                     moe::fused_max_njb(block_m), block_m);
@@ -471,11 +484,11 @@ MOE_API moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
     if (!info) return fail(MOE_ERR_NULL, "output pointer is NULL");
-    st = check_flags(flags, K, I, block_m);
+    st = check_flags(flags, K, I, block_m, M * top_k);
     if (st != MOE_OK) return st;
     const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
     info[0] = l.sp.gu_persistent ? 1 : 0;
-    info[1] = l.sp.dn_persistent ? 1 : 0;
+    info[1] = l.sp.dn_cols ? 2 : (l.sp.dn_persistent ? 1 : 0);
     info[2] = l.sp.nsplit;
     info[3] = l.sp.kb_per_split;
     info[4] = l.sp.fused ? 1 : 0;
@@ -490,7 +503,7 @@ moe_status check_stage(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k
                        size_t workspace_bytes, WsLayout *l) {
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
-    st = check_flags(flags, K, I, block_m);
+    st = check_flags(flags, K, I, block_m, M * top_k);
     if (st != MOE_OK) return st;
     *l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
     if (M == 0 || sorted_cap == 0) return MOE_OK;
@@ -635,6 +648,10 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                        num_tokens_post_padded, M, K, I, E, top_k, block_m,
                                        sorted_cap, ws, l);
     const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
+    if (l.sp.dn_cols)                          // the route sum is part of this launch
+        return hip_check(moe::launch_down_cols(da, block_m, e8, (const int32_t *)(ws + l.rpos),
+                                               (uint16_t *)out_bf16, s),
+                         "moe_fp8_down_reduce: down launch");
     st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe(da, block_m, e8, l.sp.dn_small, s)
                                                    : moe::launch_down(da, block_m, e8, s),
                    "moe_fp8_down_reduce: down launch");
@@ -742,7 +759,9 @@ moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, i
                     "W4A8: MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP and MOE_F_W13_PACKED do not apply");
     if (((flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT) == MOE_FUSE_ON)
         return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs as two stages (no MOE_FUSE_ON)");
-    st = check_flags(w4_flags(flags), K, I, block_m);
+    if (((flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT) == MOE_PATH_COLUMNS)
+        return fail(MOE_ERR_UNSUPPORTED, "W4A8: the column-split down stage takes FP8 weights only");
+    st = check_flags(w4_flags(flags), K, I, block_m, M * top_k);
     if (st != MOE_OK) return st;
     // the per-block down kernel keeps a block's intermediate rows in LDS
     const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags), true);
@@ -865,7 +884,7 @@ MOE_API moe_status moe_fp8_experts_noalloc(const uint8_t *x_q, const float *x_s,
                                            void *out_bf16, void *stream) {
     moe_status st = check_experts_shape(M, K, I, E, top_k, block_m, sorted_cap);
     if (st != MOE_OK) return st;
-    st = check_flags(flags, K, I, block_m);
+    st = check_flags(flags, K, I, block_m, M * top_k);
     if (st != MOE_OK) return st;
     const size_t need = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags).total;
     if (need > MOE_NOALLOC_SCRATCH_BYTES)

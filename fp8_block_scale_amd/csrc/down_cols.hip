@@ -1,0 +1,244 @@
+// Step 5 for small route counts: the down-projection GEMM split over output
+// columns, with the route sum in the same launch.
+//
+// Same arithmetic as down.hip (FlashInfer PR #4287, PR summary and the FP32
+// scale note of its final kernel performance section): for plan row p of
+// expert e holding route r = t * top_k + j,
+//   y[r, c] = sum_jb h_s[p, jb] * w2_s[e, c / 128, jb]
+//                  * sum_{i in jb} h_q[p, i] * W2[e, c, i]              (FP32)
+//   out[t, c] = bf16(out[t, c] + sum_j topk_weights[r] * y[r, c])
+// with the route terms added in route order in FP32 and one BF16 rounding.
+//
+// Work split.  One workgroup (one wave) owns 16 output columns.  It first
+// copies every valid route's intermediate row and row scales into LDS
+// (indexed by route, found through the route map of the gate/up stage), then
+// walks every plan block below num_tokens_post_padded: per block it
+// multiplies the block's W2 slab (its expert's 16 rows of W2 for these
+// columns, all of I) with the block's routes' rows, keeping each valid
+// route's 16 results in LDS.  Having every route of its columns, it adds each
+// token's routes itself at the end: no per-route buffer in HBM and no
+// route-sum launch.  Each W2 slab is read by exactly one workgroup.
+//
+// Pipeline.  A ring of kStages per wave, each stage one block's W2 slab
+// (16-byte chunks XOR-swizzled by row, so the MFMA operand reads hit distinct
+// banks), its route ids, expert id and W2 block scales, by direct
+// global->LDS loads kStages - 1 blocks ahead, so a block's multiply waits on
+// nothing but its stage.  One wave per workgroup: no barriers, the waits are the wave's own
+// load counts.  FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale
+// product applied per 128-deep K-block, or with power-of-two scales as E8M0
+// exponents inside the MFMA.
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCW = 16;                 // output columns per workgroup
+constexpr int kIB = 256;                // bytes of an intermediate / W2 row (I)
+constexpr int kNJB = kIB / 128;
+constexpr int kStages = 8;
+constexpr int kSlabBytes = kCW * kIB;                  // one block's W2 slab
+constexpr int kSlabInstr = kSlabBytes / 1024;          // 16-byte DMA per lane
+constexpr int kStageBytes = kSlabBytes + 128;          // + [16] route ids, expert id, W2 scales
+constexpr int kPerStage = kSlabInstr + 3;
+constexpr int64_t kMaxRoutes = 192;                    // routes whose rows fit in LDS
+static_assert((kStages - 2) * kPerStage < 64, "vmcnt range");
+
+typedef const __attribute__((address_space(4))) int32_t *const_i32_p;
+typedef const __attribute__((address_space(4))) float *const_f32_p;
+
+// LDS carve-up after the ring: intermediate rows by route [R][kIB], their
+// scales [R][kNJB], the results [R + 1][kCW] (FP32; row R takes the rows
+// that hold no route), route valid flags [R].
+struct DCLayout {
+    int h, hs, y, valid, total;
+    __host__ __device__ explicit DCLayout(int R) {
+        h = kStages * kStageBytes;
+        hs = h + R * kIB;
+        y = hs + ((R * kNJB * 4 + 15) & ~15);            // 16-byte rows of results
+        valid = y + (R + 1) * kCW * 4;
+        total = valid + ((R + 15) & ~15);
+    }
+};
+
+template <int BM, bool E8M0>
+__global__ void __launch_bounds__(64, 1)
+down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restrict__ out) {
+    static_assert(BM <= 16, "one 16-row MFMA tile per plan block");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int R = (int)a.R;
+    const DCLayout L(R);
+    uint8_t *sH = smem + L.h;
+    float *sHs = reinterpret_cast<float *>(smem + L.hs);
+    float *sY = reinterpret_cast<float *>(smem + L.y);
+    uint8_t *sValid = smem + L.valid;
+
+    const int lane = threadIdx.x;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int64_t K = a.K;
+    const int64_t c0 = (int64_t)blockIdx.x * kCW;
+
+    const int ntp = __builtin_amdgcn_readfirstlane(((const_i32_p)a.ntp)[0]);
+    int nb = ntp / BM;
+    nb = nb < a.nblocks ? nb : a.nblocks;
+
+    // ---- every valid route's intermediate row and row scales into LDS, by
+    // route (the route map of the gate/up stage gives each route's plan row,
+    // -1 if masked): first the map itself, then direct global->LDS copies,
+    // four routes (1 KB) per instruction, chunk c of route r's row at LDS
+    // chunk c ^ (r & 15); masked routes copy plan row 0 and stay flagged off
+    int *sRp = reinterpret_cast<int *>(smem);           // (in the ring's slot 0, before any refill)
+    for (int r = lane; r < R; r += 64) {
+        const int p = rpos[r];
+        sRp[r] = p >= 0 ? p : 0;
+        sValid[r] = p >= 0 ? 1 : 0;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): the map is in LDS
+    for (int r0 = 0; r0 < R; r0 += 4) {
+        const int r = r0 + (lane >> 4);
+        if (r < R) {
+            const int p = sRp[r];
+            lds_dma16(a.hq + (int64_t)p * kIB + ((l16 ^ (r & 15)) * 16), sH + (int64_t)r0 * kIB);
+        }
+    }
+    for (int q0 = 0; q0 < R * kNJB; q0 += 64) {
+        const int q = q0 + lane;                         // route q / kNJB, K-block q % kNJB
+        if (q < R * kNJB) lds_dma4(a.hs + (int64_t)sRp[q / kNJB] * kNJB + q % kNJB, sHs + q0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);                 // the map's reads are done before slot 0 refills
+
+    // ---- ring of W2 slabs: block b in slot b % kStages
+    auto issue = [&](int st, int b) {
+        uint8_t *base = smem + st * kStageBytes;
+        const int e0 = __builtin_amdgcn_readfirstlane(((const_i32_p)a.eids)[b]);
+        const int e = (e0 >= 0 && e0 < a.E) ? e0 : 0;
+        // W2 rows c0 .. c0 + 15 of expert e: LDS slot s (16 bytes) of the slab
+        // holds row s / 16, chunk (s % 16) ^ row
+        const uint8_t *wrow = a.w2 + ((int64_t)e * K + c0) * kIB;
+#pragma unroll
+        for (int i = 0; i < kSlabInstr; ++i) {
+            const int s = i * 64 + lane;
+            const int row = s >> 4, pos = s & 15;
+            lds_dma16_nt(wrow + (int64_t)row * kIB + (pos ^ row) * 16, base + i * 1024);
+        }
+        const int64_t p = (int64_t)b * BM + (lane < BM ? lane : 0);
+        uint8_t *meta = base + kSlabBytes;
+        if (lane < 16) lds_dma4(a.sorted + p, meta);
+        if (lane == 0) lds_dma4(a.eids + b, meta + 64);
+        if (lane < kNJB)
+            lds_dma4(a.w2s + ((int64_t)e * (K >> 7) + (c0 >> 7)) * kNJB + lane, meta + 68);
+    };
+
+    auto compute = [&](int st) {
+        const uint8_t *base = smem + st * kStageBytes;
+        const int *meta = reinterpret_cast<const int *>(base + kSlabBytes);
+        const int r = meta[l16], e0 = meta[16];
+        const bool ok = l16 < BM && r >= 0 && r < R && e0 >= 0 && e0 < a.E;
+        const int rr = ok ? r : 0;
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        const uint8_t *wa = base + l16 * kIB;
+        const uint8_t *ha = sH + (int64_t)rr * kIB;
+#pragma unroll
+        for (int jb = 0; jb < kNJB; ++jb) {
+            const int clo = jb * 8 + g, chi = jb * 8 + 4 + g;
+            const u32x4 a0 = lds_read16(wa + (clo ^ l16) * 16), a1 = lds_read16(wa + (chi ^ l16) * 16);
+            const u32x4 b0 = lds_read16(ha + (clo ^ (rr & 15)) * 16);
+            const u32x4 b1 = lds_read16(ha + (chi ^ (rr & 15)) * 16);
+            const v8i A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            const float sb = __int_as_float(meta[17 + jb]);
+            const float sa = sHs[rr * kNJB + jb];
+            if constexpr (E8M0)
+                acc = mfma16x16x128_e8m0(A, B, acc, e8m0_of(sb), e8m0_of(sa));
+            else
+                acc = mfma16x16x128(A, B) * (sa * sb) + acc;
+        }
+        // lane (row l16, group g) holds columns 4g .. 4g + 3 of its route.
+        // Every lane stores (rows without a route to the spare row R): a
+        // store under a lane condition would let the compiler move the MFMAs
+        // under it, where lanes outside the condition keep stale scale
+        // operands.
+        *reinterpret_cast<v4f *>(sY + (ok ? r : R) * kCW + 4 * g) = acc;
+    };
+
+    // blocks b, slots b % kStages; kStages - 1 blocks in flight ahead of the
+    // one being multiplied (loads complete in issue order; the row copy above
+    // was issued first, so the first wait covers it too)
+    for (int q = 0; q < kStages - 1; ++q)
+        if (q < nb) issue(q, q);
+    auto step = [&](auto st_c, int b) {
+        constexpr int ST = decltype(st_c)::value;
+        const int ahead = nb - 1 - b;                   // blocks issued past b, at most kStages - 2
+        switch (ahead < kStages - 2 ? ahead : kStages - 2) {
+            case 6: wait_vmcnt<6 * kPerStage>(); break;
+            case 5: wait_vmcnt<5 * kPerStage>(); break;
+            case 4: wait_vmcnt<4 * kPerStage>(); break;
+            case 3: wait_vmcnt<3 * kPerStage>(); break;
+            case 2: wait_vmcnt<2 * kPerStage>(); break;
+            case 1: wait_vmcnt<kPerStage>(); break;
+            default: wait_vmcnt<0>(); break;
+        }
+        // the refill goes into the slot of block b - 1, whose operand reads
+        // the previous step has consumed
+        if (b + kStages - 1 < nb) issue((ST + kStages - 1) % kStages, b + kStages - 1);
+        compute(ST);
+    };
+    static_assert(kStages == 8, "the step switch covers up to six stages ahead");
+    for (int b = 0; b < nb; b += kStages) {
+        step(std::integral_constant<int, 0>{}, b);
+        if (b + 1 < nb) step(std::integral_constant<int, 1>{}, b + 1);
+        if (b + 2 < nb) step(std::integral_constant<int, 2>{}, b + 2);
+        if (b + 3 < nb) step(std::integral_constant<int, 3>{}, b + 3);
+        if (b + 4 < nb) step(std::integral_constant<int, 4>{}, b + 4);
+        if (b + 5 < nb) step(std::integral_constant<int, 5>{}, b + 5);
+        if (b + 6 < nb) step(std::integral_constant<int, 6>{}, b + 6);
+        if (b + 7 < nb) step(std::integral_constant<int, 7>{}, b + 7);
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): results in LDS
+
+    // ---- route sum: lanes 16q .. 16q + 15 take token t0 + q, one column
+    // each; routes in order, FP32, then the previous output, one rounding
+    const int M = R / a.top_k;
+    for (int t0 = 0; t0 < M; t0 += 4) {
+        const int t = t0 + g;
+        if (t >= M) continue;
+        float s = 0.f;
+        for (int j = 0; j < a.top_k; ++j) {
+            const int r = t * a.top_k + j;
+            if (sValid[r]) s += a.topk_w[r] * sY[r * kCW + l16];
+        }
+        uint16_t *op = out + (int64_t)t * K + c0 + l16;
+        *op = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(*op) + s);
+    }
+}
+
+template <int BM, bool E8M0>
+hipError_t launch_dc(const DownArgs &a, const int32_t *rpos, uint16_t *out, hipStream_t st) {
+    const int64_t grid = a.K / kCW;
+    if (grid == 0 || a.nblocks == 0) return hipSuccess;
+    const int smem = DCLayout((int)a.R).total;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0>, 160 * 1024);
+    if (e != hipSuccess) return e;
+    down_cols_kernel<BM, E8M0><<<(unsigned)grid, 64, smem, st>>>(a, rpos, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool down_cols_fits(int64_t R, int64_t I, int block_m) {
+    return R >= 1 && R <= kMaxRoutes && I == kIB && (block_m == 8 || block_m == 16);
+}
+
+hipError_t launch_down_cols(const DownArgs &a, int block_m, bool e8m0, const int32_t *rpos,
+                            uint16_t *out, hipStream_t st) {
+    if (!down_cols_fits(a.R, a.I, block_m)) return hipErrorInvalidValue;
+    if (block_m == 8) return e8m0 ? launch_dc<8, true>(a, rpos, out, st) : launch_dc<8, false>(a, rpos, out, st);
+    return e8m0 ? launch_dc<16, true>(a, rpos, out, st) : launch_dc<16, false>(a, rpos, out, st);
+}
+
+}  // namespace moe

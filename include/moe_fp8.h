@@ -109,16 +109,19 @@ enum {
 #define MOE_F_SPLITK_MASK  0xFF00u
 /* Bits 16..17 and 18..19 optionally force the kernel family of the gate/up
  * and of the down stage: MOE_PATH_AUTO (0), MOE_PATH_STREAM (1: per plan
- * block, the weights streamed once per block) or MOE_PATH_PERSISTENT (2:
- * persistent workgroups over 128-row tiles of one expert; needs
- * K, I <= 32768 and no forced split-K).  A tuning and test override; the
- * same value must be given to moe_fp8_experts_workspace_size.  Other
- * values: MOE_ERR_SHAPE. */
+ * block, the weights streamed once per block), MOE_PATH_PERSISTENT (2:
+ * persistent workgroups over row tiles of one expert; needs K, I <= 32768
+ * and, for the gate/up, no forced split-K) or, for the down stage only,
+ * MOE_PATH_COLUMNS (3: one workgroup per 16 output columns over every plan
+ * block, the route sum in the same launch; needs I = 256, block_m 8 or 16
+ * and M * top_k <= 192, else MOE_ERR_UNSUPPORTED; FP8 weights only).  A
+ * tuning and test override; the same value must be given to
+ * moe_fp8_experts_workspace_size.  Other values: MOE_ERR_SHAPE. */
 #define MOE_F_GATEUP_PATH_SHIFT 16
 #define MOE_F_GATEUP_PATH_MASK  0x30000u
 #define MOE_F_DOWN_PATH_SHIFT   18
 #define MOE_F_DOWN_PATH_MASK    0xC0000u
-enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_PERSISTENT = 2 };
+enum { MOE_PATH_AUTO = 0, MOE_PATH_STREAM = 1, MOE_PATH_PERSISTENT = 2, MOE_PATH_COLUMNS = 3 };
 /* Bits 20..21 choose how moe_fp8_experts launches steps 3-5:
  *   MOE_FUSE_AUTO (0) the library's choice: currently always two stages
  *                     (the single launch measured slower on MI355X at every
@@ -256,7 +259,8 @@ moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int
 
 /* The launch schedule moe_fp8_experts would use for these sizes and flags
  * (host only, nothing enqueued): info[0] = 1 if the gate/up stage runs the
- * persistent kernel, info[1] = 1 if the down stage does, info[2] = the
+ * persistent kernel, info[1] = the down stage's kernel (0 per plan block,
+ * 1 persistent, 2 split over output columns with the route sum), info[2] = the
  * gate/up split-K factor, info[3] = K-blocks (of 128) per split, info[4] =
  * 1 if steps 3-5 run as the single launch.  info is host memory of 5
  * int32.  Errors: as moe_fp8_experts_workspace_size's

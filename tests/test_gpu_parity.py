@@ -530,6 +530,38 @@ def test_block_m_8_kernel_families(gu, dn):
                 label=f"block_m=8 paths {gu}/{dn}")
 
 
+# The down stage split over output columns with the route sum in the same
+# launch (the default while every route's intermediate row fits in LDS:
+# I = 256, block_m 8 or 16, at most 192 routes).  Forced on: the tiny and
+# decode workloads at both block sizes up to 189 routes, power-of-two scales
+# through the E8M0 MFMA, and a skew-like batch (hot experts with many
+# blocks, duplicate experts within a token, 1% masked routes, a zero-scale
+# expert) at I = 256.
+COLS = (moe.MOE_PATH_COLUMNS << moe.MOE_F_DOWN_PATH_SHIFT) | FUSE_OFF
+
+
+@pytest.mark.parametrize("name,M,bm", [("tiny", None, 16), ("tiny", None, 8), ("decode", 1, 16),
+                                       ("decode", 2, 8), ("decode", 21, 8), ("decode", 12, 16)])
+def test_column_down(name, M, bm):
+    cs = case_of(name, M=M, block_m=bm)
+    cap = moe.moe_plan_capacity(cs.M, cs.top_k, cs.E, cs.block_m)[0]
+    assert moe.moe_fp8_experts_schedule(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, cap, COLS)[1] == 2
+    full_parity(cs, flags=COLS, label=f"column down bm={bm}")
+
+
+def test_column_down_e8m0():
+    cfg = dict(CONFIGS["zipf"], M=24, E=16, K=1024, I=256, top_k=6, block_m=16, seed=43)
+    cs = make_case("zipf-i256", device=DEV, config=cfg)
+    full_parity(cs, flags=COLS | E8, act_mode=SCALE_UE8M0, label="column down e8m0")
+
+
+@pytest.mark.parametrize("dt", [torch.int32, torch.int64])
+def test_column_down_skew(dt):
+    cfg = dict(CONFIGS["skew"], M=18, I=256, block_m=16, seed=44)
+    cs = make_case("skew-i256", device=DEV, config=cfg, ids_dtype=dt)
+    full_parity(cs, flags=COLS, label=f"column down skew {dt}")
+
+
 # ------------------------------------------------- steps 3-5 in one launch
 # MOE_FUSE_ON: one launch runs the per-block gate/up items, the down items
 # (which wait for their block's intermediate rows) and the route sum (by the
@@ -550,7 +582,11 @@ def test_single_launch(name, M, flags, cover):
     tokens = _cover_tokens(cs, 6, 40) if cover else None
     g, o, _ = full_parity(cs, flags=flags | FUSE_ON, act_mode=act, tokens=tokens,
                           label="single launch")
-    two = run_gpu(cs, flags=flags | FUSE_OFF, act_mode=act)
+    # the two launches on the per-block down kernel: the single launch runs its
+    # work item and its route sum (the column-split down, the default at
+    # decode sizes, adds FP32 route terms instead of the FP16 route rows)
+    two = run_gpu(cs, flags=flags | FUSE_OFF | (moe.MOE_PATH_STREAM << moe.MOE_F_DOWN_PATH_SHIFT),
+                  act_mode=act)
     assert np.array_equal(g.out, two.out), "single launch differs from the two launches"
     rows = o.res.row_valid if tokens is None else (two.sorted[:two.P] < cs.M * cs.top_k)
     assert np.array_equal(g.h_q[:g.P][rows], two.h_q[:two.P][rows])

@@ -149,20 +149,29 @@ def test_experts_schedule():
     and their validation."""
     sched = moe.moe_fp8_experts_schedule
     GU, DN = moe.MOE_F_GATEUP_PATH_SHIFT, moe.MOE_F_DOWN_PATH_SHIFT
-    # decode: small grid, both per-block; the split fills ~3/4 of the chip in
-    # one round with the plan blocks expected under uniform routing: M=1
-    # (~9 blocks x 2 column tiles) 10 ways of 6 K-blocks, M=4 (~34 blocks)
-    # 3 ways, M=16 (~112 blocks) no split
-    assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, False, 10, 6, False)
+    # decode: per-block gate/up; the split fills ~3/4 of the chip in one
+    # round with the plan blocks expected under uniform routing: M=1 (~9
+    # blocks x 2 column tiles) 10 ways of 6 K-blocks, M=4 (~34 blocks) 3
+    # ways, M=16 (~112 blocks) no split.  The down stage: split over output
+    # columns (route sum included) up to 24 routes where it applies (I = 256,
+    # block_m 8 or 16), then persistent once its (block, 256-column) items
+    # reach twice the CU count
+    COLS, PERS, BLOCK = 2, 1, 0
+    assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, COLS, 10, 6, False)
+    assert sched(2, 7168, 256, 257, 9, 8, 288)[1] == COLS
     assert sched(4, 7168, 256, 257, 9, 16, 576)[2:4] == (3, 19)
     assert sched(16, 7168, 256, 257, 9, 16, 2304)[2] == 1
-    # the down stage goes persistent once its expected (block, 256-column)
-    # items reach twice the CU count: decode M=1 has ~9 x 28 = 252, M=4
-    # ~34 x 28, M=16 ~112 x 28
-    assert sched(4, 7168, 256, 257, 9, 16, 576)[:2] == (False, True)
-    assert sched(16, 7168, 256, 257, 9, 16, 2304)[:2] == (False, True)
-    # the tiny workload (~5 blocks x 1 item): per-block down
-    assert sched(4, 256, 256, 8, 2, 16, 128)[:2] == (False, False)
+    assert sched(4, 7168, 256, 257, 9, 16, 576)[:2] == (False, PERS)
+    assert sched(16, 7168, 256, 257, 9, 16, 2304)[:2] == (False, PERS)
+    assert sched(4, 256, 256, 8, 2, 16, 128)[1] == COLS              # the tiny workload
+    # forced: the column split up to 192 routes, the per-block or persistent down
+    assert sched(21, 7168, 256, 257, 9, 8, 2304, 3 << DN)[1] == COLS  # 189 routes
+    assert sched(16, 7168, 256, 257, 9, 16, 2304, 1 << DN)[1] == BLOCK
+    assert sched(1, 7168, 256, 257, 9, 16, 144, 2 << DN)[1] == PERS
+    assert sched(32, 7168, 256, 257, 9, 16, 4608, 1 << DN)[1] == BLOCK
+    with pytest.raises(moe.MoeError) as ei:                          # 216 routes
+        sched(24, 7168, 256, 257, 9, 16, 4608, 3 << DN)
+    assert moe.STATUS_NAMES[ei.value.status] == "MOE_ERR_UNSUPPORTED"
     # page-1 M=16 and M=1024: per-block gate/up, persistent down
     assert sched(16, 4096, 1024, 288, 8, 64, 8192)[:2] == (False, True)
     assert sched(1024, 4096, 1024, 288, 8, 64, 26368)[:2] == (False, True)
@@ -182,7 +191,7 @@ def test_experts_schedule():
     assert sched(4096, 4096, 1024, 288, 8, 64, 50944, (1 << GU) | (1 << DN))[:2] == (False, False)
     # a forced split-K factor selects the per-block gate/up
     assert sched(4096, 4096, 1024, 288, 8, 64, 50944, 2 << moe.MOE_F_SPLITK_SHIFT)[0] is False
-    for bad, status in ((3 << GU, "MOE_ERR_SHAPE"), (3 << DN, "MOE_ERR_SHAPE"),
+    for bad, status in ((3 << GU, "MOE_ERR_SHAPE"), (3 << DN, "MOE_ERR_UNSUPPORTED"),
                         ((2 << GU) | (2 << moe.MOE_F_SPLITK_SHIFT), "MOE_ERR_SHAPE"),
                         (1 << 24, "MOE_ERR_SHAPE"), (3 << FU, "MOE_ERR_SHAPE"),
                         ((2 << FU) | (2 << DN), "MOE_ERR_SHAPE")):
