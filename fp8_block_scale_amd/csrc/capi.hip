@@ -105,12 +105,11 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     // W2 stages in flight instead of three.
     c.dn_small = c.dn_persistent && !c.gu_persistent && bm <= 32;
     // The column-split down with its own route sum (no per-route buffer, no
-    // route-sum launch) where it applies; chosen by itself up to 24 routes
-    // (measured at the decode shape: faster than the per-block down at M=1
-    // and M=2, slower than the persistent one from M=4 on, where each of its
-    // one-wave workgroups walks too many blocks).
-    c.dn_cols = !w4 && fuse != MOE_FUSE_ON && moe::down_cols_fits(R, I, bm) &&
-                (dn_path == MOE_PATH_COLUMNS || (dn_path == MOE_PATH_AUTO && R <= 24));
+    // route-sum launch) wherever it applies: measured at the decode shape
+    // faster than the per-block and the persistent down at M = 1 .. 16 (down
+    // stage 7.4 / 10.3 / 14.2 / 22.2 / 36.7 us at M = 1, 2, 4, 8, 16).
+    c.dn_cols = !w4 && fuse != MOE_FUSE_ON && moe::down_cols_fits(R, I, K, bm) &&
+                (dn_path == MOE_PATH_COLUMNS || dn_path == MOE_PATH_AUTO);
     if (c.dn_cols) c.dn_persistent = c.dn_small = false;
     if (c.gu_persistent) {
         c.nsplit = 1;
@@ -456,7 +455,7 @@ moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m, in
     const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
     if (gp > MOE_PATH_PERSISTENT || dp > MOE_PATH_COLUMNS)
         return fail(MOE_ERR_SHAPE, "kernel path override must be 0, 1 or 2 (3: down stage only)");
-    if (dp == MOE_PATH_COLUMNS && R > 0 && !moe::down_cols_fits(R, I, block_m))
+    if (dp == MOE_PATH_COLUMNS && R > 0 && !moe::down_cols_fits(R, I, K, block_m))
         return fail(MOE_ERR_UNSUPPORTED,
                     "the column-split down needs I = 256, block_m 8 or 16 and M * top_k <= 192");
     if ((gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT) && (K > 32768 || I > 32768))

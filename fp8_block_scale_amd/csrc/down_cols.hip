@@ -9,24 +9,28 @@
 //   out[t, c] = bf16(out[t, c] + sum_j topk_weights[r] * y[r, c])
 // with the route terms added in route order in FP32 and one BF16 rounding.
 //
-// Work split.  One workgroup (one wave) owns 16 output columns.  It first
+// Work split.  One workgroup (four waves) owns 32 output columns.  It first
 // copies every valid route's intermediate row and row scales into LDS
 // (indexed by route, found through the route map of the gate/up stage), then
-// walks every plan block below num_tokens_post_padded: per block it
-// multiplies the block's W2 slab (its expert's 16 rows of W2 for these
-// columns, all of I) with the block's routes' rows, keeping each valid
-// route's 16 results in LDS.  Having every route of its columns, it adds each
-// token's routes itself at the end: no per-route buffer in HBM and no
-// route-sum launch.  Each W2 slab is read by exactly one workgroup.
+// walks every plan block below num_tokens_post_padded: wave w takes the
+// blocks of parity w / 2 and the 16 columns of half w % 2.  Per block a wave
+// multiplies the block's W2 slab (its expert's 16 rows of W2 for those
+// columns, all of I) with the block's routes' rows and keeps each valid
+// route's results in LDS (a route lies in one block: nothing to reduce).
+// Having every route of its columns, the workgroup adds each token's routes
+// itself at the end: no per-route buffer in HBM and no route-sum launch.
+// Each W2 slab is read by exactly one wave.
 //
 // Pipeline.  A ring of kStages per wave, each stage one block's W2 slab
 // (16-byte chunks XOR-swizzled by row, so the MFMA operand reads hit distinct
-// banks), its route ids, expert id and W2 block scales, by direct
+// banks) and its route ids, expert id and W2 block scales, by direct
 // global->LDS loads kStages - 1 blocks ahead, so a block's multiply waits on
-// nothing but its stage.  One wave per workgroup: no barriers, the waits are the wave's own
-// load counts.  FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale
-// product applied per 128-deep K-block, or with power-of-two scales as E8M0
-// exponents inside the MFMA.
+// nothing but its stage.  The rings are private to their waves: between the
+// copy of the intermediate rows and the route sum there is no barrier, the
+// waits are each wave's own load counts.  FP8 MFMA
+// (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per
+// 128-deep K-block, or with power-of-two scales as E8M0 exponents inside the
+// MFMA.
 #include <type_traits>
 
 #include "common.h"
@@ -36,36 +40,38 @@ namespace moe {
 
 namespace {
 
-constexpr int kCW = 16;                 // output columns per workgroup
+constexpr int kCW = 16;                 // output columns per wave
+constexpr int kWaves = 4;
+constexpr int kWGCols = 2 * kCW;        // output columns per workgroup
 constexpr int kIB = 256;                // bytes of an intermediate / W2 row (I)
 constexpr int kNJB = kIB / 128;
-constexpr int kStages = 8;
+constexpr int kStages = 5;
 constexpr int kSlabBytes = kCW * kIB;                  // one block's W2 slab
 constexpr int kSlabInstr = kSlabBytes / 1024;          // 16-byte DMA per lane
 constexpr int kStageBytes = kSlabBytes + 128;          // + [16] route ids, expert id, W2 scales
-constexpr int kPerStage = kSlabInstr + 3;
+constexpr int kPerStage = kSlabInstr + 1;
 constexpr int64_t kMaxRoutes = 192;                    // routes whose rows fit in LDS
 static_assert((kStages - 2) * kPerStage < 64, "vmcnt range");
 
-typedef const __attribute__((address_space(4))) int32_t *const_i32_p;
-typedef const __attribute__((address_space(4))) float *const_f32_p;
-
-// LDS carve-up after the ring: intermediate rows by route [R][kIB], their
-// scales [R][kNJB], the results [R + 1][kCW] (FP32; row R takes the rows
-// that hold no route), route valid flags [R].
+// LDS carve-up after the rings ([kWaves][kStages] stages): intermediate rows
+// by route [R][kIB], their scales [R][kNJB], the results [R + 1][kWGCols]
+// (FP32; row R takes the rows that hold no route), route valid flags [R].
+// At R = 192: 160064 bytes.
 struct DCLayout {
     int h, hs, y, valid, total;
     __host__ __device__ explicit DCLayout(int R) {
-        h = kStages * kStageBytes;
+        h = kWaves * kStages * kStageBytes;
         hs = h + R * kIB;
         y = hs + ((R * kNJB * 4 + 15) & ~15);            // 16-byte rows of results
-        valid = y + (R + 1) * kCW * 4;
+        valid = y + (R + 1) * kWGCols * 4;
         total = valid + ((R + 15) & ~15);
     }
 };
 
+typedef const __attribute__((address_space(4))) int32_t *const_i32_p;
+
 template <int BM, bool E8M0>
-__global__ void __launch_bounds__(64, 1)
+__global__ void __launch_bounds__(64 * kWaves, 1)
 down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restrict__ out) {
     static_assert(BM <= 16, "one 16-row MFMA tile per plan block");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -76,10 +82,14 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restr
     float *sY = reinterpret_cast<float *>(smem + L.y);
     uint8_t *sValid = smem + L.valid;
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = w & 1, parity = w >> 1;
     const int l16 = lane & 15, g = lane >> 4;
     const int64_t K = a.K;
-    const int64_t c0 = (int64_t)blockIdx.x * kCW;
+    const int64_t cw0 = (int64_t)blockIdx.x * kWGCols;    // the workgroup's columns
+    const int64_t c0 = cw0 + half * kCW;                  // this wave's
 
     const int ntp = __builtin_amdgcn_readfirstlane(((const_i32_p)a.ntp)[0]);
     int nb = ntp / BM;
@@ -90,50 +100,60 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restr
     // -1 if masked): first the map itself, then direct global->LDS copies,
     // four routes (1 KB) per instruction, chunk c of route r's row at LDS
     // chunk c ^ (r & 15); masked routes copy plan row 0 and stay flagged off
-    int *sRp = reinterpret_cast<int *>(smem);           // (in the ring's slot 0, before any refill)
-    for (int r = lane; r < R; r += 64) {
+    int *sRp = reinterpret_cast<int *>(smem);           // (in the rings, before any refill)
+    for (int r = tid; r < R; r += 64 * kWaves) {
         const int p = rpos[r];
         sRp[r] = p >= 0 ? p : 0;
         sValid[r] = p >= 0 ? 1 : 0;
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): the map is in LDS
-    for (int r0 = 0; r0 < R; r0 += 4) {
+    __syncthreads();
+    for (int r0 = 4 * w; r0 < R; r0 += 4 * kWaves) {
         const int r = r0 + (lane >> 4);
         if (r < R) {
             const int p = sRp[r];
             lds_dma16(a.hq + (int64_t)p * kIB + ((l16 ^ (r & 15)) * 16), sH + (int64_t)r0 * kIB);
         }
     }
-    for (int q0 = 0; q0 < R * kNJB; q0 += 64) {
+    for (int q0 = 64 * w; q0 < R * kNJB; q0 += 64 * kWaves) {
         const int q = q0 + lane;                         // route q / kNJB, K-block q % kNJB
         if (q < R * kNJB) lds_dma4(a.hs + (int64_t)sRp[q / kNJB] * kNJB + q % kNJB, sHs + q0);
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);                 // the map's reads are done before slot 0 refills
+    // every wave's copies have landed and every read of the map is done
+    // before the rings (which overwrite the map) start
+    wait_vmcnt<0>();
+    __syncthreads();
+    uint8_t *ring = smem + w * kStages * kStageBytes;
 
-    // ---- ring of W2 slabs: block b in slot b % kStages
-    auto issue = [&](int st, int b) {
-        uint8_t *base = smem + st * kStageBytes;
+    // ---- this wave's blocks: b = 2 i + parity, i < nw
+    const int nw = (nb - parity + 1) / 2;
+    auto issue = [&](int st, int i) {
+        const int b = 2 * i + parity;
+        uint8_t *base = ring + st * kStageBytes;
         const int e0 = __builtin_amdgcn_readfirstlane(((const_i32_p)a.eids)[b]);
         const int e = (e0 >= 0 && e0 < a.E) ? e0 : 0;
         // W2 rows c0 .. c0 + 15 of expert e: LDS slot s (16 bytes) of the slab
         // holds row s / 16, chunk (s % 16) ^ row
         const uint8_t *wrow = a.w2 + ((int64_t)e * K + c0) * kIB;
 #pragma unroll
-        for (int i = 0; i < kSlabInstr; ++i) {
-            const int s = i * 64 + lane;
+        for (int k = 0; k < kSlabInstr; ++k) {
+            const int s = k * 64 + lane;
             const int row = s >> 4, pos = s & 15;
-            lds_dma16_nt(wrow + (int64_t)row * kIB + (pos ^ row) * 16, base + i * 1024);
+            lds_dma16_nt(wrow + (int64_t)row * kIB + (pos ^ row) * 16, base + k * 1024);
         }
-        const int64_t p = (int64_t)b * BM + (lane < BM ? lane : 0);
-        uint8_t *meta = base + kSlabBytes;
-        if (lane < 16) lds_dma4(a.sorted + p, meta);
-        if (lane == 0) lds_dma4(a.eids + b, meta + 64);
-        if (lane < kNJB)
-            lds_dma4(a.w2s + ((int64_t)e * (K >> 7) + (c0 >> 7)) * kNJB + lane, meta + 68);
+        // metadata in one 4-byte DMA: lanes 0-15 the route ids, lane 16 the
+        // expert id, lanes 17 .. 16 + kNJB the W2 block scales
+        const void *msrc;
+        if (lane < 16)
+            msrc = a.sorted + (int64_t)b * BM + (lane < BM ? lane : 0);
+        else if (lane == 16)
+            msrc = a.eids + b;
+        else
+            msrc = a.w2s + ((int64_t)e * (K >> 7) + (c0 >> 7)) * kNJB + (lane < 17 + kNJB ? lane - 17 : 0);
+        if (lane < 17 + kNJB) lds_dma4(msrc, base + kSlabBytes);
     };
 
     auto compute = [&](int st) {
-        const uint8_t *base = smem + st * kStageBytes;
+        const uint8_t *base = ring + st * kStageBytes;
         const int *meta = reinterpret_cast<const int *>(base + kSlabBytes);
         const int r = meta[l16], e0 = meta[16];
         const bool ok = l16 < BM && r >= 0 && r < R && e0 >= 0 && e0 < a.E;
@@ -161,82 +181,76 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restr
         // store under a lane condition would let the compiler move the MFMAs
         // under it, where lanes outside the condition keep stale scale
         // operands.
-        *reinterpret_cast<v4f *>(sY + (ok ? r : R) * kCW + 4 * g) = acc;
+        *reinterpret_cast<v4f *>(sY + (ok ? r : R) * kWGCols + half * kCW + 4 * g) = acc;
     };
 
-    // blocks b, slots b % kStages; kStages - 1 blocks in flight ahead of the
-    // one being multiplied (loads complete in issue order; the row copy above
-    // was issued first, so the first wait covers it too)
+    // this wave's blocks i, slots i % kStages; kStages - 1 blocks in flight
+    // ahead of the one being multiplied (loads complete in issue order)
     for (int q = 0; q < kStages - 1; ++q)
-        if (q < nb) issue(q, q);
-    auto step = [&](auto st_c, int b) {
+        if (q < nw) issue(q, q);
+    auto step = [&](auto st_c, int i) {
         constexpr int ST = decltype(st_c)::value;
-        const int ahead = nb - 1 - b;                   // blocks issued past b, at most kStages - 2
-        switch (ahead < kStages - 2 ? ahead : kStages - 2) {
-            case 6: wait_vmcnt<6 * kPerStage>(); break;
-            case 5: wait_vmcnt<5 * kPerStage>(); break;
-            case 4: wait_vmcnt<4 * kPerStage>(); break;
-            case 3: wait_vmcnt<3 * kPerStage>(); break;
-            case 2: wait_vmcnt<2 * kPerStage>(); break;
-            case 1: wait_vmcnt<kPerStage>(); break;
-            default: wait_vmcnt<0>(); break;
-        }
-        // the refill goes into the slot of block b - 1, whose operand reads
+        const int ahead = nw - 1 - i;                   // blocks issued past i, at most kStages - 2
+        if (ahead >= 3)
+            wait_vmcnt<3 * kPerStage>();
+        else if (ahead == 2)
+            wait_vmcnt<2 * kPerStage>();
+        else if (ahead == 1)
+            wait_vmcnt<kPerStage>();
+        else
+            wait_vmcnt<0>();
+        // the refill goes into the slot of block i - 1, whose operand reads
         // the previous step has consumed
-        if (b + kStages - 1 < nb) issue((ST + kStages - 1) % kStages, b + kStages - 1);
+        if (i + kStages - 1 < nw) issue((ST + kStages - 1) % kStages, i + kStages - 1);
         compute(ST);
     };
-    static_assert(kStages == 8, "the step switch covers up to six stages ahead");
-    for (int b = 0; b < nb; b += kStages) {
-        step(std::integral_constant<int, 0>{}, b);
-        if (b + 1 < nb) step(std::integral_constant<int, 1>{}, b + 1);
-        if (b + 2 < nb) step(std::integral_constant<int, 2>{}, b + 2);
-        if (b + 3 < nb) step(std::integral_constant<int, 3>{}, b + 3);
-        if (b + 4 < nb) step(std::integral_constant<int, 4>{}, b + 4);
-        if (b + 5 < nb) step(std::integral_constant<int, 5>{}, b + 5);
-        if (b + 6 < nb) step(std::integral_constant<int, 6>{}, b + 6);
-        if (b + 7 < nb) step(std::integral_constant<int, 7>{}, b + 7);
+    static_assert(kStages == 5, "the waits cover up to three stages ahead");
+    for (int i = 0; i < nw; i += kStages) {
+        step(std::integral_constant<int, 0>{}, i);
+        if (i + 1 < nw) step(std::integral_constant<int, 1>{}, i + 1);
+        if (i + 2 < nw) step(std::integral_constant<int, 2>{}, i + 2);
+        if (i + 3 < nw) step(std::integral_constant<int, 3>{}, i + 3);
+        if (i + 4 < nw) step(std::integral_constant<int, 4>{}, i + 4);
     }
     wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): results in LDS
+    __syncthreads();                                    // every wave's results are in LDS
 
-    // ---- route sum: lanes 16q .. 16q + 15 take token t0 + q, one column
-    // each; routes in order, FP32, then the previous output, one rounding
+    // ---- route sum: thread tid takes column tid % 32 of tokens tid / 32,
+    // + 8, ...; routes in order, FP32, then the previous output, one rounding
     const int M = R / a.top_k;
-    for (int t0 = 0; t0 < M; t0 += 4) {
-        const int t = t0 + g;
-        if (t >= M) continue;
+    const int col = tid % kWGCols;
+    for (int t = tid / kWGCols; t < M; t += 64 * kWaves / kWGCols) {
         float s = 0.f;
         for (int j = 0; j < a.top_k; ++j) {
             const int r = t * a.top_k + j;
-            if (sValid[r]) s += a.topk_w[r] * sY[r * kCW + l16];
+            if (sValid[r]) s += a.topk_w[r] * sY[r * kWGCols + col];
         }
-        uint16_t *op = out + (int64_t)t * K + c0 + l16;
+        uint16_t *op = out + (int64_t)t * K + cw0 + col;
         *op = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(*op) + s);
     }
 }
 
 template <int BM, bool E8M0>
 hipError_t launch_dc(const DownArgs &a, const int32_t *rpos, uint16_t *out, hipStream_t st) {
-    const int64_t grid = a.K / kCW;
+    const int64_t grid = a.K / kWGCols;
     if (grid == 0 || a.nblocks == 0) return hipSuccess;
     const int smem = DCLayout((int)a.R).total;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t e = raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0>, 160 * 1024);
     if (e != hipSuccess) return e;
-    down_cols_kernel<BM, E8M0><<<(unsigned)grid, 64, smem, st>>>(a, rpos, out);
+    down_cols_kernel<BM, E8M0><<<(unsigned)grid, 64 * kWaves, smem, st>>>(a, rpos, out);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool down_cols_fits(int64_t R, int64_t I, int block_m) {
-    return R >= 1 && R <= kMaxRoutes && I == kIB && (block_m == 8 || block_m == 16);
+bool down_cols_fits(int64_t R, int64_t I, int64_t K, int block_m) {
+    return R >= 1 && R <= kMaxRoutes && I == kIB && K % kWGCols == 0 && (block_m == 8 || block_m == 16);
 }
 
 hipError_t launch_down_cols(const DownArgs &a, int block_m, bool e8m0, const int32_t *rpos,
                             uint16_t *out, hipStream_t st) {
-    if (!down_cols_fits(a.R, a.I, block_m)) return hipErrorInvalidValue;
+    if (!down_cols_fits(a.R, a.I, a.K, block_m)) return hipErrorInvalidValue;
     if (block_m == 8) return e8m0 ? launch_dc<8, true>(a, rpos, out, st) : launch_dc<8, false>(a, rpos, out, st);
     return e8m0 ? launch_dc<16, true>(a, rpos, out, st) : launch_dc<16, false>(a, rpos, out, st);
 }

@@ -194,11 +194,11 @@ hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, bool small, hipSt
 // of 128 rows, or (small: block_m <= 32, tiles listed by launch_tiles with
 // tile_rows 32) of 32 rows with a deeper W2 ring.
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, bool small, hipStream_t st);
-// Small route counts (down_cols.hip): one workgroup per 16 output columns
+// Small route counts (down_cols.hip): one workgroup per 32 output columns
 // over every plan block, the route sum in the same launch (no y, no
 // finalize); reads each route's plan row from rpos (the gate/up stage's route
 // map).  down_cols_fits: I = 256, block_m 8 or 16, 1 <= R <= 192.
-bool down_cols_fits(int64_t R, int64_t I, int block_m);
+bool down_cols_fits(int64_t R, int64_t I, int64_t K, int block_m);
 hipError_t launch_down_cols(const DownArgs &a, int block_m, bool e8m0, const int32_t *rpos,
                             uint16_t *out, hipStream_t st);
 // The single-launch path (fused.hip): steps 3-5 over the arguments of both

@@ -152,22 +152,24 @@ def test_experts_schedule():
     # decode: per-block gate/up; the split fills ~3/4 of the chip in one
     # round with the plan blocks expected under uniform routing: M=1 (~9
     # blocks x 2 column tiles) 10 ways of 6 K-blocks, M=4 (~34 blocks) 3
-    # ways, M=16 (~112 blocks) no split.  The down stage: split over output
-    # columns (route sum included) up to 24 routes where it applies (I = 256,
-    # block_m 8 or 16), then persistent once its (block, 256-column) items
-    # reach twice the CU count
+    # ways, M=16 (~112 blocks) no split.  The down stage splits the output
+    # columns (route sum included) wherever that applies (I = 256, block_m
+    # 8 or 16, at most 192 routes), else goes persistent once its
+    # (block, 256-column) items reach twice the CU count
     COLS, PERS, BLOCK = 2, 1, 0
     assert sched(1, 7168, 256, 257, 9, 16, 144) == (False, COLS, 10, 6, False)
-    assert sched(2, 7168, 256, 257, 9, 8, 288)[1] == COLS
     assert sched(4, 7168, 256, 257, 9, 16, 576)[2:4] == (3, 19)
     assert sched(16, 7168, 256, 257, 9, 16, 2304)[2] == 1
-    assert sched(4, 7168, 256, 257, 9, 16, 576)[:2] == (False, PERS)
-    assert sched(16, 7168, 256, 257, 9, 16, 2304)[:2] == (False, PERS)
+    assert sched(4, 7168, 256, 257, 9, 16, 576)[:2] == (False, COLS)
+    assert sched(16, 7168, 256, 257, 9, 16, 2304)[:2] == (False, COLS)
+    assert sched(21, 7168, 256, 257, 9, 8, 2304)[1] == COLS          # 189 routes
     assert sched(4, 256, 256, 8, 2, 16, 128)[1] == COLS              # the tiny workload
-    # forced: the column split up to 192 routes, the per-block or persistent down
-    assert sched(21, 7168, 256, 257, 9, 8, 2304, 3 << DN)[1] == COLS  # 189 routes
+    assert sched(32, 7168, 256, 257, 9, 16, 4608)[:2] == (False, PERS)  # 288 routes
+    assert sched(16, 7168, 256, 257, 9, 32, 4608)[1] == PERS         # block_m 32
+    # forced: the per-block or the persistent down; the column split past
+    # 192 routes is refused
     assert sched(16, 7168, 256, 257, 9, 16, 2304, 1 << DN)[1] == BLOCK
-    assert sched(1, 7168, 256, 257, 9, 16, 144, 2 << DN)[1] == PERS
+    assert sched(16, 7168, 256, 257, 9, 16, 2304, 2 << DN)[1] == PERS
     assert sched(32, 7168, 256, 257, 9, 16, 4608, 1 << DN)[1] == BLOCK
     with pytest.raises(moe.MoeError) as ei:                          # 216 routes
         sched(24, 7168, 256, 257, 9, 16, 4608, 3 << DN)
