@@ -61,7 +61,7 @@ def parse():
                     help="power-of-two scales inside the FP8 MFMA (zipf workload)")
     ap.add_argument("--splitk", type=int, default=0,
                     help="force the small-grid gate/up split-K factor (1..255; 0 = automatic)")
-    ap.add_argument("--gateup-path", choices=("auto", "stream", "persistent"), default="auto",
+    ap.add_argument("--gateup-path", choices=("auto", "stream", "persistent", "columns"), default="auto",
                     help="force the gate/up kernel family (tuning override)")
     ap.add_argument("--down-path", choices=("auto", "stream", "persistent", "columns"), default="auto",
                     help="force the down kernel family (tuning override)")
@@ -122,6 +122,7 @@ KERNEL_SOURCES = {
     "gateup_pipe_kernel": ("gateup_pipe.hip", "common.h", "internal.h"),
     "gateup_stream_kernel": ("gateup.hip", "gateup_item.h", "common.h", "internal.h"),
     "fused_experts_kernel": ("fused.hip", "gateup_item.h", "down_item.h", "common.h", "internal.h"),
+    "gateup_slices_kernel": ("gateup_slices.hip", "common.h", "internal.h"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
@@ -129,9 +130,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 def gateup_kernel_name(case, sorted_cap, flags):
     """The gate/up kernel the library picks for these sizes and flags."""
     import fp8_block_scale_amd as moe
-    gu_persistent = moe.moe_fp8_experts_schedule(case.M, case.K, case.I, case.E, case.top_k,
-                                                 case.block_m, sorted_cap, flags)[0]
-    return "gateup_pipe_kernel" if gu_persistent else "gateup_stream_kernel"
+    gu = moe.moe_fp8_experts_schedule(case.M, case.K, case.I, case.E, case.top_k,
+                                      case.block_m, sorted_cap, flags)[0]
+    return ("gateup_stream_kernel", "gateup_pipe_kernel", "gateup_slices_kernel")[gu]
 
 
 def sources_sha(kernel):

@@ -255,12 +255,13 @@ def moe_fp8_experts_workspace_layout(M, K, I, E, top_k, block_m, sorted_cap, fla
 
 
 def moe_fp8_experts_schedule(M, K, I, E, top_k, block_m, sorted_cap, flags=0):
-    """(gate/up persistent, down kernel (0 per block, 1 persistent, 2 split over
-    output columns), split-K factor, K-blocks per split, steps 3-5 as one launch)."""
+    """(gate/up kernel (0 per block, 1 persistent, 2 split over intermediate-column
+    slices), down kernel (0 per block, 1 persistent, 2 split over output columns),
+    split-K factor, K-blocks per split, steps 3-5 as one launch)."""
     info = (ctypes.c_int32 * 5)()
     _check(_c["moe_fp8_experts_schedule"](M, K, I, E, top_k, block_m, sorted_cap, flags, info),
            "moe_fp8_experts_schedule")
-    return bool(info[0]), int(info[1]), int(info[2]), int(info[3]), bool(info[4])
+    return int(info[0]), int(info[1]), int(info[2]), int(info[3]), bool(info[4])
 
 
 def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,

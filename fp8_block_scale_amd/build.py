@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmoe_fp8.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["plan.hip", "quant.hip", "gateup.hip", "gateup_pipe.hip", "down.hip", "down_pipe.hip", "down_cols.hip",
-           "fused.hip", "capi.hip"]
+           "gateup_slices.hip", "fused.hip", "capi.hip"]
 ARCH = "gfx950"
 
 

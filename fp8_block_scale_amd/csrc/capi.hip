@@ -58,11 +58,21 @@ struct SplitChoice {
     bool dn_persistent;
     bool dn_small;       // the persistent down on row tiles of 32 rows (deeper W2 ring)
     bool dn_cols;        // the down stage split over output columns, route sum included
+    bool gu_cols;        // the gate/up split over column slices (FP32 rows; needs dn_cols)
+    int gu_slice;        // its slice width: 8 or 16 intermediate columns
     bool fused;          // steps 3-5 in one launch (moe_fp8_experts only)
 };
 
 constexpr int64_t kPersistentTiles = 512;   // (block, j-tile) pairs
 constexpr double kStreamFill = 192.0;       // workgroups the stream kernel's split aims at
+// The column-slice gate/up by default only for short K with few routes:
+// measured at the tiny shape (K = 256, 8 routes) steps 3-5 took 9.8 against
+// 12.6 us (no clearing launch, no split-K), but at the decode shape (K =
+// 7168) 22.8 against 21.9 us at M = 1 and 37.6 against 28.1 at M = 2: its
+// gate/up streams no faster than the split-K kernel there, and requantising
+// the FP32 rows in the down stage costs ~2 us.
+constexpr int64_t kSlicesMaxRoutes = 32;
+constexpr int64_t kSlicesMaxK = 1024;
 
 SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtiles, int64_t K,
                          int64_t I, int32_t bm, uint32_t flags, bool w4) {
@@ -111,7 +121,16 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     c.dn_cols = !w4 && fuse != MOE_FUSE_ON && moe::down_cols_fits(R, I, K, bm) &&
                 (dn_path == MOE_PATH_COLUMNS || dn_path == MOE_PATH_AUTO);
     if (c.dn_cols) c.dn_persistent = c.dn_small = false;
-    if (c.gu_persistent) {
+    // The column-slice gate/up leaves FP32 rows that only the column-split
+    // down reads (requantising them as it loads them); it multiplies exactly
+    // (FP16-widened codes) and needs no clearing launch and no counters.
+    const bool slices_ok = c.dn_cols && !w4 && forced == 0 &&
+                           !(flags & (MOE_F_FP8_GATEUP | MOE_F_W13_PACKED));
+    c.gu_cols = slices_ok && (gu_path == MOE_PATH_COLUMNS ||
+                              (gu_path == MOE_PATH_AUTO && R <= kSlicesMaxRoutes && K <= kSlicesMaxK));
+    if (c.gu_cols) c.gu_persistent = false;
+    c.gu_slice = 16;
+    if (c.gu_persistent || c.gu_cols) {
         c.nsplit = 1;
         c.kb_per_split = (int)nkb;
         return c;
@@ -140,7 +159,7 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
 }
 
 struct WsLayout {
-    size_t hq, hs, y, ys, rpos, tiles, cnt, part, total;
+    size_t hq, hs, y, ys, rpos, tiles, cnt, part, h32, total;
     size_t splitk_words;              // split-K counters
     size_t cnt_words;                 // all counters (split-K, then the single launch's), zeroed per call
     SplitChoice sp;
@@ -174,6 +193,8 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, in
     off = align256(off + l.cnt_words * 4);
     l.part = off;
     if (l.sp.nsplit > 1) off = align256(off + ntiles * l.sp.nsplit * block_m * 256 * 4);
+    l.h32 = off;                         // FP32 SwiGLU rows [sorted_cap, I] (column-slice gate/up)
+    if (l.sp.gu_cols) off = align256(off + (size_t)sorted_cap * I * 4);
     l.total = off;
     return l;
 }
@@ -453,11 +474,17 @@ moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m, in
     if (flags & ~known) return fail(MOE_ERR_SHAPE, "unknown flag bits 0x%x", flags & ~known);
     const uint32_t gp = (flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT;
     const uint32_t dp = (flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT;
-    if (gp > MOE_PATH_PERSISTENT || dp > MOE_PATH_COLUMNS)
-        return fail(MOE_ERR_SHAPE, "kernel path override must be 0, 1 or 2 (3: down stage only)");
-    if (dp == MOE_PATH_COLUMNS && R > 0 && !moe::down_cols_fits(R, I, K, block_m))
+    if (gp > MOE_PATH_COLUMNS || dp > MOE_PATH_COLUMNS)
+        return fail(MOE_ERR_SHAPE, "kernel path override must be 0, 1, 2 or 3");
+    if ((dp == MOE_PATH_COLUMNS || gp == MOE_PATH_COLUMNS) && R > 0 &&
+        !moe::down_cols_fits(R, I, K, block_m))
         return fail(MOE_ERR_UNSUPPORTED,
-                    "the column-split down needs I = 256, block_m 8 or 16 and M * top_k <= 192");
+                    "the column-split kernels need I = 256, block_m 8 or 16 and M * top_k <= 192");
+    if (gp == MOE_PATH_COLUMNS &&
+        (dp == MOE_PATH_STREAM || dp == MOE_PATH_PERSISTENT || (flags & MOE_F_SPLITK_MASK) ||
+         (flags & (MOE_F_FP8_GATEUP | MOE_F_W13_PACKED))))
+        return fail(MOE_ERR_SHAPE, "the column-slice gate/up runs with the column-split down, "
+                                   "exact products, unpacked W13 and no split-K factor");
     if ((gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT) && (K > 32768 || I > 32768))
         return fail(MOE_ERR_UNSUPPORTED, "the persistent kernels need K, I <= 32768");
     if (gp == MOE_PATH_PERSISTENT && (flags & MOE_F_SPLITK_MASK))
@@ -466,8 +493,8 @@ moe_status check_flags(uint32_t flags, int64_t K, int64_t I, int32_t block_m, in
         return fail(MOE_ERR_SHAPE, "MOE_F_MMA_E8M0 requires MOE_F_INTER_UE8M0");
     const uint32_t fu = (flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT;
     if (fu > MOE_FUSE_ON) return fail(MOE_ERR_SHAPE, "fuse choice must be 0, 1 or 2");
-    if (fu == MOE_FUSE_ON && (gp == MOE_PATH_PERSISTENT || dp == MOE_PATH_PERSISTENT ||
-                              dp == MOE_PATH_COLUMNS))
+    if (fu == MOE_FUSE_ON && (gp == MOE_PATH_PERSISTENT || gp == MOE_PATH_COLUMNS ||
+                              dp == MOE_PATH_PERSISTENT || dp == MOE_PATH_COLUMNS))
         return fail(MOE_ERR_SHAPE, "MOE_FUSE_ON runs the per-block kernel family: no other path");
     if (fu == MOE_FUSE_ON && I / 128 > moe::fused_max_njb(block_m))
         return fail(MOE_ERR_UNSUPPORTED, "MOE_FUSE_ON needs I / 128 <= %d at block_m %d",
@@ -486,7 +513,7 @@ MOE_API moe_status moe_fp8_experts_schedule(int64_t M, int64_t K, int64_t I, int
     st = check_flags(flags, K, I, block_m, M * top_k);
     if (st != MOE_OK) return st;
     const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, flags);
-    info[0] = l.sp.gu_persistent ? 1 : 0;
+    info[0] = l.sp.gu_cols ? 2 : (l.sp.gu_persistent ? 1 : 0);
     info[1] = l.sp.dn_cols ? 2 : (l.sp.dn_persistent ? 1 : 0);
     info[2] = l.sp.nsplit;
     info[3] = l.sp.kb_per_split;
@@ -552,6 +579,7 @@ moe::GateUpArgs gateup_args(const uint8_t *x_q, const float *x_s, const uint8_t 
     ga.kb_per_split = l.sp.kb_per_split;
     ga.inter_ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
     ga.w13_packed = (flags & MOE_F_W13_PACKED) ? 1 : 0;
+    ga.h32 = l.sp.gu_cols ? (float *)(ws + l.h32) : nullptr;
     return ga;
 }
 
@@ -603,6 +631,12 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
         return fail(MOE_ERR_ALIGN, "x_q and w13 must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = (uint8_t *)workspace;
+    if (l.sp.gu_cols) {                        // no route map, no counters
+        const moe::GateUpArgs ga = gateup_args(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids,
+                                               num_tokens_post_padded, M, K, I, E, top_k, block_m,
+                                               sorted_cap, flags, ws, l);
+        return hip_check(moe::launch_gateup_slices(ga, block_m, l.sp.gu_slice, s), "moe_fp8_gate_up: launch");
+    }
     // the route map and the split-K counters are cleared by the row-tile
     // launch when a persistent kernel runs, else by a launch of their own
     if (!l.sp.gu_persistent && !l.sp.dn_persistent) {
@@ -647,10 +681,16 @@ MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                        num_tokens_post_padded, M, K, I, E, top_k, block_m,
                                        sorted_cap, ws, l);
     const bool e8 = (flags & MOE_F_MMA_E8M0) != 0;
-    if (l.sp.dn_cols)                          // the route sum is part of this launch
-        return hip_check(moe::launch_down_cols(da, block_m, e8, (const int32_t *)(ws + l.rpos),
+    if (l.sp.dn_cols) {                        // the route sum is part of this launch
+        moe::ColsRequant rq;
+        rq.h32 = l.sp.gu_cols ? (const float *)(ws + l.h32) : nullptr;
+        rq.hq = ws + l.hq;
+        rq.hs = (float *)(ws + l.hs);
+        rq.ue8m0 = (flags & MOE_F_INTER_UE8M0) ? 1 : 0;
+        return hip_check(moe::launch_down_cols(da, block_m, e8, (const int32_t *)(ws + l.rpos), rq,
                                                (uint16_t *)out_bf16, s),
                          "moe_fp8_down_reduce: down launch");
+    }
     st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe(da, block_m, e8, l.sp.dn_small, s)
                                                    : moe::launch_down(da, block_m, e8, s),
                    "moe_fp8_down_reduce: down launch");

@@ -10,8 +10,11 @@
 // with the route terms added in route order in FP32 and one BF16 rounding.
 //
 // Work split.  One workgroup (four waves) owns 32 output columns.  It first
-// copies every valid route's intermediate row and row scales into LDS
-// (indexed by route, found through the route map of the gate/up stage), then
+// puts every valid route's intermediate row and row scales into LDS, indexed
+// by route: copied from the FP8 rows of the gate/up stage (each route's plan
+// row from that stage's route map), or -- after the column-slice gate/up,
+// which leaves FP32 SwiGLU rows -- requantised from those (each route's plan
+// row from a scan of the plan); then it
 // walks every plan block below num_tokens_post_padded: wave w takes the
 // blocks of parity w / 2 and the 16 columns of half w % 2.  Per block a wave
 // multiplies the block's W2 slab (its expert's 16 rows of W2 for those
@@ -51,28 +54,41 @@ constexpr int kSlabInstr = kSlabBytes / 1024;          // 16-byte DMA per lane
 constexpr int kStageBytes = kSlabBytes + 128;          // + [16] route ids, expert id, W2 scales
 constexpr int kPerStage = kSlabInstr + 1;
 constexpr int64_t kMaxRoutes = 192;                    // routes whose rows fit in LDS
+constexpr int kScan = 12;                              // plan entries per thread loaded up front
 static_assert((kStages - 2) * kPerStage < 64, "vmcnt range");
 
 // LDS carve-up after the rings ([kWaves][kStages] stages): intermediate rows
 // by route [R][kIB], their scales [R][kNJB], the results [R + 1][kWGCols]
-// (FP32; row R takes the rows that hold no route), route valid flags [R].
-// At R = 192: 160064 bytes.
+// (FP32; row R takes the rows that hold no route), each route's plan row
+// [R] (-1: masked).  At R = 192: 160832 bytes.
 struct DCLayout {
-    int h, hs, y, valid, total;
+    int h, hs, y, rp, total;
     __host__ __device__ explicit DCLayout(int R) {
         h = kWaves * kStages * kStageBytes;
         hs = h + R * kIB;
         y = hs + ((R * kNJB * 4 + 15) & ~15);            // 16-byte rows of results
-        valid = y + (R + 1) * kWGCols * 4;
-        total = valid + ((R + 15) & ~15);
+        rp = y + (R + 1) * kWGCols * 4;
+        total = rp + R * 4;
     }
 };
+static_assert(kWaves * kStages * kStageBytes + kMaxRoutes * (kIB + kNJB * 4 + kWGCols * 4 + 4) +
+                  kWGCols * 4 <= 160 * 1024, "LDS budget at the route limit");
 
 typedef const __attribute__((address_space(4))) int32_t *const_i32_p;
 
-template <int BM, bool E8M0>
+// Workgroup barrier that waits for this wave's LDS (and scalar) accesses
+// only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0), vmcnt / expcnt at maximum
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int BM, bool E8M0, bool RQ>
 __global__ void __launch_bounds__(64 * kWaves, 1)
-down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restrict__ out) {
+down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
+                 uint16_t *__restrict__ out) {
     static_assert(BM <= 16, "one 16-row MFMA tile per plan block");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int R = (int)a.R;
@@ -80,7 +96,7 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restr
     uint8_t *sH = smem + L.h;
     float *sHs = reinterpret_cast<float *>(smem + L.hs);
     float *sY = reinterpret_cast<float *>(smem + L.y);
-    uint8_t *sValid = smem + L.valid;
+    int *sRp = reinterpret_cast<int *>(smem + L.rp);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -95,33 +111,6 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restr
     int nb = ntp / BM;
     nb = nb < a.nblocks ? nb : a.nblocks;
 
-    // ---- every valid route's intermediate row and row scales into LDS, by
-    // route (the route map of the gate/up stage gives each route's plan row,
-    // -1 if masked): first the map itself, then direct global->LDS copies,
-    // four routes (1 KB) per instruction, chunk c of route r's row at LDS
-    // chunk c ^ (r & 15); masked routes copy plan row 0 and stay flagged off
-    int *sRp = reinterpret_cast<int *>(smem);           // (in the rings, before any refill)
-    for (int r = tid; r < R; r += 64 * kWaves) {
-        const int p = rpos[r];
-        sRp[r] = p >= 0 ? p : 0;
-        sValid[r] = p >= 0 ? 1 : 0;
-    }
-    __syncthreads();
-    for (int r0 = 4 * w; r0 < R; r0 += 4 * kWaves) {
-        const int r = r0 + (lane >> 4);
-        if (r < R) {
-            const int p = sRp[r];
-            lds_dma16(a.hq + (int64_t)p * kIB + ((l16 ^ (r & 15)) * 16), sH + (int64_t)r0 * kIB);
-        }
-    }
-    for (int q0 = 64 * w; q0 < R * kNJB; q0 += 64 * kWaves) {
-        const int q = q0 + lane;                         // route q / kNJB, K-block q % kNJB
-        if (q < R * kNJB) lds_dma4(a.hs + (int64_t)sRp[q / kNJB] * kNJB + q % kNJB, sHs + q0);
-    }
-    // every wave's copies have landed and every read of the map is done
-    // before the rings (which overwrite the map) start
-    wait_vmcnt<0>();
-    __syncthreads();
     uint8_t *ring = smem + w * kStages * kStageBytes;
 
     // ---- this wave's blocks: b = 2 i + parity, i < nw
@@ -184,6 +173,103 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restr
         *reinterpret_cast<v4f *>(sY + (ok ? r : R) * kWGCols + half * kCW + 4 * g) = acc;
     };
 
+    // ---- every valid route's intermediate row and row scales into LDS, by
+    // route
+    if constexpr (RQ) {
+        // ---- each route's plan row from a scan of the plan (a valid route
+        // sits in exactly one plan row; routes not found are masked).  The
+        // first kScan x 256 entries are loaded before num_tokens_post_padded
+        // is known (entries at or beyond it are dropped afterwards), so the
+        // two loads overlap; the barrier between waits for LDS only.
+        const int cap = a.nblocks * BM;
+        int rv[kScan];
+#pragma unroll
+        for (int u = 0; u < kScan; ++u) {
+            const int p = u * 64 * kWaves + tid;
+            rv[u] = p < cap ? a.sorted[p] : -1;
+        }
+        for (int r = tid; r < R; r += 64 * kWaves) sRp[r] = -1;
+        lds_barrier();
+        const int lim = nb * BM;
+#pragma unroll
+        for (int u = 0; u < kScan; ++u) {
+            const int p = u * 64 * kWaves + tid;
+            if (p < lim && rv[u] >= 0 && rv[u] < R) sRp[rv[u]] = p;
+        }
+        for (int p = kScan * 64 * kWaves + tid; p < lim; p += 64 * kWaves) {
+            const int r = a.sorted[p];
+            if (r >= 0 && r < R) sRp[r] = p;
+        }
+        __syncthreads();
+        // ---- the FP32 SwiGLU rows requantised into LDS by route: a wave per
+        // route, lane l holds columns 4 l .. 4 l + 3, 32 lanes per 128-column
+        // group (the group maximum over them), four routes' loads in flight
+        const bool ue = rq.ue8m0 != 0;
+        const int jb = lane >> 5;
+        for (int r0 = w; r0 < R; r0 += 4 * kWaves) {
+            v4f v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + u * kWaves;
+                v[u] = v4f{0.f, 0.f, 0.f, 0.f};
+                if (r < R && sRp[r] >= 0)
+                    v[u] = *reinterpret_cast<const v4f *>(rq.h32 + (int64_t)sRp[r] * kIB + 4 * lane);
+            }
+            // the four routes' group maxima side by side (independent shuffles)
+            float amax[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                amax[u] = fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3])));
+#pragma unroll
+            for (int m = 1; m < 32; m *= 2)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) amax[u] = wave_max_xor(amax[u], m);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + u * kWaves;
+                float sc, inv;
+                group_scale(amax[u], ue, sc, inv);
+                const uint32_t code = pack_e4m3x4(v[u][0] * inv, v[u][1] * inv, v[u][2] * inv, v[u][3] * inv);
+                if (r < R && sRp[r] >= 0) {
+                    // byte 4 l of the row: chunk l / 4, stored at chunk (l / 4) ^ (r & 15)
+                    *reinterpret_cast<uint32_t *>(sH + r * kIB + (((lane >> 2) ^ (r & 15)) << 4) + 4 * (lane & 3)) = code;
+                    if ((lane & 31) == 0) sHs[r * kNJB + jb] = sc;
+                    if (blockIdx.x == 0) {
+                        const int64_t p = sRp[r];
+                        *reinterpret_cast<uint32_t *>(rq.hq + p * kIB + 4 * lane) = code;
+                        if ((lane & 31) == 0) rq.hs[p * kNJB + jb] = sc;
+                    }
+                }
+            }
+        }
+        __syncthreads();                                // rows in; the map's reads done
+    } else {
+        // ---- every valid route's FP8 row and row scales copied into LDS, by
+        // route: the route map of the gate/up stage gives each route's plan
+        // row (-1: masked), then direct global->LDS copies, four routes (1 KB)
+        // per instruction, chunk c of route r's row at LDS chunk c ^ (r & 15);
+        // masked routes copy plan row 0 and stay masked
+        for (int r = tid; r < R; r += 64 * kWaves) sRp[r] = rpos[r];
+        __syncthreads();
+        for (int r0 = 4 * w; r0 < R; r0 += 4 * kWaves) {
+            const int r = r0 + (lane >> 4);
+            if (r < R) {
+                const int p = sRp[r];
+                lds_dma16(a.hq + (int64_t)(p >= 0 ? p : 0) * kIB + ((l16 ^ (r & 15)) * 16),
+                          sH + (int64_t)r0 * kIB);
+            }
+        }
+        for (int q0 = 64 * w; q0 < R * kNJB; q0 += 64 * kWaves) {
+            const int q = q0 + lane;                     // route q / kNJB, K-block q % kNJB
+            if (q < R * kNJB) {
+                const int p = sRp[q / kNJB];
+                lds_dma4(a.hs + (int64_t)(p >= 0 ? p : 0) * kNJB + q % kNJB, sHs + q0);
+            }
+        }
+        wait_vmcnt<0>();                                 // every wave's copies have landed
+        __syncthreads();
+    }
+
     // this wave's blocks i, slots i % kStages; kStages - 1 blocks in flight
     // ahead of the one being multiplied (loads complete in issue order)
     for (int q = 0; q < kStages - 1; ++q)
@@ -223,23 +309,31 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, uint16_t *__restr
         float s = 0.f;
         for (int j = 0; j < a.top_k; ++j) {
             const int r = t * a.top_k + j;
-            if (sValid[r]) s += a.topk_w[r] * sY[r * kWGCols + col];
+            if (sRp[r] >= 0) s += a.topk_w[r] * sY[r * kWGCols + col];
         }
         uint16_t *op = out + (int64_t)t * K + cw0 + col;
         *op = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(*op) + s);
     }
 }
 
-template <int BM, bool E8M0>
-hipError_t launch_dc(const DownArgs &a, const int32_t *rpos, uint16_t *out, hipStream_t st) {
+template <int BM, bool E8M0, bool RQ>
+hipError_t launch_dc(const DownArgs &a, const int32_t *rpos, const ColsRequant &rq, uint16_t *out,
+                     hipStream_t st) {
     const int64_t grid = a.K / kWGCols;
     if (grid == 0 || a.nblocks == 0) return hipSuccess;
     const int smem = DCLayout((int)a.R).total;
     static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0>, 160 * 1024);
+    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0, RQ>, 160 * 1024);
     if (e != hipSuccess) return e;
-    down_cols_kernel<BM, E8M0><<<(unsigned)grid, 64 * kWaves, smem, st>>>(a, rpos, out);
+    down_cols_kernel<BM, E8M0, RQ><<<(unsigned)grid, 64 * kWaves, smem, st>>>(a, rpos, rq, out);
     return hipGetLastError();
+}
+
+template <int BM, bool E8M0>
+hipError_t launch_dc_src(const DownArgs &a, const int32_t *rpos, const ColsRequant &rq,
+                         uint16_t *out, hipStream_t st) {
+    return rq.h32 ? launch_dc<BM, E8M0, true>(a, rpos, rq, out, st)
+                  : launch_dc<BM, E8M0, false>(a, rpos, rq, out, st);
 }
 
 }  // namespace
@@ -249,10 +343,13 @@ bool down_cols_fits(int64_t R, int64_t I, int64_t K, int block_m) {
 }
 
 hipError_t launch_down_cols(const DownArgs &a, int block_m, bool e8m0, const int32_t *rpos,
-                            uint16_t *out, hipStream_t st) {
+                            const ColsRequant &rq, uint16_t *out, hipStream_t st) {
     if (!down_cols_fits(a.R, a.I, a.K, block_m)) return hipErrorInvalidValue;
-    if (block_m == 8) return e8m0 ? launch_dc<8, true>(a, rpos, out, st) : launch_dc<8, false>(a, rpos, out, st);
-    return e8m0 ? launch_dc<16, true>(a, rpos, out, st) : launch_dc<16, false>(a, rpos, out, st);
+    if (rq.h32 && (!rq.hq || !rq.hs)) return hipErrorInvalidValue;
+    if (!rq.h32 && !rpos) return hipErrorInvalidValue;
+    if (block_m == 8)
+        return e8m0 ? launch_dc_src<8, true>(a, rpos, rq, out, st) : launch_dc_src<8, false>(a, rpos, rq, out, st);
+    return e8m0 ? launch_dc_src<16, true>(a, rpos, rq, out, st) : launch_dc_src<16, false>(a, rpos, rq, out, st);
 }
 
 }  // namespace moe

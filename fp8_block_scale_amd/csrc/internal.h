@@ -108,6 +108,7 @@ struct GateUpArgs {
     int kb_per_split;
     int inter_ue8m0;
     int w13_packed;     // w13 in the tile layout of moe_prepack_w13 (kPackedTile bytes per K-block)
+    float *h32;         // FP32 SwiGLU rows [plan row, I] (the column-slice gate/up only)
 };
 
 // The packed W13 layout (moe_prepack_w13): per (expert, 128-column tile,
@@ -196,11 +197,29 @@ hipError_t launch_down_pipe_w4(const DownArgs &a, int block_m, bool small, hipSt
 hipError_t launch_down_pipe(const DownArgs &a, int block_m, bool e8m0, bool small, hipStream_t st);
 // Small route counts (down_cols.hip): one workgroup per 32 output columns
 // over every plan block, the route sum in the same launch (no y, no
-// finalize); reads each route's plan row from rpos (the gate/up stage's route
-// map).  down_cols_fits: I = 256, block_m 8 or 16, 1 <= R <= 192.
+// finalize).  down_cols_fits: I = 256, block_m 8 or 16, 1 <= R <= 192.
+// Two sources of the intermediate rows:
+//   rq.h32 == nullptr: the FP8 rows h_q / h_s of the gate/up stage, each
+//     route's plan row read from rpos (that stage's route map);
+//   rq.h32 != nullptr: the FP32 SwiGLU rows of the column-slice gate/up,
+//     requantised here (128-column groups, FP32 or power-of-two rule by
+//     rq.ue8m0) with the routes' plan rows found by scanning the plan;
+//     workgroup 0 also stores the codes and scales to rq.hq / rq.hs.
+struct ColsRequant {
+    const float *h32;
+    uint8_t *hq;
+    float *hs;
+    int ue8m0;
+};
 bool down_cols_fits(int64_t R, int64_t I, int64_t K, int block_m);
 hipError_t launch_down_cols(const DownArgs &a, int block_m, bool e8m0, const int32_t *rpos,
-                            uint16_t *out, hipStream_t st);
+                            const ColsRequant &rq, uint16_t *out, hipStream_t st);
+// The gate/up split over slices of 8 or 16 intermediate columns
+// (gateup_slices.hip): one workgroup per (plan block, slice), K split over its
+// eight waves and added in LDS; writes FP32 SwiGLU rows to a.h32 (rows that
+// hold no route untouched), nothing else -- no route map, no counters.
+// block_m 8 or 16, I % 16 == 0.
+hipError_t launch_gateup_slices(const GateUpArgs &a, int block_m, int slice, hipStream_t st);
 // The single-launch path (fused.hip): steps 3-5 over the arguments of both
 // stages.  Needs I / 128 <= fused_max_njb(block_m).
 int fused_max_njb(int block_m);

@@ -111,11 +111,17 @@ enum {
  * and of the down stage: MOE_PATH_AUTO (0), MOE_PATH_STREAM (1: per plan
  * block, the weights streamed once per block), MOE_PATH_PERSISTENT (2:
  * persistent workgroups over row tiles of one expert; needs K, I <= 32768
- * and, for the gate/up, no forced split-K) or, for the down stage only,
- * MOE_PATH_COLUMNS (3: one workgroup per 16 output columns over every plan
- * block, the route sum in the same launch; needs I = 256, block_m 8 or 16
- * and M * top_k <= 192, else MOE_ERR_UNSUPPORTED; FP8 weights only).  A
- * tuning and test override; the same value must be given to
+ * and, for the gate/up, no forced split-K) or MOE_PATH_COLUMNS (3; needs
+ * I = 256, block_m 8 or 16 and M * top_k <= 192, else MOE_ERR_UNSUPPORTED;
+ * FP8 weights only).  For the down stage, MOE_PATH_COLUMNS is one workgroup
+ * per 32 output columns over every plan block, the route sum in the same
+ * launch.  For the gate/up it is one workgroup per (plan block, 16
+ * intermediate columns) with K split inside the workgroup: it writes FP32
+ * SwiGLU rows that the column-split down requantises as it reads them, so
+ * it needs that down stage (down path AUTO or COLUMNS), exact products (no
+ * MOE_F_FP8_GATEUP), unpacked W13 and no forced split-K, else
+ * MOE_ERR_SHAPE; on that path h_q / h_s are written by moe_fp8_down_reduce.
+ * A tuning and test override; the same value must be given to
  * moe_fp8_experts_workspace_size.  Other values: MOE_ERR_SHAPE. */
 #define MOE_F_GATEUP_PATH_SHIFT 16
 #define MOE_F_GATEUP_PATH_MASK  0x30000u
@@ -251,15 +257,16 @@ size_t moe_fp8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E
 
 /* Byte offsets inside that workspace of the intermediate codes
  * h_q [sorted_cap, I] (E4M3, indexed by plan row) and their scales
- * h_s [sorted_cap, I/128] (FP32); valid after a call, for inspection. */
+ * h_s [sorted_cap, I/128] (FP32); valid after a call of moe_fp8_experts (or
+ * of both stages), for inspection. */
 moe_status moe_fp8_experts_workspace_layout(int64_t M, int64_t K, int64_t I, int32_t E,
                                             int32_t top_k, int32_t block_m,
                                             int64_t sorted_cap, uint32_t flags,
                                             size_t *h_q_offset, size_t *h_s_offset);
 
 /* The launch schedule moe_fp8_experts would use for these sizes and flags
- * (host only, nothing enqueued): info[0] = 1 if the gate/up stage runs the
- * persistent kernel, info[1] = the down stage's kernel (0 per plan block,
+ * (host only, nothing enqueued): info[0] = the gate/up stage's kernel (0 per
+ * plan block, 1 persistent, 2 split over intermediate-column slices), info[1] = the down stage's kernel (0 per plan block,
  * 1 persistent, 2 split over output columns with the route sum), info[2] = the
  * gate/up split-K factor, info[3] = K-blocks (of 128) per split, info[4] =
  * 1 if steps 3-5 run as the single launch.  info is host memory of 5
@@ -303,7 +310,9 @@ moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s,
  * separately (moe_fp8_experts = moe_fp8_gate_up then moe_fp8_down_reduce on
  * one stream, same workspace and flags):
  *   moe_fp8_gate_up      steps 3-4: writes the requantised SwiGLU rows h_q and
- *                        their scales h_s into the workspace;
+ *                        their scales h_s into the workspace (with the
+ *                        column-slice gate/up: the FP32 SwiGLU rows, which
+ *                        the down stage requantises);
  *   moe_fp8_down_reduce  step 5: reads them (and the work list the gate/up
  *                        stage leaves in the workspace), adds the weighted
  *                        down projections into out_bf16.

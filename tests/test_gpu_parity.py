@@ -304,14 +304,16 @@ PERSIST = ((moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT)
            | (moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT))
 
 
-@pytest.mark.parametrize("name,M,flags", [("decode", None, 0), ("decode", 16, FUSE_ON),
-                                          ("page1", 512, 0), ("page1", 512, PERSIST)])
+@pytest.mark.parametrize("name,M,flags", [("tiny", None, 0), ("decode", None, 0),
+                                          ("decode", 16, FUSE_ON), ("page1", 512, 0),
+                                          ("page1", 512, PERSIST)])
 def test_graph_replay_matches_eager(name, M, flags):
-    """The whole layer captured in a HIP graph (small-grid kernels for decode,
-    and steps 3-5 as one launch at decode M=16; at M=512 the per-block
-    gate/up with the persistent down, then both persistent kernels): every
-    replay, with eager work and synchronisations between replays, gives the
-    eager output bit for bit."""
+    """The whole layer captured in a HIP graph (the column-slice gate/up and
+    the column-split down for tiny, the split-K gate/up and the column-split
+    down for decode, steps 3-5 as one launch at decode M=16; at M=512 the
+    per-block gate/up with the persistent down, then both persistent
+    kernels): every replay, with eager work and synchronisations between
+    replays, gives the eager output bit for bit."""
     cs = case_of(name, M=M)
     log(f"[graph] {name} M={cs.M} flags={flags:#x}")
     b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, flags, DEV)
@@ -560,6 +562,56 @@ def test_column_down_skew(dt):
     cfg = dict(CONFIGS["skew"], M=18, I=256, block_m=16, seed=44)
     cs = make_case("skew-i256", device=DEV, config=cfg, ids_dtype=dt)
     full_parity(cs, flags=COLS, label=f"column down skew {dt}")
+
+
+# The gate/up split over 16-column slices of the intermediate (K split over
+# the eight waves of a workgroup, FP32 SwiGLU rows out, no split-K counters
+# and no clearing launch), whose rows the column-split down requantises as it
+# loads them.  Same cases as above; the intermediate codes compared are the
+# ones the down stage writes back.
+SLICES = (moe.MOE_PATH_COLUMNS << moe.MOE_F_GATEUP_PATH_SHIFT) | COLS
+
+
+@pytest.mark.parametrize("name,M,bm", [("tiny", None, 16), ("tiny", None, 8), ("decode", 1, 16),
+                                       ("decode", 2, 8), ("decode", 4, 16), ("decode", 21, 8),
+                                       ("decode", 12, 16)])
+def test_column_gateup(name, M, bm):
+    cs = case_of(name, M=M, block_m=bm)
+    cap = moe.moe_plan_capacity(cs.M, cs.top_k, cs.E, cs.block_m)[0]
+    assert moe.moe_fp8_experts_schedule(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, cap,
+                                        SLICES)[:3] == (2, 2, 1)
+    full_parity(cs, flags=SLICES, label=f"column gate/up bm={bm}")
+
+
+def test_column_gateup_scales():
+    """Power-of-two intermediate scales (the requantisation's other rule),
+    then with them inside the down stage's MFMA."""
+    cs = case_of("decode", M=3, block_m=16)
+    full_parity(cs, flags=SLICES | moe.MOE_F_INTER_UE8M0, label="column gate/up ue8m0 rule")
+    cfg = dict(CONFIGS["zipf"], M=24, E=16, K=1024, I=256, top_k=6, block_m=16, seed=45)
+    cz = make_case("zipf-i256", device=DEV, config=cfg)
+    full_parity(cz, flags=SLICES | E8, act_mode=SCALE_UE8M0, label="column gate/up e8m0")
+
+
+@pytest.mark.parametrize("dt", [torch.int32, torch.int64])
+def test_column_gateup_skew(dt):
+    cfg = dict(CONFIGS["skew"], M=18, I=256, block_m=16, seed=46)
+    cs = make_case("skew-i256", device=DEV, config=cfg, ids_dtype=dt)
+    full_parity(cs, flags=SLICES, label=f"column gate/up skew {dt}")
+
+
+def test_column_gateup_matches_stream():
+    """Against the per-block gate/up on the same plan: the intermediate
+    codes agree to the same bar as against the oracle (only the FP32
+    summation order differs), and so do the outputs."""
+    cs = case_of("decode", M=8, block_m=16)
+    a = run_gpu(cs, flags=SLICES)
+    b = run_gpu(cs, flags=COLS | (moe.MOE_PATH_STREAM << moe.MOE_F_GATEUP_PATH_SHIFT))
+    assert a.P == b.P and np.array_equal(a.sorted[:a.P], b.sorted[:b.P])
+    s = a.sorted[:a.P]
+    rows = (s >= 0) & (s < cs.M * cs.top_k)
+    compare_intermediate(a.h_q[:a.P], a.h_s[:a.P], b.h_q[:b.P], b.h_s[:b.P], rows)
+    compare_output(a.out, b.out)
 
 
 # ------------------------------------------------- steps 3-5 in one launch

@@ -163,7 +163,9 @@ def test_experts_schedule():
     assert sched(4, 7168, 256, 257, 9, 16, 576)[:2] == (False, COLS)
     assert sched(16, 7168, 256, 257, 9, 16, 2304)[:2] == (False, COLS)
     assert sched(21, 7168, 256, 257, 9, 8, 2304)[1] == COLS          # 189 routes
-    assert sched(4, 256, 256, 8, 2, 16, 128)[1] == COLS              # the tiny workload
+    # the tiny workload (K = 256, 8 routes): the column-slice gate/up too
+    assert sched(4, 256, 256, 8, 2, 16, 128)[:3] == (2, COLS, 1)
+    assert sched(4, 256, 256, 8, 2, 16, 128, 1 << GU)[:2] == (0, COLS)
     assert sched(32, 7168, 256, 257, 9, 16, 4608)[:2] == (False, PERS)  # 288 routes
     assert sched(16, 7168, 256, 257, 9, 32, 4608)[1] == PERS         # block_m 32
     # forced: the per-block or the persistent down; the column split past
@@ -174,6 +176,23 @@ def test_experts_schedule():
     with pytest.raises(moe.MoeError) as ei:                          # 216 routes
         sched(24, 7168, 256, 257, 9, 16, 4608, 3 << DN)
     assert moe.STATUS_NAMES[ei.value.status] == "MOE_ERR_UNSUPPORTED"
+    # the column-slice gate/up (2): no split-K, with the column-split down
+    # only; refused with another down path, FP8 products, packed W13 or a
+    # forced split-K factor, and past 192 routes
+    SLICES = 2
+    assert sched(1, 7168, 256, 257, 9, 16, 144, 3 << GU)[:4] == (SLICES, COLS, 1, 56)
+    assert sched(4, 7168, 256, 257, 9, 8, 576, (3 << GU) | (3 << DN))[:2] == (SLICES, COLS)
+    for bad in ((3 << GU) | (1 << DN), (3 << GU) | (2 << DN), (3 << GU) | moe.MOE_F_FP8_GATEUP,
+                (3 << GU) | moe.MOE_F_W13_PACKED, (3 << GU) | (4 << moe.MOE_F_SPLITK_SHIFT)):
+        with pytest.raises(moe.MoeError) as ei:
+            sched(1, 7168, 256, 257, 9, 16, 144, bad)
+        assert moe.STATUS_NAMES[ei.value.status] == "MOE_ERR_SHAPE", hex(bad)
+    with pytest.raises(moe.MoeError) as ei:
+        sched(24, 7168, 256, 257, 9, 16, 4608, 3 << GU)
+    assert moe.STATUS_NAMES[ei.value.status] == "MOE_ERR_UNSUPPORTED"
+    # its FP32 rows take sorted_cap x I x 4 more bytes of workspace
+    ws = moe.moe_fp8_experts_workspace_size
+    assert ws(1, 7168, 256, 257, 9, 16, 144, 3 << GU) >= 144 * 256 * 4
     # page-1 M=16 and M=1024: per-block gate/up, persistent down
     assert sched(16, 4096, 1024, 288, 8, 64, 8192)[:2] == (False, True)
     assert sched(1024, 4096, 1024, 288, 8, 64, 26368)[:2] == (False, True)
@@ -192,8 +211,8 @@ def test_experts_schedule():
     assert sched(16, 4096, 1024, 288, 8, 64, 8192, 1 << DN)[:2] == (False, False)
     assert sched(4096, 4096, 1024, 288, 8, 64, 50944, (1 << GU) | (1 << DN))[:2] == (False, False)
     # a forced split-K factor selects the per-block gate/up
-    assert sched(4096, 4096, 1024, 288, 8, 64, 50944, 2 << moe.MOE_F_SPLITK_SHIFT)[0] is False
-    for bad, status in ((3 << GU, "MOE_ERR_SHAPE"), (3 << DN, "MOE_ERR_UNSUPPORTED"),
+    assert sched(4096, 4096, 1024, 288, 8, 64, 50944, 2 << moe.MOE_F_SPLITK_SHIFT)[0] == 0
+    for bad, status in ((3 << GU, "MOE_ERR_UNSUPPORTED"), (3 << DN, "MOE_ERR_UNSUPPORTED"),
                         ((2 << GU) | (2 << moe.MOE_F_SPLITK_SHIFT), "MOE_ERR_SHAPE"),
                         (1 << 24, "MOE_ERR_SHAPE"), (3 << FU, "MOE_ERR_SHAPE"),
                         ((2 << FU) | (2 << DN), "MOE_ERR_SHAPE")):
