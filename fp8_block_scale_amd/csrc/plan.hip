@@ -66,15 +66,35 @@ __device__ __forceinline__ void plan_body(const IdT *__restrict__ ids, int64_t R
     const int64_t beg = (int64_t)w * chunk;
     const int64_t end = beg + chunk < R ? beg + chunk : R;
 
-    // ---- pass 1: per-wave histogram
+    // ---- pass 1: per-wave histogram.  The first kKeep groups of 64 routes
+    // keep their keys and match masks in registers for pass 2 (no second
+    // read of the ids, no second set of ballots, for chunks up to 256).
+    auto key_at = [&](int64_t base) {
+        const int64_t r = base + lane;
+        int key = E;
+        if (r < end) {
+            IdT v = ids[r];
+            if (v >= 0 && v < (IdT)E) key = (int)v;
+        }
+        return key;
+    };
+    constexpr int kKeep = 4;
+    int kkey[kKeep];
+    uint64_t kmask[kKeep];
     if (w < nwaves) {
-        for (int64_t base = beg; base < end; base += 64) {
-            int64_t r = base + lane;
-            int key = E;
-            if (r < end) {
-                IdT v = ids[r];
-                if (v >= 0 && v < (IdT)E) key = (int)v;
+#pragma unroll
+        for (int it = 0; it < kKeep; ++it) {
+            const int64_t base = beg + 64 * it;
+            kkey[it] = E;
+            kmask[it] = 0;
+            if (base < end) {
+                kkey[it] = key_at(base);
+                kmask[it] = match_mask(kkey[it], nbits);
+                if (kkey[it] < E && (kmask[it] & lower) == 0) hist[w * E + kkey[it]] += __popcll(kmask[it]);
             }
+        }
+        for (int64_t base = beg + 64 * kKeep; base < end; base += 64) {
+            const int key = key_at(base);
             uint64_t m = match_mask(key, nbits);
             if (key < E && (m & lower) == 0) hist[w * E + key] += __popcll(m);
         }
@@ -128,19 +148,21 @@ __device__ __forceinline__ void plan_body(const IdT *__restrict__ ids, int64_t R
 
     // ---- pass 2: stable scatter
     if (w < nwaves) {
-        for (int64_t base = beg; base < end; base += 64) {
-            int64_t r = base + lane;
-            int key = E;
-            if (r < end) {
-                IdT v = ids[r];
-                if (v >= 0 && v < (IdT)E) key = (int)v;
-            }
-            uint64_t m = match_mask(key, nbits);
+        auto scatter = [&](int64_t base, int key, uint64_t m) {
             if (key < E) {
                 int slot = hist[w * E + key] + __popcll(m & lower);
-                sorted[slot] = (int32_t)r;
+                sorted[slot] = (int32_t)(base + lane);
             }
             if (key < E && (m & lower) == 0) hist[w * E + key] += __popcll(m);
+        };
+#pragma unroll
+        for (int it = 0; it < kKeep; ++it) {
+            const int64_t base = beg + 64 * it;
+            if (base < end) scatter(base, kkey[it], kmask[it]);
+        }
+        for (int64_t base = beg + 64 * kKeep; base < end; base += 64) {
+            const int key = key_at(base);
+            scatter(base, key, match_mask(key, nbits));
         }
     }
 }
