@@ -118,7 +118,7 @@ SplitChoice choose_split(int64_t R, int32_t E, int64_t blocks_cap, int64_t jtile
     // route-sum launch) wherever it applies: measured at the decode shape
     // faster than the per-block and the persistent down at M = 1 .. 16 (down
     // stage 7.4 / 10.3 / 14.2 / 22.2 / 36.7 us at M = 1, 2, 4, 8, 16).
-    c.dn_cols = !w4 && fuse != MOE_FUSE_ON && moe::down_cols_fits(R, I, K, bm) &&
+    c.dn_cols = fuse != MOE_FUSE_ON && moe::down_cols_fits(R, I, K, bm) &&
                 (dn_path == MOE_PATH_COLUMNS || dn_path == MOE_PATH_AUTO);
     if (c.dn_cols) c.dn_persistent = c.dn_small = false;
     // The column-slice gate/up leaves FP32 rows that only the column-split
@@ -798,13 +798,13 @@ moe_status check_w4(int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k, i
                     "W4A8: MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP and MOE_F_W13_PACKED do not apply");
     if (((flags & MOE_F_FUSE_MASK) >> MOE_F_FUSE_SHIFT) == MOE_FUSE_ON)
         return fail(MOE_ERR_UNSUPPORTED, "W4A8 runs as two stages (no MOE_FUSE_ON)");
-    if (((flags & MOE_F_DOWN_PATH_MASK) >> MOE_F_DOWN_PATH_SHIFT) == MOE_PATH_COLUMNS)
-        return fail(MOE_ERR_UNSUPPORTED, "W4A8: the column-split down stage takes FP8 weights only");
+    if (((flags & MOE_F_GATEUP_PATH_MASK) >> MOE_F_GATEUP_PATH_SHIFT) == MOE_PATH_COLUMNS)
+        return fail(MOE_ERR_UNSUPPORTED, "W4A8: the column-slice gate/up takes FP8 weights only");
     st = check_flags(w4_flags(flags), K, I, block_m, M * top_k);
     if (st != MOE_OK) return st;
     // the per-block down kernel keeps a block's intermediate rows in LDS
     const WsLayout l = ws_layout(M, K, I, E, top_k, block_m, sorted_cap, w4_flags(flags), true);
-    if (!l.sp.dn_persistent && I / 128 > moe::down_w4_max_njb(block_m))
+    if (!l.sp.dn_persistent && !l.sp.dn_cols && I / 128 > moe::down_w4_max_njb(block_m))
         return fail(MOE_ERR_UNSUPPORTED,
                     "W4A8 on the per-block down kernel needs I / 128 <= %d at block_m %d",
                     moe::down_w4_max_njb(block_m), block_m);
@@ -868,6 +868,16 @@ MOE_API moe_status moe_w4a8_experts(const uint8_t *x_q, const float *x_s, const 
     moe::DownArgs da = down_args(w2, nullptr, topk_weights, sorted_token_ids, expert_ids,
                                  num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap, ws, l);
     da.w2e = w2_e;
+    if (l.sp.dn_cols) {                        // the route sum is part of this launch
+        moe::ColsRequant rq;
+        rq.h32 = nullptr;
+        rq.hq = nullptr;
+        rq.hs = nullptr;
+        rq.ue8m0 = 0;
+        return hip_check(moe::launch_down_cols(da, block_m, false, (const int32_t *)(ws + l.rpos), rq,
+                                               (uint16_t *)out_bf16, s),
+                         "moe_w4a8_experts: down launch");
+    }
     st = hip_check(l.sp.dn_persistent ? moe::launch_down_pipe_w4(da, block_m, l.sp.dn_small, s)
                                       : moe::launch_down_w4(da, block_m, s),
                    "moe_w4a8_experts: down launch");

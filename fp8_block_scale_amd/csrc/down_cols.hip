@@ -49,29 +49,40 @@ constexpr int kWGCols = 2 * kCW;        // output columns per workgroup
 constexpr int kIB = 256;                // bytes of an intermediate / W2 row (I)
 constexpr int kNJB = kIB / 128;
 constexpr int kStages = 5;
-constexpr int kSlabBytes = kCW * kIB;                  // one block's W2 slab
-constexpr int kSlabInstr = kSlabBytes / 1024;          // 16-byte DMA per lane
-constexpr int kStageBytes = kSlabBytes + 128;          // + [16] route ids, expert id, W2 scales
-constexpr int kPerStage = kSlabInstr + 1;
 constexpr int64_t kMaxRoutes = 192;                    // routes whose rows fit in LDS
 constexpr int kScan = 12;                              // plan entries per thread loaded up front
-static_assert((kStages - 2) * kPerStage < 64, "vmcnt range");
+
+// A ring stage: one block's W2 slab (its expert's 16 rows of the wave's
+// columns, all of I), then -- W4, the E2M1 weights -- the slab rows' K32
+// exponent bytes (8 per row), then 128 bytes of metadata: [16] route ids,
+// the expert id, (FP8) the two W2 block scales.
+template <bool W4>
+struct DCStage {
+    static constexpr int Slab = kCW * kIB / (W4 ? 2 : 1);
+    static constexpr int SlabInstr = Slab / 1024;        // 16-byte DMA per lane
+    static constexpr int Exp = W4 ? kCW * kIB / 32 : 0;
+    static constexpr int Meta = Slab + Exp;
+    static constexpr int Bytes = Meta + 128;
+    static constexpr int PerStage = SlabInstr + (W4 ? 1 : 0) + 1;
+    static_assert((kStages - 2) * PerStage < 64, "vmcnt range");
+};
 
 // LDS carve-up after the rings ([kWaves][kStages] stages): intermediate rows
 // by route [R][kIB], their scales [R][kNJB], the results [R + 1][kWGCols]
 // (FP32; row R takes the rows that hold no route), each route's plan row
 // [R] (-1: masked).  At R = 192: 160832 bytes.
+template <bool W4>
 struct DCLayout {
     int h, hs, y, rp, total;
     __host__ __device__ explicit DCLayout(int R) {
-        h = kWaves * kStages * kStageBytes;
+        h = kWaves * kStages * DCStage<W4>::Bytes;
         hs = h + R * kIB;
         y = hs + ((R * kNJB * 4 + 15) & ~15);            // 16-byte rows of results
         rp = y + (R + 1) * kWGCols * 4;
         total = rp + R * 4;
     }
 };
-static_assert(kWaves * kStages * kStageBytes + kMaxRoutes * (kIB + kNJB * 4 + kWGCols * 4 + 4) +
+static_assert(kWaves * kStages * DCStage<false>::Bytes + kMaxRoutes * (kIB + kNJB * 4 + kWGCols * 4 + 4) +
                   kWGCols * 4 <= 160 * 1024, "LDS budget at the route limit");
 
 typedef const __attribute__((address_space(4))) int32_t *const_i32_p;
@@ -85,14 +96,16 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int BM, bool E8M0, bool RQ>
+template <int BM, bool E8M0, bool RQ, bool W4>
 __global__ void __launch_bounds__(64 * kWaves, 1)
 down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
                  uint16_t *__restrict__ out) {
     static_assert(BM <= 16, "one 16-row MFMA tile per plan block");
+    static_assert(!W4 || (!E8M0 && !RQ), "E2M1 weights: FP8 intermediate rows, FP32 row scales");
+    using SC = DCStage<W4>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int R = (int)a.R;
-    const DCLayout L(R);
+    const DCLayout<W4> L(R);
     uint8_t *sH = smem + L.h;
     float *sHs = reinterpret_cast<float *>(smem + L.hs);
     float *sY = reinterpret_cast<float *>(smem + L.y);
@@ -111,59 +124,85 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
     int nb = ntp / BM;
     nb = nb < a.nblocks ? nb : a.nblocks;
 
-    uint8_t *ring = smem + w * kStages * kStageBytes;
+    uint8_t *ring = smem + w * kStages * SC::Bytes;
 
     // ---- this wave's blocks: b = 2 i + parity, i < nw
     const int nw = (nb - parity + 1) / 2;
     auto issue = [&](int st, int i) {
         const int b = 2 * i + parity;
-        uint8_t *base = ring + st * kStageBytes;
+        uint8_t *base = ring + st * SC::Bytes;
         const int e0 = __builtin_amdgcn_readfirstlane(((const_i32_p)a.eids)[b]);
         const int e = (e0 >= 0 && e0 < a.E) ? e0 : 0;
-        // W2 rows c0 .. c0 + 15 of expert e: LDS slot s (16 bytes) of the slab
-        // holds row s / 16, chunk (s % 16) ^ row
-        const uint8_t *wrow = a.w2 + ((int64_t)e * K + c0) * kIB;
+        if constexpr (W4) {
+            // W2 rows c0 .. c0 + 15 of expert e (128 B of E2M1 pairs each):
+            // LDS slot s (16 bytes) holds row s / 8, chunk (s % 8) ^ (row % 8);
+            // then their exponent dwords, lane l: row l / 2, K-block l % 2
+            const uint8_t *wrow = a.w2 + ((int64_t)e * K + c0) * (kIB / 2);
 #pragma unroll
-        for (int k = 0; k < kSlabInstr; ++k) {
-            const int s = k * 64 + lane;
-            const int row = s >> 4, pos = s & 15;
-            lds_dma16_nt(wrow + (int64_t)row * kIB + (pos ^ row) * 16, base + k * 1024);
+            for (int k = 0; k < SC::SlabInstr; ++k) {
+                const int s = k * 64 + lane;
+                const int row = s >> 3, pos = s & 7;
+                lds_dma16_nt(wrow + (int64_t)row * (kIB / 2) + (pos ^ (row & 7)) * 16, base + k * 1024);
+            }
+            if (lane < 2 * kCW)
+                lds_dma4(a.w2e + ((int64_t)e * K + c0 + (lane >> 1)) * (kIB / 32) + 4 * (lane & 1),
+                         base + SC::Slab);
+        } else {
+            // W2 rows c0 .. c0 + 15 of expert e: LDS slot s (16 bytes) of the
+            // slab holds row s / 16, chunk (s % 16) ^ row
+            const uint8_t *wrow = a.w2 + ((int64_t)e * K + c0) * kIB;
+#pragma unroll
+            for (int k = 0; k < SC::SlabInstr; ++k) {
+                const int s = k * 64 + lane;
+                const int row = s >> 4, pos = s & 15;
+                lds_dma16_nt(wrow + (int64_t)row * kIB + (pos ^ row) * 16, base + k * 1024);
+            }
         }
         // metadata in one 4-byte DMA: lanes 0-15 the route ids, lane 16 the
-        // expert id, lanes 17 .. 16 + kNJB the W2 block scales
+        // expert id, lanes 17 .. 16 + kNJB the W2 block scales (FP8)
         const void *msrc;
         if (lane < 16)
             msrc = a.sorted + (int64_t)b * BM + (lane < BM ? lane : 0);
-        else if (lane == 16)
+        else if (lane == 16 || W4)
             msrc = a.eids + b;
         else
             msrc = a.w2s + ((int64_t)e * (K >> 7) + (c0 >> 7)) * kNJB + (lane < 17 + kNJB ? lane - 17 : 0);
-        if (lane < 17 + kNJB) lds_dma4(msrc, base + kSlabBytes);
+        if (lane < (W4 ? 17 : 17 + kNJB)) lds_dma4(msrc, base + SC::Meta);
     };
 
     auto compute = [&](int st) {
-        const uint8_t *base = ring + st * kStageBytes;
-        const int *meta = reinterpret_cast<const int *>(base + kSlabBytes);
+        const uint8_t *base = ring + st * SC::Bytes;
+        const int *meta = reinterpret_cast<const int *>(base + SC::Meta);
         const int r = meta[l16], e0 = meta[16];
         const bool ok = l16 < BM && r >= 0 && r < R && e0 >= 0 && e0 < a.E;
         const int rr = ok ? r : 0;
         v4f acc = {0.f, 0.f, 0.f, 0.f};
-        const uint8_t *wa = base + l16 * kIB;
         const uint8_t *ha = sH + (int64_t)rr * kIB;
 #pragma unroll
         for (int jb = 0; jb < kNJB; ++jb) {
             const int clo = jb * 8 + g, chi = jb * 8 + 4 + g;
-            const u32x4 a0 = lds_read16(wa + (clo ^ l16) * 16), a1 = lds_read16(wa + (chi ^ l16) * 16);
             const u32x4 b0 = lds_read16(ha + (clo ^ (rr & 15)) * 16);
             const u32x4 b1 = lds_read16(ha + (chi ^ (rr & 15)) * 16);
-            const v8i A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            const float sb = __int_as_float(meta[17 + jb]);
             const float sa = sHs[rr * kNJB + jb];
-            if constexpr (E8M0)
-                acc = mfma16x16x128_e8m0(A, B, acc, e8m0_of(sb), e8m0_of(sa));
-            else
-                acc = mfma16x16x128(A, B) * (sa * sb) + acc;
+            if constexpr (W4) {
+                // lane group g: K [32 g, 32 g + 32) of this K-block, chunk
+                // 4 jb + g of the row, and that group's exponent byte
+                const uint8_t *wa = base + l16 * (kIB / 2);
+                const u32x4 a0 = lds_read16(wa + ((4 * jb + g) ^ (l16 & 7)) * 16);
+                const v8i A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+                const uint32_t ed = *reinterpret_cast<const uint32_t *>(base + SC::Slab + (2 * l16 + jb) * 4);
+                acc = mfma16x16x128_e2m1_e4m3(A, B, (int)((ed >> (8 * g)) & 0xffu)) * sa + acc;
+            } else {
+                const uint8_t *wa = base + l16 * kIB;
+                const u32x4 a0 = lds_read16(wa + (clo ^ l16) * 16), a1 = lds_read16(wa + (chi ^ l16) * 16);
+                const v8i A = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                const float sb = __int_as_float(meta[17 + jb]);
+                if constexpr (E8M0)
+                    acc = mfma16x16x128_e8m0(A, B, acc, e8m0_of(sb), e8m0_of(sa));
+                else
+                    acc = mfma16x16x128(A, B) * (sa * sb) + acc;
+            }
         }
         // lane (row l16, group g) holds columns 4g .. 4g + 3 of its route.
         // Every lane stores (rows without a route to the spare row R): a
@@ -278,11 +317,11 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
         constexpr int ST = decltype(st_c)::value;
         const int ahead = nw - 1 - i;                   // blocks issued past i, at most kStages - 2
         if (ahead >= 3)
-            wait_vmcnt<3 * kPerStage>();
+            wait_vmcnt<3 * SC::PerStage>();
         else if (ahead == 2)
-            wait_vmcnt<2 * kPerStage>();
+            wait_vmcnt<2 * SC::PerStage>();
         else if (ahead == 1)
-            wait_vmcnt<kPerStage>();
+            wait_vmcnt<SC::PerStage>();
         else
             wait_vmcnt<0>();
         // the refill goes into the slot of block i - 1, whose operand reads
@@ -316,24 +355,28 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
     }
 }
 
-template <int BM, bool E8M0, bool RQ>
+template <int BM, bool E8M0, bool RQ, bool W4>
 hipError_t launch_dc(const DownArgs &a, const int32_t *rpos, const ColsRequant &rq, uint16_t *out,
                      hipStream_t st) {
     const int64_t grid = a.K / kWGCols;
     if (grid == 0 || a.nblocks == 0) return hipSuccess;
-    const int smem = DCLayout((int)a.R).total;
+    const int smem = DCLayout<W4>((int)a.R).total;
     static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0, RQ>, 160 * 1024);
+    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0, RQ, W4>, 160 * 1024);
     if (e != hipSuccess) return e;
-    down_cols_kernel<BM, E8M0, RQ><<<(unsigned)grid, 64 * kWaves, smem, st>>>(a, rpos, rq, out);
+    down_cols_kernel<BM, E8M0, RQ, W4><<<(unsigned)grid, 64 * kWaves, smem, st>>>(a, rpos, rq, out);
     return hipGetLastError();
 }
 
-template <int BM, bool E8M0>
-hipError_t launch_dc_src(const DownArgs &a, const int32_t *rpos, const ColsRequant &rq,
-                         uint16_t *out, hipStream_t st) {
-    return rq.h32 ? launch_dc<BM, E8M0, true>(a, rpos, rq, out, st)
-                  : launch_dc<BM, E8M0, false>(a, rpos, rq, out, st);
+template <int BM>
+hipError_t launch_dc_bm(const DownArgs &a, bool e8m0, const int32_t *rpos, const ColsRequant &rq,
+                        uint16_t *out, hipStream_t st) {
+    if (a.w2e) return launch_dc<BM, false, false, true>(a, rpos, rq, out, st);
+    if (rq.h32)
+        return e8m0 ? launch_dc<BM, true, true, false>(a, rpos, rq, out, st)
+                    : launch_dc<BM, false, true, false>(a, rpos, rq, out, st);
+    return e8m0 ? launch_dc<BM, true, false, false>(a, rpos, rq, out, st)
+                : launch_dc<BM, false, false, false>(a, rpos, rq, out, st);
 }
 
 }  // namespace
@@ -342,14 +385,17 @@ bool down_cols_fits(int64_t R, int64_t I, int64_t K, int block_m) {
     return R >= 1 && R <= kMaxRoutes && I == kIB && K % kWGCols == 0 && (block_m == 8 || block_m == 16);
 }
 
+// a.w2e set: the E2M1 weights of the W4A8 variant (w2 holds E2M1 pairs
+// [E, K, I / 2], w2e the K32 exponent bytes [E, K, I / 32]); they take the
+// FP8 intermediate rows through rpos (no requantisation mode, no E8M0 MFMA).
 hipError_t launch_down_cols(const DownArgs &a, int block_m, bool e8m0, const int32_t *rpos,
                             const ColsRequant &rq, uint16_t *out, hipStream_t st) {
     if (!down_cols_fits(a.R, a.I, a.K, block_m)) return hipErrorInvalidValue;
     if (rq.h32 && (!rq.hq || !rq.hs)) return hipErrorInvalidValue;
     if (!rq.h32 && !rpos) return hipErrorInvalidValue;
-    if (block_m == 8)
-        return e8m0 ? launch_dc_src<8, true>(a, rpos, rq, out, st) : launch_dc_src<8, false>(a, rpos, rq, out, st);
-    return e8m0 ? launch_dc_src<16, true>(a, rpos, rq, out, st) : launch_dc_src<16, false>(a, rpos, rq, out, st);
+    if (a.w2e && (rq.h32 || e8m0)) return hipErrorInvalidValue;
+    if (block_m == 8) return launch_dc_bm<8>(a, e8m0, rpos, rq, out, st);
+    return launch_dc_bm<16>(a, e8m0, rpos, rq, out, st);
 }
 
 }  // namespace moe

@@ -118,9 +118,35 @@ def test_scale_spread_within_k_blocks():
 
 
 @pytest.mark.parametrize("M,flags", [(1, 0), (1, SPLIT1), (1, 7 << moe.MOE_F_SPLITK_SHIFT), (4, 0),
-                                     (16, 0)])
+                                     (16, 0), (1, 1 << moe.MOE_F_DOWN_PATH_SHIFT),
+                                     (16, 1 << moe.MOE_F_DOWN_PATH_SHIFT)])
 def test_decode(M, flags):
+    """The decode shape; by default its down stage is the column-split kernel
+    (E2M1 weight slabs, the route sum in the same launch), forced here also
+    onto the per-block down kernel with its finalize."""
     parity(case_of("decode", M=M), flags=flags, label="decode")
+
+
+COLS = moe.MOE_PATH_COLUMNS << moe.MOE_F_DOWN_PATH_SHIFT
+
+
+@pytest.mark.parametrize("name,M,bm", [("tiny", None, 8), ("decode", 2, 8), ("decode", 21, 8),
+                                       ("decode", 12, 16)])
+def test_column_down(name, M, bm):
+    """The column-split down on E2M1 weights, forced: both block sizes, up
+    to 189 routes."""
+    cs = case_of(name, M=M, block_m=bm)
+    parity(cs, flags=COLS, label=f"column down bm={bm}")
+
+
+@pytest.mark.parametrize("dt", [torch.int32, torch.int64])
+def test_column_down_skew(dt):
+    """A skew-like batch at I = 256 on the column-split down: hot experts
+    with several blocks, duplicate experts within a token, 1% masked routes,
+    a zero-scale expert."""
+    cfg = dict(CONFIGS["skew"], M=18, I=256, block_m=16, seed=47)
+    cs = make_case("skew-i256", device=DEV, config=cfg, ids_dtype=dt, fmt="w4a8")
+    parity(cs, flags=COLS, label=f"column down skew {dt}")
 
 
 def test_page1_small():
@@ -209,7 +235,7 @@ def test_rejects_what_does_not_apply():
     out = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
     fuse_on = moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT
     for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0, fuse_on,
-               moe.MOE_F_W13_PACKED):
+               moe.MOE_F_W13_PACKED, moe.MOE_PATH_COLUMNS << moe.MOE_F_GATEUP_PATH_SHIFT):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_w4a8_experts(b.x_q, b.x_s, cs.w13, cs.w13_s, cs.w2, cs.w2_s, cs.topk_weights,
                                  b.sorted_ids, b.expert_ids, b.ntp, cs.top_k, cs.block_m, out,
@@ -217,7 +243,8 @@ def test_rejects_what_does_not_apply():
         assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("name,M,flags", [("decode", 16, 0), ("page1", 512, 0),
+@pytest.mark.parametrize("name,M,flags", [("decode", 16, 0), ("decode", 16, DN_STREAM),
+                                          ("page1", 512, 0),
                                           ("page1", 512, GU_PERSIST | DN_PERSIST)])
 def test_graph_replay_matches_eager(name, M, flags):
     """The W4A8 layer (plan + quantisation + moe_w4a8_experts, per-block and

@@ -308,9 +308,14 @@ def test_w4a8_validation_before_any_device_call():
                  a["E"], a["k"], a["bm"], a["sc"], a["fl"], FAKE, a["ws"], a["wsb"], None)
 
     for fl in (moe.MOE_F_FP8_GATEUP, moe.MOE_F_INTER_UE8M0 | moe.MOE_F_MMA_E8M0,
-               moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT, moe.MOE_F_W13_PACKED):
+               moe.MOE_FUSE_ON << moe.MOE_F_FUSE_SHIFT, moe.MOE_F_W13_PACKED,
+               moe.MOE_PATH_COLUMNS << moe.MOE_F_GATEUP_PATH_SHIFT):
         assert _err(call(fl=fl)) == "MOE_ERR_UNSUPPORTED", fl
         assert moe.moe_w4a8_experts_workspace_size(4, 256, 256, 8, 2, 16, 128, fl) == 0
+    # the column-split down takes E2M1 weights too (at most 192 routes)
+    cols = moe.MOE_PATH_COLUMNS << moe.MOE_F_DOWN_PATH_SHIFT
+    assert moe.moe_w4a8_experts_workspace_size(4, 256, 256, 8, 2, 16, 128, cols) > 0
+    assert moe.moe_w4a8_experts_workspace_size(100, 256, 256, 8, 2, 16, 512, cols) == 0
     # the per-block down kernel keeps a block's intermediate rows in LDS:
     # I / 128 <= 512 / 64 at block_m 64 (unless the down stage is persistent)
     assert _err(call(I=2048, bm=64, sc=128)) == "MOE_ERR_UNSUPPORTED"
