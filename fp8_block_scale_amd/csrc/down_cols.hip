@@ -208,8 +208,12 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
         // Every lane stores (rows without a route to the spare row R): a
         // store under a lane condition would let the compiler move the MFMAs
         // under it, where lanes outside the condition keep stale scale
-        // operands.
-        *reinterpret_cast<v4f *>(sY + (ok ? r : R) * kWGCols + half * kCW + 4 * g) = acc;
+        // operands.  A block whose expert id is out of range adds nothing:
+        // its routes' results are zero (as on the other paths, where such a
+        // block's routes stay masked).
+        const bool routed = l16 < BM && r >= 0 && r < R;
+        if (!(e0 >= 0 && e0 < a.E)) acc = v4f{0.f, 0.f, 0.f, 0.f};    // (uniform per block)
+        *reinterpret_cast<v4f *>(sY + (routed ? r : R) * kWGCols + half * kCW + 4 * g) = acc;
     };
 
     // ---- every valid route's intermediate row and row scales into LDS, by

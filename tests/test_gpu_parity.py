@@ -15,7 +15,7 @@ import torch
 
 import fp8_block_scale_amd as moe
 from moe_workloads import make_case, CONFIGS, SKEW_ZERO_SCALE_EXPERT
-from oracle import e4m3_encode, plan_ref, quant_act_ref, FLT_MIN
+from oracle import e4m3_encode, experts_ref, plan_ref, quant_act_ref, FLT_MIN
 from oracle.quant import SCALE_FP32, SCALE_UE8M0
 
 from parity import (CODE_MISMATCH_MAX, check_plan, check_tail_untouched, compare_intermediate,
@@ -612,6 +612,40 @@ def test_column_gateup_matches_stream():
     rows = (s >= 0) & (s < cs.M * cs.top_k)
     compare_intermediate(a.h_q[:a.P], a.h_s[:a.P], b.h_q[:b.P], b.h_s[:b.P], rows)
     compare_output(a.out, b.out)
+
+
+@pytest.mark.parametrize("flags", [
+    SLICES, COLS | (moe.MOE_PATH_STREAM << moe.MOE_F_GATEUP_PATH_SHIFT),
+    (moe.MOE_PATH_STREAM << moe.MOE_F_GATEUP_PATH_SHIFT) | (moe.MOE_PATH_STREAM << moe.MOE_F_DOWN_PATH_SHIFT),
+    (moe.MOE_PATH_PERSISTENT << moe.MOE_F_GATEUP_PATH_SHIFT)
+    | (moe.MOE_PATH_PERSISTENT << moe.MOE_F_DOWN_PATH_SHIFT)])
+def test_block_with_out_of_range_expert_adds_nothing(flags):
+    """A plan block whose expert id is out of range (a caller's plan, not
+    one moe_plan builds) is skipped by every kernel family: its routes add
+    nothing, the rest of the layer is as the oracle computes it with those
+    routes masked."""
+    cs = case_of("tiny")
+    h = host_inputs(cs)
+    sorted_ref, eids_ref, P = plan_ref(h["ids"], cs.E, cs.block_m)
+    bad = 1                                              # a block that holds routes
+    R = cs.M * cs.top_k
+    assert P >= 2 * cs.block_m and np.any(sorted_ref[bad * cs.block_m:(bad + 1) * cs.block_m] < R)
+    b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, flags, DEV)
+    b.workspace.fill_(0x5A)
+    moe.moe_plan(cs.topk_ids, cs.E, cs.block_m, b.sorted_ids, b.expert_ids, b.ntp, b.plan_ws)
+    moe.moe_quant_act(cs.x, b.x_q, b.x_s, SCALE_FP32)
+    b.expert_ids[bad] = cs.E
+    out = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
+    moe.moe_fp8_experts(b.x_q, b.x_s, cs.w13, cs.w13_s, cs.w2, cs.w2_s, cs.topk_weights,
+                        b.sorted_ids, b.expert_ids, b.ntp, cs.top_k, cs.block_m, out, b.workspace,
+                        flags)
+    torch.cuda.synchronize()
+    masked = sorted_ref.copy()
+    masked[bad * cs.block_m:(bad + 1) * cs.block_m] = R
+    x_q, x_s = quant_act_ref(h["x"], SCALE_FP32)
+    res = experts_ref(x_q, x_s, h["w13"], h["w13_s"], h["w2"], h["w2_s"], h["w"], masked, eids_ref,
+                      P, cs.top_k, cs.block_m)
+    compare_output(out.float().cpu().numpy().astype(np.float64), res.ref64)
 
 
 # ------------------------------------------------- steps 3-5 in one launch
