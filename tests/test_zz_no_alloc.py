@@ -58,3 +58,30 @@ def test_noalloc_matches_workspace_entry_point():
         o = run_oracle(cs)
         st = compare_output(g.float().cpu().numpy().astype(np.float64), o.res.ref64)
         log(f"[noalloc]   M={cs.M} ok: {st}")
+
+
+def test_noalloc_column_slice_path():
+    """The same through the column-slice gate/up and the column-split down
+    (FP32 rows in the scratch, requantised by the down stage): decode M=2,
+    then M=1 on what the first call left."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    flags = ((moe.MOE_PATH_COLUMNS << moe.MOE_F_GATEUP_PATH_SHIFT)
+             | (moe.MOE_PATH_COLUMNS << moe.MOE_F_DOWN_PATH_SHIFT))
+    first = make_case("decode", M=2, device=DEV)
+    w = (first.w13, first.w13_s, first.w2, first.w2_s)
+    second = make_case("decode", M=1, device=DEV, weights=w)
+    calls = [(first, flags), (second, flags)]
+    bufs = [_prepare(cs, fl) for cs, fl in calls]
+    refs = [_experts(cs, b, fl, noalloc=False) for (cs, fl), b in zip(calls, bufs)]
+    torch.cuda.synchronize()
+    got = []
+    for (cs, fl), b in zip(calls, bufs):
+        log(f"[noalloc] column slices decode M={cs.M} flags={fl:#x}")
+        got.append(_experts(cs, b, fl, noalloc=True))
+    torch.cuda.synchronize()
+    for (cs, fl), r, g in zip(calls, refs, got):
+        assert torch.equal(g, r), f"M={cs.M}: no-alloc output differs from the workspace call"
+        o = run_oracle(cs)
+        st = compare_output(g.float().cpu().numpy().astype(np.float64), o.res.ref64)
+        log(f"[noalloc]   M={cs.M} ok: {st}")
