@@ -33,7 +33,12 @@
 // waits are each wave's own load counts.  FP8 MFMA
 // (v_mfma_f32_16x16x128_f8f6f4) with the FP32 scale product applied per
 // 128-deep K-block, or with power-of-two scales as E8M0 exponents inside the
-// MFMA.
+// MFMA.  With E2M1 weights (the W4A8 variant, sglang-glm53-flash-sm120 PR
+// #13, description) a stage holds the slab's E2M1 pairs and their K32
+// exponent bytes, and the mixed E2M1 x E4M3 MFMA takes each K32 group's
+// exponent as the weight operand's E8M0 scale:
+//   y[r, c] = sum_jb h_s[p, jb] * sum_{q in jb} 2^(w2_e[e, c, q] - 127)
+//                  * sum_{i in q} h_q[p, i] * W2[e, c, i]               (FP32)
 #include <type_traits>
 
 #include "common.h"
