@@ -112,15 +112,17 @@ enum {
  * block, the weights streamed once per block), MOE_PATH_PERSISTENT (2:
  * persistent workgroups over row tiles of one expert; needs K, I <= 32768
  * and, for the gate/up, no forced split-K) or MOE_PATH_COLUMNS (3; needs
- * I = 256, block_m 8 or 16 and M * top_k <= 192, else MOE_ERR_UNSUPPORTED;
- * FP8 weights only).  For the down stage, MOE_PATH_COLUMNS is one workgroup
- * per 32 output columns over every plan block, the route sum in the same
- * launch.  For the gate/up it is one workgroup per (plan block, 16
- * intermediate columns) with K split inside the workgroup: it writes FP32
+ * I = 256, block_m 8 or 16 and M * top_k <= 192, else MOE_ERR_UNSUPPORTED).
+ * For the down stage, MOE_PATH_COLUMNS is one workgroup per 32 output
+ * columns over every plan block, the route sum in the same launch.  For the
+ * gate/up it is one workgroup per (plan block, 16 intermediate columns)
+ * with K split inside the workgroup: it writes FP32
  * SwiGLU rows that the column-split down requantises as it reads them, so
  * it needs that down stage (down path AUTO or COLUMNS), exact products (no
  * MOE_F_FP8_GATEUP), unpacked W13 and no forced split-K, else
  * MOE_ERR_SHAPE; on that path h_q / h_s are written by moe_fp8_down_reduce.
+ * The W4A8 entry point takes the column-split down (E2M1 weights) but not
+ * the column-slice gate/up.
  * A tuning and test override; the same value must be given to
  * moe_fp8_experts_workspace_size.  Other values: MOE_ERR_SHAPE. */
 #define MOE_F_GATEUP_PATH_SHIFT 16
@@ -376,13 +378,14 @@ moe_status moe_prepack_w13(const uint8_t *w13, int64_t E, int64_t I, int64_t K,
  * Gate/up products are exact (FP16 MFMA on widened codes, FP32 sums) while
  * the four K32 exponents of a weight row within each 128-wide K-block span
  * at most 23; beyond that the smaller groups' products round to FP16.
- * Each stage runs the per-block or the persistent kernel family, chosen
- * (or forced by flag bits 16-19) as for moe_fp8_experts.  Constraints:
- * those of moe_fp8_experts; w13 / w2 16-byte and w13_e / w2_e 4-byte
- * aligned; when the down stage runs the per-block kernel, I / 128 <=
- * 512 / min(max(block_m, 16), 64).  Flags MOE_F_INTER_UE8M0, a forced
- * split-K and the path bits apply; MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP,
- * MOE_FUSE_ON and MOE_F_W13_PACKED give MOE_ERR_UNSUPPORTED.  The workspace is sized by
+ * Each stage runs the per-block or the persistent kernel family, and the
+ * down stage also the column split, chosen (or forced by flag bits 16-19)
+ * as for moe_fp8_experts.  Constraints: those of moe_fp8_experts; w13 / w2
+ * 16-byte and w13_e / w2_e 4-byte aligned; when the down stage runs the
+ * per-block kernel, I / 128 <= 512 / min(max(block_m, 16), 64).  Flags
+ * MOE_F_INTER_UE8M0, a forced split-K and the path bits apply;
+ * MOE_F_MMA_E8M0, MOE_F_FP8_GATEUP, MOE_FUSE_ON, MOE_F_W13_PACKED and the
+ * column-slice gate/up give MOE_ERR_UNSUPPORTED.  The workspace is sized by
  * moe_w4a8_experts_workspace_size (0 if the arguments are rejected); the
  * intermediate rows sit where moe_fp8_experts_workspace_layout says. */
 size_t moe_w4a8_experts_workspace_size(int64_t M, int64_t K, int64_t I, int32_t E,
