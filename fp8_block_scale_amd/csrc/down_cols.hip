@@ -9,14 +9,15 @@
 //   out[t, c] = bf16(out[t, c] + sum_j topk_weights[r] * y[r, c])
 // with the route terms added in route order in FP32 and one BF16 rounding.
 //
-// Work split.  One workgroup (four waves) owns 32 output columns.  It first
+// Work split.  One workgroup (eight waves, or four where the LDS is needed
+// for many routes' rows) owns 32 output columns.  It first
 // puts every valid route's intermediate row and row scales into LDS, indexed
 // by route: copied from the FP8 rows of the gate/up stage (each route's plan
 // row from that stage's route map), or -- after the column-slice gate/up,
 // which leaves FP32 SwiGLU rows -- requantised from those (each route's plan
 // row from a scan of the plan); then it
 // walks every plan block below num_tokens_post_padded: wave w takes the
-// blocks of parity w / 2 and the 16 columns of half w % 2.  Per block a wave
+// blocks b = w / 2 (mod NW / 2) and the 16 columns of half w % 2.  Per block a wave
 // multiplies the block's W2 slab (its expert's 16 rows of W2 for those
 // columns, all of I) with the block's routes' rows and keeps each valid
 // route's results in LDS (a route lies in one block: nothing to reduce).
@@ -24,10 +25,11 @@
 // itself at the end: no per-route buffer in HBM and no route-sum launch.
 // Each W2 slab is read by exactly one wave.
 //
-// Pipeline.  A ring of kStages per wave, each stage one block's W2 slab
+// Pipeline.  A ring of NS stages per wave (three with eight waves, five
+// with four), each stage one block's W2 slab
 // (16-byte chunks XOR-swizzled by row, so the MFMA operand reads hit distinct
 // banks) and its route ids, expert id and W2 block scales, by direct
-// global->LDS loads kStages - 1 blocks ahead, so a block's multiply waits on
+// global->LDS loads NS - 1 blocks ahead, so a block's multiply waits on
 // nothing but its stage.  The rings are private to their waves: between the
 // copy of the intermediate rows and the route sum there is no barrier, the
 // waits are each wave's own load counts.  FP8 MFMA
@@ -49,11 +51,12 @@ namespace moe {
 namespace {
 
 constexpr int kCW = 16;                 // output columns per wave
-constexpr int kWaves = 4;
+constexpr int kWavesMin = 4;            // waves per workgroup: 4 (5-stage rings) or 8 (3-stage)
 constexpr int kWGCols = 2 * kCW;        // output columns per workgroup
 constexpr int kIB = 256;                // bytes of an intermediate / W2 row (I)
 constexpr int kNJB = kIB / 128;
-constexpr int kStages = 5;
+constexpr int kStagesMin = 5;
+constexpr int kStagesMax = 5;
 constexpr int64_t kMaxRoutes = 192;                    // routes whose rows fit in LDS
 constexpr int kScan = 12;                              // plan entries per thread loaded up front
 
@@ -69,25 +72,25 @@ struct DCStage {
     static constexpr int Meta = Slab + Exp;
     static constexpr int Bytes = Meta + 128;
     static constexpr int PerStage = SlabInstr + (W4 ? 1 : 0) + 1;
-    static_assert((kStages - 2) * PerStage < 64, "vmcnt range");
+    static_assert((kStagesMax - 2) * PerStage < 64, "vmcnt range");
 };
 
-// LDS carve-up after the rings ([kWaves][kStages] stages): intermediate rows
+// LDS carve-up after the rings ([NW waves][NS] stages): intermediate rows
 // by route [R][kIB], their scales [R][kNJB], the results [R + 1][kWGCols]
 // (FP32; row R takes the rows that hold no route), each route's plan row
 // [R] (-1: masked).  At R = 192: 160832 bytes.
-template <bool W4>
+template <bool W4, int NW, int NS>
 struct DCLayout {
     int h, hs, y, rp, total;
     __host__ __device__ explicit DCLayout(int R) {
-        h = kWaves * kStages * DCStage<W4>::Bytes;
+        h = NW * NS * DCStage<W4>::Bytes;
         hs = h + R * kIB;
         y = hs + ((R * kNJB * 4 + 15) & ~15);            // 16-byte rows of results
         rp = y + (R + 1) * kWGCols * 4;
         total = rp + R * 4;
     }
 };
-static_assert(kWaves * kStages * DCStage<false>::Bytes + kMaxRoutes * (kIB + kNJB * 4 + kWGCols * 4 + 4) +
+static_assert(kWavesMin * kStagesMin * DCStage<false>::Bytes + kMaxRoutes * (kIB + kNJB * 4 + kWGCols * 4 + 4) +
                   kWGCols * 4 <= 160 * 1024, "LDS budget at the route limit");
 
 typedef const __attribute__((address_space(4))) int32_t *const_i32_p;
@@ -101,8 +104,32 @@ __device__ __forceinline__ void lds_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int BM, bool E8M0, bool RQ, bool W4>
-__global__ void __launch_bounds__(64 * kWaves, 1)
+// Wait until at most min(ahead, K) stages' loads are outstanding (ahead is
+// wave-uniform: the blocks issued past the one about to be multiplied).
+template <int PS, int K>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+    if constexpr (K == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= K) wait_vmcnt<K * PS>();
+        else wait_ahead<PS, K - 1>(ahead);
+    }
+}
+
+// step(stage S, block i + S) for S = S0 .. NS - 1 while i + S < nw, with the
+// stage index a compile-time constant
+template <int S, int NS, typename F>
+__device__ __forceinline__ void steps_from(F &step, int i, int nw) {
+    if constexpr (S < NS) {
+        if (i + S < nw) {
+            step(std::integral_constant<int, S>{}, i + S);
+            steps_from<S + 1, NS>(step, i, nw);
+        }
+    }
+}
+
+template <int BM, bool E8M0, bool RQ, bool W4, int NW, int NS>
+__global__ void __launch_bounds__(64 * NW, 1)
 down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
                  uint16_t *__restrict__ out) {
     static_assert(BM <= 16, "one 16-row MFMA tile per plan block");
@@ -110,7 +137,9 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
     using SC = DCStage<W4>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int R = (int)a.R;
-    const DCLayout<W4> L(R);
+    const DCLayout<W4, NW, NS> L(R);
+    constexpr int kWaves = NW;
+    constexpr int NP = NW / 2;                          // block parities (waves per column half)
     uint8_t *sH = smem + L.h;
     float *sHs = reinterpret_cast<float *>(smem + L.hs);
     float *sY = reinterpret_cast<float *>(smem + L.y);
@@ -129,12 +158,12 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
     int nb = ntp / BM;
     nb = nb < a.nblocks ? nb : a.nblocks;
 
-    uint8_t *ring = smem + w * kStages * SC::Bytes;
+    uint8_t *ring = smem + w * NS * SC::Bytes;
 
-    // ---- this wave's blocks: b = 2 i + parity, i < nw
-    const int nw = (nb - parity + 1) / 2;
+    // ---- this wave's blocks: b = NP i + parity, i < nw
+    const int nw = (nb - parity + NP - 1) / NP;
     auto issue = [&](int st, int i) {
-        const int b = 2 * i + parity;
+        const int b = NP * i + parity;
         uint8_t *base = ring + st * SC::Bytes;
         const int e0 = __builtin_amdgcn_readfirstlane(((const_i32_p)a.eids)[b]);
         const int e = (e0 >= 0 && e0 < a.E) ? e0 : 0;
@@ -318,34 +347,19 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
         __syncthreads();
     }
 
-    // this wave's blocks i, slots i % kStages; kStages - 1 blocks in flight
-    // ahead of the one being multiplied (loads complete in issue order)
-    for (int q = 0; q < kStages - 1; ++q)
+    // this wave's blocks i, slots i % NS; NS - 1 blocks in flight ahead of
+    // the one being multiplied (loads complete in issue order)
+    for (int q = 0; q < NS - 1; ++q)
         if (q < nw) issue(q, q);
     auto step = [&](auto st_c, int i) {
         constexpr int ST = decltype(st_c)::value;
-        const int ahead = nw - 1 - i;                   // blocks issued past i, at most kStages - 2
-        if (ahead >= 3)
-            wait_vmcnt<3 * SC::PerStage>();
-        else if (ahead == 2)
-            wait_vmcnt<2 * SC::PerStage>();
-        else if (ahead == 1)
-            wait_vmcnt<SC::PerStage>();
-        else
-            wait_vmcnt<0>();
+        wait_ahead<SC::PerStage, NS - 2>(nw - 1 - i);  // blocks issued past i: at most NS - 2
         // the refill goes into the slot of block i - 1, whose operand reads
         // the previous step has consumed
-        if (i + kStages - 1 < nw) issue((ST + kStages - 1) % kStages, i + kStages - 1);
+        if (i + NS - 1 < nw) issue((ST + NS - 1) % NS, i + NS - 1);
         compute(ST);
     };
-    static_assert(kStages == 5, "the waits cover up to three stages ahead");
-    for (int i = 0; i < nw; i += kStages) {
-        step(std::integral_constant<int, 0>{}, i);
-        if (i + 1 < nw) step(std::integral_constant<int, 1>{}, i + 1);
-        if (i + 2 < nw) step(std::integral_constant<int, 2>{}, i + 2);
-        if (i + 3 < nw) step(std::integral_constant<int, 3>{}, i + 3);
-        if (i + 4 < nw) step(std::integral_constant<int, 4>{}, i + 4);
-    }
+    for (int i = 0; i < nw; i += NS) steps_from<0, NS>(step, i, nw);
     wait_vmcnt<0>();
     __syncthreads();                                    // every wave's results are in LDS
 
@@ -364,17 +378,29 @@ down_cols_kernel(DownArgs a, const int32_t *__restrict__ rpos, ColsRequant rq,
     }
 }
 
+template <int BM, bool E8M0, bool RQ, bool W4, int NW, int NS>
+hipError_t launch_dc_cfg(const DownArgs &a, const int32_t *rpos, const ColsRequant &rq, uint16_t *out,
+                         hipStream_t st) {
+    const int64_t grid = a.K / kWGCols;
+    const int smem = DCLayout<W4, NW, NS>((int)a.R).total;
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e =
+        raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0, RQ, W4, NW, NS>, 160 * 1024);
+    if (e != hipSuccess) return e;
+    down_cols_kernel<BM, E8M0, RQ, W4, NW, NS><<<(unsigned)grid, 64 * NW, smem, st>>>(a, rpos, rq, out);
+    return hipGetLastError();
+}
+
+// Eight waves (two per SIMD, so one wave's LDS reads and MFMAs overlap the
+// other's) with three-stage rings wherever the LDS holds them next to the
+// routes' rows; else four waves with five-stage rings.
 template <int BM, bool E8M0, bool RQ, bool W4>
 hipError_t launch_dc(const DownArgs &a, const int32_t *rpos, const ColsRequant &rq, uint16_t *out,
                      hipStream_t st) {
-    const int64_t grid = a.K / kWGCols;
-    if (grid == 0 || a.nblocks == 0) return hipSuccess;
-    const int smem = DCLayout<W4>((int)a.R).total;
-    static std::atomic<uint64_t> lds_set{0};
-    const hipError_t e = raise_lds_limit(lds_set, (const void *)down_cols_kernel<BM, E8M0, RQ, W4>, 160 * 1024);
-    if (e != hipSuccess) return e;
-    down_cols_kernel<BM, E8M0, RQ, W4><<<(unsigned)grid, 64 * kWaves, smem, st>>>(a, rpos, rq, out);
-    return hipGetLastError();
+    if (a.K / kWGCols == 0 || a.nblocks == 0) return hipSuccess;
+    if (DCLayout<W4, 8, 3>((int)a.R).total <= 160 * 1024)
+        return launch_dc_cfg<BM, E8M0, RQ, W4, 8, 3>(a, rpos, rq, out, st);
+    return launch_dc_cfg<BM, E8M0, RQ, W4, kWavesMin, kStagesMin>(a, rpos, rq, out, st);
 }
 
 template <int BM>
