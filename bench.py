@@ -312,6 +312,14 @@ def main():
 
     experts_fn = moe.moe_w4a8_experts if args.w4a8 else moe.moe_fp8_experts
 
+    def stage_layer(stream, k):
+        # all five steps in one call (moe_fp8_layer): the per-block gate/up's
+        # clearing launch folds into the plan's at decode sizes
+        w13, w13_s, w2, w2_s = wsets[k % nsets]
+        moe.moe_fp8_layer(case.x, case.topk_ids, case.topk_weights, w13, w13_s, w2, w2_s,
+                          case.block_m, b.sorted_ids, b.expert_ids, b.ntp, b.x_q, b.x_s, out,
+                          b.workspace, flags, act_mode, b.plan_ws, stream)
+
     def stage_experts(stream, k):
         w13, w13_s, w2, w2_s = wsets[k % nsets]
         experts_fn(b.x_q, b.x_s, w13, w13_s, w2, w2_s, case.topk_weights, b.sorted_ids,
@@ -387,7 +395,8 @@ def main():
             torch.cuda.synchronize()
             return t_start.elapsed_time(t_end) / args.steps
 
-        ms = replay_ms(capture(stages))
+        one_call = not (args.router or args.w4a8 or args.separate_plan_quant)
+        ms = replay_ms(capture([stage_layer] if one_call else stages))
         plan_quant, experts = (replay_ms(capture([fn])) for fn in stages)
         if not fused and not args.w4a8:   # the two stages of steps 3-5, each timed alone
             gate_up, down = (replay_ms(capture([fn])) for fn in (stage_gate_up, stage_down))
@@ -480,6 +489,9 @@ def main():
         "weights": "e2m1 + K32 exponent bytes" if args.w4a8 else "e4m3 + 128x128 fp32 scales",
         "router": bool(args.router),
         "launch": "eager" if args.eager else "hip graph (K steps per replay)",
+        "step_call": ("moe_fp8_layer" if (not args.eager and not (args.router or args.w4a8
+                                                                   or args.separate_plan_quant))
+                      else "plan call + experts call"),
         "weight_sets": nsets,
         "layer_GBs": round(nb["layer"] / (ms * 1e-3) / 1e9, 1),
         "roofline": roof,

@@ -44,7 +44,7 @@ EXPORTED = ("moe_plan_capacity", "moe_plan_workspace_size", "moe_plan", "moe_qua
             "moe_last_hip_error", "moe_last_error", "moe_debug_e4m3_encode",
             "moe_debug_count_non_pow2", "moe_fp8_experts_noalloc", "moe_route_plan",
             "moe_w4a8_experts_workspace_size", "moe_w4a8_experts", "moe_prepack_w13_size",
-            "moe_prepack_w13")
+            "moe_prepack_w13", "moe_fp8_layer")
 
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -92,6 +92,9 @@ _c = {
     "moe_fp8_experts": _proto("moe_fp8_experts", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _u32, _vp, _vp, _sz,
                               _vp),
+    "moe_fp8_layer": _proto("moe_fp8_layer", _i32, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
+                            _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _i64, _vp,
+                            _vp, _vp, _vp, _sz, _u32, _vp, _vp, _sz, _vp),
     "moe_fp8_gate_up": _proto("moe_fp8_gate_up", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                               _i64, _i32, _i32, _i32, _i64, _u32, _vp, _sz, _vp),
     "moe_fp8_down_reduce": _proto("moe_fp8_down_reduce", _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
@@ -264,6 +267,28 @@ def moe_fp8_experts_schedule(M, K, I, E, top_k, block_m, sorted_cap, flags=0):
     return int(info[0]), int(info[1]), int(info[2]), int(info[3]), bool(info[4])
 
 
+def moe_fp8_layer(x_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s, block_m, sorted_token_ids,
+                  expert_ids, num_tokens_post_padded, x_q, x_s, out_bf16, workspace, flags=0,
+                  scale_mode=MOE_SCALE_FP32, plan_workspace=None, stream=None):
+    """All five steps (moe_plan_quant then moe_fp8_experts) in one call, with
+    one launch fewer at decode sizes; same outputs."""
+    pa = _plan_args(topk_ids, w13.shape[0], block_m, sorted_token_ids, expert_ids,
+                    num_tokens_post_padded, plan_workspace)
+    ids_ptr, dt, M, top_k, E, _, s_ptr, s_cap, e_ptr, e_cap, n_ptr, pw_ptr, pw_bytes = pa
+    Mx, K, ld = _quant_args(x_bf16, x_q, x_s)
+    assert Mx == M, "x_bf16 and topk_ids disagree on M"
+    I = w13.shape[1] // 2
+    for t in (w13, w13_s, w2, w2_s, topk_weights, out_bf16, workspace):
+        assert t.is_contiguous()
+    assert out_bf16.dtype == torch.bfloat16 and topk_weights.dtype == torch.float32
+    _check(_c["moe_fp8_layer"](_ptr(x_bf16), ld, scale_mode, ids_ptr, dt, _ptr(topk_weights),
+                               _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s), M, K, I, E, top_k,
+                               block_m, s_ptr, s_cap, e_ptr, e_cap, n_ptr, _ptr(x_q), _ptr(x_s),
+                               pw_ptr, pw_bytes, flags, _ptr(out_bf16), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_fp8_layer")
+
+
 def moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
                     num_tokens_post_padded, top_k, block_m, out_bf16, workspace, flags=0,
                     stream=None):
@@ -434,9 +459,8 @@ class MoeLayerBuffers:
 
 def moe_layer(bufs, x_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s, out_bf16,
               act_scale_mode=MOE_SCALE_FP32, stream=None):
-    """All five steps on one stream: plan with activation quantisation, experts."""
-    moe_plan_quant(topk_ids, bufs.E, bufs.block_m, bufs.sorted_ids, bufs.expert_ids, bufs.ntp,
-                   x_bf16, bufs.x_q, bufs.x_s, act_scale_mode, bufs.plan_ws, stream)
-    moe_fp8_experts(bufs.x_q, bufs.x_s, w13, w13_s, w2, w2_s, topk_weights, bufs.sorted_ids,
-                    bufs.expert_ids, bufs.ntp, bufs.top_k, bufs.block_m, out_bf16,
-                    bufs.workspace, bufs.flags, stream)
+    """All five steps on one stream (moe_fp8_layer: plan with activation
+    quantisation, experts)."""
+    moe_fp8_layer(x_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s, bufs.block_m,
+                  bufs.sorted_ids, bufs.expert_ids, bufs.ntp, bufs.x_q, bufs.x_s, out_bf16,
+                  bufs.workspace, bufs.flags, act_scale_mode, bufs.plan_ws, stream)

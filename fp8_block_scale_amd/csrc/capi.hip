@@ -10,6 +10,7 @@
 
 #include "../../include/moe_fp8.h"
 #include "internal.h"
+#include "layer.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
@@ -615,12 +616,16 @@ moe::DownArgs down_args(const uint8_t *w2, const float *w2_s, const float *topk_
 
 }  // namespace
 
-MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
-                                   const float *w13_s, const int32_t *sorted_token_ids,
-                                   const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
-                                   int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
-                                   int32_t block_m, int64_t sorted_cap, uint32_t flags,
-                                   void *workspace, size_t workspace_bytes, void *stream) {
+namespace {
+
+// prep_done: the route map and the split-K counters were cleared by the
+// plan's launch (moe_fp8_layer)
+moe_status gate_up_stage(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                         const float *w13_s, const int32_t *sorted_token_ids,
+                         const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
+                         int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                         int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                         void *workspace, size_t workspace_bytes, void *stream, bool prep_done) {
     WsLayout l;
     moe_status st = check_stage(M, K, I, E, top_k, block_m, sorted_cap, flags, workspace,
                                 workspace_bytes, &l);
@@ -639,7 +644,7 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
     }
     // the route map and the split-K counters are cleared by the row-tile
     // launch when a persistent kernel runs, else by a launch of their own
-    if (!l.sp.gu_persistent && !l.sp.dn_persistent) {
+    if (!l.sp.gu_persistent && !l.sp.dn_persistent && !prep_done) {
         st = hip_check(moe::launch_prep((uint32_t *)(ws + l.rpos), (size_t)M * top_k,
                                         (uint32_t *)(ws + l.cnt), l.cnt_words, s),
                        "moe_fp8_gate_up: clear route map and counters");
@@ -657,6 +662,19 @@ MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const u
         if (st != MOE_OK) return st;
     }
     return hip_check(moe::launch_gateup(ga, block_m, fp8, e8, s), "moe_fp8_gate_up: launch");
+}
+
+}  // namespace
+
+MOE_API moe_status moe_fp8_gate_up(const uint8_t *x_q, const float *x_s, const uint8_t *w13,
+                                   const float *w13_s, const int32_t *sorted_token_ids,
+                                   const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
+                                   int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                                   int32_t block_m, int64_t sorted_cap, uint32_t flags,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    return gate_up_stage(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                         M, K, I, E, top_k, block_m, sorted_cap, flags, workspace, workspace_bytes,
+                         stream, false);
 }
 
 MOE_API moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
@@ -755,6 +773,72 @@ MOE_API moe_status moe_fp8_experts(const uint8_t *x_q, const float *x_s, const u
     return moe_fp8_down_reduce(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
                                num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap,
                                flags, out_bf16, workspace, workspace_bytes, stream);
+}
+
+MOE_API moe_status moe_fp8_layer(const void *x_bf16, int64_t ld_x, int32_t scale_mode,
+                                 const void *topk_ids, int32_t ids_dtype, const float *topk_weights,
+                                 const uint8_t *w13, const float *w13_s, const uint8_t *w2,
+                                 const float *w2_s, int64_t M, int64_t K, int64_t I, int32_t E,
+                                 int32_t top_k, int32_t block_m, int32_t *sorted_token_ids,
+                                 int64_t sorted_cap, int32_t *expert_ids, int64_t blocks_cap,
+                                 int32_t *num_tokens_post_padded, uint8_t *x_q, float *x_s,
+                                 void *plan_workspace, size_t plan_workspace_bytes, uint32_t flags,
+                                 void *out_bf16, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    // validate both halves before enqueuing anything
+    int groups = 0;
+    moe_status st = check_plan(topk_ids, ids_dtype, M, top_k, E, block_m, sorted_token_ids, sorted_cap,
+                               expert_ids, blocks_cap, num_tokens_post_padded, plan_workspace,
+                               plan_workspace_bytes, &groups);
+    if (st != MOE_OK) return st;
+    st = check_quant(x_bf16, M, K, ld_x, x_q, x_s, scale_mode);
+    if (st != MOE_OK) return st;
+    WsLayout l;
+    st = check_stage(M, K, I, E, top_k, block_m, sorted_cap, flags, workspace, workspace_bytes, &l);
+    if (st != MOE_OK) return st;
+    if (M > 0 && sorted_cap > 0) {
+        if (!w13 || !w13_s || !w2 || !w2_s || !topk_weights || !out_bf16)
+            return fail(MOE_ERR_NULL, "all tensor arguments and the workspace are required");
+        if (!aligned16(x_q) || !aligned16(w13) || !aligned16(w2) || !aligned16(out_bf16))
+            return fail(MOE_ERR_ALIGN, "x_q, w13, w2 and out must be 16-byte aligned");
+    }
+    // the clearing launch of the per-block gate/up folds into the plan's
+    // one-workgroup launch; every other schedule runs the two calls as they are
+    const bool fold = M > 0 && sorted_cap > 0 && groups == 0 && !l.sp.fused && !l.sp.gu_persistent &&
+                      !l.sp.dn_persistent && !l.sp.gu_cols;
+    if (!fold) {
+        st = moe_plan_quant(topk_ids, ids_dtype, M, top_k, E, block_m, sorted_token_ids, sorted_cap,
+                            expert_ids, blocks_cap, num_tokens_post_padded, plan_workspace,
+                            plan_workspace_bytes, x_bf16, K, ld_x, x_q, x_s, scale_mode, stream);
+        if (st != MOE_OK) return st;
+        return moe_fp8_experts(x_q, x_s, w13, w13_s, w2, w2_s, topk_weights, sorted_token_ids,
+                               expert_ids, num_tokens_post_padded, M, K, I, E, top_k, block_m,
+                               sorted_cap, flags, out_bf16, workspace, workspace_bytes, stream);
+    }
+    uint8_t *ws = (uint8_t *)workspace;
+    moe::QuantJob q;
+    q.x = (const uint16_t *)x_bf16;
+    q.M = M;
+    q.K = K;
+    q.ld = ld_x;
+    q.xq = x_q;
+    q.xs = x_s;
+    moe::ClearJob c;
+    c.rpos = (uint32_t *)(ws + l.rpos);
+    c.nr = (size_t)M * top_k;
+    c.cnt = (uint32_t *)(ws + l.cnt);
+    c.nc = l.cnt_words;
+    st = hip_check(moe::launch_plan_quant_clear(topk_ids, ids_dtype == MOE_IDS_I64, M * top_k, E, block_m,
+                                                sorted_token_ids, expert_ids, num_tokens_post_padded, q,
+                                                scale_mode == MOE_SCALE_UE8M0, c, (hipStream_t)stream),
+                   "moe_fp8_layer: plan launch");
+    if (st != MOE_OK) return st;
+    st = gate_up_stage(x_q, x_s, w13, w13_s, sorted_token_ids, expert_ids, num_tokens_post_padded, M, K,
+                       I, E, top_k, block_m, sorted_cap, flags, workspace, workspace_bytes, stream, true);
+    if (st != MOE_OK) return st;
+    return moe_fp8_down_reduce(w2, w2_s, topk_weights, sorted_token_ids, expert_ids,
+                               num_tokens_post_padded, M, K, I, E, top_k, block_m, sorted_cap, flags,
+                               out_bf16, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------------- weight prepack

@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "layer.h"
 
 namespace moe {
 
@@ -191,6 +192,48 @@ plan_quant_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwa
     quant_act_group<UE8M0>(q.x, q.M, q.K, q.ld, q.xq, q.xs,
                            ((int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x) >> 4,
                            threadIdx.x & 15);
+}
+
+// plan_quant_kernel plus the clearing of a ClearJob by the workgroups past
+// the quantisation's: workgroup 0 plans, 1 .. qwg quantise, the rest clear.
+template <typename IdT, bool UE8M0>
+__global__ void __launch_bounds__(kPlanThreads)
+plan_quant_clear_kernel(const IdT *__restrict__ ids, int64_t R, int E, int bm, int nwaves,
+                        int32_t *__restrict__ sorted, int32_t *__restrict__ expert_ids,
+                        int32_t *__restrict__ ntp, QuantJob q, int64_t qwg, ClearJob c) {
+    extern __shared__ int smem[];
+    if (blockIdx.x == 0) {
+        plan_body(ids, R, E, bm, nwaves, sorted, expert_ids, ntp, smem);
+        return;
+    }
+    if ((int64_t)blockIdx.x <= qwg) {
+        quant_act_group<UE8M0>(q.x, q.M, q.K, q.ld, q.xq, q.xs,
+                               ((int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x) >> 4,
+                               threadIdx.x & 15);
+        return;
+    }
+    const size_t stride = (size_t)(gridDim.x - 1 - qwg) * kPlanThreads;
+    for (size_t i = (size_t)(blockIdx.x - 1 - qwg) * kPlanThreads + threadIdx.x; i < c.nr + c.nc;
+         i += stride) {
+        if (i < c.nr) c.rpos[i] = 0xffffffffu;
+        else c.cnt[i - c.nr] = 0u;
+    }
+}
+
+template <typename IdT, bool UE8M0>
+hipError_t launch_pqc_t(const IdT *ids, int64_t R, int E, int bm, int32_t *sorted,
+                        int32_t *expert_ids, int32_t *ntp, const QuantJob &q, const ClearJob &c,
+                        hipStream_t st) {
+    const int64_t qgroups = q.M * (q.K >> 7);
+    const int nwaves = E <= 512 ? 16 : 8;
+    const size_t lds = ((size_t)nwaves * E + E + 32) * sizeof(int);
+    const int64_t qwg = (qgroups + kPlanThreads / 16 - 1) / (kPlanThreads / 16);
+    const size_t n = c.nr + c.nc;
+    int64_t cwg = (int64_t)((n + kPlanThreads - 1) / kPlanThreads);
+    cwg = cwg > 64 ? 64 : cwg;
+    plan_quant_clear_kernel<IdT, UE8M0><<<(unsigned)(1 + qwg + cwg), kPlanThreads, lds, st>>>(
+        ids, R, E, bm, nwaves, sorted, expert_ids, ntp, q, qwg, c);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -766,6 +809,16 @@ hipError_t launch_route_plan(const float *logits, int64_t M, int E_routed, int t
         case 8: return route_plan_npl<8>(j, block_m, sorted, expert_ids, ntp, ws, groups, q, ue8m0, st);
         default: return route_plan_npl<16>(j, block_m, sorted, expert_ids, ntp, ws, groups, q, ue8m0, st);
     }
+}
+
+hipError_t launch_plan_quant_clear(const void *ids, bool ids_i64, int64_t R, int E, int block_m,
+                                   int32_t *sorted, int32_t *expert_ids, int32_t *ntp,
+                                   const QuantJob &q, bool ue8m0, const ClearJob &c, hipStream_t st) {
+    if (ids_i64)
+        return ue8m0 ? launch_pqc_t<int64_t, true>((const int64_t *)ids, R, E, block_m, sorted, expert_ids, ntp, q, c, st)
+                     : launch_pqc_t<int64_t, false>((const int64_t *)ids, R, E, block_m, sorted, expert_ids, ntp, q, c, st);
+    return ue8m0 ? launch_pqc_t<int32_t, true>((const int32_t *)ids, R, E, block_m, sorted, expert_ids, ntp, q, c, st)
+                 : launch_pqc_t<int32_t, false>((const int32_t *)ids, R, E, block_m, sorted, expert_ids, ntp, q, c, st);
 }
 
 }  // namespace moe

@@ -336,6 +336,27 @@ moe_status moe_fp8_down_reduce(const uint8_t *w2, const float *w2_s,
                                void *out_bf16, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* All five steps in one call: moe_plan_quant then moe_fp8_experts (arguments,
+ * constraints and errors those of the two calls, validated in full before
+ * anything is enqueued; outputs bit-identical to the two calls).  When the
+ * plan runs as one workgroup (no plan workspace, or fewer routes than the
+ * several-workgroup build takes) and the gate/up stage runs the per-block
+ * kernel, the route map and split-K counters that stage would clear in a
+ * launch of its own are cleared inside the plan's launch: one launch fewer
+ * per layer at decode sizes.  x_q / x_s receive the activation codes and
+ * scales, sorted_token_ids / expert_ids / num_tokens_post_padded the plan,
+ * as from moe_plan_quant. */
+moe_status moe_fp8_layer(const void *x_bf16, int64_t ld_x, int32_t scale_mode,
+                         const void *topk_ids, int32_t ids_dtype, const float *topk_weights,
+                         const uint8_t *w13, const float *w13_s,
+                         const uint8_t *w2, const float *w2_s,
+                         int64_t M, int64_t K, int64_t I, int32_t E, int32_t top_k,
+                         int32_t block_m, int32_t *sorted_token_ids, int64_t sorted_cap,
+                         int32_t *expert_ids, int64_t blocks_cap,
+                         int32_t *num_tokens_post_padded, uint8_t *x_q, float *x_s,
+                         void *plan_workspace, size_t plan_workspace_bytes, uint32_t flags,
+                         void *out_bf16, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------ weight prepack -- */
 
 /* Offline reordering of W13 into the order the gate/up kernels consume it,

@@ -832,3 +832,43 @@ def test_m_zero_is_a_no_op():
     moe.moe_layer(b, x, ids, w, cs.w13, cs.w13_s, cs.w2, cs.w2_s, out)
     torch.cuda.synchronize()
     assert int(b.ntp.item()) == 0
+
+
+# ------------------------------------------------------- all five steps, one call
+
+@pytest.mark.parametrize("name,M,flags", [("decode", 1, 0), ("decode", 4, 0), ("decode", 16, 0),
+                                          ("tiny", None, 0), ("page1", 512, 0),
+                                          ("decode", 2, moe.MOE_F_INTER_UE8M0)])
+def test_layer_call_matches_two_calls(name, M, flags):
+    """moe_fp8_layer against moe_plan_quant then moe_fp8_experts on the same
+    inputs, workspaces filled with garbage: plan, activation codes, output and
+    intermediate codes bit for bit -- at decode sizes the clearing launch is
+    folded into the plan's, elsewhere the two calls run as they are."""
+    cs = case_of(name, M=M)
+    log(f"[layer] {name} M={cs.M} flags={flags:#x}")
+    outs = []
+    for one_call in (False, True):
+        b = moe.MoeLayerBuffers(cs.M, cs.K, cs.I, cs.E, cs.top_k, cs.block_m, flags, DEV)
+        b.workspace.fill_(0x5A)
+        b.sorted_ids.fill_(0x7F7F7F7F)
+        b.expert_ids.fill_(0x7F7F7F7F)
+        out = torch.zeros((cs.M, cs.K), dtype=torch.bfloat16, device=DEV)
+        if one_call:
+            moe.moe_fp8_layer(cs.x, cs.topk_ids, cs.topk_weights, cs.w13, cs.w13_s, cs.w2, cs.w2_s,
+                              cs.block_m, b.sorted_ids, b.expert_ids, b.ntp, b.x_q, b.x_s, out,
+                              b.workspace, flags, SCALE_FP32, b.plan_ws)
+        else:
+            moe.moe_plan_quant(cs.topk_ids, cs.E, cs.block_m, b.sorted_ids, b.expert_ids, b.ntp,
+                               cs.x, b.x_q, b.x_s, SCALE_FP32, b.plan_ws)
+            moe.moe_fp8_experts(b.x_q, b.x_s, cs.w13, cs.w13_s, cs.w2, cs.w2_s, cs.topk_weights,
+                                b.sorted_ids, b.expert_ids, b.ntp, cs.top_k, cs.block_m, out,
+                                b.workspace, flags)
+        torch.cuda.synchronize()
+        hq, hs = b.intermediate()
+        P = int(b.ntp.item())
+        outs.append((P, b.sorted_ids.clone(), b.expert_ids.clone(), b.x_q.clone(), b.x_s.clone(),
+                     out, hq[:P].clone(), hs[:P].clone()))
+    (P0, *a), (P1, *c) = outs
+    assert P0 == P1
+    for u, v, what in zip(a, c, ("sorted", "expert_ids", "x_q", "x_s", "out", "h_q", "h_s")):
+        assert torch.equal(u, v), f"{what} differs between the one call and the two"

@@ -247,6 +247,29 @@ def test_plan_quant_validation():
     assert _err(call(p=None)) == "MOE_ERR_NULL"
 
 
+def test_layer_validation():
+    """moe_fp8_layer validates the plan, the quantisation and the experts
+    arguments before launching anything (these calls run without a GPU)."""
+    f = _raw("moe_fp8_layer")
+    base = dict(x=FAKE, ld=256, mode=0, ids=FAKE, dt=0, w=FAKE, M=4, K=256, I=256, E=8, k=2, bm=16,
+                s=FAKE, sc=128, e=FAKE, bc=8, p=FAKE, ws=FAKE, wsb=1 << 30, fl=0, out=FAKE)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["x"], a["ld"], a["mode"], a["ids"], a["dt"], a["w"], FAKE, FAKE, FAKE, FAKE,
+                 a["M"], a["K"], a["I"], a["E"], a["k"], a["bm"], a["s"], a["sc"], a["e"], a["bc"],
+                 a["p"], FAKE, FAKE, None, 0, a["fl"], a["out"], a["ws"], a["wsb"], None)
+
+    assert _err(call(sc=127)) == "MOE_ERR_CAPACITY"             # plan
+    assert _err(call(mode=5)) == "MOE_ERR_SHAPE"                # quantisation
+    assert _err(call(x=None)) == "MOE_ERR_NULL"
+    assert _err(call(wsb=16)) == "MOE_ERR_CAPACITY"             # experts workspace
+    assert _err(call(w=None)) == "MOE_ERR_NULL"
+    assert _err(call(out=None)) == "MOE_ERR_NULL"
+    assert _err(call(I=200)) == "MOE_ERR_SHAPE"
+    assert _err(call(fl=1 << 24)) == "MOE_ERR_SHAPE"
+
+
 def test_noalloc_validation_before_any_device_call():
     """moe_fp8_experts_noalloc validates like moe_fp8_experts and rejects
     sizes whose workspace exceeds the static scratch, all before touching the
