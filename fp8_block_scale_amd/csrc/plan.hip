@@ -32,6 +32,15 @@ namespace {
 constexpr int kPlanThreads = 1024;
 constexpr int64_t kPlanMultiMin = 4096;      // routes from which several workgroups pay off
 
+// Waves of the one-workgroup plan that count routes: one per 64 routes, at
+// most 16 (8 for E > 512, whose per-wave histogram rows take more LDS);
+// fewer rows mean less LDS to clear and to add up per expert.
+inline int plan_waves(int64_t R, int E) {
+    const int cap = E <= 512 ? 16 : 8;
+    const int64_t w = (R + 63) / 64;
+    return w < 1 ? 1 : (w > cap ? cap : (int)w);
+}
+
 __device__ __forceinline__ uint64_t match_mask(int key, int nbits) {
     uint64_t m = ~0ull;
     for (int b = 0; b < nbits; ++b) {
@@ -225,7 +234,7 @@ hipError_t launch_pqc_t(const IdT *ids, int64_t R, int E, int bm, int32_t *sorte
                         int32_t *expert_ids, int32_t *ntp, const QuantJob &q, const ClearJob &c,
                         hipStream_t st) {
     const int64_t qgroups = q.M * (q.K >> 7);
-    const int nwaves = E <= 512 ? 16 : 8;
+    const int nwaves = plan_waves(R, E);
     const size_t lds = ((size_t)nwaves * E + E + 32) * sizeof(int);
     const int64_t qwg = (qgroups + kPlanThreads / 16 - 1) / (kPlanThreads / 16);
     const size_t n = c.nr + c.nc;
@@ -664,7 +673,7 @@ hipError_t launch_plan_quant_t(const IdT *ids, int64_t R, int E, int bm, int32_t
         plan_scatter_kernel<IdT><<<G, kMT, lds, st>>>(ids, R, E, chunk, ws, sorted);
         return hipGetLastError();
     }
-    const int nwaves = E <= 512 ? 16 : 8;
+    const int nwaves = plan_waves(R, E);
     const size_t lds = ((size_t)nwaves * E + E + 32) * sizeof(int);
     const int64_t qwg = (qgroups + kPlanThreads / 16 - 1) / (kPlanThreads / 16);
     plan_quant_kernel<IdT, UE8M0><<<(unsigned)(1 + qwg), kPlanThreads, lds, st>>>(ids, R, E, bm, nwaves, sorted,
@@ -700,7 +709,7 @@ hipError_t launch_route_plan_t(const RouteJob &j, int bm, int32_t *sorted, int32
                                                                                    sorted);
         return hipGetLastError();
     }
-    const int nwaves = E <= 512 ? 16 : 8;
+    const int nwaves = plan_waves(R, E);
     const size_t lds = ((size_t)nwaves * E + E + 32 + (size_t)R) * sizeof(int);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int64_t qwg = (qgroups + kPlanThreads / 16 - 1) / (kPlanThreads / 16);
@@ -754,7 +763,7 @@ hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int bloc
                                  expert_ids, ntp, st);
     }
     const int T = kPlanThreads;
-    const int nwaves = E <= 512 ? 16 : 8;
+    const int nwaves = plan_waves(R, E);
     size_t lds = ((size_t)nwaves * E + E + 32) * sizeof(int);
     if (ids_i64)
         plan_kernel<int64_t><<<1, T, lds, st>>>((const int64_t *)ids, R, E, block_m, nwaves,
@@ -770,7 +779,7 @@ hipError_t launch_plan(const void *ids, bool ids_i64, int64_t R, int E, int bloc
 namespace moe {
 
 size_t route_plan_single_lds(int64_t R, int E) {
-    const int nwaves = E <= 512 ? 16 : 8;
+    const int nwaves = plan_waves(R, E);
     return ((size_t)nwaves * E + E + 32 + (size_t)R) * sizeof(int);
 }
 
